@@ -1,0 +1,90 @@
+"""CSA and HCA core attention with the sliding-window branch, float64
+(test infrastructure only).
+
+Source: hyper.ai page for arXiv 2606.19348 ("DeepSeek-V4"), section 方法
+(Method). CSA paragraph: core attention is MQA with shared keys and values
+over the top-k compressed entries. HCA paragraph: dense attention over all
+heavily compressed entries; both mechanisms include a supplementary
+sliding-window attention branch that keeps causality and models local
+dependencies.
+
+Readings of what the pages leave open:
+
+* Shared keys and values: K = V = the stored entry (all D dims, RoPE dims
+  included), shared by all query heads; each head's output has D dims.
+* Scale: logits are scale * <q_h, e>, scale = 1/sqrt(D) by default.
+* The window branch covers raw positions max(0, t-W+1) .. t of the query's
+  sequence. Recent tokens can appear both raw and inside compressed
+  entries; nothing is de-duplicated.
+* The two branches are combined by log-sum-exp, i.e. one joint softmax over
+  the union of compressed entries and window tokens.
+* HCA entry j is visible at t iff (j + 1) * m' - 1 <= t.
+* An empty entry set gives o = 0 and lse = -inf.
+* lse is the natural log of the softmax denominator of the scaled logits.
+"""
+
+import numpy as np
+
+
+def attend(q, E, scale):
+    """Softmax attention of heads q [h, D] over entries E [n, D] with K = V = E.
+
+    Returns (o [h, D], lse [h]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
+    h, D = q.shape
+    if E.shape[0] == 0:
+        return np.zeros((h, D)), np.full(h, -np.inf)
+    logits = scale * (q @ E.T)                   # [h, n]
+    mx = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - mx)
+    den = p.sum(axis=1, keepdims=True)
+    o = (p @ E) / den
+    return o, mx[:, 0] + np.log(den[:, 0])
+
+
+def window_positions(t, W):
+    """Raw positions of the sliding-window branch of a query at position t."""
+    return np.arange(max(0, t - W + 1), t + 1)
+
+
+def merge(o1, lse1, o2, lse2):
+    """Log-sum-exp merge of two partial attentions over disjoint entry sets."""
+    lse = np.logaddexp(lse1, lse2)
+    w1 = np.where(np.isneginf(lse1), 0.0, np.exp(lse1 - lse))
+    w2 = np.where(np.isneginf(lse2), 0.0, np.exp(lse2 - lse))
+    return w1[:, None] * o1 + w2[:, None] * o2, lse
+
+
+def csa(q, t, entries, idx, raw, W, scale):
+    """CSA core attention of one query.
+
+    q [h, D]; t: absolute position; entries [n, D]: decoded compressed
+    entries of the sequence; idx: selected entry indices (-1 = padding);
+    raw: callable or array mapping raw positions -> decoded rows [., D]
+    (the window store); W: window length.
+    """
+    idx = np.asarray(idx)
+    sel = idx[idx >= 0]
+    assert len(np.unique(sel)) == len(sel), "duplicate selection"
+    win = _rows(raw, window_positions(t, W))
+    E = np.concatenate([np.asarray(entries, np.float64)[sel], win], axis=0)
+    return attend(q, E, scale)
+
+
+def hca(q, t, entries, m_prime, raw, W, scale):
+    """HCA core attention of one query over all visible heavily compressed
+    entries plus the window."""
+    n_vis = (t + 1) // m_prime
+    entries = np.asarray(entries, np.float64)
+    assert n_vis <= entries.shape[0], "visible entries missing from the store"
+    win = _rows(raw, window_positions(t, W))
+    E = np.concatenate([entries[:n_vis], win], axis=0)
+    return attend(q, E, scale)
+
+
+def _rows(raw, positions):
+    if callable(raw):
+        return np.asarray(raw(positions), np.float64).reshape(len(positions), -1)
+    return np.asarray(raw, np.float64)[positions]
