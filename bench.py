@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA + HCA hybrid-attention decode step at 1M-token context
+on one MI355X.
+
+A step is one pass of the hot path over a batch of 4 decode queries (one per
+sequence, position t = 2^20 - 1): lightning-indexer top-k (MXFP4 keys, k =
+1024) + CSA sparse MQA attention over the selected entries and the 128-token
+window (one layer) + HCA dense MQA attention over all 8192 entries and the
+window (another layer); 64 heads, D = 448 FP8 + 64 bf16. Inputs are seeded
+synthetic tensors already resident in HBM. Steps rotate over 16 independent
+input copies (about 55 MB of freshly read data each, the CSA store shared) so
+that the 256 MB Infinity Cache cannot serve a step from the previous ones.
+The steps are captured in one HIP graph and replayed.
+
+Prints one JSON line on stdout. Also measures compression of 2^20 raw bf16
+tokens (csa_compress + hca_compress) and the oracle on the host cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MXFP4_PEAK_TFLOPS = 10100.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--copies", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-compress", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(a decode batch shards by sequence with no communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from long_context_attention_hca_amd import workloads as W
+
+    dev = "cuda"
+    B, L, H, D, k, W_, m, mp, HI = 4, 1 << 20, 64, 512, 1024, 128, 4, 128, 4
+    n_c, n_h = L // m, L // mp
+    R = args.copies
+    K = max(R, (args.steps + R - 1) // R * R)
+    Wm = max(R, (args.warmup + R - 1) // R * R)
+
+    log(f"generating {R} input copies (B={B}, L={L})")
+    base = synth.decode_1m(seed=1003, B=B, L=L, device=dev)
+    shared = {s: base.t[f"csa_{s}"] for s in ("nope", "scale", "rope")}
+    cases = [base] + [synth.decode_1m(seed=1003 + 7919 * i, B=B, L=L, device=dev, csa_store=shared)
+                      for i in range(1, R)]
+    ws = W.Workspace(dev)
+    runs = [W.Decode1M(c, ws=ws) for c in cases]
+    for r in runs:
+        r.step()
+    torch.cuda.synchronize()
+    eager = [(r.idx.clone(), r.o_csa.clone(), r.lse_csa.clone(), r.o_hca.clone(), r.lse_hca.clone()) for r in runs]
+
+    log("capturing the step graph")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in runs:
+            r.step()
+    # per-entry-point graphs (for the kernel breakdown)
+    parts = []
+    for r in runs:
+        gi, gc, gh = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gi):
+            r.index()
+        with torch.cuda.graph(gc):
+            r.csa_attention()
+        with torch.cuda.graph(gh):
+            r.hca_attention()
+        parts.append((gi, gc, gh))
+    torch.cuda.synchronize()
+
+    # graph replays must reproduce the eager results, replay after replay
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        for r, e in zip(runs, eager):
+            got = (r.idx, r.o_csa, r.lse_csa, r.o_hca, r.lse_hca)
+            assert all(torch.equal(x, y) for x, y in zip(got, e)), "graph replay differs from eager"
+
+    for _ in range(Wm // R):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    # a bounded spin kernel first keeps the GPU busy while the host enqueues the timed work, so
+    # host launch latency never shows up between the events
+    torch.cuda._sleep(50_000_000)
+    t0.record()
+    for _ in range(K // R):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+
+    # breakdown: events around each entry point's graph, rotating over the copies
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda._sleep(200_000_000)
+    for i in range(K):
+        gi, gc, gh = parts[i % R]
+        e = ev[i]
+        e[0].record()
+        gi.replay()
+        e[1].record()
+        gc.replay()
+        e[2].record()
+        gh.replay()
+        e[3].record()
+    torch.cuda.synchronize()
+    t_idx = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    t_csa = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    t_hca = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+
+    # algorithmic bytes / flops (what the method must move or compute)
+    entry = 448 + 4 + 64 * 2
+    by_idx = B * n_c * 34 + B * HI * 34 + B * HI * 4 + B * k * 4
+    by_csa = B * (k + W_) * entry + B * k * 4 + 2 * B * H * D * 2 + B * H * 4
+    by_hca = B * (n_h + W_) * entry + 2 * B * H * D * 2 + B * H * 4
+    fl_idx = B * n_c * HI * 64 * 2
+    fl_csa = B * (k + W_) * H * D * 4
+    fl_hca = B * (n_h + W_) * H * D * 4
+    step_bytes = by_idx + by_csa + by_hca
+    step_flops = fl_idx + fl_csa + fl_hca
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    tfs = step_flops / (ms_step * 1e-3) / 1e12
+    qtok_s = B / (ms_step * 1e-3)
+
+    comp = None
+    if not args.no_compress:
+        log("compression throughput")
+        del g, parts
+        cc = synth.compression(seed=1004, L=L, device=dev)
+        csa_st = W.empty_store(2, n_c, 448, 64, dev)
+        hca_st = W.empty_store(2, n_h, 448, 64, dev)
+        from long_context_attention_hca_amd import csa_compress, hca_compress
+        t = cc.t
+        for _ in range(3):
+            csa_compress(t["raw"], 0, t["logits_csa"], t["bias_csa"], m, 8, 0, n_c, csa_st)
+            hca_compress(t["raw"], 0, t["logits_hca"], t["bias_hca"], mp, 0, n_h, hca_st)
+        torch.cuda.synchronize()
+        n_rep = 10
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(n_rep):
+            csa_compress(t["raw"], 0, t["logits_csa"], t["bias_csa"], m, 8, 0, n_c, csa_st)
+        e[1].record()
+        for _ in range(n_rep):
+            hca_compress(t["raw"], 0, t["logits_hca"], t["bias_hca"], mp, 0, n_h, hca_st)
+        e[2].record()
+        torch.cuda.synchronize()
+        tc, th = e[0].elapsed_time(e[1]) / n_rep, e[1].elapsed_time(e[2]) / n_rep
+        row = D * 2
+        by_c = L * row * 2 + 8 * D * 4 + n_c * entry
+        by_h = L * row * 2 + mp * D * 4 + n_h * entry
+        comp = {"workload": "2^20 raw bf16 tokens, D=512, per-channel logits -> split FP8/bf16 entries",
+                "csa_compress_ms": round(tc, 4), "csa_tokens_per_s": round(L / (tc * 1e-3)),
+                "csa_gbs": round(by_c / (tc * 1e-3) / 1e9, 1),
+                "csa_frac_hbm": round(by_c / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                "hca_compress_ms": round(th, 4), "hca_tokens_per_s": round(L / (th * 1e-3)),
+                "hca_gbs": round(by_h / (th * 1e-3) / 1e9, 1),
+                "hca_frac_hbm": round(by_h / (th * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+        del cc, csa_st, hca_st
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("oracle on the host cores")
+        import numpy as np
+        from oracle import pipeline as OP
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001
+            blas_threads = 1
+        a = {kk: v.cpu().numpy() for kk, v in base.t.items()}
+        n_done, t_start = 0, time.perf_counter()
+        while True:
+            OP.decode_1m_query(base.params, a, n_done % B)
+            n_done += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or n_done >= 64:
+                break
+        cpu = {"value": round(n_done / el, 4), "unit": "query-tokens/s", "cores": int(blas_threads),
+               "kind": "oracle",
+               "sample": f"{n_done} decode query-tokens of the same 1M-context batch (index + CSA + HCA per "
+                         f"query, float64 numpy) in {el:.1f} s; elementwise numpy single-threaded, BLAS "
+                         f"on {blas_threads} threads"}
+
+    out = {
+        "metric": "CSA+HCA decode query-tokens/s at 1M ctx; achieved HBM GB/s vs peak",
+        "value": round(qtok_s, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4+bf16 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "decode at 1M context: batch 4, 64 heads MQA, KV 448 FP8 E4M3 + 64 bf16, "
+                               "CSA m=4 top-k=1024 with MXFP4 indexer (4 heads x 64), HCA m'=128, window 128",
+                   "batch": B, "context": L, "heads": H, "head_dim": D, "topk": k, "window": W_,
+                   "graph": f"{R} rotating input copies per replay"},
+        "gb_per_s": round(gbs, 1), "frac_hbm_step": round(gbs / HBM_PEAK_GBS, 4),
+        "tflops": round(tfs, 2),
+        "step_bytes": step_bytes, "step_flops": step_flops,
+        "breakdown_ms": {"lightning_index_topk": round(t_idx, 5), "csa_sparse_mqa_attn": round(t_csa, 5),
+                         "hca_dense_mqa_attn": round(t_hca, 5)},
+        "roofline": {"kernel": "lightning_index_topk (score + select kernels)", "bound": "hbm",
+                     "achieved": round(by_idx / (t_idx * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(by_idx / (t_idx * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": by_idx},
+        "rooflines": {
+            "csa_sparse_mqa_attn": {"bound": "hbm", "achieved": round(by_csa / (t_csa * 1e-3) / 1e9, 1),
+                                    "frac": round(by_csa / (t_csa * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    "tflops": round(fl_csa / (t_csa * 1e-3) / 1e12, 2)},
+            "hca_dense_mqa_attn": {"bound": "hbm", "achieved": round(by_hca / (t_hca * 1e-3) / 1e9, 1),
+                                   "frac": round(by_hca / (t_hca * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "tflops": round(fl_hca / (t_hca * 1e-3) / 1e12, 2),
+                                   "frac_mfma_bf16": round(fl_hca / (t_hca * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        },
+        "compress": comp,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

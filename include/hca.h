@@ -1,0 +1,230 @@
+/*
+ * hca.h — C ABI of the CSA + HCA hybrid-attention library for AMD MI355X
+ * (gfx950).
+ *
+ * The method: hyper.ai paper page for arXiv 2606.19348 ("DeepSeek-V4"),
+ * section 方法 (Method), paragraphs on CSA, HCA and efficiency. CSA
+ * compresses every m tokens of KV into one entry with learnable compression
+ * weights and a position bias, a lightning indexer picks the top-k
+ * compressed entries per query, and MQA core attention with shared keys and
+ * values runs over them; HCA merges every m' >> m tokens into one entry
+ * without overlap and runs dense attention over all entries; both add a
+ * sliding-window branch. KV entries keep BF16 RoPE dims and FP8 for the
+ * rest; the indexer runs in FP4. The model card's "Tensor type" list
+ * (F8_E4M3, F8_E8M0) fixes FP8 = OCP E4M3FN and FP4 = MX E2M1 with E8M0
+ * block scales (block 32).
+ *
+ * Conventions shared by every entry point:
+ *  - Pure, stream-ordered functions. The caller owns every buffer (inputs,
+ *    outputs, workspace). The library allocates no device memory and keeps
+ *    no state besides its loaded kernels; it is thread-safe.
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *    tensors); `hca_store` structs themselves live in host memory and are
+ *    read during the call only. `stream` is a hipStream_t (NULL = the null
+ *    stream). Work is enqueued on `stream`; results are valid once the
+ *    caller synchronises it.
+ *  - Every argument that the host can check is checked before anything is
+ *    enqueued; a failing check returns a negative status and enqueues
+ *    nothing. Contents of device arrays (positions, row offsets, indices)
+ *    are preconditions stated per function: violating them gives unspecified
+ *    values but never an out-of-bounds access, because every kernel clamps
+ *    its reads to the `n_rows` of the views it is given.
+ *  - Device pointers must be 16-byte aligned, and row strides must keep
+ *    every row 16-byte aligned (status HCA_ERR_INVALID_ARG otherwise).
+ *  - Positions are absolute token positions (int64). Entry indices are
+ *    relative to the first row of their sequence in a store (int32/int64).
+ *  - hca_last_error() returns a message for the last failing call on the
+ *    calling thread.
+ */
+#ifndef HCA_H_
+#define HCA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HCA_ABI_VERSION 1
+
+/* Status codes. */
+#define HCA_OK 0
+#define HCA_ERR_INVALID_ARG (-1) /* NULL, range, alignment, raw rows missing  */
+#define HCA_ERR_UNSUPPORTED (-2) /* dtype / layout / shape combination        */
+#define HCA_ERR_WORKSPACE (-3)   /* workspace smaller than required           */
+#define HCA_ERR_HIP (-4)         /* a HIP launch failed                       */
+
+/* Element types. */
+#define HCA_F32 0
+#define HCA_BF16 1
+#define HCA_FP8_E4M3 2
+#define HCA_MXFP4 3
+
+/* Layouts of a store of KV rows (compressed entries or raw window tokens). */
+#define HCA_LAYOUT_F32 0   /* dense rows of D float32                          */
+#define HCA_LAYOUT_BF16 1  /* dense rows of D bf16                             */
+#define HCA_LAYOUT_SPLIT 2 /* per row: d_nope E4M3 bytes, one float32 power-of-
+                              two scale (value = code * scale), d_rope bf16
+                              (the efficiency paragraph: FP8 for the non-RoPE
+                              dims, BF16 for the RoPE dims)                   */
+
+/*
+ * A view of n_rows KV rows of width D = d_nope + d_rope. The first d_nope
+ * columns are the non-RoPE dims, the last d_rope the RoPE dims.
+ *  dense layouts: row r is `data + r * row_stride` (elements of the layout's
+ *                 type); scale/rope/rope_stride are unused.
+ *  split layout:  row r's FP8 codes are `data + r * row_stride` (bytes), its
+ *                 scale is `scale[r]`, its RoPE dims are
+ *                 `rope + r * rope_stride` (bf16 elements).
+ */
+typedef struct hca_store {
+  int32_t layout;
+  int32_t d_nope;
+  int32_t d_rope;
+  int32_t reserved; /* must be 0 */
+  int64_t n_rows;
+  void* data;
+  int64_t row_stride;
+  float* scale;
+  void* rope;
+  int64_t rope_stride;
+} hca_store;
+
+int hca_abi_version(void);
+const char* hca_status_string(int status);
+const char* hca_last_error(void);
+
+/*
+ * csa_compress — CSA compressor (CSA paragraph: every m tokens into one
+ * entry with learnable compression weights and a position bias; CSA windows
+ * overlap since only HCA is said to compress without overlap).
+ *
+ * Entry j of a sequence covers the w raw positions [j*m - (w-m), j*m + m)
+ * that are >= 0; window position p = t - (j*m - (w-m)). For every channel c:
+ *   y[j, c] = sum_p softmax_p(z[t_p, c] + pos_bias[p, c]) * x[t_p, c].
+ * Entries first_entry .. first_entry + n_entries - 1 are written to rows
+ * out_row0 .. of `out`; a split output gets a per-row scale
+ * 2^e, e the smallest integer (>= -126) with max|y[j, :d_nope]| <= 448 * 2^e,
+ * and E4M3 codes RNE(y / 2^e); bf16 outputs round to nearest even.
+ *
+ * raw:     [n_rows, D] of raw_dtype (HCA_F32 or HCA_BF16), row stride
+ *          raw_row_stride elements; row r holds absolute position first_pos+r.
+ * logits:  same dtype as raw; element (r, c) at
+ *          logits + r * logit_row_stride + c * logit_col_stride; a column
+ *          stride of 0 means one logit per token (1 is the only other value).
+ * pos_bias: float32 [w, D], contiguous.
+ * Requires 1 <= m <= w <= 1024; the raw rows must cover every position the
+ * requested entries read (HCA_ERR_INVALID_ARG otherwise); D <= 1024 (bf16)
+ * or 512 (f32), D a multiple of 8 (bf16) or 4 (f32), d_nope likewise;
+ * out_row0 + n_entries <= out->n_rows.
+ * Output layouts: HCA_LAYOUT_F32, HCA_LAYOUT_BF16, HCA_LAYOUT_SPLIT.
+ */
+int csa_compress(const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int64_t n_rows,
+                 int64_t first_pos, const void* logits, int64_t logit_row_stride,
+                 int64_t logit_col_stride, const float* pos_bias, int32_t m, int32_t w,
+                 int64_t first_entry, int64_t n_entries, const hca_store* out, int64_t out_row0,
+                 void* stream);
+
+/*
+ * hca_compress — HCA compressor (HCA paragraph: every m' tokens merge into
+ * one entry, without overlap). Identical to csa_compress with w = m = m_prime:
+ * entry j covers [j*m', (j+1)*m'); pos_bias is float32 [m_prime, D].
+ */
+int hca_compress(const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int64_t n_rows,
+                 int64_t first_pos, const void* logits, int64_t logit_row_stride,
+                 int64_t logit_col_stride, const float* pos_bias, int32_t m_prime,
+                 int64_t first_entry, int64_t n_entries, const hca_store* out, int64_t out_row0,
+                 void* stream);
+
+/*
+ * lightning_index_topk — the lightning indexer (CSA paragraph: it selects
+ * the top-k compressed KV entries for core attention; efficiency paragraph:
+ * FP4 indexer).
+ *
+ * For query i in sequence b = q_seq[i] at position t = q_pos[i], the
+ * visible entries are j < n_vis = floor((t+1)/m) (entry j's last raw
+ * position (j+1)m-1 must be <= t), and
+ *   s[j] = sum_h w_idx[i, h] * max(0, <q_idx[i, h, :], k_idx[k_row_begin[b] + j, :]>).
+ * out_idx[i, :] receives the k entries with the largest s (ties to the
+ * lower j; all n_vis entries if n_vis <= k) in ascending order of j,
+ * padded with -1.
+ *
+ * idx_dtype HCA_F32 / HCA_BF16: q_idx [nq, H, d] and k_idx [k_rows, d]
+ *   elements, contiguous; scores accumulate in float32.
+ * idx_dtype HCA_MXFP4: q_idx [nq, H, d/2] and k_idx [k_rows, d/2] packed
+ *   E2M1 bytes (element 2i in the low nibble of byte i), q_idx_scale
+ *   [nq, H, d/32] and k_idx_scale [k_rows, d/32] E8M0 bytes. Each per-head
+ *   dot product is then exact in float32 provided, per head, the summed
+ *   block exponents of q and key differ by at most 10 between the two
+ *   blocks; the score is defined bit-exactly as s = w0*r0, then
+ *   s = s + w_h*r_h in head order, each product and sum rounded to float32
+ *   (no fused multiply-add).
+ * w_idx: float32 [nq, H]. Requires d == 64, 1 <= H <= 8, 1 <= k <= 2048,
+ * m >= 1, 1 <= nq. Preconditions: q_seq[i] indexes k_row_begin; every
+ * n_vis <= max_visible and k_row_begin[b] + n_vis <= k_rows (reads are
+ * clamped to both bounds).
+ * Workspace: lightning_index_topk_workspace(nq, max_visible, k) bytes
+ * process all queries at once; any ws_bytes >= the value for nq = 1 works
+ * (queries are then processed in batches, in order, on `stream`).
+ */
+size_t lightning_index_topk_workspace(int32_t nq, int64_t max_visible, int32_t k);
+int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx,
+                         int32_t n_idx_heads, int32_t d_idx, int32_t idx_dtype, const void* k_idx,
+                         const uint8_t* k_idx_scale, int64_t k_rows, const int64_t* k_row_begin,
+                         const int32_t* q_seq, const int64_t* q_pos, int32_t nq,
+                         int64_t max_visible, int32_t m, int32_t k, int32_t* out_idx, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * csa_sparse_mqa_attn — CSA core attention (CSA paragraph: MQA with shared
+ * keys and values over the selected entries; HCA paragraph: plus a
+ * sliding-window branch).
+ *
+ * For query i (sequence b, position t) and every head h, one softmax over
+ * the set E = {cache row cache_row_begin[b] + idx[i, r] : r < k, idx >= 0}
+ * U {window row win_row_begin[b] + (p - win_pos0[b]) :
+ *     max(0, t-W+1) <= p <= t}, with K = V = the stored row (all D dims):
+ *   o[i, h] = sum_e softmax_e(scale * <q[i, h], e>) e,
+ *   lse[i, h] = log sum_e exp(scale * <q[i, h], e>)  (natural log).
+ * An empty set gives o = 0, lse = -inf.
+ *
+ * q: [nq, n_heads, D] of q_dtype, contiguous. o: [nq, n_heads, D] of o_dtype,
+ * contiguous. lse: float32 [nq, n_heads].
+ * Supported: q, o, cache, window all F32 (any D <= 1024, n_heads * D <=
+ * 16384); or q BF16, o BF16 or F32, cache and window BF16 or SPLIT with
+ * D = 512, n_heads a multiple of 16.
+ * Preconditions: idx entries are distinct and < the sequence's stored entry
+ * count; win_pos0[b] <= max(0, t-W+1); the window rows exist.
+ * Workspace: mqa_attn_workspace(q_dtype, nq, n_heads, D, k + W) bytes (the
+ * split-K partials; 0 when one block per query and head group suffices).
+ */
+size_t mqa_attn_workspace(int32_t q_dtype, int32_t nq, int32_t n_heads, int32_t d,
+                          int64_t max_entries);
+int csa_sparse_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                        const hca_store* cache, const int64_t* cache_row_begin,
+                        const int32_t* idx, int32_t k, const hca_store* window,
+                        const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W,
+                        const int32_t* q_seq, const int64_t* q_pos, float scale, void* o,
+                        int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * hca_dense_mqa_attn — HCA core attention (HCA paragraph: dense attention
+ * over all heavily compressed entries plus the sliding-window branch).
+ * As csa_sparse_mqa_attn, with the compressed part of E being every visible
+ * entry j < n_vis = min(floor((t+1)/m_prime), max_visible):
+ * cache rows cache_row_begin[b] + j.
+ * Workspace: mqa_attn_workspace(q_dtype, nq, n_heads, D, max_visible + W) bytes.
+ */
+int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                       const hca_store* cache, const int64_t* cache_row_begin, int32_t m_prime,
+                       int64_t max_visible, const hca_store* window, const int64_t* win_row_begin,
+                       const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
+                       const int64_t* q_pos, float scale, void* o, int32_t o_dtype, float* lse,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCA_H_ */

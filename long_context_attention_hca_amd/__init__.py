@@ -1,0 +1,190 @@
+"""Python binding of libhca.so, the MI355X (gfx950) CSA + HCA hybrid-attention library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/hca.h. Tensors are torch CUDA tensors (device memory) and
+work is enqueued on the current torch stream unless `stream` is given. There is
+no fallback: if libhca.so is missing or fails to load, importing this module
+raises.
+
+Function names, argument order and meaning follow include/hca.h.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "F32", "BF16", "FP8_E4M3", "MXFP4", "LAYOUT_F32", "LAYOUT_BF16", "LAYOUT_SPLIT",
+    "HcaError", "Store", "abi_version", "csa_compress", "hca_compress",
+    "lightning_index_topk_workspace", "lightning_index_topk", "mqa_attn_workspace",
+    "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "library_path",
+]
+
+F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
+LAYOUT_F32, LAYOUT_BF16, LAYOUT_SPLIT = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libhca.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(f"{library_path} is not built; run `python -m long_context_attention_hca_amd.build` "
+                      "(or __graft_entry__.build())")
+_lib = ctypes.CDLL(library_path)
+
+
+class _StoreC(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("n_rows", ctypes.c_int64), ("data", ctypes.c_void_p),
+                ("row_stride", ctypes.c_int64), ("scale", ctypes.c_void_p), ("rope", ctypes.c_void_p),
+                ("rope_stride", ctypes.c_int64)]
+
+
+_P, _I32, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_SP = ctypes.POINTER(_StoreC)
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_abi = _sig("hca_abi_version", ctypes.c_int, [])
+_status_string = _sig("hca_status_string", ctypes.c_char_p, [ctypes.c_int])
+_last_error = _sig("hca_last_error", ctypes.c_char_p, [])
+_compress_args = [_P, _I32, _I64, _I64, _I64, _P, _I64, _I64, _P]
+_csa_compress = _sig("csa_compress", ctypes.c_int, _compress_args + [_I32, _I32, _I64, _I64, _SP, _I64, _P])
+_hca_compress = _sig("hca_compress", ctypes.c_int, _compress_args + [_I32, _I64, _I64, _SP, _I64, _P])
+_index_ws = _sig("lightning_index_topk_workspace", _SZ, [_I32, _I64, _I32])
+_index = _sig("lightning_index_topk", ctypes.c_int,
+              [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P])
+_attn_ws = _sig("mqa_attn_workspace", _SZ, [_I32, _I32, _I32, _I32, _I64])
+_attn_tail = [_SP, _P, _P, _I32, _P, _P, _F, _P, _I32, _P, _P, _SZ, _P]
+_csa_attn = _sig("csa_sparse_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP, _P, _P, _I32] + _attn_tail)
+_hca_attn = _sig("hca_dense_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail)
+
+
+class HcaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def _check(status):
+    if status != 0:
+        raise HcaError(status, _last_error().decode())
+
+
+def abi_version():
+    return _abi()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    if t.dtype == torch.uint8:
+        return MXFP4
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+class Store:
+    """A view of KV rows (compressed entries or raw window tokens) for the C ABI.
+
+    dense: `data` [n_rows, >=D] float32 or bf16 (torch.bfloat16 / int16 bits).
+    split: `data` uint8 E4M3 codes [n_rows, >=d_nope], `scale` float32 [n_rows],
+           `rope` bf16 bits [n_rows, >=d_rope].
+    Tensors are kept referenced by the Store.
+    """
+
+    def __init__(self, layout, d_nope, d_rope, data, scale=None, rope=None):
+        self.layout, self.d_nope, self.d_rope = layout, int(d_nope), int(d_rope)
+        self.data, self.scale, self.rope = data, scale, rope
+        self._c = _StoreC(layout, self.d_nope, self.d_rope, 0, data.shape[0], data.data_ptr(), data.stride(0),
+                          scale.data_ptr() if scale is not None else None,
+                          rope.data_ptr() if rope is not None else None,
+                          rope.stride(0) if rope is not None else 0)
+
+    @classmethod
+    def dense(cls, data, d_nope, d_rope):
+        layout = LAYOUT_F32 if data.dtype == torch.float32 else LAYOUT_BF16
+        return cls(layout, d_nope, d_rope, data)
+
+    @classmethod
+    def split(cls, nope, scale, rope):
+        return cls(LAYOUT_SPLIT, nope.shape[1], rope.shape[1], nope, scale, rope)
+
+    @property
+    def n_rows(self):
+        return self.data.shape[0]
+
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def csa_compress(raw, first_pos, logits, pos_bias, m, w, first_entry, n_entries, out, out_row0=0,
+                 scalar_logits=False, stream=None):
+    _check(_csa_compress(_ptr(raw), _dtype_code(raw), raw.stride(0), raw.shape[0], first_pos, _ptr(logits),
+                         logits.stride(0), 0 if scalar_logits else 1, _ptr(pos_bias), m, w, first_entry,
+                         n_entries, out.c(), out_row0, _stream(stream)))
+
+
+def hca_compress(raw, first_pos, logits, pos_bias, m_prime, first_entry, n_entries, out, out_row0=0,
+                 scalar_logits=False, stream=None):
+    _check(_hca_compress(_ptr(raw), _dtype_code(raw), raw.stride(0), raw.shape[0], first_pos, _ptr(logits),
+                         logits.stride(0), 0 if scalar_logits else 1, _ptr(pos_bias), m_prime, first_entry,
+                         n_entries, out.c(), out_row0, _stream(stream)))
+
+
+def lightning_index_topk_workspace(nq, max_visible, k):
+    return _index_ws(nq, max_visible, k)
+
+
+def lightning_index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out_idx, ws,
+                         q_idx_scale=None, k_idx_scale=None, idx_dtype=None, stream=None):
+    """q_idx [nq, H, d] (f32/bf16) or [nq, H, d/2] uint8 (MXFP4, with scales)."""
+    dt = _dtype_code(q_idx) if idx_dtype is None else idx_dtype
+    nq, H = q_idx.shape[0], q_idx.shape[1]
+    d = q_idx.shape[2] * (2 if dt == MXFP4 else 1)
+    _check(_index(_ptr(q_idx), _ptr(q_idx_scale), _ptr(w_idx), H, d, dt, _ptr(k_idx), _ptr(k_idx_scale),
+                  k_idx.shape[0], _ptr(k_row_begin), _ptr(q_seq), _ptr(q_pos), nq, max_visible, m, k,
+                  _ptr(out_idx), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mqa_attn_workspace(q_dtype, nq, n_heads, d, max_entries):
+    return _attn_ws(q_dtype, nq, n_heads, d, max_entries)
+
+
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def csa_sparse_mqa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale,
+                        o, lse, ws=None, stream=None):
+    wp, wb = _ws_args(ws)
+    _check(_csa_attn(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin),
+                     _ptr(idx), idx.shape[1], window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq),
+                     _ptr(q_pos), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb, _stream(stream)))
+
+
+def hca_dense_mqa_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq,
+                       q_pos, scale, o, lse, ws=None, stream=None):
+    wp, wb = _ws_args(ws)
+    _check(_hca_attn(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin), m_prime,
+                     max_visible, window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq), _ptr(q_pos),
+                     scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb, _stream(stream)))

@@ -1,0 +1,335 @@
+// C ABI of the hybrid-attention library: argument validation and kernel dispatch.
+// Every host-checkable argument is validated before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "hca.h"
+#include "internal.h"
+
+namespace hca {
+hipError_t attention_init();
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fn, const char* msg) {
+  g_last_error = std::string(fn) + ": " + msg;
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ensure_init(const char* fn) {
+  static std::once_flag once;
+  static hipError_t err = hipSuccess;
+  std::call_once(once, [] { err = hca::attention_init(); });
+  if (err != hipSuccess) {
+    g_last_error = std::string(fn) + ": HIP init failed: " + hipGetErrorString(err);
+    return HCA_ERR_HIP;
+  }
+  return HCA_OK;
+}
+
+int launched(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return HCA_OK;
+  g_last_error = std::string(fn) + ": launch failed: " + hipGetErrorString(e);
+  return HCA_ERR_HIP;
+}
+
+// Validates a store view; `what` names it in messages.
+int check_store(const char* fn, const hca_store* s, const char* what, std::string* msg) {
+  char buf[256];
+  auto bad = [&](const char* m) {
+    snprintf(buf, sizeof buf, "%s: %s", what, m);
+    *msg = buf;
+    return HCA_ERR_INVALID_ARG;
+  };
+  (void)fn;
+  if (!s) return bad("NULL store");
+  if (s->reserved != 0) return bad("reserved field must be 0");
+  if (s->d_nope < 0 || s->d_rope < 0 || s->d_nope + s->d_rope <= 0) return bad("bad d_nope/d_rope");
+  if (s->n_rows < 0) return bad("negative n_rows");
+  const int64_t D = (int64_t)s->d_nope + s->d_rope;
+  switch (s->layout) {
+    case HCA_LAYOUT_F32:
+    case HCA_LAYOUT_BF16: {
+      const int64_t es = s->layout == HCA_LAYOUT_F32 ? 4 : 2;
+      if (s->n_rows > 0 && !s->data) return bad("NULL data");
+      if (!aligned16(s->data)) return bad("data not 16-byte aligned");
+      if (s->row_stride < D) return bad("row_stride < D");
+      if ((s->row_stride * es) % 16) return bad("rows not 16-byte aligned");
+      return HCA_OK;
+    }
+    case HCA_LAYOUT_SPLIT:
+      if (s->n_rows > 0 && (!s->data || !s->scale || !s->rope)) return bad("NULL data/scale/rope");
+      if (!aligned16(s->data) || !aligned16(s->rope)) return bad("data/rope not 16-byte aligned");
+      if (s->row_stride < s->d_nope || s->row_stride % 16) return bad("bad FP8 row_stride");
+      if (s->rope_stride < s->d_rope || (s->rope_stride * 2) % 16) return bad("bad rope_stride");
+      if (s->d_nope % 8 || s->d_rope % 8) return bad("d_nope and d_rope must be multiples of 8");
+      return HCA_OK;
+    default:
+      return bad("unknown layout");
+  }
+}
+
+hca::StoreView view_of(const hca_store* s) {
+  hca::StoreView v;
+  v.layout = s->layout;
+  v.d_nope = s->d_nope;
+  v.d_rope = s->d_rope;
+  v.n_rows = s->n_rows;
+  v.data = s->data;
+  v.row_stride = s->row_stride;
+  v.scale = s->scale;
+  v.rope = s->rope;
+  v.rope_stride = s->rope_stride;
+  return v;
+}
+
+int compress_impl(const char* fn, const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int64_t n_rows,
+                  int64_t first_pos, const void* logits, int64_t logit_row_stride, int64_t logit_col_stride,
+                  const float* pos_bias, int32_t m, int32_t w, int64_t first_entry, int64_t n_entries,
+                  const hca_store* out, int64_t out_row0, void* stream) {
+  if (!raw || !logits || !pos_bias) return fail(HCA_ERR_INVALID_ARG, fn, "NULL raw/logits/pos_bias");
+  if (raw_dtype != HCA_F32 && raw_dtype != HCA_BF16) return fail(HCA_ERR_UNSUPPORTED, fn, "raw dtype must be F32 or BF16");
+  std::string msg;
+  if (check_store(fn, out, "out", &msg) != HCA_OK) return fail(HCA_ERR_INVALID_ARG, fn, msg.c_str());
+  if (m < 1 || w < m || w > 1024) return fail(HCA_ERR_INVALID_ARG, fn, "need 1 <= m <= w <= 1024");
+  if (n_rows < 0 || first_pos < 0 || first_entry < 0 || n_entries < 0 || out_row0 < 0)
+    return fail(HCA_ERR_INVALID_ARG, fn, "negative size or offset");
+  const int64_t D = (int64_t)out->d_nope + out->d_rope;
+  const int64_t es = raw_dtype == HCA_F32 ? 4 : 2;
+  const int64_t vec = 16 / es;
+  if (D % vec || out->d_nope % vec) return fail(HCA_ERR_UNSUPPORTED, fn, "D and d_nope must be multiples of 16 bytes of raw");
+  if (D > 2 * 64 * vec) return fail(HCA_ERR_UNSUPPORTED, fn, "D too large (1024 bf16 / 512 f32 max)");
+  if (raw_row_stride < D || (raw_row_stride * es) % 16) return fail(HCA_ERR_INVALID_ARG, fn, "bad raw_row_stride");
+  if (!aligned16(raw) || !aligned16(pos_bias)) return fail(HCA_ERR_INVALID_ARG, fn, "raw/pos_bias not 16-byte aligned");
+  if (logit_col_stride != 0 && logit_col_stride != 1) return fail(HCA_ERR_INVALID_ARG, fn, "logit_col_stride must be 0 or 1");
+  if (logit_col_stride == 1) {
+    if (!aligned16(logits) || logit_row_stride < D || (logit_row_stride * es) % 16)
+      return fail(HCA_ERR_INVALID_ARG, fn, "bad logits alignment or row stride");
+  } else if (logit_row_stride < 1) {
+    return fail(HCA_ERR_INVALID_ARG, fn, "bad logit_row_stride");
+  }
+  if (out_row0 + n_entries > out->n_rows) return fail(HCA_ERR_INVALID_ARG, fn, "output rows out of range");
+  if (n_entries > 0) {
+    const int64_t lo = std::max<int64_t>(0, first_entry * m - (w - m));
+    const int64_t hi = (first_entry + n_entries) * m;  // exclusive
+    if (lo < first_pos || hi > first_pos + n_rows)
+      return fail(HCA_ERR_INVALID_ARG, fn, "raw rows do not cover the windows of the requested entries");
+  }
+  hca::CompressArgs a;
+  a.raw = raw; a.raw_stride = raw_row_stride;
+  a.logits = logits; a.logit_row_stride = logit_row_stride; a.logit_col_stride = logit_col_stride;
+  a.bias = pos_bias;
+  a.n_rows = n_rows; a.first_pos = first_pos; a.first_entry = first_entry; a.n_entries = n_entries;
+  a.m = m; a.w = w; a.D = (int)D; a.d_nope = out->d_nope;
+  a.raw_dtype = raw_dtype; a.out_layout = out->layout;
+  a.out = out->data; a.out_stride = out->row_stride; a.out_scale = out->scale;
+  a.out_rope = out->rope; a.out_rope_stride = out->rope_stride; a.out_row0 = out_row0;
+  return launched(fn, hca::launch_compress(a, static_cast<hipStream_t>(stream)));
+}
+
+constexpr size_t kWsSlack = 1024;
+
+size_t index_ws(int64_t nq, int64_t max_visible) {
+  return kWsSlack + (size_t)nq * hca::index_ws_per_query(max_visible);
+}
+
+uint8_t* align256(uint8_t* p) { return reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255)); }
+
+size_t attn_ws(int q_dtype, int64_t nq, int H, int D, int64_t max_entries, int* n_split, int* per) {
+  hca::attn_split_policy((int)nq, H, D, max_entries, q_dtype == HCA_BF16, n_split, per);
+  if (*n_split <= 1) return 0;
+  return 512 + (size_t)nq * (size_t)(*n_split) * (size_t)H * ((size_t)D + 1) * 4;
+}
+
+int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+              const hca_store* cache, const int64_t* cache_row_begin, const int32_t* idx, int32_t k,
+              int32_t m_prime, int64_t max_visible, const hca_store* window, const int64_t* win_row_begin,
+              const int64_t* win_pos0, int32_t W, const int32_t* q_seq, const int64_t* q_pos, float scale,
+              void* o, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !cache_row_begin || !win_row_begin || !win_pos0 || !q_seq || !q_pos || !o || !lse)
+    return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
+  if (csa && k > 0 && !idx) return fail(HCA_ERR_INVALID_ARG, fn, "NULL idx");
+  if (nq < 0 || n_heads < 1 || W < 0) return fail(HCA_ERR_INVALID_ARG, fn, "bad nq/n_heads/W");
+  if (csa && (k < 0 || k > 65536)) return fail(HCA_ERR_INVALID_ARG, fn, "k out of range");
+  if (!csa && (m_prime < 1 || max_visible < 0)) return fail(HCA_ERR_INVALID_ARG, fn, "bad m_prime/max_visible");
+  if (!std::isfinite(scale)) return fail(HCA_ERR_INVALID_ARG, fn, "non-finite scale");
+  std::string msg;
+  if (check_store(fn, cache, "cache", &msg) != HCA_OK) return fail(HCA_ERR_INVALID_ARG, fn, msg.c_str());
+  if (check_store(fn, window, "window", &msg) != HCA_OK) return fail(HCA_ERR_INVALID_ARG, fn, msg.c_str());
+  if (cache->d_nope != window->d_nope || cache->d_rope != window->d_rope)
+    return fail(HCA_ERR_INVALID_ARG, fn, "cache and window widths differ");
+  if (!aligned16(q) || !aligned16(o) || (reinterpret_cast<uintptr_t>(lse) & 3))
+    return fail(HCA_ERR_INVALID_ARG, fn, "q/o not 16-byte aligned");
+  const int D = cache->d_nope + cache->d_rope;
+  const hca::StoreView cv = view_of(cache), wv = view_of(window);
+  const bool mfma = hca::attn_mfma_supported(q_dtype, o_dtype, cv, wv, n_heads, D);
+  if (!mfma) {
+    const bool valu = q_dtype == HCA_F32 && o_dtype == HCA_F32 && cache->layout == HCA_LAYOUT_F32 &&
+                      window->layout == HCA_LAYOUT_F32 && D <= 512 && (int64_t)n_heads * D <= 8192;
+    if (!valu) return fail(HCA_ERR_UNSUPPORTED, fn, "unsupported dtype/layout/shape combination");
+  }
+  if (nq == 0) return HCA_OK;
+  const int64_t max_entries = (csa ? (int64_t)k : max_visible) + W;
+  int n_split = 1, per = 1;
+  const size_t need = attn_ws(q_dtype, nq, n_heads, D, max_entries, &n_split, &per);
+  if (need > 0 && (!ws || ws_bytes < need)) return fail(HCA_ERR_WORKSPACE, fn, "workspace too small");
+  int st = ensure_init(fn);
+  if (st != HCA_OK) return st;
+  hca::AttnArgs a;
+  a.q = q; a.q_dtype = q_dtype; a.nq = nq; a.H = n_heads; a.D = D;
+  a.cache = cv; a.win = wv;
+  a.cache_row_begin = cache_row_begin;
+  a.idx = csa ? idx : nullptr;
+  a.k = csa ? k : 0;
+  a.m_prime = csa ? 1 : m_prime;
+  a.max_visible = csa ? 0 : max_visible;
+  a.win_row_begin = win_row_begin; a.win_pos0 = win_pos0; a.W = W;
+  a.q_seq = q_seq; a.q_pos = q_pos; a.scale = scale;
+  a.o = o; a.o_dtype = o_dtype; a.lse = lse;
+  a.n_split = n_split; a.per_split = per;
+  a.part_o = nullptr; a.part_lse = nullptr;
+  if (n_split > 1) {
+    uint8_t* p = align256(static_cast<uint8_t*>(ws));
+    a.part_o = reinterpret_cast<float*>(p);
+    a.part_lse = a.part_o + (size_t)nq * n_split * n_heads * D;
+  }
+  return launched(fn, hca::launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+#define HCA_EXPORT __attribute__((visibility("default")))
+
+HCA_EXPORT int hca_abi_version(void) { return HCA_ABI_VERSION; }
+
+HCA_EXPORT const char* hca_status_string(int status) {
+  switch (status) {
+    case HCA_OK: return "ok";
+    case HCA_ERR_INVALID_ARG: return "invalid argument";
+    case HCA_ERR_UNSUPPORTED: return "unsupported dtype/layout/shape combination";
+    case HCA_ERR_WORKSPACE: return "workspace too small";
+    case HCA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+HCA_EXPORT const char* hca_last_error(void) { return g_last_error.c_str(); }
+
+HCA_EXPORT int csa_compress(const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int64_t n_rows, int64_t first_pos,
+                 const void* logits, int64_t logit_row_stride, int64_t logit_col_stride, const float* pos_bias,
+                 int32_t m, int32_t w, int64_t first_entry, int64_t n_entries, const hca_store* out,
+                 int64_t out_row0, void* stream) {
+  return compress_impl("csa_compress", raw, raw_dtype, raw_row_stride, n_rows, first_pos, logits, logit_row_stride,
+                       logit_col_stride, pos_bias, m, w, first_entry, n_entries, out, out_row0, stream);
+}
+
+HCA_EXPORT int hca_compress(const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int64_t n_rows, int64_t first_pos,
+                 const void* logits, int64_t logit_row_stride, int64_t logit_col_stride, const float* pos_bias,
+                 int32_t m_prime, int64_t first_entry, int64_t n_entries, const hca_store* out,
+                 int64_t out_row0, void* stream) {
+  return compress_impl("hca_compress", raw, raw_dtype, raw_row_stride, n_rows, first_pos, logits, logit_row_stride,
+                       logit_col_stride, pos_bias, m_prime, m_prime, first_entry, n_entries, out, out_row0, stream);
+}
+
+HCA_EXPORT size_t lightning_index_topk_workspace(int32_t nq, int64_t max_visible, int32_t k) {
+  (void)k;
+  if (nq < 0 || max_visible < 0) return 0;
+  return index_ws(nq, max_visible);
+}
+
+HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx, int32_t n_idx_heads,
+                         int32_t d_idx, int32_t idx_dtype, const void* k_idx, const uint8_t* k_idx_scale,
+                         int64_t k_rows, const int64_t* k_row_begin, const int32_t* q_seq, const int64_t* q_pos,
+                         int32_t nq, int64_t max_visible, int32_t m, int32_t k, int32_t* out_idx, void* ws,
+                         size_t ws_bytes, void* stream) {
+  const char* fn = "lightning_index_topk";
+  if (!q_idx || !w_idx || !k_idx || !k_row_begin || !q_seq || !q_pos || !out_idx)
+    return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
+  if (idx_dtype != HCA_F32 && idx_dtype != HCA_BF16 && idx_dtype != HCA_MXFP4)
+    return fail(HCA_ERR_UNSUPPORTED, fn, "indexer dtype must be F32, BF16 or MXFP4");
+  if (idx_dtype == HCA_MXFP4 && (!q_idx_scale || !k_idx_scale)) return fail(HCA_ERR_INVALID_ARG, fn, "NULL MXFP4 scales");
+  if (d_idx != 64) return fail(HCA_ERR_UNSUPPORTED, fn, "indexer dim must be 64");
+  if (n_idx_heads < 1 || n_idx_heads > 8) return fail(HCA_ERR_UNSUPPORTED, fn, "indexer heads must be 1..8");
+  if (k < 1 || k > 2048) return fail(HCA_ERR_INVALID_ARG, fn, "k must be 1..2048");
+  if (m < 1 || nq < 0 || max_visible < 0 || k_rows < 0) return fail(HCA_ERR_INVALID_ARG, fn, "bad m/nq/max_visible/k_rows");
+  if (max_visible > (int64_t)INT32_MAX - 1) return fail(HCA_ERR_INVALID_ARG, fn, "max_visible too large");
+  if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(HCA_ERR_INVALID_ARG, fn, "q_idx/k_idx not 16-byte aligned");
+  if (nq == 0) return HCA_OK;
+  const size_t per_q = hca::index_ws_per_query(max_visible);
+  if (!ws || ws_bytes < kWsSlack + per_q) return fail(HCA_ERR_WORKSPACE, fn, "workspace too small");
+  const int64_t batch = std::min<int64_t>(nq, (int64_t)((ws_bytes - kWsSlack) / per_q));
+  const int64_t mv = (max_visible + 63) / 64 * 64;
+  const int64_t q_row = idx_dtype == HCA_MXFP4 ? (int64_t)n_idx_heads * d_idx / 2
+                                               : (int64_t)n_idx_heads * d_idx * (idx_dtype == HCA_F32 ? 4 : 2);
+  for (int64_t q0 = 0; q0 < nq; q0 += batch) {
+    const int64_t nb = std::min<int64_t>(batch, nq - q0);
+    uint8_t* p = align256(static_cast<uint8_t*>(ws));
+    hca::IndexArgs a;
+    a.scores = reinterpret_cast<float*>(p);
+    p = align256(p + (size_t)nb * mv * 4);
+    a.cand = reinterpret_cast<uint64_t*>(p);
+    p = align256(p + (size_t)nb * mv * 8);
+    a.hist = reinterpret_cast<uint32_t*>(p);
+    p = align256(p + (size_t)nb * hca::kHistBins * 4);
+    a.counters = reinterpret_cast<uint32_t*>(p);
+    a.q = static_cast<const uint8_t*>(q_idx) + q0 * q_row;
+    a.q_scale = idx_dtype == HCA_MXFP4 ? q_idx_scale + q0 * n_idx_heads * (d_idx / 32) : nullptr;
+    a.w = w_idx + q0 * n_idx_heads;
+    a.H = n_idx_heads;
+    a.d = d_idx;
+    a.dtype = idx_dtype;
+    a.keys = k_idx;
+    a.key_scale = k_idx_scale;
+    a.k_rows = k_rows;
+    a.k_row_begin = k_row_begin;
+    a.q_seq = q_seq + q0;
+    a.q_pos = q_pos + q0;
+    a.nq = (int)nb;
+    a.max_visible = max_visible;
+    a.m = m;
+    a.k = k;
+    a.out = out_idx + q0 * k;
+    hipError_t e = hca::launch_index_topk(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return launched(fn, e);
+  }
+  return HCA_OK;
+}
+
+HCA_EXPORT size_t mqa_attn_workspace(int32_t q_dtype, int32_t nq, int32_t n_heads, int32_t d, int64_t max_entries) {
+  if (nq <= 0 || n_heads < 1 || d < 1 || max_entries < 0) return 0;
+  int n_split, per;
+  return attn_ws(q_dtype, nq, n_heads, d, max_entries, &n_split, &per);
+}
+
+HCA_EXPORT int csa_sparse_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads, const hca_store* cache,
+                        const int64_t* cache_row_begin, const int32_t* idx, int32_t k, const hca_store* window,
+                        const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
+                        const int64_t* q_pos, float scale, void* o, int32_t o_dtype, float* lse, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return attn_impl("csa_sparse_mqa_attn", true, q, q_dtype, nq, n_heads, cache, cache_row_begin, idx, k, 1, 0,
+                   window, win_row_begin, win_pos0, W, q_seq, q_pos, scale, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+HCA_EXPORT int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads, const hca_store* cache,
+                       const int64_t* cache_row_begin, int32_t m_prime, int64_t max_visible, const hca_store* window,
+                       const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
+                       const int64_t* q_pos, float scale, void* o, int32_t o_dtype, float* lse, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return attn_impl("hca_dense_mqa_attn", false, q, q_dtype, nq, n_heads, cache, cache_row_begin, nullptr, 0,
+                   m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale, o, o_dtype, lse,
+                   ws, ws_bytes, stream);
+}
+
+}  // extern "C"

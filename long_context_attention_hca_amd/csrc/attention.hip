@@ -1,0 +1,479 @@
+// CSA sparse and HCA dense MQA core attention with the sliding-window branch, gfx950.
+//
+// Method: hyper.ai paper page for arXiv 2606.19348 ("DeepSeek-V4"), section 方法
+// (Method). CSA paragraph: MQA with shared keys and values over the top-k
+// compressed entries; HCA paragraph: dense attention over all heavily compressed
+// entries, both with a supplementary sliding-window branch. Per query and head,
+// one softmax runs over the union of the compressed entries and the raw window
+// tokens (the log-sum-exp merge of the two branches), with K = V = the stored
+// row; scores are scale * <q_h, e>.
+//
+// Each query's entry list is: compressed part (CSA: idx[q, r], r < k, skipping
+// -1; HCA: entries 0 .. n_vis-1), then window positions t-n_w+1 .. t. The list is
+// cut into n_split ranges (split-K); each block writes a normalised partial
+// (o, lse) that a combine kernel merges, or the final output when n_split == 1.
+//
+// MFMA kernel (bf16 queries; bf16 or split FP8/bf16 stores; D = 512):
+//  * block = (query, group of 16 heads, split); its 4 waves take the split's
+//    32-entry chunks round-robin and keep independent online-softmax states that
+//    are merged through LDS at the end. The 4 head-group blocks of one range are
+//    adjacent after the XCD remap, so their entry reads share one XCD's L2.
+//  * a wave stages its chunk in LDS as bf16 rows (FP8 codes times the entry's
+//    power-of-two scale via v_cvt_scalef32_pk_bf16_fp8, exact), rows padded by
+//    16 bytes so the operand reads below are bank-conflict free.
+//  * scores S^T = K Q^T with v_mfma_f32_16x16x32_bf16: entries are the M
+//    dimension and the 16 heads the N dimension, so each lane's accumulators all
+//    belong to one head and the online softmax needs only two cross-lane maxima.
+//  * O^T = V^T P^T: P^T is taken straight from the score accumulators (the
+//    contraction order of the 32 entries is permuted identically on both
+//    operands), and V^T tiles come from ds_read_b64_tr_b16 transpose reads of the
+//    row-major chunk.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace hca {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct QueryCtx {
+  int64_t t, n_c, n_w, cache_rb, win_rb, win_p0;
+};
+
+__device__ __forceinline__ QueryCtx query_ctx(const AttnArgs& a, int qi) {
+  QueryCtx c;
+  const int b = a.q_seq[qi];
+  c.t = a.q_pos[qi];
+  if (a.idx) {
+    c.n_c = a.k;
+  } else {
+    int64_t nv = c.t >= 0 ? (c.t + 1) / a.m_prime : 0;
+    c.n_c = min(nv, a.max_visible);
+  }
+  c.n_w = c.t >= 0 ? min<int64_t>(a.W, c.t + 1) : 0;
+  c.cache_rb = a.cache_row_begin[b];
+  c.win_rb = a.win_row_begin[b];
+  c.win_p0 = a.win_pos0[b];
+  return c;
+}
+
+// Row of list position r, or -1 (padding / outside the stores). *win set for window rows.
+__device__ __forceinline__ int64_t list_row(const AttnArgs& a, const QueryCtx& c, int qi, int64_t r, bool* win) {
+  if (r < c.n_c) {
+    *win = false;
+    int64_t j = r;
+    if (a.idx) {
+      j = a.idx[(int64_t)qi * a.k + r];
+      if (j < 0) return -1;
+    }
+    const int64_t row = c.cache_rb + j;
+    return (row >= 0 && row < a.cache.n_rows) ? row : -1;
+  }
+  *win = true;
+  if (r >= c.n_c + c.n_w) return -1;
+  const int64_t p = c.t - c.n_w + 1 + (r - c.n_c);
+  const int64_t row = c.win_rb + (p - c.win_p0);
+  return (row >= 0 && row < a.win.n_rows) ? row : -1;
+}
+
+// ---------------------------------------------------------------------------------------
+// float32 path (vector ALUs): block = (query, split), 256 threads, 16-entry chunks in LDS.
+constexpr int kValuChunk = 16;
+
+__device__ __forceinline__ float load_f32(const StoreView& v, int64_t row, int d) {
+  return static_cast<const float*>(v.data)[row * v.row_stride + d];
+}
+
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
+  extern __shared__ float smem_f[];
+  const int H = a.H, D = a.D;
+  float* qs = smem_f;                       // [H*D]
+  float* ent = qs + H * D;                  // [16][D]
+  float* pr = ent + kValuChunk * D;         // [H][16]
+  float* mrun = pr + H * kValuChunk;        // [H]
+  float* lrun = mrun + H;                   // [H]
+  float* corr = lrun + H;                   // [H]
+  __shared__ int valid[kValuChunk];
+  const int qi = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+  const QueryCtx c = query_ctx(a, qi);
+  const int64_t N = c.n_c + c.n_w;
+  const int64_t lo = (int64_t)s * a.per_split, hi = min<int64_t>(N, lo + a.per_split);
+  const float* q = static_cast<const float*>(a.q) + (int64_t)qi * H * D;
+  for (int i = tid; i < H * D; i += 256) qs[i] = q[i];
+  for (int h = tid; h < H; h += 256) { mrun[h] = -INFINITY; lrun[h] = 0.f; }
+  constexpr int kMaxOut = 32;  // H*D <= 8192
+  float O[kMaxOut];
+#pragma unroll
+  for (int i = 0; i < kMaxOut; ++i) O[i] = 0.f;
+  const float sc = a.scale;
+  __syncthreads();
+  for (int64_t base = lo; base < hi; base += kValuChunk) {
+    if (tid < kValuChunk) {
+      bool w;
+      const int64_t r = base + tid;
+      valid[tid] = r < hi ? (int)(list_row(a, c, qi, r, &w) >= 0) : 0;
+    }
+    for (int i = tid; i < kValuChunk * D; i += 256) {
+      const int e = i / D, d = i % D;
+      bool w;
+      const int64_t r = base + e;
+      const int64_t row = r < hi ? list_row(a, c, qi, r, &w) : -1;
+      ent[i] = row >= 0 ? load_f32(w ? a.win : a.cache, row, d) : 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < H * kValuChunk; i += 256) {
+      const int h = i / kValuChunk, e = i % kValuChunk;
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = fmaf(qs[h * D + d], ent[e * D + d], acc);
+      pr[i] = valid[e] ? acc * sc : -INFINITY;
+    }
+    __syncthreads();
+    for (int h = tid; h < H; h += 256) {
+      float mx = -INFINITY;
+      for (int e = 0; e < kValuChunk; ++e) mx = fmaxf(mx, pr[h * kValuChunk + e]);
+      const float mo = mrun[h], mn = fmaxf(mo, mx);
+      const float cr = mn == -INFINITY ? 1.f : expf(mo - mn);
+      float sum = 0.f;
+      for (int e = 0; e < kValuChunk; ++e) {
+        const float p = mn == -INFINITY ? 0.f : expf(pr[h * kValuChunk + e] - mn);
+        pr[h * kValuChunk + e] = p;
+        sum += p;
+      }
+      lrun[h] = lrun[h] * cr + sum;
+      mrun[h] = mn;
+      corr[h] = cr;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxOut; ++k) {
+      const int i = tid + 256 * k;
+      if (i < H * D) {
+        const int h = i / D, d = i % D;
+        float acc = O[k] * corr[h];
+        for (int e = 0; e < kValuChunk; ++e) acc = fmaf(pr[h * kValuChunk + e], ent[e * D + d], acc);
+        O[k] = acc;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxOut; ++k) {
+    const int i = tid + 256 * k;
+    if (i < H * D) {
+      const int h = i / D, d = i % D;
+      const float l = lrun[h];
+      const float o = l > 0.f ? O[k] / l : 0.f;
+      if (a.n_split == 1) {
+        static_cast<float*>(a.o)[(int64_t)qi * H * D + i] = o;
+        if (d == 0) a.lse[(int64_t)qi * H + h] = l > 0.f ? mrun[h] + logf(l) : -INFINITY;
+      } else {
+        const int64_t pi = ((int64_t)qi * a.n_split + s) * H + h;
+        a.part_o[pi * D + d] = o;
+        if (d == 0) a.part_lse[pi] = l > 0.f ? mrun[h] + logf(l) : -INFINITY;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// MFMA path.
+constexpr int kD = 512;
+constexpr int kChunk = 32;
+constexpr int kRowB = kD * 2 + 16;           // padded bf16 row in LDS
+constexpr int kWaveLds = kChunk * kRowB;      // 33,280 bytes per wave
+constexpr int kMfmaLds = 4 * kWaveLds;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 8 consecutive dims [8*seg, 8*seg+8) of a stored row as 8 bf16 (16 bytes).
+__device__ __forceinline__ uint4 load_seg8(const StoreView& v, int64_t row, int seg) {
+  const int d0 = seg * 8;
+  if (v.layout == HCA_LAYOUT_BF16) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(v.data) + row * v.row_stride + d0);
+  }
+  if (d0 < v.d_nope) {
+    const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(v.data) + row * v.row_stride + d0);
+    const float sc = v.scale[row];
+    const bf16x2 r0 = fp8x2_to_bf16x2(b.x, sc, false), r1 = fp8x2_to_bf16x2(b.x, sc, true);
+    const bf16x2 r2 = fp8x2_to_bf16x2(b.y, sc, false), r3 = fp8x2_to_bf16x2(b.y, sc, true);
+    uint4 o;
+    o.x = __builtin_bit_cast(uint32_t, r0); o.y = __builtin_bit_cast(uint32_t, r1);
+    o.z = __builtin_bit_cast(uint32_t, r2); o.w = __builtin_bit_cast(uint32_t, r3);
+    return o;
+  }
+  return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(v.rope) + row * v.rope_stride + (d0 - v.d_nope));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg, int total) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= total) return;
+  const int hg = id % n_hg;
+  const int rest = id / n_hg;
+  const int s = rest % a.n_split;
+  const int qi = rest / a.n_split;
+  const int H = a.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int head = hg * 16 + c;
+  uint8_t* lds = smem + wave * kWaveLds;
+
+  const QueryCtx ctx = query_ctx(a, qi);
+  const int64_t N = ctx.n_c + ctx.n_w;
+  const int64_t lo = (int64_t)s * a.per_split;
+  const int64_t hi = min<int64_t>(N, lo + a.per_split);
+
+  // Q^T operand (B of S^T = K Q^T): lane holds Q[head][32ks + 8g .. +8).
+  bf16x8 qv[kD / 32];
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * H + head) * kD + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < kD / 32; ++ks)
+    qv[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * ks));
+
+  f32x4 O[kD / 16];
+#pragma unroll
+  for (int i = 0; i < kD / 16; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale * kLog2e;
+
+  for (int64_t base = lo + (int64_t)wave * kChunk; base < hi; base += 4 * kChunk) {
+    // stage 32 rows as bf16: segment sg = lane + 64*i -> entry sg / 64, dims 8*(sg % 64)
+#pragma unroll 4
+    for (int i = 0; i < kChunk; ++i) {
+      const int e = i, seg = lane;
+      const int64_t r = base + e;
+      bool w = false;
+      const int64_t row = r < hi ? list_row(a, ctx, qi, r, &w) : -1;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (row >= 0) val = load_seg8(w ? a.win : a.cache, row, seg);
+      *reinterpret_cast<uint4*>(lds + e * kRowB + seg * 16) = val;
+    }
+    // validity of the 8 entries this lane scores: 16mt + 4g + i
+    bool vld[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = base + 16 * mt + 4 * g + i;
+        bool w;
+        vld[mt][i] = r < hi && list_row(a, ctx, qi, r, &w) >= 0;
+      }
+    wave_lds_sync();
+
+    // S^T = K Q^T
+    f32x4 st[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* rowp = lds + (16 * mt + c) * kRowB + 16 * g;
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowp + 64 * ks));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[ks], acc, 0, 0, 0);
+      }
+      st[mt] = acc;
+    }
+    // online softmax (log2 domain); lanes c, c+16, c+32, c+48 share head c
+    float sv[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[4 * mt + i] = vld[mt][i] ? st[mt][i] * sl2 : -INFINITY;
+        cmax = fmaxf(cmax, sv[4 * mt + i]);
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_new = fmaxf(m_run, cmax);
+    const bool none = m_new == -INFINITY;
+    const float corr = none ? 1.f : exp2f(m_run - m_new);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = none ? 0.f : exp2f(sv[i] - m_new);
+      psum += p[i];
+    }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < kD / 16; ++dt) O[dt] *= corr;
+    // P^T operand: contraction order [4g..4g+3, 16+4g..16+4g+3]
+    const uint4 pu = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pu);
+    // O^T += V^T P^T; V^T via transpose reads: lane (4r + qd) of group g reads
+    // row 4g + r (and 16 + 4g + r), dims 16dt + 4qd .. +4.
+    const int rsel = c >> 2, qd = c & 3;
+    const uint8_t* v0 = lds + (4 * g + rsel) * kRowB + 8 * qd;
+    const uint8_t* v1 = v0 + 16 * kRowB;
+#pragma unroll
+    for (int dt = 0; dt < kD / 16; ++dt) {
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * dt));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * dt));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, O[dt], 0, 0, 0);
+    }
+    wave_lds_sync();
+  }
+
+  // per-head totals over the 4 lane groups
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // merge the 4 waves through LDS: region of wave w = [m(16) | l(16) | O 16 x 512 fp32]
+  float* wm = reinterpret_cast<float*>(lds);
+  float* wl = wm + 16;
+  float* wo = wl + 16;
+  if (g == 0) { wm[c] = m_run; wl[c] = l_run; }
+#pragma unroll
+  for (int dt = 0; dt < kD / 16; ++dt)
+    *reinterpret_cast<f32x4*>(wo + c * kD + 16 * dt + 4 * g) = O[dt];
+  __syncthreads();
+
+  // thread -> head hc = tid / 16, dims 4 * (tid % 16) + 64 * k
+  const int hc = tid >> 4, dl = (tid & 15) * 4;
+  float mw[4], fw[4];
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = reinterpret_cast<const float*>(smem + w * kWaveLds)[hc];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    fw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
+    L += fw[w] * reinterpret_cast<const float*>(smem + w * kWaveLds)[16 + hc];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float lse = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  const int hd = hg * 16 + hc;
+#pragma unroll
+  for (int k = 0; k < kD / 64; ++k) {
+    const int d = dl + 64 * k;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x4 ow = *reinterpret_cast<const f32x4*>(
+          reinterpret_cast<const float*>(smem + w * kWaveLds) + 32 + hc * kD + d);
+      acc += ow * fw[w];
+    }
+    acc *= inv;
+    if (a.n_split == 1) {
+      const int64_t oi = ((int64_t)qi * H + hd) * kD + d;
+      if (a.o_dtype == HCA_BF16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + oi) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + oi) = acc;
+      }
+    } else {
+      const int64_t pi = ((int64_t)qi * a.n_split + s) * H + hd;
+      *reinterpret_cast<f32x4*>(a.part_o + pi * kD + d) = acc;
+    }
+  }
+  if ((tid & 15) == 0) {
+    if (a.n_split == 1) a.lse[(int64_t)qi * H + hd] = lse;
+    else a.part_lse[((int64_t)qi * a.n_split + s) * H + hd] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Log-sum-exp merge of the split partials. grid = (H, nq), 128 threads.
+__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
+  __shared__ float wts[1024];
+  __shared__ float s_m, s_inv, s_lse;
+  const int h = blockIdx.x, qi = blockIdx.y, tid = threadIdx.x;
+  const int S = a.n_split, H = a.H, D = a.D;
+  const float* pl = a.part_lse + (int64_t)qi * S * H + h;
+  if (tid == 0) {
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, pl[(int64_t)s * H]);
+    float L = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float l = pl[(int64_t)s * H];
+      const float wv = (M == -INFINITY || l == -INFINITY) ? 0.f : expf(l - M);
+      wts[s] = wv;
+      L += wv;
+    }
+    s_m = M;
+    s_inv = L > 0.f ? 1.f / L : 0.f;
+    s_lse = L > 0.f ? M + logf(L) : -INFINITY;
+  }
+  __syncthreads();
+  const float inv = s_inv;
+  for (int d = tid; d < D; d += 128) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float wv = wts[s];
+      if (wv != 0.f) acc = fmaf(wv, a.part_o[(((int64_t)qi * S + s) * H + h) * D + d], acc);
+    }
+    acc *= inv;
+    const int64_t oi = ((int64_t)qi * H + h) * D + d;
+    if (a.o_dtype == HCA_BF16) static_cast<uint16_t*>(a.o)[oi] = (uint16_t)f32_to_bf16_rne(acc);
+    else static_cast<float*>(a.o)[oi] = acc;
+  }
+  if (tid == 0) a.lse[(int64_t)qi * H + h] = s_lse;
+}
+
+}  // namespace
+
+bool attn_mfma_supported(int q_dtype, int o_dtype, const StoreView& c, const StoreView& w, int H, int D) {
+  auto ok_store = [](const StoreView& v) {
+    if (v.layout == HCA_LAYOUT_BF16) return true;
+    return v.layout == HCA_LAYOUT_SPLIT && v.d_nope % 8 == 0 && v.d_rope % 8 == 0;
+  };
+  return q_dtype == HCA_BF16 && (o_dtype == HCA_BF16 || o_dtype == HCA_F32) && D == kD && H % 16 == 0 &&
+         ok_store(c) && ok_store(w);
+}
+
+void attn_split_policy(int nq, int H, int D, int64_t max_entries, bool mfma, int* n_split, int* per_split) {
+  (void)D;
+  const int n_hg = mfma ? H / 16 : 1;
+  const int64_t align = mfma ? 4 * kChunk : kValuChunk;
+  const int64_t target = 512;
+  int64_t want = (target + (int64_t)nq * n_hg - 1) / ((int64_t)nq * n_hg);
+  const int64_t max_split = std::max<int64_t>(1, (max_entries + align - 1) / align);
+  want = std::max<int64_t>(1, std::min(want, max_split));
+  int64_t per = (max_entries + want - 1) / want;
+  per = std::max<int64_t>(align, (per + align - 1) / align * align);
+  const int64_t ns = std::max<int64_t>(1, (max_entries + per - 1) / per);
+  *n_split = (int)ns;
+  *per_split = (int)per;
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  const bool mfma = a.q_dtype == HCA_BF16;
+  if (mfma) {
+    const int n_hg = a.H / 16;
+    const int total = a.nq * a.n_split * n_hg;
+    const int grid = (total + 7) / 8 * 8;
+    hipLaunchKernelGGL(attn_mfma_kernel, dim3(grid), dim3(256), kMfmaLds, s, a, n_hg, total);
+  } else {
+    const size_t lds = sizeof(float) * ((size_t)a.H * a.D + (size_t)kValuChunk * a.D + (size_t)a.H * kValuChunk + 3 * a.H);
+    hipLaunchKernelGGL(attn_valu_kernel, dim3(a.n_split, a.nq), dim3(256), lds, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.n_split > 1) {
+    hipLaunchKernelGGL(combine_kernel, dim3(a.H, a.nq), dim3(128), 0, s, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t attention_init() {
+  return hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
+}
+
+}  // namespace hca

@@ -1,0 +1,98 @@
+// Internal launch interfaces between the C ABI layer (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hca.h"
+
+namespace hca {
+
+struct CompressArgs {
+  const void* raw;
+  int64_t raw_stride;  // elements
+  const void* logits;
+  int64_t logit_row_stride;  // elements
+  int64_t logit_col_stride;  // 0 or 1
+  const float* bias;         // [w, D]
+  int64_t n_rows, first_pos, first_entry, n_entries;
+  int m, w, D, d_nope;
+  int raw_dtype;   // HCA_F32 / HCA_BF16
+  int out_layout;  // HCA_LAYOUT_*
+  void* out;
+  int64_t out_stride;  // dense: elements; split: bytes
+  float* out_scale;
+  void* out_rope;
+  int64_t out_rope_stride;  // elements
+  int64_t out_row0;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+
+struct IndexArgs {
+  const void* q;
+  const uint8_t* q_scale;
+  const float* w;
+  int H, d, dtype;
+  const void* keys;
+  const uint8_t* key_scale;
+  int64_t k_rows;
+  const int64_t* k_row_begin;
+  const int32_t* q_seq;
+  const int64_t* q_pos;
+  int nq;  // queries of this batch (pointers above already offset to the batch)
+  int64_t max_visible;
+  int m, k;
+  int32_t* out;  // [nq, k]
+  // workspace views for the batch
+  float* scores;      // [nq, max_visible]
+  uint32_t* hist;     // [nq, kHistBins]
+  uint32_t* counters; // [nq, 4]
+  uint64_t* cand;     // [nq, max_visible]
+};
+constexpr int kHistBins = 2048;
+size_t index_ws_per_query(int64_t max_visible);
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
+
+struct StoreView {
+  int layout, d_nope, d_rope;
+  int64_t n_rows;
+  const void* data;
+  int64_t row_stride;
+  const float* scale;
+  const void* rope;
+  int64_t rope_stride;
+};
+
+struct AttnArgs {
+  const void* q;
+  int q_dtype;
+  int nq, H, D;
+  StoreView cache, win;
+  const int64_t* cache_row_begin;
+  const int32_t* idx;  // CSA: [nq, k]; HCA: nullptr
+  int k;               // CSA selection width
+  int m_prime;         // HCA
+  int64_t max_visible; // HCA
+  const int64_t* win_row_begin;
+  const int64_t* win_pos0;
+  int W;
+  const int32_t* q_seq;
+  const int64_t* q_pos;
+  float scale;
+  void* o;
+  int o_dtype;
+  float* lse;
+  // split-K
+  int n_split;
+  int per_split;    // list positions per split
+  float* part_o;    // [nq, n_split, H, D]
+  float* part_lse;  // [nq, n_split, H]
+};
+// Chooses the split-K factor for a launch; the workspace query uses the same policy.
+void attn_split_policy(int nq, int H, int D, int64_t max_entries, bool mfma, int* n_split,
+                       int* per_split);
+bool attn_mfma_supported(int q_dtype, int o_dtype, const StoreView& c, const StoreView& w, int H,
+                         int D);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace hca

@@ -1,0 +1,255 @@
+"""Runs the hybrid-attention hot path on the GPU for the workloads of the
+benchmark and the tests: compression (CSA and HCA), lightning-indexer top-k,
+CSA sparse and HCA dense MQA attention.
+
+Every step is a call into libhca.so through the binding; torch only allocates
+outputs and workspaces and provides the stream. A workload is described by a
+`case` object with `.params` (dict) and `.t` (dict of CUDA tensors), as the
+seeded generators in `synth` produce.
+"""
+
+import math
+
+import torch
+
+from . import (BF16, F32, LAYOUT_BF16, LAYOUT_F32, LAYOUT_SPLIT, Store, csa_compress, csa_sparse_mqa_attn,
+               hca_compress, hca_dense_mqa_attn, lightning_index_topk, lightning_index_topk_workspace,
+               mqa_attn_workspace)
+
+
+def _i64(vals, dev):
+    return torch.tensor(vals, dtype=torch.int64, device=dev)
+
+
+def empty_store(layout, n, d_nope, d_rope, dev):
+    """Zero-filled store of n rows."""
+    if layout == LAYOUT_F32:
+        return Store.dense(torch.zeros(n, d_nope + d_rope, dtype=torch.float32, device=dev), d_nope, d_rope)
+    if layout == LAYOUT_BF16:
+        return Store.dense(torch.zeros(n, d_nope + d_rope, dtype=torch.int16, device=dev), d_nope, d_rope)
+    return Store.split(torch.zeros(n, d_nope, dtype=torch.uint8, device=dev),
+                       torch.zeros(n, dtype=torch.float32, device=dev),
+                       torch.zeros(n, d_rope, dtype=torch.int16, device=dev))
+
+
+def split_store(t, prefix):
+    return Store.split(t[f"{prefix}_nope"], t[f"{prefix}_scale"], t[f"{prefix}_rope"])
+
+
+class Workspace:
+    """Grow-only byte buffers reused across calls."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.bufs = {}
+
+    def get(self, name, nbytes):
+        b = self.bufs.get(name)
+        if b is None or b.numel() < nbytes:
+            b = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.dev)
+            self.bufs[name] = b
+        return b
+
+
+def index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, ws, q_idx_scale=None,
+               k_idx_scale=None, out=None, stream=None):
+    nq = q_idx.shape[0]
+    if out is None:
+        out = torch.empty(nq, k, dtype=torch.int32, device=q_idx.device)
+    # all queries at once up to 4 GiB of workspace; beyond that the library batches queries
+    need = lightning_index_topk_workspace(nq, max_visible, k)
+    one = lightning_index_topk_workspace(1, max_visible, k)
+    buf = ws.get("index", min(need, max(one, 4 << 30)))
+    lightning_index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out, buf,
+                         q_idx_scale=q_idx_scale, k_idx_scale=k_idx_scale, stream=stream)
+    return out
+
+
+def csa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale, ws,
+             o_dtype=None, o=None, lse=None, stream=None):
+    nq, H, D = q.shape
+    if o is None:
+        o = torch.empty(nq, H, D, dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(nq, H, dtype=torch.float32, device=q.device)
+    qd = F32 if q.dtype == torch.float32 else BF16
+    buf = ws.get("csa", mqa_attn_workspace(qd, nq, H, D, idx.shape[1] + W))
+    csa_sparse_mqa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale,
+                        o, lse, buf, stream=stream)
+    return o, lse
+
+
+def hca_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos,
+             scale, ws, o_dtype=None, o=None, lse=None, stream=None):
+    nq, H, D = q.shape
+    if o is None:
+        o = torch.empty(nq, H, D, dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(nq, H, dtype=torch.float32, device=q.device)
+    qd = F32 if q.dtype == torch.float32 else BF16
+    buf = ws.get("hca", mqa_attn_workspace(qd, nq, H, D, max_visible + W))
+    hca_dense_mqa_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq,
+                       q_pos, scale, o, lse, buf, stream=stream)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------------------------
+# Workloads
+
+
+def tiny_fp32(case, ws=None):
+    """Full pipeline on one fp32 sequence: compress (CSA, HCA), index, attend."""
+    p, t = case.params, case.t
+    dev = t["raw"].device
+    ws = ws or Workspace(dev)
+    L, m, w, mp, W, k = p["L"], p["m"], p["w"], p["m_prime"], p["W"], p["topk"]
+    dn, dr = p["d_nope"], p["d_rope"]
+    n_c, n_h = L // m, L // mp
+    csa = empty_store(LAYOUT_F32, n_c, dn, dr, dev)
+    hca = empty_store(LAYOUT_F32, n_h, dn, dr, dev)
+    csa_compress(t["raw"], 0, t["logits_csa"], t["bias_csa"], m, w, 0, n_c, csa)
+    hca_compress(t["raw"], 0, t["logits_hca"], t["bias_hca"], mp, 0, n_h, hca)
+    zero = _i64([0], dev)
+    idx = index_topk(t["q_idx"], t["w_idx"], t["k_idx"], zero, t["q_seq"], t["q_pos"], n_c, m, k, ws)
+    win = Store.dense(t["raw"], dn, dr)
+    scale = 1.0 / math.sqrt(dn + dr)
+    o_c, l_c = csa_attn(t["q"], csa, zero, idx, win, zero, zero, W, t["q_seq"], t["q_pos"], scale, ws)
+    o_h, l_h = hca_attn(t["q"], hca, zero, mp, n_h, win, zero, zero, W, t["q_seq"], t["q_pos"], scale, ws)
+    return dict(csa=csa, hca=hca, idx=idx, o_csa=o_c, lse_csa=l_c, o_hca=o_h, lse_hca=l_h)
+
+
+def decode_bf16(case, ws=None):
+    """B decode queries over bf16 KV: compress every sequence's caches (bf16 stores), index, attend."""
+    p, t = case.params, case.t
+    dev = t["raw"].device
+    ws = ws or Workspace(dev)
+    B, L, m, w, mp, W, k = p["B"], p["L"], p["m"], p["w"], p["m_prime"], p["W"], p["topk"]
+    dn, dr = p["d_nope"], p["d_rope"]
+    n_c, n_h = L // m, L // mp
+    raw = t["raw"].view(B, L, -1)
+    lc = t["logits_csa"].view(B, L, -1)
+    lh = t["logits_hca"].view(B, L, -1)
+    csa = empty_store(LAYOUT_BF16, B * n_c, dn, dr, dev)
+    hca = empty_store(LAYOUT_BF16, B * n_h, dn, dr, dev)
+    for b in range(B):
+        csa_compress(raw[b], 0, lc[b], t["bias_csa"], m, w, 0, n_c, csa, out_row0=b * n_c)
+        hca_compress(raw[b], 0, lh[b], t["bias_hca"], mp, 0, n_h, hca, out_row0=b * n_h)
+    crb = _i64([b * n_c for b in range(B)], dev)
+    hrb = _i64([b * n_h for b in range(B)], dev)
+    wrb = _i64([b * L for b in range(B)], dev)
+    wp0 = _i64([0] * B, dev)
+    idx = index_topk(t["q_idx"], t["w_idx"], t["k_idx"], crb, t["q_seq"], t["q_pos"], n_c, m, k, ws)
+    win = Store.dense(t["raw"], dn, dr)
+    scale = 1.0 / math.sqrt(dn + dr)
+    q = t["q"].view(torch.bfloat16)
+    o_c, l_c = csa_attn(q, csa, crb, idx, win, wrb, wp0, W, t["q_seq"], t["q_pos"], scale, ws)
+    o_h, l_h = hca_attn(q, hca, hrb, mp, n_h, win, wrb, wp0, W, t["q_seq"], t["q_pos"], scale, ws)
+    return dict(csa=csa, hca=hca, idx=idx, o_csa=o_c, lse_csa=l_c, o_hca=o_h, lse_hca=l_h)
+
+
+class Decode1M:
+    """Decode step over precompressed split-layout caches and MXFP4 indexer keys
+    (index + CSA attention for one layer, HCA attention for another), with all
+    outputs and workspaces preallocated so that `step()` only enqueues kernels."""
+
+    def __init__(self, case, ws=None):
+        p, t = case.params, case.t
+        self.case = case
+        dev = t["q_csa"].device
+        self.ws = ws or Workspace(dev)
+        B, L, m, mp, W, k = p["B"], p["L"], p["m"], p["m_prime"], p["W"], p["topk"]
+        self.B, self.m, self.mp, self.W, self.k = B, m, mp, W, k
+        self.n_c, self.n_h = L // m, L // mp
+        self.csa = split_store(t, "csa")
+        self.hca = split_store(t, "hca")
+        self.win_csa = split_store(t, "win_csa")
+        self.win_hca = split_store(t, "win_hca")
+        self.crb = _i64([b * self.n_c for b in range(B)], dev)
+        self.hrb = _i64([b * self.n_h for b in range(B)], dev)
+        self.wrb = _i64([b * W for b in range(B)], dev)
+        self.wp0 = _i64([L - W] * B, dev)
+        self.q_csa = t["q_csa"].view(torch.bfloat16)
+        self.q_hca = t["q_hca"].view(torch.bfloat16)
+        self.scale = 1.0 / math.sqrt(p["d_nope"] + p["d_rope"])
+        H, D = p["heads"], p["D"]
+        self.idx = torch.empty(B, k, dtype=torch.int32, device=dev)
+        self.o_csa = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
+        self.o_hca = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
+        self.lse_csa = torch.empty(B, H, dtype=torch.float32, device=dev)
+        self.lse_hca = torch.empty(B, H, dtype=torch.float32, device=dev)
+        # size workspaces up front
+        self.ws.get("index", lightning_index_topk_workspace(B, self.n_c, k))
+        self.ws.get("csa", mqa_attn_workspace(BF16, B, H, D, k + W))
+        self.ws.get("hca", mqa_attn_workspace(BF16, B, H, D, self.n_h + W))
+
+    def index(self, stream=None):
+        t = self.case.t
+        return index_topk(t["q_idx"], t["w_idx"], t["k_idx"], self.crb, t["q_seq"], t["q_pos"], self.n_c, self.m,
+                          self.k, self.ws, q_idx_scale=t["q_idx_scale"], k_idx_scale=t["k_idx_scale"], out=self.idx,
+                          stream=stream)
+
+    def csa_attention(self, stream=None):
+        t = self.case.t
+        return csa_attn(self.q_csa, self.csa, self.crb, self.idx, self.win_csa, self.wrb, self.wp0, self.W,
+                        t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_csa, lse=self.lse_csa, stream=stream)
+
+    def hca_attention(self, stream=None):
+        t = self.case.t
+        return hca_attn(self.q_hca, self.hca, self.hrb, self.mp, self.n_h, self.win_hca, self.wrb, self.wp0, self.W,
+                        t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_hca, lse=self.lse_hca, stream=stream)
+
+    def step(self, stream=None):
+        self.index(stream)
+        self.csa_attention(stream)
+        self.hca_attention(stream)
+
+
+def compress_1m(case, out_csa=None, out_hca=None, stream=None):
+    """csa_compress + hca_compress of one long bf16 sequence into split-layout stores."""
+    p, t = case.params, case.t
+    dev = t["raw"].device
+    L, m, w, mp = p["L"], p["m"], p["w"], p["m_prime"]
+    dn, dr = p["d_nope"], p["d_rope"]
+    if out_csa is None:
+        out_csa = empty_store(LAYOUT_SPLIT, L // m, dn, dr, dev)
+    if out_hca is None:
+        out_hca = empty_store(LAYOUT_SPLIT, L // mp, dn, dr, dev)
+    csa_compress(t["raw"], 0, t["logits_csa"], t["bias_csa"], m, w, 0, L // m, out_csa, stream=stream)
+    hca_compress(t["raw"], 0, t["logits_hca"], t["bias_hca"], mp, 0, L // mp, out_hca, stream=stream)
+    return out_csa, out_hca
+
+
+def chunked_prefill(case, ws=None):
+    """Chunked prefill for S sequences: compress each chunk into the sequence's
+    caches (CSA with a w-m row halo from the prefix), index every chunk query,
+    then CSA and HCA attention for all queries."""
+    p, t = case.params, case.t
+    dev = t["raw"].device
+    ws = ws or Workspace(dev)
+    S, chunk, m, w, mp, W, k = p["S"], p["chunk"], p["m"], p["w"], p["m_prime"], p["W"], p["topk"]
+    dn, dr = p["d_nope"], p["d_rope"]
+    csa, hca = split_store(t, "csa"), split_store(t, "hca")
+    rows = W + chunk
+    raw = t["raw"].view(S, rows, -1)
+    lc = t["logits_csa"].view(S, rows, -1)
+    lh = t["logits_hca"].view(S, rows, -1)
+    for b, P in enumerate(p["prefixes"]):
+        first_pos = P - W
+        csa_compress(raw[b], first_pos, lc[b], t["bias_csa"], m, w, P // m, chunk // m, csa,
+                     out_row0=p["csa_row_begin"][b] + P // m)
+        hca_compress(raw[b], first_pos, lh[b], t["bias_hca"], mp, P // mp, chunk // mp, hca,
+                     out_row0=p["hca_row_begin"][b] + P // mp)
+    crb = _i64(p["csa_row_begin"], dev)
+    hrb = _i64(p["hca_row_begin"], dev)
+    wrb = _i64(p["win_row_begin"], dev)
+    wp0 = _i64(p["win_pos0"], dev)
+    max_c = max((P + chunk) // m for P in p["prefixes"])
+    max_h = max((P + chunk) // mp for P in p["prefixes"])
+    idx = index_topk(t["q_idx"], t["w_idx"], t["k_idx"], crb, t["q_seq"], t["q_pos"], max_c, m, k, ws,
+                     q_idx_scale=t["q_idx_scale"], k_idx_scale=t["k_idx_scale"])
+    win = Store.dense(t["raw"], dn, dr)
+    scale = 1.0 / math.sqrt(dn + dr)
+    q = t["q"].view(torch.bfloat16)
+    o_c, l_c = csa_attn(q, csa, crb, idx, win, wrb, wp0, W, t["q_seq"], t["q_pos"], scale, ws)
+    o_h, l_h = hca_attn(q, hca, hrb, mp, max_h, win, wrb, wp0, W, t["q_seq"], t["q_pos"], scale, ws)
+    return dict(csa=csa, hca=hca, idx=idx, o_csa=o_c, lse_csa=l_c, o_hca=o_h, lse_hca=l_h)

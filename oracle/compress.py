@@ -65,13 +65,14 @@ def compress(x, z, beta, m, w, first_entry, count, first_pos=0):
 
 
 def pow2_scale(amax):
-    """Smallest power of two s with amax <= 448 * s (1 where amax == 0).
+    """Smallest power of two s = 2**e with amax <= 448 * s and e >= -126
+    (1 where amax == 0).
 
     Per-entry scale of the FP8 part of a split entry (a reading: the pages
-    name FP8 but no scale granularity)."""
+    name FP8 but no scale granularity). The floor keeps s a normal float32."""
     amax = np.asarray(amax, dtype=np.float64)
     mant, ex = np.frexp(amax)                      # amax = mant * 2**ex, mant in [0.5, 1)
-    e = ex - 9 + (mant > 0.875)                    # 448 = 0.875 * 2**9
+    e = np.maximum(ex - 9 + (mant > 0.875), -126)  # 448 = 0.875 * 2**9
     s = np.ldexp(1.0, e)
     return np.where(amax == 0, 1.0, s)
 

@@ -1,0 +1,144 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before anything is enqueued
+(no GPU is needed: validation never touches device memory)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hca.h")
+
+hca = pytest.importorskip("long_context_attention_hca_amd", reason="libhca.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*([A-Za-z_]\w*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"csa_compress", "hca_compress", "lightning_index_topk", "csa_sparse_mqa_attn",
+            "hca_dense_mqa_attn"} <= set(names)
+    lib = ctypes.CDLL(hca.library_path)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version_and_status_strings():
+    assert hca.abi_version() == 1
+    for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small")]:
+        assert hca._status_string(code) == text
+
+
+# fake, never-dereferenced device addresses (16-byte aligned)
+P = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(16)]
+
+
+def store(layout=2, d_nope=448, d_rope=64, n_rows=100, row_stride=448, rope_stride=64, data=None, reserved=0):
+    return hca._StoreC(layout, d_nope, d_rope, reserved, n_rows, data if data is not None else 0x9000000,
+                       row_stride, 0xA000000, 0xB000000, rope_stride)
+
+
+def compress_call(**kw):
+    a = dict(raw=P[0], dt=1, rs=512, n_rows=100, first_pos=0, logits=P[1], lrs=512, lcs=1, bias=P[2], m=4, w=8,
+             fe=0, ne=24, out=store(), row0=0)
+    a.update(kw)
+    return hca._csa_compress(a["raw"], a["dt"], a["rs"], a["n_rows"], a["first_pos"], a["logits"], a["lrs"],
+                             a["lcs"], a["bias"], a["m"], a["w"], a["fe"], a["ne"], ctypes.byref(a["out"]),
+                             a["row0"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(raw=None), -1, "NULL"),
+    (dict(dt=3), -2, "raw dtype"),
+    (dict(m=0), -1, "m <= w"),
+    (dict(w=2), -1, "m <= w"),
+    (dict(ne=26), -1, "raw rows do not cover"),          # entries 0..25 need rows up to 103
+    (dict(first_pos=1, fe=1, ne=2), -1, "raw rows do not cover"),   # entry 1 reads position 0
+    (dict(out=store(n_rows=10)), -1, "output rows"),
+    (dict(lcs=2), -1, "logit_col_stride"),
+    (dict(raw=ctypes.c_void_p(0x100008)), -1, "aligned"),
+    (dict(rs=500), -1, "raw_row_stride"),
+    (dict(out=store(d_nope=444, d_rope=68, rope_stride=72)), -1, "multiples of 8"),
+    (dict(out=store(reserved=1)), -1, "reserved"),
+    (dict(out=store(layout=7)), -1, "unknown layout"),
+    (dict(out=store(row_stride=440)), -1, "row_stride"),
+])
+def test_compress_rejects_bad_arguments(kw, status, msg):
+    assert compress_call(**kw) == status
+    assert msg in hca._last_error().decode()
+
+
+def test_compress_offsets_with_halo_pass_validation_then_need_a_gpu():
+    # entries 5..12 read positions 16..51: rows 16.. suffice; the call then fails only at launch time
+    r = compress_call(first_pos=16, n_rows=36, fe=5, ne=8)
+    if r == -4:
+        assert "launch" in hca._last_error().decode()
+    else:
+        assert r == 0
+
+
+def index_call(**kw):
+    a = dict(q=P[0], qs=P[1], w=P[2], H=4, d=64, dt=3, k_idx=P[3], ks=P[4], k_rows=1000, krb=P[5], qseq=P[6],
+             qpos=P[7], nq=4, mv=1000, m=4, k=64, out=P[8], ws=P[9], wsb=1 << 30)
+    a.update(kw)
+    return hca._index(a["q"], a["qs"], a["w"], a["H"], a["d"], a["dt"], a["k_idx"], a["ks"], a["k_rows"], a["krb"],
+                      a["qseq"], a["qpos"], a["nq"], a["mv"], a["m"], a["k"], a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(qs=None), -1), (dict(d=128), -2), (dict(H=9), -2), (dict(H=0), -2),
+    (dict(k=0), -1), (dict(k=4096), -1), (dict(m=0), -1), (dict(dt=2), -2), (dict(wsb=100), -3),
+    (dict(ws=None), -3), (dict(k_idx=ctypes.c_void_p(0x100004)), -1),
+])
+def test_index_rejects_bad_arguments(kw, status):
+    assert index_call(**kw) == status
+
+
+def test_index_workspace_is_monotone_and_batches():
+    one = hca.lightning_index_topk_workspace(1, 262144, 1024)
+    four = hca.lightning_index_topk_workspace(4, 262144, 1024)
+    assert one > 262144 * 12 and four > 3 * one
+    assert index_call(nq=0) == 0                    # nothing to do
+    r = index_call(wsb=one)                         # enough for one query at a time
+    assert r in (0, -4)
+
+
+def attn_call(csa=True, **kw):
+    a = dict(q=P[0], qdt=1, nq=4, H=64, cache=store(), crb=P[1], idx=P[2], k=64, mp=128, mv=100,
+             win=store(), wrb=P[3], wp0=P[4], W=128, qseq=P[5], qpos=P[6], scale=0.04, o=P[7], odt=1, lse=P[8],
+             ws=P[9], wsb=1 << 30)
+    a.update(kw)
+    if csa:
+        return hca._csa_attn(a["q"], a["qdt"], a["nq"], a["H"], ctypes.byref(a["cache"]), a["crb"], a["idx"], a["k"],
+                             ctypes.byref(a["win"]), a["wrb"], a["wp0"], a["W"], a["qseq"], a["qpos"], a["scale"],
+                             a["o"], a["odt"], a["lse"], a["ws"], a["wsb"], None)
+    return hca._hca_attn(a["q"], a["qdt"], a["nq"], a["H"], ctypes.byref(a["cache"]), a["crb"], a["mp"], a["mv"],
+                         ctypes.byref(a["win"]), a["wrb"], a["wp0"], a["W"], a["qseq"], a["qpos"], a["scale"],
+                         a["o"], a["odt"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("csa", [True, False])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(H=0), -1), (dict(W=-1), -1), (dict(scale=float("inf")), -1),
+    (dict(H=40), -2),                                        # MFMA path needs multiples of 16 heads
+    (dict(qdt=0), -2),                                       # fp32 q with split stores
+    (dict(cache=store(layout=0, d_nope=448, d_rope=64, row_stride=512)), -2),
+    (dict(win=store(d_nope=384, d_rope=128, rope_stride=128)), -1),
+    (dict(cache=store(d_nope=192, d_rope=64)), -1),           # widths differ from the window
+    (dict(wsb=16), -3),
+])
+def test_attention_rejects_bad_arguments(csa, kw, status):
+    assert attn_call(csa, **kw) == status
+
+
+def test_attention_workspace_policy():
+    # decode: few queries -> split-K partials; prefill: many queries -> no workspace
+    assert hca.mqa_attn_workspace(1, 4, 64, 512, 8192 + 128) > 0
+    assert hca.mqa_attn_workspace(1, 24576, 64, 512, 2048 + 128) == 0
+    assert hca.mqa_attn_workspace(0, 16, 16, 192, 64 + 128) > 0

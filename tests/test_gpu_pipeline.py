@@ -1,0 +1,189 @@
+"""GPU parity of whole workloads against the oracle: compression, indexer top-k
+and CSA/HCA attention, at sizes the oracle finishes in seconds and at the full
+benchmark sizes (sampled where the oracle must go entry by entry)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import compress as OC
+from oracle import pipeline as OP
+from tests._common import (case_numpy, check_attention, check_bf16_entries, check_f32_entries, check_idx,
+                           check_split_entries, np_, tie_margin_ok, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def W():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_attention_hca_amd import workloads
+    return workloads
+
+
+def _tie_free_tiny(seed, **kw):
+    for s in range(seed, seed + 10):
+        c = synth.tiny_fp32(seed=s, **kw)
+        a = case_numpy(c)
+        p = c.params
+        ok = all(tie_margin_ok(a["q_idx"][i].astype(np.float64), a["w_idx"][i].astype(np.float64),
+                               a["k_idx"].astype(np.float64), (int(t) + 1) // p["m"], p["topk"])
+                 for i, t in enumerate(a["q_pos"]))
+        if ok:
+            return c, a
+    raise AssertionError("no tie-free draw")
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(L=1000, n_queries=7, topk=64)])
+def test_tiny_fp32_pipeline(W, kw):
+    _say(f"tiny_fp32 {kw}")
+    c, a = _tie_free_tiny(1001, **kw)
+    p = c.params
+    ref = OP.tiny_fp32(p, a)
+    got = W.tiny_fp32(to_device(c))
+    torch.cuda.synchronize()
+    check_f32_entries(np_(got["csa"].data), ref["y_csa"], ref["yabs_csa"], "csa entries")
+    check_f32_entries(np_(got["hca"].data), ref["y_hca"], ref["yabs_hca"], "hca entries")
+    check_idx(np_(got["idx"]), np.stack(ref["idx"]), "top-k")
+    check_attention(np_(got["o_csa"]), np_(got["lse_csa"]), np.stack(ref["o_csa"]), np.stack(ref["lse_csa"]),
+                    "fp32", "csa attention")
+    check_attention(np_(got["o_hca"]), np_(got["lse_hca"]), np.stack(ref["o_hca"]), np.stack(ref["lse_hca"]),
+                    "fp32", "hca attention")
+
+
+def _decode_bf16_case(B, L, topk, dev="cpu"):
+    for s in range(1002, 1012):
+        c = synth.decode_bf16(seed=s, B=B, L=L, topk=topk, device=dev)
+        a = case_numpy(c, keys={"q_idx", "w_idx", "k_idx"})
+        n_c = L // 4
+        from oracle.codecs import decode_bf16
+        if all(tie_margin_ok(decode_bf16(a["q_idx"][b].view(np.uint16)), a["w_idx"][b].astype(np.float64),
+                             decode_bf16(a["k_idx"][b * n_c:(b + 1) * n_c].view(np.uint16)), n_c, topk)
+               for b in range(B)):
+            return c
+    raise AssertionError("no tie-free draw")
+
+
+@pytest.mark.parametrize("B,L,topk,seqs", [(3, 8192, 512, [0, 1, 2]), (8, 131072, 512, [0, 7])])
+def test_decode_bf16(W, B, L, topk, seqs):
+    _say(f"decode_bf16 B={B} L={L}")
+    c = _decode_bf16_case(B, L, topk, dev="cuda" if L > 8192 else "cpu")
+    a = case_numpy(c)
+    ref = OP.decode_bf16(c.params, a, seqs)
+    got = W.decode_bf16(to_device(c))
+    torch.cuda.synchronize()
+    p = c.params
+    n_c, n_h = L // p["m"], L // p["m_prime"]
+    idx = np_(got["idx"])
+    csa_rows = np_(got["csa"].data)
+    hca_rows = np_(got["hca"].data)
+    o_c, l_c, o_h, l_h = (np_(got[k]).astype(np.float64) if k.startswith("lse") else
+                          np_(got[k].float()) for k in ("o_csa", "lse_csa", "o_hca", "lse_hca"))
+    for b in seqs:
+        r = ref[b]
+        check_idx(idx[b], r["idx"], f"top-k seq {b}")
+        sel = [j for j in r["idx"] if j >= 0]
+        ys = np.stack([r["csa_y"][j] for j in sel])
+        ya = np.stack([r["csa_yabs"][j] for j in sel])
+        check_bf16_entries(csa_rows[b * n_c + np.array(sel)], ys, f"csa entries seq {b}", ya)
+        check_bf16_entries(hca_rows[b * n_h:(b + 1) * n_h], r["y_hca"], f"hca entries seq {b}", r["yabs_hca"])
+        check_attention(o_c[b], l_c[b], r["o_csa"], r["lse_csa"], "low", f"csa attention seq {b}")
+        check_attention(o_h[b], l_h[b], r["o_hca"], r["lse_hca"], "low", f"hca attention seq {b}")
+
+
+@pytest.mark.parametrize("B,L,seqs", [(3, 1 << 16, [0, 1, 2]), (4, 1 << 20, [0, 1, 2, 3])])
+def test_decode_1m(W, B, L, seqs):
+    _say(f"decode_1m B={B} L={L}")
+    c = synth.decode_1m(seed=1003, B=B, L=L, device="cuda")
+    run = W.Decode1M(c)
+    run.step()
+    torch.cuda.synchronize()
+    a = case_numpy(c)
+    idx = np_(run.idx)
+    o_c, o_h = np_(run.o_csa.float()), np_(run.o_hca.float())
+    l_c, l_h = np_(run.lse_csa), np_(run.lse_hca)
+    for b in seqs:
+        r = OP.decode_1m_query(c.params, a, b)
+        check_idx(idx[b], r["idx"], f"top-k seq {b}")
+        check_attention(o_c[b], l_c[b], r["o_csa"], r["lse_csa"], "low", f"csa attention seq {b}")
+        check_attention(o_h[b], l_h[b], r["o_hca"], r["lse_hca"], "low", f"hca attention seq {b}")
+
+
+@pytest.mark.parametrize("L", [4096 + 128 * 3, 1 << 20])
+def test_compression_split(W, L):
+    _say(f"compression L={L}")
+    c = synth.compression(seed=1004, L=L, device="cuda")
+    csa, hca = W.compress_1m(c)
+    torch.cuda.synchronize()
+    p = c.params
+    m, w, mp, dn, dr = p["m"], p["w"], p["m_prime"], p["d_nope"], p["d_rope"]
+    n_c, n_h = L // m, L // mp
+    rng = np.random.default_rng(0)
+    cj = np.unique(np.concatenate([[0, 1, 2, n_c - 1], rng.integers(0, n_c, 200)]))
+    hj = np.unique(np.concatenate([[0, n_h - 1], rng.integers(0, n_h, 12)]))
+    from oracle.codecs import decode_bf16
+    raw = c.t["raw"]
+    for name, js, mm, ww, lg, bias, st in (("csa", cj, m, w, "logits_csa", "bias_csa", csa),
+                                           ("hca", hj, mp, mp, "logits_hca", "bias_hca", hca)):
+        ys, ya = [], []
+        for j in js:
+            lo, hi = max(0, j * mm - (ww - mm)), (j + 1) * mm
+            x = decode_bf16(np_(raw[lo:hi]).view(np.uint16))
+            z = decode_bf16(np_(c.t[lg][lo:hi]).view(np.uint16))
+            ys.append(OC.compress(x, z, np_(c.t[bias]), mm, ww, int(j), 1, first_pos=lo)[0])
+            ya.append(OC.compress(np.abs(x), z, np_(c.t[bias]), mm, ww, int(j), 1, first_pos=lo)[0])
+        ys, ya = np.stack(ys), np.stack(ya)
+        check_split_entries(np_(st.data)[js], np_(st.scale)[js], np_(st.rope)[js], ys, dn, f"{name} entries", ya)
+
+
+@pytest.mark.parametrize("prefixes,chunk,nsample", [((4096, 8192, 16384), 512, 24), ((32768, 131072, 262144), 8192, 6)])
+def test_chunked_prefill(W, prefixes, chunk, nsample):
+    _say(f"prefill prefixes={prefixes} chunk={chunk}")
+    c = synth.chunked_prefill(seed=1005, prefixes=prefixes, chunk=chunk, device="cuda")
+    a_in = case_numpy(c, keys={"raw", "logits_csa", "logits_hca", "bias_csa", "bias_hca", "csa_nope", "csa_scale",
+                               "csa_rope", "hca_nope", "hca_scale", "hca_rope", "k_idx", "k_idx_scale", "q_seq",
+                               "q_pos"})
+    got = W.chunked_prefill(c)
+    torch.cuda.synchronize()
+    p = c.params
+    S = p["S"]
+    rng = np.random.default_rng(1)
+    picks = []
+    for b in range(S):
+        base = b * chunk
+        picks += [base, base + 1, base + chunk - 1] + list(base + rng.integers(0, chunk, nsample - 3))
+    picks = sorted(set(picks))
+    t = c.t
+    a = dict(a_in)
+    for k in ("q", "q_idx", "q_idx_scale", "w_idx"):
+        rows = np_(t[k][picks])
+        a[k] = {qi: rows[n] for n, qi in enumerate(picks)}
+    chunk_ent = {b: OP.prefill_chunk_entries(p, a, b) for b in range(S)}
+    idx = np_(got["idx"])
+    m, mp, dn = p["m"], p["m_prime"], p["d_nope"]
+    # the chunk's compressed entries
+    for b, P in enumerate(prefixes):
+        y_c, _, y_h, _, ya_c, ya_h = chunk_ent[b]
+        r0 = p["csa_row_begin"][b] + P // m
+        rows = np.arange(r0, r0 + chunk // m)
+        st = got["csa"]
+        check_split_entries(np_(st.data)[rows], np_(st.scale)[rows], np_(st.rope)[rows], y_c, dn, f"csa chunk {b}", ya_c)
+        r0 = p["hca_row_begin"][b] + P // mp
+        rows = np.arange(r0, r0 + chunk // mp)
+        st = got["hca"]
+        check_split_entries(np_(st.data)[rows], np_(st.scale)[rows], np_(st.rope)[rows], y_h, dn, f"hca chunk {b}", ya_h)
+    o_c, l_c = np_(got["o_csa"][picks].float()), np_(got["lse_csa"][picks])
+    o_h, l_h = np_(got["o_hca"][picks].float()), np_(got["lse_hca"][picks])
+    for n, qi in enumerate(picks):
+        r = OP.prefill_query(p, a, qi, lambda b: chunk_ent[b][1], lambda b: chunk_ent[b][3])
+        check_idx(idx[qi], r["idx"], f"top-k query {qi}")
+        check_attention(o_c[n], l_c[n], r["o_csa"], r["lse_csa"], "low", f"csa attention query {qi}")
+        check_attention(o_h[n], l_h[n], r["o_hca"], r["lse_hca"], "low", f"hca attention query {qi}")

@@ -128,6 +128,7 @@ def test_pow2_scale_is_the_smallest_power_of_two_covering_448():
     assert np.all(amax <= 448 * s) and np.all(amax > 224 * s)
     assert np.array_equal(C.pow2_scale(448.0 * 2.0 ** np.arange(-5, 5)), 2.0 ** np.arange(-5, 5))
     assert C.pow2_scale(np.array([0.0]))[0] == 1.0
+    assert C.pow2_scale(np.array([1e-40]))[0] == 2.0 ** -126           # floor: a normal float32
 
 
 def test_split_encoding_error_within_half_an_ulp():
