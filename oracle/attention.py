@@ -86,5 +86,6 @@ def hca(q, t, entries, m_prime, raw, W, scale):
 
 def _rows(raw, positions):
     if callable(raw):
-        return np.asarray(raw(positions), np.float64).reshape(len(positions), -1)
+        r = np.asarray(raw(positions), np.float64)
+        return r if r.ndim == 2 else r.reshape(len(positions), -1)
     return np.asarray(raw, np.float64)[positions]

@@ -102,3 +102,17 @@ def test_lse_merge_of_any_partition():
 def test_empty_set():
     o, lse = A.attend(np.ones((2, 3)), np.zeros((0, 3)), 1.0)
     assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_window_store_as_callable_including_empty_window():
+    x, q, sc = _setup(seed=7)
+    ent = C.compress(x, np.zeros_like(x), np.zeros((1, x.shape[1])), 1, 1, 0, len(x))
+    rows = lambda pos: x[np.asarray(pos)]
+    for W in (0, 1, 6):
+        a = A.csa(q, 30, ent, np.arange(20), rows, W, sc)
+        b = A.csa(q, 30, ent, np.arange(20), x, W, sc)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # W = 0 with the first 20 entries only: plain attention over them
+    o, lse = A.csa(q, 30, ent, np.arange(20), rows, 0, sc)
+    ro, rl = _sdpa(q, x[:20], sc)
+    assert np.allclose(o, ro, atol=1e-13) and np.allclose(lse, rl, atol=1e-13)
