@@ -30,7 +30,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int ensure_init(const char* fn) {
   static std::once_flag once;
   static hipError_t err = hipSuccess;
-  std::call_once(once, [] { err = hca::attention_init(); });
+  std::call_once(once, [] {
+    err = hca::attention_init();
+    if (err == hipSuccess) err = hca::index_init();
+  });
   if (err != hipSuccess) {
     g_last_error = std::string(fn) + ": HIP init failed: " + hipGetErrorString(err);
     return HCA_ERR_HIP;
@@ -138,11 +141,8 @@ int compress_impl(const char* fn, const void* raw, int32_t raw_dtype, int64_t ra
   return launched(fn, hca::launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 
-constexpr size_t kWsSlack = 1024;
 
-size_t index_ws(int64_t nq, int64_t max_visible) {
-  return kWsSlack + (size_t)nq * hca::index_ws_per_query(max_visible);
-}
+size_t index_ws(int64_t nq, int64_t max_visible) { return hca::index_ws_layout(nq, max_visible, nullptr, nullptr); }
 
 uint8_t* align256(uint8_t* p) { return reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255)); }
 
@@ -267,23 +267,17 @@ HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scal
   if (max_visible > (int64_t)INT32_MAX - 1) return fail(HCA_ERR_INVALID_ARG, fn, "max_visible too large");
   if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(HCA_ERR_INVALID_ARG, fn, "q_idx/k_idx not 16-byte aligned");
   if (nq == 0) return HCA_OK;
-  const size_t per_q = hca::index_ws_per_query(max_visible);
-  if (!ws || ws_bytes < kWsSlack + per_q) return fail(HCA_ERR_WORKSPACE, fn, "workspace too small");
-  const int64_t batch = std::min<int64_t>(nq, (int64_t)((ws_bytes - kWsSlack) / per_q));
-  const int64_t mv = (max_visible + 63) / 64 * 64;
+  if (!ws || ws_bytes < index_ws(1, max_visible)) return fail(HCA_ERR_WORKSPACE, fn, "workspace too small");
+  int64_t batch = nq;
+  while (batch > 1 && index_ws(batch, max_visible) > ws_bytes) batch = std::max<int64_t>(1, batch / 2);
   const int64_t q_row = idx_dtype == HCA_MXFP4 ? (int64_t)n_idx_heads * d_idx / 2
                                                : (int64_t)n_idx_heads * d_idx * (idx_dtype == HCA_F32 ? 4 : 2);
+  int st = ensure_init(fn);
+  if (st != HCA_OK) return st;
   for (int64_t q0 = 0; q0 < nq; q0 += batch) {
     const int64_t nb = std::min<int64_t>(batch, nq - q0);
-    uint8_t* p = align256(static_cast<uint8_t*>(ws));
     hca::IndexArgs a;
-    a.scores = reinterpret_cast<float*>(p);
-    p = align256(p + (size_t)nb * mv * 4);
-    a.cand = reinterpret_cast<uint64_t*>(p);
-    p = align256(p + (size_t)nb * mv * 8);
-    a.hist = reinterpret_cast<uint32_t*>(p);
-    p = align256(p + (size_t)nb * hca::kHistBins * 4);
-    a.counters = reinterpret_cast<uint32_t*>(p);
+    hca::index_ws_layout(nb, max_visible, ws, &a);
     a.q = static_cast<const uint8_t*>(q_idx) + q0 * q_row;
     a.q_scale = idx_dtype == HCA_MXFP4 ? q_idx_scale + q0 * n_idx_heads * (d_idx / 32) : nullptr;
     a.w = w_idx + q0 * n_idx_heads;

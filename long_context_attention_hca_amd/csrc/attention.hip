@@ -245,27 +245,37 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg,
   const float sl2 = a.scale * kLog2e;
 
   for (int64_t base = lo + (int64_t)wave * kChunk; base < hi; base += 4 * kChunk) {
-    // stage 32 rows as bf16: segment sg = lane + 64*i -> entry sg / 64, dims 8*(sg % 64)
-#pragma unroll 4
-    for (int i = 0; i < kChunk; ++i) {
-      const int e = i, seg = lane;
-      const int64_t r = base + e;
-      bool w = false;
-      const int64_t row = r < hi ? list_row(a, ctx, qi, r, &w) : -1;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (row >= 0) val = load_seg8(w ? a.win : a.cache, row, seg);
-      *reinterpret_cast<uint4*>(lds + e * kRowB + seg * 16) = val;
+    // rows of the chunk: lane e < 32 resolves list position base + e once; the wave then
+    // stages the 32 rows as bf16 (lane = 16-byte segment of dims 8*lane .. +8), 8 rows in flight
+    int64_t myrow = -1;
+    bool mywin = false;
+    if (lane < kChunk) {
+      const int64_t r = base + lane;
+      myrow = r < hi ? list_row(a, ctx, qi, r, &mywin) : -1;
+    }
+    const uint64_t vmask = __ballot(lane < kChunk && myrow >= 0);
+    const uint64_t wmask = __ballot(lane < kChunk && mywin);
+    const int row_lo = (int)(uint32_t)myrow, row_hi = (int)((uint64_t)myrow >> 32);
+#pragma unroll
+    for (int e0 = 0; e0 < kChunk; e0 += 8) {
+      uint4 val[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u;
+        const int64_t row = (int64_t)(((uint64_t)(uint32_t)__shfl(row_hi, e, 64) << 32) |
+                                      (uint64_t)(uint32_t)__shfl(row_lo, e, 64));
+        val[u] = make_uint4(0, 0, 0, 0);
+        if ((vmask >> e) & 1) val[u] = load_seg8(((wmask >> e) & 1) ? a.win : a.cache, row, lane);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(lds + (e0 + u) * kRowB + lane * 16) = val[u];
     }
     // validity of the 8 entries this lane scores: 16mt + 4g + i
     bool vld[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t r = base + 16 * mt + 4 * g + i;
-        bool w;
-        vld[mt][i] = r < hi && list_row(a, ctx, qi, r, &w) >= 0;
-      }
+      for (int i = 0; i < 4; ++i) vld[mt][i] = (vmask >> (16 * mt + 4 * g + i)) & 1;
     wave_lds_sync();
 
     // S^T = K Q^T
@@ -389,44 +399,337 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg,
 }
 
 // ---------------------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials. grid = (H, nq), 128 threads.
+// MFMA path for split stores (FP8 E4M3 non-RoPE dims + power-of-two scale + bf16 RoPE dims,
+// 448 + 64), cache and window alike. Rows stay FP8 in LDS (half the bytes of bf16 rows):
+//  * a wave stages its 32-entry chunk with global_load_lds (16 bytes per lane straight into
+//    LDS, no VGPRs): 19 instructions fill 32 rows of 592 bytes (448 FP8 + 128 bf16 + 16 pad);
+//  * S^T = K Q^T: FP8 K operands are converted to bf16 with scale 1 after the LDS read; the
+//    entry's scale multiplies the FP8 part of the score, the RoPE part is added unscaled;
+//  * O^T += V^T P^T: V^T for the FP8 dims comes from ds_read_b64_tr_b8 transpose reads (8 entries
+//    of one dim per lane), the entry scales are folded into P (exact: powers of two); the RoPE
+//    dims use ds_read_b64_tr_b16 with the unscaled P;
+//  * each wave double-buffers: the DMA of its next chunk is in flight while it computes the
+//    current one (the waits on the DMA are explicit: s_waitcnt before a buffer is read or
+//    refilled), so 4 waves x 19 KB per CU are always on their way from HBM.
+constexpr int kNope = 448;
+constexpr int kRope = 64;
+constexpr int kRowF8 = 592;                    // 448 + 128 + 16 pad
+constexpr int kBufF8 = 19 * 1024;              // 32 rows + the tail of the 19th load
+constexpr int kWaveF8 = 2 * kBufF8;            // double buffer
+constexpr int kFp8Lds = 4 * kWaveF8;
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = fp8x2_to_bf16x2(lo, 1.0f, false), b = fp8x2_to_bf16x2(lo, 1.0f, true);
+  const bf16x2 c = fp8x2_to_bf16x2(hi, 1.0f, false), d = fp8x2_to_bf16x2(hi, 1.0f, true);
+  uint4 u;
+  u.x = __builtin_bit_cast(uint32_t, a); u.y = __builtin_bit_cast(uint32_t, b);
+  u.z = __builtin_bit_cast(uint32_t, c); u.w = __builtin_bit_cast(uint32_t, d);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Rows of the 32 list positions base .. base+31 (lane e < 32 holds entry e): row (-1 if
+// none), which store, and the entry scale (its load is left in flight).
+struct ChunkRows {
+  int row;
+  float esc;
+  uint64_t vmask, wmask;
+};
+
+__device__ __forceinline__ ChunkRows chunk_rows(const AttnArgs& a, const QueryCtx& ctx, int qi, int64_t base,
+                                                int64_t hi, int lane) {
+  ChunkRows cr;
+  bool win = false;
+  int64_t row = -1;
+  if (lane < kChunk) {
+    const int64_t r = base + lane;
+    row = r < hi ? list_row(a, ctx, qi, r, &win) : -1;
+  }
+  cr.row = (int)row;
+  cr.esc = row >= 0 ? (win ? a.win.scale : a.cache.scale)[row] : 0.f;
+  cr.vmask = __ballot(lane < kChunk && row >= 0);
+  cr.wmask = __ballot(lane < kChunk && win);
+  return cr;
+}
+
+// 19 global_load_lds of 16 bytes fill the 32 rows of 592 bytes (FP8 dims, RoPE dims, pad).
+__device__ __forceinline__ void chunk_dma(const AttnArgs& a, const ChunkRows& cr, uint8_t* buf, int lane) {
+  const uint8_t* dummy = static_cast<const uint8_t*>(a.q);
+#pragma unroll 1
+  for (int i = 0; i < 19; ++i) {
+    const int b = 1024 * i + 16 * lane;
+    const int e = b / kRowF8;
+    const int off = b - e * kRowF8;
+    const int ee = e < kChunk ? e : kChunk - 1;
+    const int row = __shfl(cr.row, ee, 64);
+    const bool valid = e < kChunk && ((cr.vmask >> ee) & 1);
+    const StoreView& v = ((cr.wmask >> ee) & 1) ? a.win : a.cache;
+    const uint8_t* src = dummy;
+    if (valid && off < kNope) src = static_cast<const uint8_t*>(v.data) + (int64_t)row * v.row_stride + off;
+    else if (valid && off < kNope + 2 * kRope)
+      src = static_cast<const uint8_t*>(v.rope) + ((int64_t)row * v.rope_stride) * 2 + (off - kNope);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + 1024 * i), 16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, int total) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= total) return;
+  const int hg = id % n_hg;
+  const int rest = id / n_hg;
+  const int s = rest % a.n_split;
+  const int qi = rest / a.n_split;
+  const int H = a.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int head = hg * 16 + c;
+  uint8_t* wbuf = smem + wave * kWaveF8;
+
+  const QueryCtx ctx = query_ctx(a, qi);
+  const int64_t N = ctx.n_c + ctx.n_w;
+  const int64_t lo = (int64_t)s * a.per_split;
+  const int64_t hi = min<int64_t>(N, lo + a.per_split);
+
+  bf16x8 qv[kD / 32];
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * H + head) * kD + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < kD / 32; ++ks)
+    qv[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * ks));
+
+  f32x4 O[kD / 16];
+#pragma unroll
+  for (int i = 0; i < kD / 16; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale * kLog2e;
+
+  int64_t base = lo + (int64_t)wave * kChunk;
+  ChunkRows cur = chunk_rows(a, ctx, qi, base, hi, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (base < hi) chunk_dma(a, cur, wbuf, lane);
+  for (int it = 0; base < hi; ++it, base += 4 * kChunk) {
+    uint8_t* buf = wbuf + (it & 1) * kBufF8;
+    const int64_t nbase = base + 4 * kChunk;
+    ChunkRows nxt = chunk_rows(a, ctx, qi, nbase, hi, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // this chunk's DMA and the next chunk's rows have landed
+    __builtin_amdgcn_wave_barrier();
+    if (nbase < hi) chunk_dma(a, nxt, wbuf + ((it + 1) & 1) * kBufF8, lane);
+    const float esc = cur.esc;
+    const uint64_t vmask = cur.vmask;
+
+    // scores of the 8 entries this lane holds: 16mt + 4g + i
+    float escl[2][4];
+    bool vld[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 16 * mt + 4 * g + i;
+        escl[mt][i] = __shfl(esc, e, 64);
+        vld[mt][i] = (vmask >> e) & 1;
+      }
+    f32x4 st[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 an = {0.f, 0.f, 0.f, 0.f}, ar = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* rowp = buf + (16 * mt + c) * kRowF8;
+#pragma unroll
+      for (int ks = 0; ks < kNope / 32; ++ks) {
+        const uint2 w8 = *reinterpret_cast<const uint2*>(rowp + 32 * ks + 8 * g);
+        an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(w8.x, w8.y), qv[ks], an, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kRope / 32; ++ks) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowp + kNope + 64 * ks + 16 * g));
+        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[kNope / 32 + ks], ar, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[mt][i] = fmaf(escl[mt][i], an[i], ar[i]);
+    }
+    float sv[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[4 * mt + i] = vld[mt][i] ? st[mt][i] * sl2 : -INFINITY;
+        cmax = fmaxf(cmax, sv[4 * mt + i]);
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_new = fmaxf(m_run, cmax);
+    const bool none = m_new == -INFINITY;
+    const float corr = none ? 1.f : exp2f(m_run - m_new);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = none ? 0.f : exp2f(sv[i] - m_new);
+      psum += p[i];
+    }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    if (__ballot(corr != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < kD / 16; ++dt) O[dt] *= corr;
+    }
+    // P^T operands, contraction order [4g..4g+3, 16+4g..16+4g+3]; the FP8 one carries the scales
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+    const bf16x8 pbs = __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16x2(p[0] * escl[0][0], p[1] * escl[0][1]), pack_bf16x2(p[2] * escl[0][2], p[3] * escl[0][3]),
+                           pack_bf16x2(p[4] * escl[1][0], p[5] * escl[1][1]), pack_bf16x2(p[6] * escl[1][2], p[7] * escl[1][3])));
+    // FP8 dims: lane 2r + h of group g reads entry K_g[r], dims 16dt + 8h .. +8; lane i then holds
+    // that dim 16dt + i of the 8 entries K_g[0..7]
+    {
+      const int r = c >> 1, hsel = c & 1;
+      const int ent = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
+      const uint8_t* vp = buf + ent * kRowF8 + 8 * hsel;
+#pragma unroll
+      for (int dt = 0; dt < kNope / 16; ++dt) {
+        const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * dt));
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]), pbs, O[dt],
+                                                        0, 0, 0);
+      }
+    }
+    // RoPE dims (bf16): lane 4r + qd of group g reads entry 4g + r (and 16 + 4g + r), dims 4qd .. +4
+    {
+      const int rsel = c >> 2, qd = c & 3;
+      const uint8_t* v0 = buf + (4 * g + rsel) * kRowF8 + kNope + 8 * qd;
+      const uint8_t* v1 = v0 + 16 * kRowF8;
+#pragma unroll
+      for (int dt = 0; dt < kRope / 16; ++dt) {
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * dt));
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * dt));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+        O[kNope / 16 + dt] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, O[kNope / 16 + dt], 0, 0, 0);
+      }
+    }
+    cur = nxt;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // merge the 4 waves through LDS in two halves of 256 dims (16 KB of O per wave each)
+  float* wm = reinterpret_cast<float*>(wbuf);
+  float* wl = wm + 16;
+  float* wo = wl + 16;
+  const int hc = tid >> 4, dl = (tid & 15) * 4;
+  const int hd = hg * 16 + hc;
+  __syncthreads();
+  if (g == 0) { wm[c] = m_run; wl[c] = l_run; }
+  float fw[4], inv = 0.f, lse = -INFINITY;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+      *reinterpret_cast<f32x4*>(wo + c * (kD / 2) + 16 * dt + 4 * g) = O[half * (kD / 32) + dt];
+    __syncthreads();
+    if (half == 0) {
+      float mw[4], M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        mw[w] = reinterpret_cast<const float*>(smem + w * kWaveF8)[hc];
+        M = fmaxf(M, mw[w]);
+      }
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        fw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
+        L += fw[w] * reinterpret_cast<const float*>(smem + w * kWaveF8)[16 + hc];
+      }
+      inv = L > 0.f ? 1.f / L : 0.f;
+      lse = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < kD / 128; ++k) {
+      const int dh = dl + 64 * k;           // dim within the half
+      const int d = half * (kD / 2) + dh;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        acc += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(smem + w * kWaveF8) + 32 + hc * (kD / 2) + dh) * fw[w];
+      acc *= inv;
+      if (a.n_split == 1) {
+        const int64_t oi = ((int64_t)qi * H + hd) * kD + d;
+        if (a.o_dtype == HCA_BF16) {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + oi) =
+              make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + oi) = acc;
+        }
+      } else {
+        const int64_t pi = ((int64_t)qi * a.n_split + s) * H + hd;
+        *reinterpret_cast<f32x4*>(a.part_o + pi * kD + d) = acc;
+      }
+    }
+    __syncthreads();
+  }
+  if ((tid & 15) == 0) {
+    if (a.n_split == 1) a.lse[(int64_t)qi * H + hd] = lse;
+    else a.part_lse[((int64_t)qi * a.n_split + s) * H + hd] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Log-sum-exp merge of the split partials. grid = (H, nq), 128 threads; D % 4 == 0.
 __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
   __shared__ float wts[1024];
-  __shared__ float s_m, s_inv, s_lse;
+  __shared__ float s_inv, s_lse;
   const int h = blockIdx.x, qi = blockIdx.y, tid = threadIdx.x;
   const int S = a.n_split, H = a.H, D = a.D;
-  const float* pl = a.part_lse + (int64_t)qi * S * H + h;
-  if (tid == 0) {
+  if (tid < 64) {
+    const float* pl = a.part_lse + (int64_t)qi * S * H + h;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pl[(int64_t)s * H]);
+    for (int s = tid; s < S; s += 64) M = fmaxf(M, pl[(int64_t)s * H]);
+    M = wave_max(M);
     float L = 0.f;
-    for (int s = 0; s < S; ++s) {
+    for (int s = tid; s < S; s += 64) {
       const float l = pl[(int64_t)s * H];
       const float wv = (M == -INFINITY || l == -INFINITY) ? 0.f : expf(l - M);
       wts[s] = wv;
       L += wv;
     }
-    s_m = M;
-    s_inv = L > 0.f ? 1.f / L : 0.f;
-    s_lse = L > 0.f ? M + logf(L) : -INFINITY;
+    L = wave_sum(L);
+    if (tid == 0) {
+      s_inv = L > 0.f ? 1.f / L : 0.f;
+      s_lse = L > 0.f ? M + logf(L) : -INFINITY;
+    }
   }
   __syncthreads();
   const float inv = s_inv;
-  for (int d = tid; d < D; d += 128) {
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float wv = wts[s];
-      if (wv != 0.f) acc = fmaf(wv, a.part_o[(((int64_t)qi * S + s) * H + h) * D + d], acc);
-    }
+  const float* po = a.part_o + ((int64_t)qi * S * H + h) * D;
+  const int64_t sstride = (int64_t)H * D;
+  for (int d = tid * 4; d < D; d += 512) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) acc += wts[s] * *reinterpret_cast<const f32x4*>(po + s * sstride + d);
     acc *= inv;
     const int64_t oi = ((int64_t)qi * H + h) * D + d;
-    if (a.o_dtype == HCA_BF16) static_cast<uint16_t*>(a.o)[oi] = (uint16_t)f32_to_bf16_rne(acc);
-    else static_cast<float*>(a.o)[oi] = acc;
+    if (a.o_dtype == HCA_BF16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + oi) =
+          make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + oi) = acc;
+    }
   }
   if (tid == 0) a.lse[(int64_t)qi * H + h] = s_lse;
 }
 
 }  // namespace
+
+// Both stores split with 448 FP8 + 64 bf16 dims, rows addressable with 32-bit indices.
+bool attn_fp8_supported(const StoreView& c, const StoreView& w) {
+  auto ok = [](const StoreView& v) {
+    return v.layout == HCA_LAYOUT_SPLIT && v.d_nope == kNope && v.d_rope == kRope && v.n_rows < (1ll << 31);
+  };
+  return ok(c) && ok(w);
+}
 
 bool attn_mfma_supported(int q_dtype, int o_dtype, const StoreView& c, const StoreView& w, int H, int D) {
   auto ok_store = [](const StoreView& v) {
@@ -454,7 +757,13 @@ void attn_split_policy(int nq, int H, int D, int64_t max_entries, bool mfma, int
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const bool mfma = a.q_dtype == HCA_BF16;
-  if (mfma) {
+  const bool fp8 = mfma && attn_fp8_supported(a.cache, a.win);
+  if (fp8) {
+    const int n_hg = a.H / 16;
+    const int total = a.nq * a.n_split * n_hg;
+    const int grid = (total + 7) / 8 * 8;
+    hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(256), kFp8Lds, s, a, n_hg, total);
+  } else if (mfma) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;
@@ -473,7 +782,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t attention_init() {
-  return hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
+  hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)attn_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kFp8Lds);
 }
 
 }  // namespace hca

@@ -45,11 +45,10 @@ __device__ __forceinline__ int64_t visible_keys(const IndexArgs& a, int qi, int6
   return nv;
 }
 
-__global__ __launch_bounds__(256) void clear_kernel(uint32_t* hist, uint32_t* counters, int nq) {
+// Zeroes n words (the histograms and counters, laid out back to back in the workspace).
+__global__ __launch_bounds__(256) void clear_kernel(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nh = (int64_t)nq * kHistBins;
-  if (i < nh) hist[i] = 0;
-  else if (i < nh + 4 * nq) counters[i - nh] = 0;
+  if (i < n) p[i] = 0;
 }
 
 __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* ghist) {
@@ -182,29 +181,79 @@ __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
   flush_hist(lhist, a.hist + (int64_t)qi * kHistBins);
 }
 
-// Wave-aggregated append: returns this lane's slot (only meaningful where pred is true).
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
-  const uint64_t mask = __ballot(pred);
-  if (mask == 0) return 0;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((long long)mask) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-  base = __shfl(base, leader, 64);
-  return base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+// ---------------------------------------------------------------------------------------
+// Block-wide helpers (blockDim.x = NT, a multiple of 64).
+
+// Exclusive prefix sum of v over the block (thread order); *total gets the block sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds_tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(x, off, 64);
+    if (lane >= off) x += t;
+  }
+  if (lane == 63) lds_tmp[wave] = x;
+  __syncthreads();
+  uint32_t wbase = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t t = lds_tmp[w];
+    wbase += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + x - v;
 }
 
-// grid = (ceil(max(max_visible, k) / 4096), nq).
-__global__ __launch_bounds__(256) void select_kernel(IndexArgs a) {
+// Over counters c[0..n) in LDS (n = 256 * per, per in {1, 4, 8}): the largest index d with
+// sum_{i >= d} c[i] >= rem, and above = sum_{i > d} c[i]. Wave 0 must call it; the result is
+// written to *d_out / *above_out (LDS) by one lane. Requires sum c >= rem >= 1.
+template <int PER>
+__device__ __forceinline__ void find_crossing(const uint32_t* c, uint32_t rem, int* d_out, uint32_t* above_out) {
+  const int lane = threadIdx.x & 63;
+  constexpr int G = 4 * PER;  // counters per lane
+  uint32_t v[G];
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    v[i] = c[G * lane + i];
+    own += v[i];
+  }
+  uint32_t suf = own;  // inclusive suffix sum over lanes lane..63
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += t;
+  }
+  uint32_t nxt = __shfl_down(suf, 1, 64);
+  if (lane == 63) nxt = 0;
+  if (suf >= rem && nxt < rem) {
+    uint32_t acc = nxt;
+    int d = G * lane;
+#pragma unroll
+    for (int i = G - 1; i >= 0; --i) {
+      if (acc + v[i] >= rem) { d = G * lane + i; break; }
+      acc += v[i];
+    }
+    *d_out = d;
+    *above_out = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Classification: each block takes 4096 scores of one query, finds the threshold bin b* of the
+// top-11-bit histogram (the bin holding the k-th largest), appends every entry above b* to the
+// selected list and every entry in b* to the candidate lists, and histograms the candidates'
+// next 11 key bits. grid = (ceil(max(max_visible, k) / 4096), nq), 256 threads.
+__global__ __launch_bounds__(256) void classify_kernel(IndexArgs a) {
   __shared__ uint32_t sh[kHistBins];
   __shared__ uint32_t part[256];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_above;
-  __shared__ int s_last;
-  __shared__ uint32_t s_slot;
-  __shared__ uint64_t s_prefix;
-  __shared__ uint32_t s_rem;
-  __shared__ int s_done;
+  __shared__ uint32_t tmp[8];
+  __shared__ int s_d, s_bin;
+  __shared__ uint32_t s_above, s_above2, s_base[2];
   const int qi = blockIdx.y, tid = threadIdx.x;
   const int K = a.k;
   int64_t rb;
@@ -218,115 +267,252 @@ __global__ __launch_bounds__(256) void select_kernel(IndexArgs a) {
   }
   if (j0 >= nv) return;
 
-  // 1. threshold bin: the largest bin b with sum_{b' >= b} hist[b'] >= K
   const uint32_t* gh = a.hist + (int64_t)qi * kHistBins;
   uint32_t loc = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    sh[tid * 8 + i] = gh[tid * 8 + i];
-    loc += sh[tid * 8 + i];
+    const uint32_t h = gh[tid * 8 + i];
+    sh[tid * 8 + i] = h;
+    loc += h;
   }
   part[tid] = loc;
+  // this block's scores, 16 per thread
+  const float* sc = a.scores + (int64_t)qi * a.max_visible;
+  uint32_t key[kSelBlock / 256];
+#pragma unroll
+  for (int it = 0; it < kSelBlock / 256; ++it) {
+    const int64_t j = j0 + it * 256 + tid;
+    key[it] = j < nv ? float_key(sc[j]) : 0u;
+  }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t acc = 0;
-    int t = 255;
-    for (; t >= 0; --t) {
-      if (acc + part[t] >= (uint32_t)K) break;
-      acc += part[t];
-    }
-    int b = t * 8 + 7;
-    for (; b >= t * 8; --b) {
+  if (tid < 64) find_crossing<1>(part, (uint32_t)K, &s_d, &s_above);
+  __syncthreads();
+  if (tid == s_d) {
+    uint32_t acc = s_above;
+    int b = 8 * tid + 7;
+    for (; b > 8 * tid; --b) {
       if (acc + sh[b] >= (uint32_t)K) break;
       acc += sh[b];
     }
     s_bin = b;
-    s_above = acc;
   }
   __syncthreads();
-  const uint32_t bstar = (uint32_t)s_bin, above = s_above;
-
-  // 2. classify this block's scores
-  uint32_t* cnt = a.counters + (int64_t)qi * 4;  // [0] selected, [1] candidates, [2] done blocks
-  const float* sc = a.scores + (int64_t)qi * a.max_visible;
-  uint64_t* cand = a.cand + (int64_t)qi * a.max_visible;
+  const uint32_t bstar = (uint32_t)s_bin;
+  uint32_t nhi = 0, neq = 0;
+#pragma unroll
   for (int it = 0; it < kSelBlock / 256; ++it) {
     const int64_t j = j0 + it * 256 + tid;
-    const bool valid = j < nv;
-    const uint32_t key = valid ? float_key(sc[j]) : 0u;
-    const uint32_t bin = key >> 21;
-    const bool hi = valid && bin > bstar;
-    const bool eq = valid && bin == bstar;
-    const uint32_t s1 = wave_append(hi, &cnt[0]);
-    if (hi) out[s1] = (int32_t)j;
-    const uint32_t s2 = wave_append(eq, &cnt[1]);
-    if (eq) cand[s2] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+    const uint32_t bin = key[it] >> 21;
+    nhi += (j < nv && bin > bstar);
+    neq += (j < nv && bin == bstar);
   }
-  __threadfence();
-  __syncthreads();
+  uint32_t thi, teq;
+  uint32_t ohi = block_exclusive_scan<256>(nhi, tmp, &thi);
+  uint32_t oeq = block_exclusive_scan<256>(neq, tmp + 4, &teq);
+  uint32_t* cnt = a.counters + (int64_t)qi * 4;
   if (tid == 0) {
-    const uint32_t nblk = (uint32_t)((nv + kSelBlock - 1) / kSelBlock);
-    s_last = atomicAdd(&cnt[2], 1u) == nblk - 1;
+    s_base[0] = thi ? atomicAdd(&cnt[0], thi) : 0u;
+    s_base[1] = teq ? atomicAdd(&cnt[1], teq) : 0u;
   }
+  for (int i = tid; i < kHistBins; i += 256) sh[i] = 0;
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  int32_t* sel = a.sel + (int64_t)qi * kMaxTopK;
+  uint32_t* ck = a.cand_key + (int64_t)qi * a.max_visible;
+  int32_t* ci = a.cand_idx + (int64_t)qi * a.max_visible;
+  ohi += s_base[0];
+  oeq += s_base[1];
+#pragma unroll
+  for (int it = 0; it < kSelBlock / 256; ++it) {
+    const int64_t j = j0 + it * 256 + tid;
+    const uint32_t bin = key[it] >> 21;
+    if (j < nv && bin > bstar) sel[ohi++] = (int32_t)j;
+    if (j < nv && bin == bstar) {
+      ck[oeq] = key[it];
+      ci[oeq] = (int32_t)j;
+      ++oeq;
+      atomicAdd(&sh[(key[it] >> 10) & 2047u], 1u);
+    }
+  }
+  if (teq) flush_hist(sh, a.hist2 + (int64_t)qi * kHistBins);
+}
 
-  // 3. last block: radix-select the remaining `need` among the candidates (unique 64-bit keys)
-  const uint32_t need = (uint32_t)K - above;
-  const uint32_t nc = atomicAdd(&cnt[1], 0u);
-  const volatile uint64_t* vc = cand;
-  if (tid == 0) { s_prefix = 0; s_rem = need; s_done = 0; }
-  __syncthreads();
-  uint64_t thr = 0;
+// Finalisation, one block of 1024 threads per query. With T the 32-bit key of the k-th largest
+// score (found from the second-level histogram and a third-level one over the candidates), the
+// selection is: every entry above T, plus the r lowest-index entries whose key equals T. The
+// selection is assembled in an LDS bitmap over the visible entries and compacted in ascending
+// order. Beyond kBitmapBits visible entries a 64-bit radix select and a bitonic sort are used.
+constexpr int kFinThreads = 1024;
+constexpr int64_t kBitmapBits = 1 << 19;
+
+__host__ __device__ __forceinline__ int64_t bitmap_words(int64_t nv) { return (nv + 31) >> 5; }
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t part[256];
+  __shared__ uint32_t tmp[32];
+  __shared__ int s_d, s_b;
+  __shared__ uint32_t s_above, s_acc, s_cut_word, s_cut_bit;
+  const int qi = blockIdx.x, tid = threadIdx.x;
+  const int K = a.k;
+  int64_t rb;
+  const int64_t nv = visible_keys(a, qi, &rb);
+  if (nv <= K) return;
+  int32_t* out = a.out + (int64_t)qi * K;
+  const uint32_t* cnt = a.counters + (int64_t)qi * 4;
+  const uint32_t above = cnt[0], nc = cnt[1];
+  const int32_t* sel = a.sel + (int64_t)qi * kMaxTopK;
+  const uint32_t* ck = a.cand_key + (int64_t)qi * a.max_visible;
+  const int32_t* ci = a.cand_idx + (int64_t)qi * a.max_visible;
+  const uint32_t rem = (uint32_t)K - above;  // >= 1
+
+  if (nv <= kBitmapBits) {
+    // level 2: next 11 bits of the candidates
+    const uint32_t* g2 = a.hist2 + (int64_t)qi * kHistBins;
+    for (int i = tid; i < kHistBins; i += kFinThreads) h[i] = g2[i];
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t sum = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += h[8 * tid + i];
+      part[tid] = sum;
+    }
+    __syncthreads();
+    if (tid < 64) find_crossing<1>(part, rem, &s_d, &s_above);
+    __syncthreads();
+    if (tid == s_d) {
+      uint32_t acc = s_above;
+      int b = 8 * tid + 7;
+      for (; b > 8 * tid; --b) {
+        if (acc + h[b] >= rem) break;
+        acc += h[b];
+      }
+      s_b = b;
+      s_acc = acc;
+    }
+    __syncthreads();
+    const uint32_t b2 = (uint32_t)s_b, rem2 = rem - s_acc;
+    __syncthreads();
+    // level 3: the last 10 bits of the candidates in (b*, b2)
+    h[tid] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < nc; i += kFinThreads) {
+      const uint32_t k32 = ck[i];
+      if (((k32 >> 10) & 2047u) == b2) atomicAdd(&h[k32 & 1023u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) find_crossing<4>(h, rem2, &s_d, &s_above);
+    __syncthreads();
+    const uint32_t b3 = (uint32_t)s_d, r = rem2 - s_above;  // r >= 1 entries with key == T
+    const uint32_t T = nc ? ((ck[0] >> 21) << 21) | (b2 << 10) | b3 : 0u;
+    // bitmaps: A = selection, B = entries whose key equals T
+    const int64_t nw = bitmap_words(nv);
+    uint32_t* A = dyn;
+    uint32_t* Bm = dyn + nw;
+    for (int64_t i = tid; i < 2 * nw; i += kFinThreads) dyn[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < above; i += kFinThreads) {
+      const int32_t j = sel[i];
+      atomicOr(&A[j >> 5], 1u << (j & 31));
+    }
+    for (uint32_t i = tid; i < nc; i += kFinThreads) {
+      const uint32_t k32 = ck[i];
+      const int32_t j = ci[i];
+      if (k32 > T) atomicOr(&A[j >> 5], 1u << (j & 31));
+      else if (k32 == T) atomicOr(&Bm[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    // the r lowest set bits of B join A: find the word holding the r-th set bit
+    const int64_t per = (nw + kFinThreads - 1) / kFinThreads;
+    const int64_t w0 = tid * per, w1 = min<int64_t>(nw, w0 + per);
+    uint32_t pc = 0;
+    for (int64_t w = w0; w < w1; ++w) pc += __popc(Bm[w]);
+    uint32_t tot;
+    uint32_t before = block_exclusive_scan<kFinThreads>(pc, tmp, &tot);
+    if (before < r && before + pc >= r) {
+      uint32_t acc = before;
+      for (int64_t w = w0; w < w1; ++w) {
+        const uint32_t c = __popc(Bm[w]);
+        if (acc + c >= r) {
+          // the (r - acc)-th set bit of this word
+          uint32_t bits = Bm[w], need = r - acc;
+          int bit = 0;
+          for (int b = 0; b < 32; ++b) {
+            if ((bits >> b) & 1u) {
+              if (--need == 0) { bit = b; break; }
+            }
+          }
+          s_cut_word = (uint32_t)w;
+          s_cut_bit = (uint32_t)bit;
+          break;
+        }
+        acc += c;
+      }
+    }
+    __syncthreads();
+    const uint32_t cw = s_cut_word, cb = s_cut_bit;
+    for (int64_t w = w0; w < w1; ++w) {
+      uint32_t bits = Bm[w];
+      if ((uint32_t)w > cw) bits = 0;
+      else if ((uint32_t)w == cw) bits &= (cb == 31) ? 0xFFFFFFFFu : ((2u << cb) - 1u);
+      A[w] |= bits;
+    }
+    __syncthreads();
+    // compaction in ascending order
+    pc = 0;
+    for (int64_t w = w0; w < w1; ++w) pc += __popc(A[w]);
+    uint32_t pos = block_exclusive_scan<kFinThreads>(pc, tmp, &tot);
+    for (int64_t w = w0; w < w1; ++w) {
+      uint32_t bits = A[w];
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (pos < (uint32_t)K) out[pos] = (int32_t)(w * 32 + b);
+        ++pos;
+      }
+    }
+    return;
+  }
+
+  // Fallback for very long sequences: 64-bit keys (score key << 32 | ~j) of the candidates,
+  // 8-bit radix passes over L2, then a bitonic sort of the k indices.
+  uint64_t prefix = 0, thr = 0;
+  uint32_t rr = rem;
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
-    for (int i = tid; i < 256; i += 256) sh[i] = 0;
+    if (tid < 256) h[tid] = 0;
     __syncthreads();
-    const uint64_t prefix = s_prefix;
-    for (uint32_t i = tid; i < nc; i += 256) {
-      const uint64_t key = vc[i];
+    for (uint32_t i = tid; i < nc; i += kFinThreads) {
+      const uint64_t key = ((uint64_t)ck[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)ci[i]);
       const bool match = pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8));
-      if (match) atomicAdd(&sh[(key >> shift) & 255u], 1u);
+      if (match) atomicAdd(&h[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t acc = 0, rem = s_rem;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (acc + sh[d] >= rem) break;
-        acc += sh[d];
-      }
-      rem -= acc;
-      s_prefix = prefix | ((uint64_t)d << shift);
-      s_rem = rem;
-      s_done = sh[d] == rem;
-    }
+    if (tid < 64) find_crossing<1>(h, rr, &s_d, &s_above);
     __syncthreads();
-    if (s_done) { thr = s_prefix; break; }
+    const int d = s_d;
+    rr -= s_above;
+    prefix |= (uint64_t)d << shift;
+    const bool done = h[d] == rr;
+    __syncthreads();
+    if (done) { thr = prefix; break; }
   }
-  if (tid == 0) s_slot = 0;
+  int32_t* buf = reinterpret_cast<int32_t*>(h);
+  if (tid == 0) s_acc = 0;
   __syncthreads();
-  for (uint32_t i = tid; i < nc; i += 256) {
-    const uint64_t key = vc[i];
-    if (key >= thr) {
-      const uint32_t slot = atomicAdd(&s_slot, 1u);
-      out[above + slot] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
-    }
+  for (uint32_t i = tid; i < above; i += kFinThreads) buf[i] = sel[i];
+  for (uint32_t i = tid; i < nc; i += kFinThreads) {
+    const uint64_t key = ((uint64_t)ck[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)ci[i]);
+    if (key >= thr) buf[above + atomicAdd(&s_acc, 1u)] = ci[i];
   }
-  __threadfence_block();
   __syncthreads();
-
-  // 4. sort the k selected indices ascending (bitonic in LDS, padded with INT_MAX)
   int N = 1;
   while (N < K) N <<= 1;
-  int32_t* buf = reinterpret_cast<int32_t*>(sh);
-  volatile int32_t* vout = out;
-  for (int i = tid; i < N; i += 256) buf[i] = i < K ? vout[i] : 0x7FFFFFFF;
+  for (int i = K + tid; i < N; i += kFinThreads) buf[i] = 0x7FFFFFFF;
   __syncthreads();
   for (int k2 = 2; k2 <= N; k2 <<= 1) {
     for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < N; i += 256) {
+      for (int i = tid; i < N; i += kFinThreads) {
         const int ixj = i ^ jj;
         if (ixj > i) {
           const int32_t x = buf[i], y = buf[ixj];
@@ -337,19 +523,48 @@ __global__ __launch_bounds__(256) void select_kernel(IndexArgs a) {
       __syncthreads();
     }
   }
-  for (int i = tid; i < K; i += 256) out[i] = buf[i];
+  for (int i = tid; i < K; i += kFinThreads) out[i] = buf[i];
 }
 
 }  // namespace
 
-size_t index_ws_per_query(int64_t max_visible) {
+size_t index_ws_layout(int64_t nq, int64_t max_visible, void* ws, IndexArgs* a) {
   const int64_t mv = (max_visible + 63) / 64 * 64;
-  return (size_t)(mv * 4 + mv * 8 + (int64_t)kHistBins * 4 + 16);
+  uintptr_t p = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
+  const uintptr_t p0 = reinterpret_cast<uintptr_t>(ws);
+  auto take = [&](size_t bytes) {
+    const uintptr_t q = p;
+    p = (p + bytes + 255) & ~uintptr_t(255);
+    return reinterpret_cast<void*>(q);
+  };
+  void* scores = take((size_t)nq * mv * 4);
+  void* ckey = take((size_t)nq * mv * 4);
+  void* cidx = take((size_t)nq * mv * 4);
+  void* sel = take((size_t)nq * kMaxTopK * 4);
+  void* hist = take((size_t)nq * kHistBins * 4);
+  void* hist2 = take((size_t)nq * kHistBins * 4);
+  void* counters = take((size_t)nq * 4 * 4);
+  if (a) {
+    a->scores = static_cast<float*>(scores);
+    a->cand_key = static_cast<uint32_t*>(ckey);
+    a->cand_idx = static_cast<int32_t*>(cidx);
+    a->sel = static_cast<int32_t*>(sel);
+    a->hist = static_cast<uint32_t*>(hist);
+    a->hist2 = static_cast<uint32_t*>(hist2);
+    a->counters = static_cast<uint32_t*>(counters);
+  }
+  return (size_t)(p - p0) + 256;
+}
+
+hipError_t index_init() {
+  return hipFuncSetAttribute((const void*)finalize_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)(2 * bitmap_words(kBitmapBits) * 4));
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
-  const int64_t nclear = (int64_t)a.nq * (kHistBins + 4);
-  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((nclear + 255) / 256)), dim3(256), 0, s, a.hist, a.counters, a.nq);
+  // clear both histograms and the counters (laid out back to back by index_ws_layout)
+  const int64_t nclr = (a.counters + 4 * (int64_t)a.nq) - a.hist;
+  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((nclr + 255) / 256)), dim3(256), 0, s, a.hist, nclr);
   if (a.max_visible > a.k) {
     if (a.dtype == HCA_MXFP4) {
       const dim3 g((unsigned)((a.max_visible + kScoreBlockKeys - 1) / kScoreBlockKeys), (unsigned)a.nq);
@@ -364,7 +579,12 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
   }
   const int64_t span = a.max_visible > a.k ? a.max_visible : a.k;
   const dim3 g((unsigned)((span + kSelBlock - 1) / kSelBlock), (unsigned)a.nq);
-  hipLaunchKernelGGL(select_kernel, g, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(classify_kernel, g, dim3(256), 0, s, a);
+  if (a.max_visible > a.k) {
+    const int64_t mvb = a.max_visible < kBitmapBits ? a.max_visible : kBitmapBits;
+    const size_t lds = (size_t)(2 * bitmap_words(mvb) * 4);
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.nq), dim3(kFinThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 

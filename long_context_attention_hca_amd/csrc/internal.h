@@ -43,15 +43,21 @@ struct IndexArgs {
   int64_t max_visible;
   int m, k;
   int32_t* out;  // [nq, k]
-  // workspace views for the batch
-  float* scores;      // [nq, max_visible]
-  uint32_t* hist;     // [nq, kHistBins]
-  uint32_t* counters; // [nq, 4]
-  uint64_t* cand;     // [nq, max_visible]
+  // workspace views for the batch (set by index_ws_layout)
+  float* scores;       // [nq, max_visible]
+  uint32_t* cand_key;  // [nq, max_visible] order-preserving score keys of the threshold bin
+  int32_t* cand_idx;   // [nq, max_visible] their entry indices
+  int32_t* sel;        // [nq, kMaxTopK] entries above the threshold bin
+  uint32_t* hist;      // [nq, kHistBins] top 11 key bits of all scores
+  uint32_t* hist2;     // [nq, kHistBins] next 11 key bits of the candidates
+  uint32_t* counters;  // [nq, 4]: selected, candidates
 };
 constexpr int kHistBins = 2048;
-size_t index_ws_per_query(int64_t max_visible);
+constexpr int kMaxTopK = 2048;
+// Lays out the workspace of a batch of nq queries at `ws` (nullptr: only size it); returns bytes.
+size_t index_ws_layout(int64_t nq, int64_t max_visible, void* ws, IndexArgs* a);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
+hipError_t index_init();
 
 struct StoreView {
   int layout, d_nope, d_rope;

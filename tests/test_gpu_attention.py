@@ -1,0 +1,129 @@
+"""GPU parity of csa_sparse_mqa_attn / hca_dense_mqa_attn against the oracle on
+edge cases, for each store layout (split FP8/bf16, dense bf16, dense fp32): empty
+entry sets (o = 0, lse = -inf), W = 0 and W = 1, -1 padding anywhere in idx,
+split-K (few queries) and single-block (many queries) launches, fp32 output from
+bf16 queries, 16/32/64 heads, a window store in a different layout from the cache."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as OA
+from oracle import compress as OC
+from tests._common import check_attention, np_
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hca():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_attention_hca_amd as m
+    from long_context_attention_hca_amd import workloads
+    return m, workloads
+
+
+def make_store(layout, n, seed, dn=448, dr=64):
+    g = synth.generator(seed)
+    if layout == "split":
+        st = synth.split_entries(g, n, dn, dr)
+        dec = OC.decode({k: np_(v) for k, v in st.items()}, "split")
+        return st, dec
+    v = synth.normal(g, (n, dn + dr))
+    if layout == "bf16":
+        bits = synth.bf16_bits(v)
+        return {"data": bits}, OC.decode({"data": np_(bits).view(np.uint16)}, "bf16")
+    return {"data": v}, v.double().numpy()
+
+
+def to_store(hca_mod, st, dn, dr):
+    if "nope" in st:
+        return hca_mod.Store.split(st["nope"].cuda(), st["scale"].cuda(), st["rope"].cuda())
+    return hca_mod.Store.dense(st["data"].cuda(), dn, dr)
+
+
+CASES = [
+    # cache layout, window layout, q dtype, o dtype, heads, D split
+    ("split", "split", "bf16", "bf16", 64, (448, 64)),
+    ("split", "split", "bf16", "f32", 16, (448, 64)),
+    ("bf16", "bf16", "bf16", "bf16", 32, (448, 64)),
+    ("split", "bf16", "bf16", "bf16", 64, (448, 64)),
+    ("f32", "f32", "f32", "f32", 16, (128, 64)),
+]
+
+
+@pytest.mark.parametrize("cl,wl,qd,od,H,dims", CASES)
+@pytest.mark.parametrize("nq", [3, 300])
+def test_attention_layouts_and_edges(hca, cl, wl, qd, od, H, dims, nq):
+    m, W_ = hca
+    dn, dr = dims
+    D = dn + dr
+    n_cache, n_win, k, W, mp = 1500, 400, 96, 37, 16
+    cache_st, cache_dec = make_store(cl, n_cache, 5, dn, dr)
+    win_st, win_dec = make_store(wl, n_win, 6, dn, dr)
+    rng = np.random.default_rng(nq)
+    # two sequences: cache rows [0, 800) and [800, 1500); window rows 0..199 hold positions
+    # 5000.., rows 200..399 positions 300..
+    crb, wrb, wp0 = [0, 800], [0, 200], [5000, 300]
+    q_seq = rng.integers(0, 2, nq).astype(np.int32)
+    q_pos = np.where(q_seq == 0, rng.integers(5000 + W, 5200, nq), rng.integers(300 + W, 500, nq)).astype(np.int64)
+    q_pos[0], q_seq[0] = 5000 + W - 1, 0                 # first query: smallest legal position
+    idx = np.full((nq, k), -1, np.int32)
+    for i in range(nq):
+        nvis = 700 if q_seq[i] == 0 else 650
+        cnt = rng.integers(0, k + 1)
+        sel = rng.choice(nvis, size=cnt, replace=False)
+        slots = rng.choice(k, size=cnt, replace=False)   # -1 padding anywhere
+        idx[i, slots] = sel
+    g = synth.generator(77)
+    qf = synth.normal(g, (nq, H, D))
+    q = qf if qd == "f32" else qf.bfloat16()
+    qdec = q.double().numpy()
+    scale = 1.0 / math.sqrt(D)
+    dev = "cuda"
+    cache = to_store(m, cache_st, dn, dr)
+    win = to_store(m, win_st, dn, dr)
+    t_seq = torch.tensor(q_seq, device=dev)
+    t_pos = torch.tensor(q_pos, device=dev)
+    ws = W_.Workspace(dev)
+    o_dt = torch.float32 if od == "f32" else torch.bfloat16
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=dev)
+    for Wx in (W, 0, 1):
+        o, lse = W_.csa_attn(q.to(dev), cache, i64(crb), torch.tensor(idx, device=dev), win, i64(wrb), i64(wp0), Wx,
+                             t_seq, t_pos, scale, ws, o_dtype=o_dt)
+        o2, lse2 = W_.hca_attn(q.to(dev), cache, i64(crb), mp, 60, win, i64(wrb), i64(wp0), Wx, t_seq, t_pos, scale,
+                               ws, o_dtype=o_dt)
+        torch.cuda.synchronize()
+        o, lse, o2, lse2 = np_(o.float()), np_(lse), np_(o2.float()), np_(lse2)
+        kind = "fp32" if qd == "f32" else "low"
+        for i in range(min(nq, 40)):
+            b, t = int(q_seq[i]), int(q_pos[i])
+            ent = cache_dec[crb[b]:]
+            raw = lambda pos, b=b: win_dec[wrb[b] + np.asarray(pos) - wp0[b]]
+            ro, rl = OA.csa(qdec[i], t, ent, idx[i], raw, Wx, scale)
+            check_attention(o[i], lse[i], ro, rl, kind, f"csa q{i} W={Wx}")
+            # HCA: the visible entries are the first min((t+1)//mp, max_visible = 60)
+            nv = min((t + 1) // mp, 60)
+            ro, rl = OA.attend(qdec[i], np.concatenate([ent[:nv], raw(OA.window_positions(t, Wx))]), scale)
+            check_attention(o2[i], lse2[i], ro, rl, kind, f"hca q{i} W={Wx}")
+
+
+def test_empty_sets_give_zero_and_neg_inf(hca):
+    m, W_ = hca
+    st, _ = make_store("split", 64, 9)
+    cache = to_store(m, st, 448, 64)
+    dev = "cuda"
+    q = synth.normal(synth.generator(3), (2, 64, 512)).bfloat16().to(dev)
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=dev)
+    ws = W_.Workspace(dev)
+    idx = torch.full((2, 32), -1, dtype=torch.int32, device=dev)
+    seq = torch.tensor([0, 0], dtype=torch.int32, device=dev)
+    pos = torch.tensor([5, 100], dtype=torch.int64, device=dev)
+    o, lse = W_.csa_attn(q, cache, i64([0]), idx, cache, i64([0]), i64([0]), 0, seq, pos, 0.05, ws)
+    o2, lse2 = W_.hca_attn(q, cache, i64([0]), 128, 64, cache, i64([0]), i64([0]), 0, seq, pos, 0.05, ws)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(o2.float() == 0) and torch.all(torch.isneginf(lse2))

@@ -1,0 +1,133 @@
+"""GPU parity of lightning_index_topk against the oracle on edge cases: exact
+ties (all-equal keys, all-zero scores), fewer visible entries than k, no visible
+entry, several sequences, batching forced by a small workspace, 1 and 8 indexer
+heads, k = 1 and k = 2048, and the path for more than 2^19 visible entries."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import codecs
+from oracle import indexer as OI
+from tests._common import check_idx, np_, tie_margin_ok
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hca():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_attention_hca_amd as m
+    return m
+
+
+def run(hca, q, w, keys, row_begin, q_seq, q_pos, max_visible, m, k, q_scale=None, k_scale=None, ws_bytes=None):
+    dev = "cuda"
+    nq = q.shape[0]
+    out = torch.full((nq, k), -7, dtype=torch.int32, device=dev)
+    need = hca.lightning_index_topk_workspace(nq, max_visible, k)
+    ws = torch.empty(ws_bytes or need, dtype=torch.uint8, device=dev)
+    hca.lightning_index_topk(q.to(dev), w.to(dev), keys.to(dev), torch.tensor(row_begin, dtype=torch.int64, device=dev),
+                             torch.tensor(q_seq, dtype=torch.int32, device=dev),
+                             torch.tensor(q_pos, dtype=torch.int64, device=dev), max_visible, m, k, out, ws,
+                             q_idx_scale=None if q_scale is None else q_scale.to(dev),
+                             k_idx_scale=None if k_scale is None else k_scale.to(dev))
+    torch.cuda.synchronize()
+    return np_(out)
+
+
+def oracle_mxfp4(q, qs, w, keys, ks, row_begin, q_seq, q_pos, m, k):
+    kd = codecs.decode_mxfp4(np_(keys), np_(ks))
+    res = []
+    for i in range(q.shape[0]):
+        b, t = q_seq[i], q_pos[i]
+        qd = codecs.decode_mxfp4(np_(q[i]), np_(qs[i]))
+        nv = min((t + 1) // m, kd.shape[0] - row_begin[b])
+        s = OI.scores_mxfp4(qd, np_(w[i]), kd[row_begin[b]:row_begin[b] + nv])
+        res.append(OI.topk(s, nv, k))
+    return np.stack(res)
+
+
+def mx_case(seed, n_keys, nq, H=4):
+    g = synth.generator(seed)
+    kp, ks = synth.mxfp4_rows(g, n_keys, 64)
+    qp, qs = synth.mxfp4_rows(g, nq * H, 64)
+    w = synth.normal(g, (nq, H), 0.125)
+    return qp.view(nq, H, 32), qs.view(nq, H, 2), w, kp, ks
+
+
+@pytest.mark.parametrize("H", [1, 4, 8])
+@pytest.mark.parametrize("k", [1, 64, 2048])
+def test_mxfp4_random(hca, H, k):
+    q, qs, w, kp, ks = mx_case(11 + H, 20000, 6, H)
+    q_seq, q_pos, rb = [0, 1, 1, 0, 1, 0], [19999, 39999, 4000, 79, 8191 * 4 + 3, 3], [0, 10000]
+    keys = torch.cat([kp, kp[:10000]])          # two sequences sharing rows of one key store
+    kss = torch.cat([ks, ks[:10000]])
+    got = run(hca, q, w, keys, rb, q_seq, q_pos, 20000, 4, k, qs, kss)
+    ref = oracle_mxfp4(q, qs, w, keys, kss, rb, q_seq, q_pos, 4, k)
+    check_idx(got, ref, f"mxfp4 H={H} k={k}")
+
+
+def test_mxfp4_all_equal_keys(hca):
+    q, qs, w, kp, ks = mx_case(3, 9000, 2)
+    kp[:] = kp[0]
+    ks[:] = ks[0]
+    got = run(hca, q, w, kp, [0], [0, 0], [35999, 20000], 9000, 4, 1024, qs, ks)
+    assert (got == np.arange(1024)).all()      # every score ties: the lowest indices win
+    check_idx(got, oracle_mxfp4(q, qs, w, kp, ks, [0], [0, 0], [35999, 20000], 4, 1024), "all equal")
+
+
+def test_mxfp4_zero_scores_dominate(hca):
+    # all head weights negative: the best score is 0 (every ReLU off), held by many entries
+    q, qs, w, kp, ks = mx_case(4, 30000, 3)
+    w = -w.abs()
+    got = run(hca, q, w, kp, [0], [0, 0, 0], [119999, 60000, 100], 30000, 4, 1024, qs, ks)
+    ref = oracle_mxfp4(q, qs, w, kp, ks, [0], [0, 0, 0], [119999, 60000, 100], 4, 1024)
+    check_idx(got, ref, "zero scores")
+
+
+def test_few_and_no_visible_entries(hca):
+    q, qs, w, kp, ks = mx_case(5, 5000, 4)
+    q_pos = [2, 3, 4098, 11]                    # n_vis = 0, 1, 1024, 3 with m = 4
+    got = run(hca, q, w, kp, [0], [0] * 4, q_pos, 5000, 4, 1024, qs, ks)
+    assert (got[0] == -1).all()
+    assert got[1, 0] == 0 and (got[1, 1:] == -1).all()
+    assert (got[2] == np.arange(1024)).all()
+    check_idx(got, oracle_mxfp4(q, qs, w, kp, ks, [0], [0] * 4, q_pos, 4, 1024), "few visible")
+
+
+def test_small_workspace_batches_queries(hca):
+    q, qs, w, kp, ks = mx_case(6, 12000, 7)
+    q_pos = [47999 - 1000 * i for i in range(7)]
+    one = hca.lightning_index_topk_workspace(1, 12000, 512)
+    got = run(hca, q, w, kp, [0], [0] * 7, q_pos, 12000, 4, 512, qs, ks, ws_bytes=one + 100)
+    check_idx(got, oracle_mxfp4(q, qs, w, kp, ks, [0], [0] * 7, q_pos, 4, 512), "batched")
+
+
+def test_more_than_2_19_visible_entries(hca):
+    n = 600000
+    q, qs, w, kp, ks = mx_case(7, n, 2)
+    got = run(hca, q, w, kp, [0], [0, 0], [n - 1, n - 5000], n, 1, 1000, qs, ks)
+    check_idx(got, oracle_mxfp4(q, qs, w, kp, ks, [0], [0, 0], [n - 1, n - 5000], 1, 1000), "fallback path")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_float_indexer(hca, dtype):
+    for seed in range(20, 40):
+        g = synth.generator(seed)
+        keys = synth.normal(g, (16000, 64))
+        q = synth.normal(g, (3, 4, 64))
+        w = synth.normal(g, (3, 4), 0.125)
+        if dtype == "bf16":
+            keys, q = keys.bfloat16().float(), q.bfloat16().float()
+        q_pos = [63999, 30000, 9000]
+        kd, qd = keys.double().numpy(), q.double().numpy()
+        if all(tie_margin_ok(qd[i], w[i].double().numpy(), kd, (q_pos[i] + 1) // 4, 300) for i in range(3)):
+            break
+    kk = keys if dtype == "f32" else keys.bfloat16()
+    qq = q if dtype == "f32" else q.bfloat16()
+    got = run(hca, qq, w, kk, [0], [0] * 3, q_pos, 16000, 4, 300)
+    ref = np.stack([OI.topk(OI.scores(qd[i], w[i].double().numpy(), kd[:(q_pos[i] + 1) // 4]),
+                            (q_pos[i] + 1) // 4, 300) for i in range(3)])
+    check_idx(got, ref, dtype)
