@@ -415,8 +415,10 @@ constexpr int kNope = 448;
 constexpr int kRope = 64;
 constexpr int kRowF8 = 592;                    // 448 + 128 + 16 pad
 constexpr int kBufF8 = 19 * 1024;              // 32 rows + the tail of the 19th load
-constexpr int kWaveF8 = 2 * kBufF8;            // double buffer
+constexpr int kTabF8 = kChunk * 16;            // per entry: FP8-row and RoPE-row addresses
+constexpr int kWaveF8 = 2 * kBufF8 + kTabF8;   // double buffer + address table
 constexpr int kFp8Lds = 4 * kWaveF8;
+constexpr int kMergeRow = kD / 2 + 4;          // padded row (floats) of the per-wave O half in LDS
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
@@ -455,23 +457,37 @@ __device__ __forceinline__ ChunkRows chunk_rows(const AttnArgs& a, const QueryCt
 }
 
 // 19 global_load_lds of 16 bytes fill the 32 rows of 592 bytes (FP8 dims, RoPE dims, pad).
-__device__ __forceinline__ void chunk_dma(const AttnArgs& a, const ChunkRows& cr, uint8_t* buf, int lane) {
-  const uint8_t* dummy = static_cast<const uint8_t*>(a.q);
-#pragma unroll 1
+// Lanes 0..31 first publish their entry's FP8-row address and RoPE-row address (minus 448, so
+// that adding the in-row byte offset works for both parts) in a per-wave LDS table; every lane
+// then reads the addresses its 19 loads need from the table with independent LDS reads.
+__device__ __forceinline__ void chunk_dma(const AttnArgs& a, const ChunkRows& cr, uint8_t* buf, uint64_t* tab,
+                                          int lane) {
+  const uint64_t dummy = reinterpret_cast<uint64_t>(a.q);
+  if (lane < kChunk) {
+    uint64_t np = dummy, rp = dummy;
+    if ((cr.vmask >> lane) & 1) {
+      const StoreView& v = ((cr.wmask >> lane) & 1) ? a.win : a.cache;
+      np = reinterpret_cast<uint64_t>(v.data) + (uint64_t)((int64_t)cr.row * v.row_stride);
+      rp = reinterpret_cast<uint64_t>(v.rope) + (uint64_t)((int64_t)cr.row * v.rope_stride * 2) - kNope;
+    }
+    tab[2 * lane] = np;
+    tab[2 * lane + 1] = rp;
+  }
+  wave_lds_sync();
+  uint64_t src[19];
+#pragma unroll
   for (int i = 0; i < 19; ++i) {
     const int b = 1024 * i + 16 * lane;
     const int e = b / kRowF8;
     const int off = b - e * kRowF8;
-    const int ee = e < kChunk ? e : kChunk - 1;
-    const int row = __shfl(cr.row, ee, 64);
-    const bool valid = e < kChunk && ((cr.vmask >> ee) & 1);
-    const StoreView& v = ((cr.wmask >> ee) & 1) ? a.win : a.cache;
-    const uint8_t* src = dummy;
-    if (valid && off < kNope) src = static_cast<const uint8_t*>(v.data) + (int64_t)row * v.row_stride + off;
-    else if (valid && off < kNope + 2 * kRope)
-      src = static_cast<const uint8_t*>(v.rope) + ((int64_t)row * v.rope_stride) * 2 + (off - kNope);
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + 1024 * i), 16, 0, 0);
+    const bool data = e < kChunk && off < kNope + 2 * kRope;
+    const uint64_t t = tab[2 * (e < kChunk ? e : 0) + (off < kNope ? 0 : 1)];
+    src[i] = data ? t + (uint64_t)off : dummy;
   }
+#pragma unroll
+  for (int i = 0; i < 19; ++i)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src[i]),
+                                     (__attribute__((address_space(3))) void*)(buf + 1024 * i), 16, 0, 0);
 }
 
 __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, int total) {
@@ -483,10 +499,11 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   const int s = rest % a.n_split;
   const int qi = rest / a.n_split;
   const int H = a.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const int head = hg * 16 + c;
   uint8_t* wbuf = smem + wave * kWaveF8;
+  uint64_t* tab = reinterpret_cast<uint64_t*>(wbuf + 2 * kBufF8);
 
   const QueryCtx ctx = query_ctx(a, qi);
   const int64_t N = ctx.n_c + ctx.n_w;
@@ -508,14 +525,23 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   int64_t base = lo + (int64_t)wave * kChunk;
   ChunkRows cur = chunk_rows(a, ctx, qi, base, hi, lane);
   __builtin_amdgcn_s_waitcnt(0);
-  if (base < hi) chunk_dma(a, cur, wbuf, lane);
+  if (base < hi) chunk_dma(a, cur, wbuf, tab, lane);
   for (int it = 0; base < hi; ++it, base += 4 * kChunk) {
     uint8_t* buf = wbuf + (it & 1) * kBufF8;
     const int64_t nbase = base + 4 * kChunk;
     ChunkRows nxt = chunk_rows(a, ctx, qi, nbase, hi, lane);
     __builtin_amdgcn_s_waitcnt(0);  // this chunk's DMA and the next chunk's rows have landed
     __builtin_amdgcn_wave_barrier();
-    if (nbase < hi) chunk_dma(a, nxt, wbuf + ((it + 1) & 1) * kBufF8, lane);
+    // rows of invalid entries were filled from a dummy address: zero them (their scores are
+    // masked, but 0 * NaN would still reach O)
+    uint32_t inval = ~(uint32_t)cur.vmask;
+    while (inval) {
+      const int e = __builtin_ctz(inval);
+      inval &= inval - 1;
+      if (lane < kRowF8 / 16) *reinterpret_cast<uint4*>(buf + e * kRowF8 + 16 * lane) = make_uint4(0, 0, 0, 0);
+    }
+    wave_lds_sync();
+    if (nbase < hi) chunk_dma(a, nxt, wbuf + ((it + 1) & 1) * kBufF8, tab, lane);
     const float esc = cur.esc;
     const uint64_t vmask = cur.vmask;
 
@@ -559,18 +585,21 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
       }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const bool none = m_new == -INFINITY;
-    const float corr = none ? 1.f : exp2f(m_run - m_new);
+    // lazy rescaling: the reference max moves only when a score exceeds it by more than 2^8
+    // (log2 units), so p <= 256 and O is rescaled rarely instead of every chunk
+    const bool grow = cmax > m_run + 8.f;
+    const float m_ref = grow ? cmax : m_run;
+    const bool none = m_ref == -INFINITY;
+    const float corr = grow ? exp2f(m_run - cmax) : 1.f;
     float p[8], psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = none ? 0.f : exp2f(sv[i] - m_new);
+      p[i] = none ? 0.f : exp2f(sv[i] - m_ref);
       psum += p[i];
     }
     l_run = l_run * corr + psum;
-    m_run = m_new;
-    if (__ballot(corr != 1.f)) {
+    m_run = m_ref;
+    if (__ballot(grow)) {
 #pragma unroll
       for (int dt = 0; dt < kD / 16; ++dt) O[dt] *= corr;
     }
@@ -628,7 +657,7 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
-      *reinterpret_cast<f32x4*>(wo + c * (kD / 2) + 16 * dt + 4 * g) = O[half * (kD / 32) + dt];
+      *reinterpret_cast<f32x4*>(wo + c * kMergeRow + 16 * dt + 4 * g) = O[half * (kD / 32) + dt];
     __syncthreads();
     if (half == 0) {
       float mw[4], M = -INFINITY;
@@ -653,7 +682,8 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        acc += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(smem + w * kWaveF8) + 32 + hc * (kD / 2) + dh) * fw[w];
+        acc += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(smem + w * kWaveF8) + 32 + hc * kMergeRow + dh) *
+               fw[w];
       acc *= inv;
       if (a.n_split == 1) {
         const int64_t oi = ((int64_t)qi * H + hd) * kD + d;
@@ -744,7 +774,7 @@ void attn_split_policy(int nq, int H, int D, int64_t max_entries, bool mfma, int
   (void)D;
   const int n_hg = mfma ? H / 16 : 1;
   const int64_t align = mfma ? 4 * kChunk : kValuChunk;
-  const int64_t target = 512;
+  const int64_t target = mfma ? 256 : 512;  // MFMA kernels run one block per CU
   int64_t want = (target + (int64_t)nq * n_hg - 1) / ((int64_t)nq * n_hg);
   const int64_t max_split = std::max<int64_t>(1, (max_entries + align - 1) / align);
   want = std::max<int64_t>(1, std::min(want, max_split));

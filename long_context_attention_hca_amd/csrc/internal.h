@@ -44,13 +44,12 @@ struct IndexArgs {
   int m, k;
   int32_t* out;  // [nq, k]
   // workspace views for the batch (set by index_ws_layout)
-  float* scores;       // [nq, max_visible]
-  uint32_t* cand_key;  // [nq, max_visible] order-preserving score keys of the threshold bin
+  int nblk;            // score blocks per query: ceil(max_visible / 1024)
+  uint32_t* scores;    // [nq, max_visible] order-preserving score keys
+  uint32_t* cand_key;  // [nq, max_visible] candidate score keys
   int32_t* cand_idx;   // [nq, max_visible] their entry indices
-  int32_t* sel;        // [nq, kMaxTopK] entries above the threshold bin
-  uint32_t* hist;      // [nq, kHistBins] top 11 key bits of all scores
-  uint32_t* hist2;     // [nq, kHistBins] next 11 key bits of the candidates
-  uint32_t* counters;  // [nq, 4]: selected, candidates
+  int32_t* blk_bin;    // [nq, nblk] threshold bin of each score block
+  uint32_t* counters;  // [nq, 4]: candidates
 };
 constexpr int kHistBins = 2048;
 constexpr int kMaxTopK = 2048;

@@ -150,9 +150,13 @@ def decode_bf16(case, ws=None):
 class Decode1M:
     """Decode step over precompressed split-layout caches and MXFP4 indexer keys
     (index + CSA attention for one layer, HCA attention for another), with all
-    outputs and workspaces preallocated so that `step()` only enqueues kernels."""
+    outputs and workspaces preallocated so that `step()` only enqueues kernels.
 
-    def __init__(self, case, ws=None):
+    HCA attention does not depend on the indexer, so `step()` forks it onto a side
+    stream (default priority) and joins it back: it runs concurrently with
+    index -> CSA attention, on the GPU and inside a captured graph alike."""
+
+    def __init__(self, case, ws=None, overlap=True):
         p, t = case.params, case.t
         self.case = case
         dev = t["q_csa"].device
@@ -181,6 +185,7 @@ class Decode1M:
         self.ws.get("index", lightning_index_topk_workspace(B, self.n_c, k))
         self.ws.get("csa", mqa_attn_workspace(BF16, B, H, D, k + W))
         self.ws.get("hca", mqa_attn_workspace(BF16, B, H, D, self.n_h + W))
+        self.side = torch.cuda.Stream(device=dev) if overlap else None
 
     def index(self, stream=None):
         t = self.case.t
@@ -198,10 +203,19 @@ class Decode1M:
         return hca_attn(self.q_hca, self.hca, self.hrb, self.mp, self.n_h, self.win_hca, self.wrb, self.wp0, self.W,
                         t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_hca, lse=self.lse_hca, stream=stream)
 
-    def step(self, stream=None):
-        self.index(stream)
-        self.csa_attention(stream)
-        self.hca_attention(stream)
+    def step(self):
+        if self.side is None:
+            self.index()
+            self.csa_attention()
+            self.hca_attention()
+            return
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            self.hca_attention()
+        self.index()
+        self.csa_attention()
+        main.wait_stream(self.side)
 
 
 def compress_1m(case, out_csa=None, out_hca=None, stream=None):
