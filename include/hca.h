@@ -161,7 +161,8 @@ int hca_compress(const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int
  *   s = s + w_h*r_h in head order, each product and sum rounded to float32
  *   (no fused multiply-add).
  * w_idx: float32 [nq, H]. Requires d == 64, 1 <= H <= 8, 1 <= k <= 2048,
- * m >= 1, 1 <= nq. Preconditions: q_seq[i] indexes k_row_begin; every
+ * m >= 1, 1 <= nq, max_visible <= 2^21 (HCA_ERR_UNSUPPORTED beyond).
+ * Preconditions: q_seq[i] indexes k_row_begin; every
  * n_vis <= max_visible and k_row_begin[b] + n_vis <= k_rows (reads are
  * clamped to both bounds).
  * Workspace: lightning_index_topk_workspace(nq, max_visible, k) bytes

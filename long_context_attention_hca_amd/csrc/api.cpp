@@ -264,7 +264,7 @@ HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scal
   if (n_idx_heads < 1 || n_idx_heads > 8) return fail(HCA_ERR_UNSUPPORTED, fn, "indexer heads must be 1..8");
   if (k < 1 || k > 2048) return fail(HCA_ERR_INVALID_ARG, fn, "k must be 1..2048");
   if (m < 1 || nq < 0 || max_visible < 0 || k_rows < 0) return fail(HCA_ERR_INVALID_ARG, fn, "bad m/nq/max_visible/k_rows");
-  if (max_visible > (int64_t)INT32_MAX - 1) return fail(HCA_ERR_INVALID_ARG, fn, "max_visible too large");
+  if (max_visible > ((int64_t)1 << 21)) return fail(HCA_ERR_UNSUPPORTED, fn, "max_visible above 2^21");
   if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(HCA_ERR_INVALID_ARG, fn, "q_idx/k_idx not 16-byte aligned");
   if (nq == 0) return HCA_OK;
   if (!ws || ws_bytes < index_ws(1, max_visible)) return fail(HCA_ERR_WORKSPACE, fn, "workspace too small");

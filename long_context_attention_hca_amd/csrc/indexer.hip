@@ -18,16 +18,19 @@
 //    folded in head order with separately rounded multiplies and adds
 //    (__fmul_rn / __fadd_rn), which makes it bit-exact and the top-k unique.
 //  * Selection is on the 64-bit key (order-preserving score bits << 32 | ~j), which
-//    is unique per entry. Every score block (1024 entries) keeps its keys in LDS,
-//    histograms their top 11 bits there, and emits as candidates the entries at or
-//    above the bin holding its L-th largest key (L about twice the block's expected
-//    share of the top-k, at least 32), recording that bin. One block per query then
-//    selects the k-th largest candidate key T by 8-bit radix passes in LDS. Entries
-//    a block did not emit all lie below its recorded bin, so if no recorded bin is
-//    above T's bin the candidates contain the whole top-k; otherwise the blocks in
-//    question are rescanned from their stored keys and the selection is repeated,
-//    which keeps the result exact for any input (ties included). The k indices are
-//    emitted in ascending order through an LDS bitmap over the visible entries.
+//    is unique per entry. Every score block (1024 entries) keeps its keys in LDS and
+//    emits, into a region of the workspace that only it writes, the keys at or above
+//    a threshold thr_b: the top 11-bit bin holding its L-th largest key when that
+//    bin is small (L is about twice the block's expected share of the top-k, at
+//    least 16), else exactly its L largest keys, found by two more histogram passes
+//    over the lower key bits with equal scores broken by index. No atomics leave the
+//    block. One block per query then gathers the candidates into LDS and finds the
+//    k-th largest candidate key T with 11-bit radix passes that start below the bits
+//    all candidates share. A block whose thr_b exceeds T may hold unemitted keys in
+//    [T, thr_b); such blocks are rescanned from their stored keys and the selection
+//    is repeated once, after which every key >= the new T is a candidate, so the
+//    result is exact for any input (ties included). The k indices are emitted in
+//    ascending order through an LDS bitmap over the visible entries.
 #include "common.h"
 #include "internal.h"
 
@@ -38,6 +41,7 @@ constexpr int kBlockKeys = 1024;        // entries per score block
 constexpr int kFinThreads = 1024;       // finalize block
 constexpr int64_t kBitmapBits = 1 << 19;
 constexpr int kCandCap = 16384;         // candidates held in LDS by finalize (128 KB)
+constexpr int kMaxBlk = 2048;           // score blocks per query (max_visible <= 2^21)
 
 __device__ __forceinline__ int64_t visible_keys(const IndexArgs& a, int qi, int64_t* row0) {
   const int b = a.q_seq[qi];
@@ -49,12 +53,6 @@ __device__ __forceinline__ int64_t visible_keys(const IndexArgs& a, int qi, int6
   if (rb < 0 || nv < 0) nv = 0;
   *row0 = rb;
   return nv;
-}
-
-// Zeroes n words (the per-query counters).
-__global__ __launch_bounds__(256) void clear_kernel(uint32_t* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -125,63 +123,129 @@ struct BlockLds {
   uint32_t part[256];
   uint32_t tmp[8];
   int d, bin;
-  uint32_t above, base;
+  uint32_t above, above_bin;
+  uint64_t thr;
 };
 
+// Over the 2048 counters lds.hist (256 threads): the largest bin d with sum_{i >= d} >= rem
+// and above = sum_{i > d}. Requires sum >= rem >= 1. Ends with the block synchronised.
+__device__ __forceinline__ void block_crossing(BlockLds& lds, uint32_t rem, int* d, uint32_t* above) {
+  const int tid = threadIdx.x;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += lds.hist[8 * tid + i];
+  lds.part[tid] = sum;
+  __syncthreads();
+  if (tid < 64) find_crossing<1>(lds.part, rem, &lds.d, &lds.above);
+  __syncthreads();
+  if (tid == lds.d) {
+    uint32_t acc = lds.above;
+    int b = 8 * tid + 7;
+    for (; b > 8 * tid; --b) {
+      if (acc + lds.hist[b] >= rem) break;
+      acc += lds.hist[b];
+    }
+    lds.bin = b;
+    lds.above_bin = acc;
+  }
+  __syncthreads();
+  *d = lds.bin;
+  *above = lds.above_bin;
+}
+
+// Candidates of a block: L = max(16, ceil(2 k 1024 / n_vis)), about twice the block's share of
+// the top-k when the top-k is spread evenly over the blocks.
+__device__ __forceinline__ uint32_t block_quota(int k, int64_t nv) {
+  return (uint32_t)max<int64_t>(16, (2 * (int64_t)k * kBlockKeys + nv - 1) / nv);
+}
+
 // Candidate emission of one score block (all 256 threads; lds.key / lds.hist complete).
+// Thread tid owns block positions 4 tid .. 4 tid + 3.
 __device__ void emit_candidates(const IndexArgs& a, int qi, int64_t jb, int64_t nv, BlockLds& lds) {
   const int tid = threadIdx.x;
   const int nvalid = (int)min<int64_t>(kBlockKeys, nv - jb);
-  const int64_t L = max<int64_t>(32, (2 * (int64_t)a.k * kBlockKeys + nv - 1) / nv);
-  uint32_t tb = 0;
-  if (nvalid > L) {
-    uint32_t sum = 0;
+  const uint32_t L = block_quota(a.k, nv);
+  const uint4 kv = reinterpret_cast<const uint4*>(lds.key)[tid];
+  const uint32_t kk[4] = {kv.x, kv.y, kv.z, kv.w};
+  const int t0 = 4 * tid;
+  uint64_t thr = 0;  // emit keys >= thr
+  if ((uint32_t)nvalid > L) {
+    int d;
+    uint32_t above;
+    block_crossing(lds, L, &d, &above);
+    uint32_t rem = L - above;
+    if (above + lds.hist[d] <= 2 * L) {
+      thr = (uint64_t)d << 53;  // the whole bin
+    } else {
+      // exactly the L largest keys: refine on key bits 20..10, then 9..0, then break ties by index
+      uint32_t pre = (uint32_t)d;
+      __syncthreads();
+      for (int i = tid; i < kHistBins; i += 256) lds.hist[i] = 0;
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sum += lds.hist[8 * tid + i];
-    lds.part[tid] = sum;
-    __syncthreads();
-    if (tid < 64) find_crossing<1>(lds.part, (uint32_t)L, &lds.d, &lds.above);
-    __syncthreads();
-    if (tid == lds.d) {
-      uint32_t acc = lds.above;
-      int b = 8 * tid + 7;
-      for (; b > 8 * tid; --b) {
-        if (acc + lds.hist[b] >= (uint32_t)L) break;
-        acc += lds.hist[b];
+      for (int i = 0; i < 4; ++i)
+        if (t0 + i < nvalid && (kk[i] >> 21) == pre) atomicAdd(&lds.hist[(kk[i] >> 10) & 2047u], 1u);
+      __syncthreads();
+      block_crossing(lds, rem, &d, &above);
+      rem -= above;
+      pre = (pre << 11) | (uint32_t)d;
+      if (lds.hist[d] == rem) {
+        thr = (uint64_t)pre << 42;
+      } else {
+        __syncthreads();
+        for (int i = tid; i < kHistBins; i += 256) lds.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + i < nvalid && (kk[i] >> 10) == pre) atomicAdd(&lds.hist[kk[i] & 1023u], 1u);
+        __syncthreads();
+        block_crossing(lds, rem, &d, &above);
+        rem -= above;
+        const uint32_t v = (pre << 10) | (uint32_t)d;
+        // rem of the keys equal to v are taken, the lowest positions first
+        uint32_t nt = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nt += (t0 + i < nvalid && kk[i] == v);
+        uint32_t tot;
+        uint32_t r = block_exclusive_scan<256>(nt, lds.tmp, &tot);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (t0 + i < nvalid && kk[i] == v) {
+            if (r == rem - 1) lds.thr = ((uint64_t)v << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(jb + t0 + i));
+            ++r;
+          }
+        }
+        __syncthreads();
+        thr = lds.thr;
       }
-      lds.bin = b;
     }
-    __syncthreads();
-    tb = (uint32_t)lds.bin;
   }
+  uint64_t k64[4];
   uint32_t n = 0;
 #pragma unroll
-  for (int i = 0; i < kBlockKeys / 256; ++i) {
-    const int t = tid + 256 * i;
-    n += (t < nvalid && (lds.key[t] >> 21) >= tb);
+  for (int i = 0; i < 4; ++i) {
+    k64[i] = ((uint64_t)kk[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(jb + t0 + i));
+    n += (t0 + i < nvalid && k64[i] >= thr);
   }
   uint32_t tot;
   uint32_t off = block_exclusive_scan<256>(n, lds.tmp, &tot);
-  if (tid == 0) lds.base = atomicAdd(&a.counters[(int64_t)qi * 4], tot);
-  __syncthreads();
-  off += lds.base;
-  uint32_t* ck = a.cand_key + (int64_t)qi * a.max_visible;
-  int32_t* ci = a.cand_idx + (int64_t)qi * a.max_visible;
-  uint32_t* sk = a.scores + (int64_t)qi * a.max_visible;
+  const int64_t slot = (int64_t)qi * a.nblk + blockIdx.x;
+  uint64_t* dst = a.cand + slot * kBlockKeys;
 #pragma unroll
-  for (int i = 0; i < kBlockKeys / 256; ++i) {
-    const int t = tid + 256 * i;
-    if (t < nvalid) {
-      const uint32_t key = lds.key[t];
-      sk[jb + t] = key;
-      if ((key >> 21) >= tb) {
-        ck[off] = key;
-        ci[off] = (int32_t)(jb + t);
-        ++off;
-      }
-    }
+  for (int i = 0; i < 4; ++i)
+    if (t0 + i < nvalid && k64[i] >= thr) dst[off++] = k64[i];
+  uint32_t* sk = a.scores + (int64_t)qi * a.nblk * kBlockKeys + jb;
+  if (t0 + 3 < nvalid) {
+    *reinterpret_cast<uint4*>(sk + t0) = kv;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (t0 + i < nvalid) sk[t0 + i] = kk[i];
   }
-  if (tid == 0) a.blk_bin[(int64_t)qi * a.nblk + blockIdx.x] = (int32_t)tb;
+  if (tid == 0) {
+    a.blk_cnt[slot] = tot;
+    a.blk_thr[slot] = thr;
+  }
 }
 
 // MXFP4 scores via the scaled MFMA. grid = (nblk, nq), 256 threads, 1024 keys per block.
@@ -314,46 +378,147 @@ __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
 // ---------------------------------------------------------------------------------------
 // Finalisation: one block of 1024 threads per query.
 
-// The K-th largest of nc unique 64-bit keys (from LDS, or rebuilt from the global candidate
-// arrays), by 8-bit radix passes with early exit: returns T such that exactly K keys are >= T.
-template <bool kLds>
-__device__ uint64_t select_kth(const uint64_t* lk, const uint32_t* gk, const int32_t* gi, uint32_t nc, uint32_t K,
-                               uint32_t* h, int* s_d, uint32_t* s_above) {
-  const int tid = threadIdx.x;
-  uint64_t prefix = 0;
-  uint32_t rem = K;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    if (tid < 256) h[tid] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < nc; i += kFinThreads) {
-      const uint64_t key = kLds ? lk[i] : (((uint64_t)gk[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)gi[i]));
-      const bool match = pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8));
-      if (match) atomicAdd(&h[(key >> shift) & 255u], 1u);
+struct FinLds {
+  uint32_t h[kHistBins];        // radix histogram; list of flagged blocks
+  int32_t sel[kMaxTopK];        // the selected entries
+  uint32_t pre[kMaxBlk + 1];    // exclusive prefix of the per-block candidate counts
+  uint32_t tmp[32];
+  uint64_t kmin, kmax;
+  int d;
+  uint32_t above, nsel, nflag;
+};
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Calls f(key) once for every candidate: from LDS (lk[0..nc)) or from the per-block regions.
+template <bool kLds, class F>
+__device__ __forceinline__ void for_each_cand(const uint64_t* lk, uint32_t nc, const uint64_t* cq, const FinLds& f,
+                                              int nb, F fn) {
+  if (kLds) {
+    for (uint32_t i = threadIdx.x; i < nc; i += kFinThreads) fn(lk[i]);
+  } else {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int b = wave; b < nb; b += kFinThreads / 64) {
+      const uint32_t c = f.pre[b + 1] - f.pre[b];
+      for (uint32_t i = lane; i < c; i += 64) fn(cq[(int64_t)b * kBlockKeys + i]);
     }
-    __syncthreads();
-    if (tid < 64) find_crossing<1>(h, rem, s_d, s_above);
-    __syncthreads();
-    const int d = *s_d;
-    rem -= *s_above;
-    prefix |= (uint64_t)d << shift;
-    const bool done = h[d] == rem;
-    __syncthreads();
-    if (done) break;
   }
-  return prefix;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64), hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o < v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64), hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Per-block counts -> f.pre, then (if they fit) the candidates into lk; f.kmin / f.kmax get
+// the smallest and largest candidate key. Returns the candidate count.
+__device__ uint32_t gather_candidates(const uint32_t* cnt, const uint64_t* cq, int nb, uint64_t* lk, FinLds& f) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t c0 = 2 * tid < nb ? cnt[2 * tid] : 0u, c1 = 2 * tid + 1 < nb ? cnt[2 * tid + 1] : 0u;
+  uint32_t nc;
+  const uint32_t off = block_exclusive_scan<kFinThreads>(c0 + c1, f.tmp, &nc);
+  f.pre[2 * tid] = off;
+  f.pre[2 * tid + 1] = off + c0;
+  if (tid == 0) {
+    f.pre[nb] = nc;
+    f.kmin = ~0ull;
+    f.kmax = 0;
+  }
+  __syncthreads();
+  uint64_t lo = ~0ull, hi = 0;
+  if (nc <= (uint32_t)kCandCap) {
+    constexpr int kBatch = 8, kStride = kFinThreads / 64;
+    for (int b0 = wave; b0 < nb; b0 += kStride * kBatch) {
+      uint64_t v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int b = b0 + kStride * u;
+        const uint32_t c = b < nb ? f.pre[b + 1] - f.pre[b] : 0u;
+        v[u] = (uint32_t)lane < c ? cq[(int64_t)b * kBlockKeys + lane] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int b = b0 + kStride * u;
+        const uint32_t c = b < nb ? f.pre[b + 1] - f.pre[b] : 0u;
+        for (uint32_t i = lane; i < c; i += 64) {
+          const uint64_t x = i == (uint32_t)lane ? v[u] : cq[(int64_t)b * kBlockKeys + i];
+          lk[f.pre[b] + i] = x;
+          lo = x < lo ? x : lo;
+          hi = x > hi ? x : hi;
+        }
+      }
+    }
+  } else {
+    for_each_cand<false>(lk, nc, cq, f, nb, [&](uint64_t x) {
+      lo = x < lo ? x : lo;
+      hi = x > hi ? x : hi;
+    });
+  }
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  if (lane == 0) {
+    atomicMin(reinterpret_cast<unsigned long long*>(&f.kmin), (unsigned long long)lo);
+    atomicMax(reinterpret_cast<unsigned long long*>(&f.kmax), (unsigned long long)hi);
+  }
+  __syncthreads();
+  return nc;
+}
+
+// The K-th largest of the nc >= K unique candidate keys: returns T such that exactly K
+// candidates are >= T. Radix passes of 11 bits start below the bits every candidate shares
+// and stop once the bin holding the K-th key is taken whole.
+template <bool kLds>
+__device__ uint64_t select_kth(const uint64_t* lk, uint32_t nc, const uint64_t* cq, FinLds& f, int nb, uint32_t K) {
+  const int tid = threadIdx.x;
+  const uint64_t kmin = f.kmin, kmax = f.kmax;
+  if (kmin == kmax) return kmin;
+  int lo = 64 - __clzll((long long)(kmin ^ kmax));  // bits >= lo are common to all candidates
+  uint64_t prefix = lo >= 64 ? 0ull : (kmax >> lo) << lo;
+  uint32_t rem = K;
+  while (true) {
+    const int hi = lo, width = min(11, lo);
+    lo -= width;
+    for (int i = tid; i < kHistBins; i += kFinThreads) f.h[i] = 0;
+    __syncthreads();
+    const uint64_t want = hi >= 64 ? 0ull : prefix >> hi;
+    const uint32_t dmask = (1u << width) - 1u;
+    for_each_cand<kLds>(lk, nc, cq, f, nb, [&](uint64_t key) {
+      if (hi >= 64 || (key >> hi) == want) atomicAdd(&f.h[(uint32_t)(key >> lo) & dmask], 1u);
+    });
+    __syncthreads();
+    if (tid < 64) find_crossing<8>(f.h, rem, &f.d, &f.above);
+    __syncthreads();
+    const int d = f.d;
+    rem -= f.above;
+    prefix |= (uint64_t)d << lo;
+    const bool done = f.h[d] == rem || lo == 0;
+    __syncthreads();
+    if (done) return prefix;
+  }
 }
 
 __host__ __device__ __forceinline__ int64_t bitmap_words(int64_t nv) { return (nv + 31) >> 5; }
 
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
   extern __shared__ uint64_t lk[];  // kCandCap candidate keys, later the output bitmap
-  __shared__ uint32_t h[256];
-  __shared__ uint32_t tmp[32];
-  __shared__ int32_t sel[kMaxTopK];
-  __shared__ int s_d;
-  __shared__ uint32_t s_above, s_slot, s_flag;
-  const int qi = blockIdx.x, tid = threadIdx.x;
+  __shared__ FinLds f;
+  const int qi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.k;
   int64_t rb;
   const int64_t nv = visible_keys(a, qi, &rb);
@@ -362,64 +527,70 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     for (int j = tid; j < K; j += kFinThreads) out[j] = j < nv ? j : -1;
     return;
   }
-  uint32_t* cnt = a.counters + (int64_t)qi * 4;
-  uint32_t* gk = a.cand_key + (int64_t)qi * a.max_visible;
-  int32_t* gi = a.cand_idx + (int64_t)qi * a.max_visible;
-  const uint32_t* sk = a.scores + (int64_t)qi * a.max_visible;
-  const int32_t* bb = a.blk_bin + (int64_t)qi * a.nblk;
-  const int nblk = (int)((nv + kBlockKeys - 1) / kBlockKeys);
-  uint32_t nc = cnt[0];
-  uint64_t T = 0;
-  bool in_lds = false;
-  for (int round = 0; round < 2; ++round) {
-    in_lds = nc <= (uint32_t)kCandCap;
-    if (in_lds) {
-      for (uint32_t i = tid; i < nc; i += kFinThreads)
-        lk[i] = ((uint64_t)gk[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)gi[i]);
-      __syncthreads();
-      T = select_kth<true>(lk, gk, gi, nc, (uint32_t)K, h, &s_d, &s_above);
-    } else {
-      T = select_kth<false>(lk, gk, gi, nc, (uint32_t)K, h, &s_d, &s_above);
-    }
-    if (round == 1) break;
-    // would any block's unemitted entries (all below its recorded bin) reach T?
-    const int32_t tbin = (int32_t)(T >> 53);
-    if (tid == 0) s_flag = 0;
-    __syncthreads();
-    for (int b = tid; b < nblk; b += kFinThreads)
-      if (bb[b] > tbin) s_flag = 1;
-    __syncthreads();
-    if (!s_flag) break;
-    // rescan those blocks: append their unemitted entries whose key is >= T
-    for (int b = 0; b < nblk; ++b) {
-      const int32_t tb = bb[b];
-      if (tb <= tbin) continue;
-      for (int t = tid; t < kBlockKeys; t += kFinThreads) {
-        const int64_t j = (int64_t)b * kBlockKeys + t;
-        if (j >= nv) continue;
-        const uint32_t k32 = sk[j];
-        if ((int32_t)(k32 >> 21) >= tb) continue;  // already a candidate
-        const uint64_t k64 = ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-        if (k64 >= T) {
-          const uint32_t slot = atomicAdd(&cnt[0], 1u);
-          gk[slot] = k32;
-          gi[slot] = (int32_t)j;
-        }
+  const int nb = (int)((nv + kBlockKeys - 1) / kBlockKeys);
+  const int64_t q_blk = (int64_t)qi * a.nblk;
+  uint32_t* cnt = a.blk_cnt + q_blk;
+  const uint64_t* thr = a.blk_thr + q_blk;
+  uint64_t* cq = a.cand + q_blk * kBlockKeys;
+  const uint32_t* sk = a.scores + q_blk * kBlockKeys;
+  uint32_t nc = gather_candidates(cnt, cq, nb, lk, f);
+  bool in_lds = nc <= (uint32_t)kCandCap;
+  uint64_t T = in_lds ? select_kth<true>(lk, nc, cq, f, nb, (uint32_t)K) : select_kth<false>(lk, nc, cq, f, nb, (uint32_t)K);
+  // blocks whose unemitted keys (all below their threshold) may reach T
+  if (tid == 0) f.nflag = 0;
+  __syncthreads();
+  for (int b = tid; b < nb; b += kFinThreads)
+    if (thr[b] > T) f.h[atomicAdd(&f.nflag, 1u)] = (uint32_t)b;
+  __syncthreads();
+  const uint32_t nflag = f.nflag;
+  if (nflag > 0) {
+    // append their unemitted keys >= T to their own regions, one wave per block
+    for (uint32_t fi = wave; fi < nflag; fi += kFinThreads / 64) {
+      const int b = (int)f.h[fi];
+      const int64_t jb = (int64_t)b * kBlockKeys;
+      const uint64_t tb = thr[b];
+      uint32_t c = cnt[b];
+      uint32_t kv[kBlockKeys / 64];
+#pragma unroll
+      for (int r = 0; r < kBlockKeys / 64; ++r) {
+        const int64_t j = jb + lane + 64 * r;
+        kv[r] = j < nv ? sk[j] : 0u;
       }
+#pragma unroll
+      for (int r = 0; r < kBlockKeys / 64; ++r) {
+        const int64_t j = jb + lane + 64 * r;
+        const uint64_t k64 = ((uint64_t)kv[r] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+        const bool p = j < nv && k64 < tb && k64 >= T;
+        const uint64_t m = __ballot(p);
+        if (p) cq[jb + c + lanes_below(m)] = k64;
+        c += (uint32_t)__popcll(m);
+      }
+      if (lane == 0) cnt[b] = c;
     }
-    __threadfence();
+    __threadfence_block();
     __syncthreads();
-    nc = atomicAdd(&cnt[0], 0u);
-    __syncthreads();
+    nc = gather_candidates(cnt, cq, nb, lk, f);
+    in_lds = nc <= (uint32_t)kCandCap;
+    T = in_lds ? select_kth<true>(lk, nc, cq, f, nb, (uint32_t)K) : select_kth<false>(lk, nc, cq, f, nb, (uint32_t)K);
   }
-  // the K selected entries: keys >= T
-  if (tid == 0) s_slot = 0;
+  // the K selected entries: candidate keys >= T (one LDS atomic per wave and pass)
+  if (tid == 0) f.nsel = 0;
   __syncthreads();
-  for (uint32_t i = tid; i < nc; i += kFinThreads) {
-    const uint64_t key = in_lds ? lk[i] : (((uint64_t)gk[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)gi[i]));
-    if (key >= T) sel[atomicAdd(&s_slot, 1u)] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
-  }
+  auto collect = [&](uint64_t key) {
+    const bool p = key >= T;
+    const uint64_t m = __ballot(p);
+    if (m == 0) return;
+    const int leader = __ffsll((long long)m) - 1;
+    uint32_t base = 0;
+    if (lane == leader) base = atomicAdd(&f.nsel, (uint32_t)__popcll(m));
+    base = __shfl(base, leader, 64);
+    const uint32_t slot = base + lanes_below(m);
+    if (p && slot < (uint32_t)K) f.sel[slot] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+  };
+  if (in_lds) for_each_cand<true>(lk, nc, cq, f, nb, collect);
+  else for_each_cand<false>(lk, nc, cq, f, nb, collect);
   __syncthreads();
+  int32_t* sel = f.sel;
   if (nv <= kBitmapBits) {
     // ascending order through a bitmap over the visible entries (reusing the candidate LDS)
     uint32_t* bm = reinterpret_cast<uint32_t*>(lk);
@@ -433,7 +604,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     uint32_t pc = 0;
     for (int64_t w = w0; w < w1; ++w) pc += __popc(bm[w]);
     uint32_t tot;
-    uint32_t pos = block_exclusive_scan<kFinThreads>(pc, tmp, &tot);
+    uint32_t pos = block_exclusive_scan<kFinThreads>(pc, f.tmp, &tot);
     for (int64_t w = w0; w < w1; ++w) {
       uint32_t bits = bm[w];
       while (bits) {
@@ -469,8 +640,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
 }  // namespace
 
 size_t index_ws_layout(int64_t nq, int64_t max_visible, void* ws, IndexArgs* a) {
-  const int64_t mv = (max_visible + 63) / 64 * 64;
-  const int64_t nblk = (max_visible + kBlockKeys - 1) / kBlockKeys;
+  const int64_t nblk = std::max<int64_t>(1, (max_visible + kBlockKeys - 1) / kBlockKeys);
   uintptr_t p = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
   const uintptr_t p0 = reinterpret_cast<uintptr_t>(ws);
   auto take = [&](size_t bytes) {
@@ -478,18 +648,16 @@ size_t index_ws_layout(int64_t nq, int64_t max_visible, void* ws, IndexArgs* a) 
     p = (p + bytes + 255) & ~uintptr_t(255);
     return reinterpret_cast<void*>(q);
   };
-  void* scores = take((size_t)nq * mv * 4);
-  void* ckey = take((size_t)nq * mv * 4);
-  void* cidx = take((size_t)nq * mv * 4);
-  void* bins = take((size_t)nq * (nblk > 0 ? nblk : 1) * 4);
-  void* counters = take((size_t)nq * 4 * 4);
+  void* scores = take((size_t)nq * nblk * kBlockKeys * 4);
+  void* cand = take((size_t)nq * nblk * kBlockKeys * 8);
+  void* cnt = take((size_t)nq * nblk * 4);
+  void* thr = take((size_t)nq * nblk * 8);
   if (a) {
     a->nblk = (int)nblk;
     a->scores = static_cast<uint32_t*>(scores);
-    a->cand_key = static_cast<uint32_t*>(ckey);
-    a->cand_idx = static_cast<int32_t*>(cidx);
-    a->blk_bin = static_cast<int32_t*>(bins);
-    a->counters = static_cast<uint32_t*>(counters);
+    a->cand = static_cast<uint64_t*>(cand);
+    a->blk_cnt = static_cast<uint32_t*>(cnt);
+    a->blk_thr = static_cast<uint64_t*>(thr);
   }
   return (size_t)(p - p0) + 256;
 }
@@ -500,8 +668,6 @@ hipError_t index_init() {
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
-  const int64_t nclr = 4 * (int64_t)a.nq;
-  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((nclr + 255) / 256)), dim3(256), 0, s, a.counters, nclr);
   if (a.max_visible > a.k) {
     const dim3 g((unsigned)a.nblk, (unsigned)a.nq);
     if (a.dtype == HCA_MXFP4) hipLaunchKernelGGL(score_mxfp4_kernel, g, dim3(256), 0, s, a);

@@ -44,12 +44,11 @@ struct IndexArgs {
   int m, k;
   int32_t* out;  // [nq, k]
   // workspace views for the batch (set by index_ws_layout)
-  int nblk;            // score blocks per query: ceil(max_visible / 1024)
-  uint32_t* scores;    // [nq, max_visible] order-preserving score keys
-  uint32_t* cand_key;  // [nq, max_visible] candidate score keys
-  int32_t* cand_idx;   // [nq, max_visible] their entry indices
-  int32_t* blk_bin;    // [nq, nblk] threshold bin of each score block
-  uint32_t* counters;  // [nq, 4]: candidates
+  int nblk;             // score blocks per query: ceil(max_visible / 1024)
+  uint32_t* scores;     // [nq, max_visible] order-preserving score keys
+  uint64_t* cand;       // [nq, nblk * 1024] per-block candidate keys (score key << 32 | ~j)
+  uint32_t* blk_cnt;    // [nq, nblk] candidates held by each score block's region
+  uint64_t* blk_thr;    // [nq, nblk] a block emitted exactly its keys >= this threshold
 };
 constexpr int kHistBins = 2048;
 constexpr int kMaxTopK = 2048;

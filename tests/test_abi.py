@@ -94,7 +94,7 @@ def index_call(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(qs=None), -1), (dict(d=128), -2), (dict(H=9), -2), (dict(H=0), -2),
     (dict(k=0), -1), (dict(k=4096), -1), (dict(m=0), -1), (dict(dt=2), -2), (dict(wsb=100), -3),
-    (dict(ws=None), -3), (dict(k_idx=ctypes.c_void_p(0x100004)), -1),
+    (dict(ws=None), -3), (dict(k_idx=ctypes.c_void_p(0x100004)), -1), (dict(mv=(1 << 21) + 1), -2),
 ])
 def test_index_rejects_bad_arguments(kw, status):
     assert index_call(**kw) == status
