@@ -400,25 +400,31 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg,
 
 // ---------------------------------------------------------------------------------------
 // MFMA path for split stores (FP8 E4M3 non-RoPE dims + power-of-two scale + bf16 RoPE dims,
-// 448 + 64), cache and window alike. Rows stay FP8 in LDS (half the bytes of bf16 rows):
-//  * a wave stages its 32-entry chunk with global_load_lds (16 bytes per lane straight into
-//    LDS, no VGPRs): 19 instructions fill 32 rows of 592 bytes (448 FP8 + 128 bf16 + 16 pad);
-//  * S^T = K Q^T: FP8 K operands are converted to bf16 with scale 1 after the LDS read; the
-//    entry's scale multiplies the FP8 part of the score, the RoPE part is added unscaled;
-//  * O^T += V^T P^T: V^T for the FP8 dims comes from ds_read_b64_tr_b8 transpose reads (8 entries
-//    of one dim per lane), the entry scales are folded into P (exact: powers of two); the RoPE
-//    dims use ds_read_b64_tr_b16 with the unscaled P;
-//  * each wave double-buffers: the DMA of its next chunk is in flight while it computes the
-//    current one (the waits on the DMA are explicit: s_waitcnt before a buffer is read or
-//    refilled), so 4 waves x 19 KB per CU are always on their way from HBM.
+// 448 + 64), cache and window alike. block = (query, group of 16 heads, split), 8 waves:
+//  * the split's list is walked in chunks of 128 entries staged in LDS as FP8 rows (double
+//    buffered); wave w stages and scores entries 16w .. 16w+15 of every chunk, one
+//    global_load_lds per row (36 lanes x 16 bytes: 448 FP8 bytes, then 128 RoPE bytes);
+//  * S^T = K Q^T runs on v_mfma_scale_f32_16x16x128_f8f6f4 with the FP8 rows as stored: the
+//    bf16 query is split into an FP8 high part and an FP8 residual, each with power-of-two
+//    scales per 32 dims, so hi + lo carries the query to about 2^-8 relative; the entry's
+//    scale multiplies the FP8 part of the score and the RoPE dims use
+//    v_mfma_f32_16x16x32_bf16;
+//  * the online softmax keeps one reference maximum per head for the whole block (the
+//    waves' chunk maxima meet in LDS), and P goes to LDS in bf16, with and without the entry
+//    scales;
+//  * O^T += V^T P^T is split by output dims: wave w owns dims 64w .. 64w+63 over all 128
+//    entries of the chunk (waves 0-6 the FP8 dims, read with ds_read_b64_tr_b8 and converted
+//    to bf16; wave 7 the RoPE dims, read with ds_read_b64_tr_b16), so O is never merged
+//    across waves.
 constexpr int kNope = 448;
 constexpr int kRope = 64;
-constexpr int kRowF8 = 592;                    // 448 + 128 + 16 pad
-constexpr int kBufF8 = 19 * 1024;              // 32 rows + the tail of the 19th load
-constexpr int kTabF8 = kChunk * 16;            // per entry: FP8-row and RoPE-row addresses
-constexpr int kWaveF8 = 2 * kBufF8 + kTabF8;   // double buffer + address table
-constexpr int kFp8Lds = 4 * kWaveF8;
-constexpr int kMergeRow = kD / 2 + 4;          // padded row (floats) of the per-wave O half in LDS
+constexpr int kRowF8 = 592;                 // 448 FP8 + 128 RoPE + 16 pad: conflict-free row reads
+constexpr int kCh = 128;                    // entries per chunk
+constexpr int kBufF8 = kCh * kRowF8;        // 75,776 bytes
+constexpr int kPRow = kCh + 8;              // bf16 per P row (padded)
+constexpr int kPBytes = 16 * kPRow * 2;     // 4,352 bytes
+constexpr int kF8Lds = 2 * kBufF8 + 2 * kPBytes + 2 * 8 * 16 * 4;  // 161,280 bytes
+static_assert(kF8Lds <= 160 * 1024, "LDS");
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
@@ -432,65 +438,52 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Rows of the 32 list positions base .. base+31 (lane e < 32 holds entry e): row (-1 if
-// none), which store, and the entry scale (its load is left in flight).
-struct ChunkRows {
-  int row;
-  float esc;
-  uint64_t vmask, wmask;
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Row sources of one wave's 16 entries of a chunk: lane e < 16 holds list position base + e.
+struct WaveRows {
+  uint64_t np, rp;  // FP8-row and RoPE-row addresses (lane e)
+  float esc;        // entry scale (lane e; its load is left in flight)
+  uint32_t vmask;   // valid entries
 };
 
-__device__ __forceinline__ ChunkRows chunk_rows(const AttnArgs& a, const QueryCtx& ctx, int qi, int64_t base,
-                                                int64_t hi, int lane) {
-  ChunkRows cr;
+__device__ __forceinline__ WaveRows wave_rows(const AttnArgs& a, const QueryCtx& ctx, int qi, int64_t base,
+                                              int64_t hi, int lane) {
+  WaveRows w;
   bool win = false;
   int64_t row = -1;
-  if (lane < kChunk) {
-    const int64_t r = base + lane;
-    row = r < hi ? list_row(a, ctx, qi, r, &win) : -1;
-  }
-  cr.row = (int)row;
-  cr.esc = row >= 0 ? (win ? a.win.scale : a.cache.scale)[row] : 0.f;
-  cr.vmask = __ballot(lane < kChunk && row >= 0);
-  cr.wmask = __ballot(lane < kChunk && win);
-  return cr;
+  if (lane < 16 && base + lane < hi) row = list_row(a, ctx, qi, base + lane, &win);
+  const StoreView& v = win ? a.win : a.cache;
+  w.np = reinterpret_cast<uint64_t>(v.data) + (uint64_t)(row * v.row_stride);
+  w.rp = reinterpret_cast<uint64_t>(v.rope) + (uint64_t)(row * v.rope_stride * 2) - kNope;
+  w.esc = row >= 0 ? v.scale[row] : 0.f;
+  w.vmask = (uint32_t)__ballot(lane < 16 && row >= 0);
+  return w;
 }
 
-// 19 global_load_lds of 16 bytes fill the 32 rows of 592 bytes (FP8 dims, RoPE dims, pad).
-// Lanes 0..31 first publish their entry's FP8-row address and RoPE-row address (minus 448, so
-// that adding the in-row byte offset works for both parts) in a per-wave LDS table; every lane
-// then reads the addresses its 19 loads need from the table with independent LDS reads.
-__device__ __forceinline__ void chunk_dma(const AttnArgs& a, const ChunkRows& cr, uint8_t* buf, uint64_t* tab,
-                                          int lane) {
-  const uint64_t dummy = reinterpret_cast<uint64_t>(a.q);
-  if (lane < kChunk) {
-    uint64_t np = dummy, rp = dummy;
-    if ((cr.vmask >> lane) & 1) {
-      const StoreView& v = ((cr.wmask >> lane) & 1) ? a.win : a.cache;
-      np = reinterpret_cast<uint64_t>(v.data) + (uint64_t)((int64_t)cr.row * v.row_stride);
-      rp = reinterpret_cast<uint64_t>(v.rope) + (uint64_t)((int64_t)cr.row * v.rope_stride * 2) - kNope;
+// One global_load_lds per valid row (lanes 0-27: FP8 bytes, 28-35: RoPE bytes); invalid rows
+// are zeroed so that their (masked) P = 0 never meets a NaN.
+__device__ __forceinline__ void stage_rows(const WaveRows& w, uint8_t* dst, int lane) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    uint8_t* rowp = dst + e * kRowF8;
+    if ((w.vmask >> e) & 1) {
+      const uint64_t n = readlane64(w.np, e), r = readlane64(w.rp, e);
+      const uint64_t src = (lane < 28 ? n : r) + 16 * (uint64_t)lane;
+      if (lane < 36)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (__attribute__((address_space(3))) void*)rowp, 16, 0, 0);
+    } else if (lane < kRowF8 / 16) {
+      *reinterpret_cast<uint4*>(rowp + 16 * lane) = make_uint4(0, 0, 0, 0);
     }
-    tab[2 * lane] = np;
-    tab[2 * lane + 1] = rp;
   }
-  wave_lds_sync();
-  uint64_t src[19];
-#pragma unroll
-  for (int i = 0; i < 19; ++i) {
-    const int b = 1024 * i + 16 * lane;
-    const int e = b / kRowF8;
-    const int off = b - e * kRowF8;
-    const bool data = e < kChunk && off < kNope + 2 * kRope;
-    const uint64_t t = tab[2 * (e < kChunk ? e : 0) + (off < kNope ? 0 : 1)];
-    src[i] = data ? t + (uint64_t)off : dummy;
-  }
-#pragma unroll
-  for (int i = 0; i < 19; ++i)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src[i]),
-                                     (__attribute__((address_space(3))) void*)(buf + 1024 * i), 16, 0, 0);
 }
 
-__global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, int total) {
+__global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, int total) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= total) return;
@@ -502,207 +495,250 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const int head = hg * 16 + c;
-  uint8_t* wbuf = smem + wave * kWaveF8;
-  uint64_t* tab = reinterpret_cast<uint64_t*>(wbuf + 2 * kBufF8);
+  uint16_t* pbs = reinterpret_cast<uint16_t*>(smem + 2 * kBufF8);  // [16][kPRow] P x entry scale
+  uint16_t* pb = pbs + 16 * kPRow;                                  // [16][kPRow] P
+  float* wmax = reinterpret_cast<float*>(pb + 16 * kPRow);          // [8][16]
+  float* wsum = wmax + 8 * 16;                                      // [8][16]
+
+  // query: FP8 hi/lo parts of the 448 non-RoPE dims. Operand layout of the 16x16x128 FP8
+  // MFMA: in K step ks, lane (g, c) holds dims 128ks + 16g .. +16 in bytes 0-15 and dims
+  // 128ks + 64 + 16g .. +16 in bytes 16-31; the 32-dim scale block b of the step is the pair
+  // of half rows (g = 0/1 low halves: b = 0, high halves: b = 2; g = 2/3: b = 1 and 3), and
+  // lane group g supplies block g's scale. Waves 0-3 build K step ks = wave for all lanes in
+  // the second chunk buffer (unused until the first chunk is staged); every wave then loads
+  // all four steps.
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * H + head) * kD;
+  uint8_t* qbuf = smem + kBufF8;  // [4 ks][64 lanes][32 hi + 32 lo bytes], then [4][64] scale words
+  uint32_t* qsc = reinterpret_cast<uint32_t*>(qbuf + 4 * 64 * 64);
+  uint4 qraw[4];
+  if (wave < 4) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int d0 = 128 * wave + 64 * half + 16 * g;
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+        qraw[2 * half + v] = d0 < kNope ? *reinterpret_cast<const uint4*>(qp + d0 + 8 * v) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  bf16x8 qr[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    qr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + kNope + 32 * ks + 8 * g));
 
   const QueryCtx ctx = query_ctx(a, qi);
   const int64_t N = ctx.n_c + ctx.n_w;
   const int64_t lo = (int64_t)s * a.per_split;
   const int64_t hi = min<int64_t>(N, lo + a.per_split);
+  // first chunk's rows in flight while the query is prepared
+  WaveRows cur = wave_rows(a, ctx, qi, lo + 16 * wave, hi, lane);
 
-  bf16x8 qv[kD / 32];
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * H + head) * kD + 8 * g;
+  if (wave < 4) {
+    float x[32];
 #pragma unroll
-  for (int ks = 0; ks < kD / 32; ++ks)
-    qv[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * ks));
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t w4[4] = {qraw[v].x, qraw[v].y, qraw[v].z, qraw[v].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * v + 2 * k] = __uint_as_float(w4[k] << 16);
+        x[8 * v + 2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+      }
+    }
+    float am[2] = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) am[j >> 4] = fmaxf(am[j >> 4], fabsf(x[j]));
+    int eb[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const float m = fmaxf(am[half], __shfl_xor(am[half], 16, 64));  // the other half row of the block
+      int E = 0;
+      if (m > 0.f) (void)frexpf(m, &E);  // m < 2^E: scaled values stay below 256
+      eb[half] = m > 0.f ? min(max(E - 8, -120), 120) : 0;
+    }
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = eb[j >> 2];
+      const float inv_hi = __builtin_ldexpf(1.f, -e), inv_lo = __builtin_ldexpf(1.f, 4 - e);
+      const float sc_hi = __builtin_ldexpf(1.f, e);
+      const float* xj = x + 4 * j;
+      int h2 = __builtin_amdgcn_cvt_pk_fp8_f32(xj[0] * inv_hi, xj[1] * inv_hi, 0, false);
+      h2 = __builtin_amdgcn_cvt_pk_fp8_f32(xj[2] * inv_hi, xj[3] * inv_hi, h2, true);
+      const float r0 = xj[0] - __builtin_amdgcn_cvt_f32_fp8(h2, 0) * sc_hi;
+      const float r1 = xj[1] - __builtin_amdgcn_cvt_f32_fp8(h2, 1) * sc_hi;
+      const float r2 = xj[2] - __builtin_amdgcn_cvt_f32_fp8(h2, 2) * sc_hi;
+      const float r3 = xj[3] - __builtin_amdgcn_cvt_f32_fp8(h2, 3) * sc_hi;
+      int l2 = __builtin_amdgcn_cvt_pk_fp8_f32(r0 * inv_lo, r1 * inv_lo, 0, false);
+      l2 = __builtin_amdgcn_cvt_pk_fp8_f32(r2 * inv_lo, r3 * inv_lo, l2, true);
+      hw[j] = (uint32_t)h2;
+      lw[j] = (uint32_t)l2;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(qbuf + (64 * wave + lane) * 64);
+    dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    dst[2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    dst[3] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+    // block g's exponent: g0 its low half, g1 the low half of g2 (block 1), g2 the high half of
+    // g0 (block 2), g3 its high half (block 3)
+    const int from_lo2 = __shfl(eb[0], 32 + c, 64), from_hi0 = __shfl(eb[1], c, 64);
+    const int eop = g == 0 ? eb[0] : g == 1 ? from_lo2 : g == 2 ? from_hi0 : eb[1];
+    qsc[64 * wave + lane] = (uint32_t)(eop + 127) | ((uint32_t)(eop - 4 + 127) << 8);
+  }
+  if (lo < hi) stage_rows(cur, smem + 16 * wave * kRowF8, lane);
+  __syncthreads();
+  i32x8 qh[4], ql[4];
+  uint32_t sh = 0, sl = 0;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4* src = reinterpret_cast<const uint4*>(qbuf + (64 * ks + lane) * 64);
+    const uint4 h0 = src[0], h1 = src[1], l0 = src[2], l1 = src[3];
+    qh[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+    ql[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+    const uint32_t sw = qsc[64 * ks + lane];
+    sh |= (sw & 255u) << (8 * ks);
+    sl |= ((sw >> 8) & 255u) << (8 * ks);
+  }
 
-  f32x4 O[kD / 16];
+  f32x4 O[4];
 #pragma unroll
-  for (int i = 0; i < kD / 16; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
   const float sl2 = a.scale * kLog2e;
 
-  int64_t base = lo + (int64_t)wave * kChunk;
-  ChunkRows cur = chunk_rows(a, ctx, qi, base, hi, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  if (base < hi) chunk_dma(a, cur, wbuf, tab, lane);
-  for (int it = 0; base < hi; ++it, base += 4 * kChunk) {
-    uint8_t* buf = wbuf + (it & 1) * kBufF8;
-    const int64_t nbase = base + 4 * kChunk;
-    ChunkRows nxt = chunk_rows(a, ctx, qi, nbase, hi, lane);
-    __builtin_amdgcn_s_waitcnt(0);  // this chunk's DMA and the next chunk's rows have landed
-    __builtin_amdgcn_wave_barrier();
-    // rows of invalid entries were filled from a dummy address: zero them (their scores are
-    // masked, but 0 * NaN would still reach O)
-    uint32_t inval = ~(uint32_t)cur.vmask;
-    while (inval) {
-      const int e = __builtin_ctz(inval);
-      inval &= inval - 1;
-      if (lane < kRowF8 / 16) *reinterpret_cast<uint4*>(buf + e * kRowF8 + 16 * lane) = make_uint4(0, 0, 0, 0);
-    }
-    wave_lds_sync();
-    if (nbase < hi) chunk_dma(a, nxt, wbuf + ((it + 1) & 1) * kBufF8, tab, lane);
-    const float esc = cur.esc;
-    const uint64_t vmask = cur.vmask;
+  for (int it = 0; lo + (int64_t)it * kCh < hi; ++it) {
+    const int64_t base = lo + (int64_t)it * kCh;
+    uint8_t* buf = smem + (it & 1) * kBufF8;
+    const bool more = base + kCh < hi;
+    WaveRows nxt = wave_rows(a, ctx, qi, base + kCh + 16 * wave, hi, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // this chunk's rows staged by this wave; next rows known
+    __syncthreads();                // all rows of the chunk; the other buffer is free
+    if (more) stage_rows(nxt, smem + ((it + 1) & 1) * kBufF8 + 16 * wave * kRowF8, lane);
 
-    // scores of the 8 entries this lane holds: 16mt + 4g + i
-    float escl[2][4];
-    bool vld[2][4];
+    // scores of this wave's 16 entries (lane: entries 4g + i, head c)
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, sr = s0;
+    {
+      const uint8_t* rowp = buf + (16 * wave + c) * kRowF8 + 16 * g;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 16 * mt + 4 * g + i;
-        escl[mt][i] = __shfl(esc, e, 64);
-        vld[mt][i] = (vmask >> e) & 1;
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(rowp + 128 * ks);
+        uint4 x1 = make_uint4(0, 0, 0, 0);  // dims 448.. (K step 3, bytes 16-31) are RoPE bytes: zero
+        if (ks < 3) x1 = *reinterpret_cast<const uint4*>(rowp + 128 * ks + 64);
+        const i32x8 A = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qh[ks], s0, 0, 0, 0, 127, 0, (int)((sh >> (8 * ks)) & 255u));
+        s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, ql[ks], s1, 0, 0, 0, 127, 0, (int)((sl >> (8 * ks)) & 255u));
       }
-    f32x4 st[2];
+      const uint8_t* ropep = buf + (16 * wave + c) * kRowF8 + kNope + 16 * g;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4 an = {0.f, 0.f, 0.f, 0.f}, ar = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* rowp = buf + (16 * mt + c) * kRowF8;
-#pragma unroll
-      for (int ks = 0; ks < kNope / 32; ++ks) {
-        const uint2 w8 = *reinterpret_cast<const uint2*>(rowp + 32 * ks + 8 * g);
-        an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(w8.x, w8.y), qv[ks], an, 0, 0, 0);
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ropep + 64 * ks));
+        sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qr[ks], sr, 0, 0, 0);
       }
-#pragma unroll
-      for (int ks = 0; ks < kRope / 32; ++ks) {
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowp + kNope + 64 * ks + 16 * g));
-        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[kNope / 32 + ks], ar, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[mt][i] = fmaf(escl[mt][i], an[i], ar[i]);
     }
-    float sv[8];
+    float sv[4], escl[4];
     float cmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[4 * mt + i] = vld[mt][i] ? st[mt][i] * sl2 : -INFINITY;
-        cmax = fmaxf(cmax, sv[4 * mt + i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * g + i;
+      escl[i] = __shfl(cur.esc, e, 64);
+      const float st = fmaf(escl[i], s0[i] + s1[i], sr[i]);
+      sv[i] = ((cur.vmask >> e) & 1) ? st * sl2 : -INFINITY;
+      cmax = fmaxf(cmax, sv[i]);
+    }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    if (g == 0) wmax[16 * wave + c] = cmax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 8; ++w) cmax = fmaxf(cmax, wmax[16 * w + c]);
     // lazy rescaling: the reference max moves only when a score exceeds it by more than 2^8
     // (log2 units), so p <= 256 and O is rescaled rarely instead of every chunk
     const bool grow = cmax > m_run + 8.f;
     const float m_ref = grow ? cmax : m_run;
     const bool none = m_ref == -INFINITY;
     const float corr = grow ? exp2f(m_run - cmax) : 1.f;
-    float p[8], psum = 0.f;
+    float p[4], psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       p[i] = none ? 0.f : exp2f(sv[i] - m_ref);
       psum += p[i];
     }
-    l_run = l_run * corr + psum;
+    l_part = l_part * corr + psum;
     m_run = m_ref;
     if (__ballot(grow)) {
 #pragma unroll
-      for (int dt = 0; dt < kD / 16; ++dt) O[dt] *= corr;
+      for (int dt = 0; dt < 4; ++dt) O[dt] *= corr;
     }
-    // P^T operands, contraction order [4g..4g+3, 16+4g..16+4g+3]; the FP8 one carries the scales
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
-    const bf16x8 pbs = __builtin_bit_cast(
-        bf16x8, make_uint4(pack_bf16x2(p[0] * escl[0][0], p[1] * escl[0][1]), pack_bf16x2(p[2] * escl[0][2], p[3] * escl[0][3]),
-                           pack_bf16x2(p[4] * escl[1][0], p[5] * escl[1][1]), pack_bf16x2(p[6] * escl[1][2], p[7] * escl[1][3])));
-    // FP8 dims: lane 2r + h of group g reads entry K_g[r], dims 16dt + 8h .. +8; lane i then holds
-    // that dim 16dt + i of the 8 entries K_g[0..7]
     {
+      const int pe = c * kPRow + 16 * wave + 4 * g;
+      *reinterpret_cast<uint2*>(pbs + pe) =
+          make_uint2(pack_bf16x2(p[0] * escl[0], p[1] * escl[1]), pack_bf16x2(p[2] * escl[2], p[3] * escl[3]));
+      *reinterpret_cast<uint2*>(pb + pe) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    }
+    __syncthreads();
+    // O^T (this wave's 64 dims x 16 heads) += V^T P^T over the chunk's 128 entries
+    if (wave < 7) {
       const int r = c >> 1, hsel = c & 1;
-      const int ent = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
-      const uint8_t* vp = buf + ent * kRowF8 + 8 * hsel;
 #pragma unroll
-      for (int dt = 0; dt < kNope / 16; ++dt) {
-        const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * dt));
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]), pbs, O[dt],
-                                                        0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pbs + c * kPRow + 32 * kk + 8 * g));
+        const uint8_t* vp = buf + (32 * kk + 8 * g + r) * kRowF8 + 64 * wave + 8 * hsel;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * dt));
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]), B, O[dt],
+                                                          0, 0, 0);
+        }
       }
-    }
-    // RoPE dims (bf16): lane 4r + qd of group g reads entry 4g + r (and 16 + 4g + r), dims 4qd .. +4
-    {
-      const int rsel = c >> 2, qd = c & 3;
-      const uint8_t* v0 = buf + (4 * g + rsel) * kRowF8 + kNope + 8 * qd;
-      const uint8_t* v1 = v0 + 16 * kRowF8;
+    } else {
+      const int rs = c >> 2, qd = c & 3;
 #pragma unroll
-      for (int dt = 0; dt < kRope / 16; ++dt) {
-        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * dt));
-        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * dt));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
-        O[kNope / 16 + dt] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, O[kNope / 16 + dt], 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + c * kPRow + 32 * kk + 8 * g));
+        const uint8_t* v0 = buf + (32 * kk + 8 * g + rs) * kRowF8 + kNope + 8 * qd;
+        const uint8_t* v1 = v0 + 4 * kRowF8;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * dt));
+          const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * dt));
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), B, O[dt], 0, 0, 0);
+        }
       }
     }
     cur = nxt;
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-
-  // merge the 4 waves through LDS in two halves of 256 dims (16 KB of O per wave each)
-  float* wm = reinterpret_cast<float*>(wbuf);
-  float* wl = wm + 16;
-  float* wo = wl + 16;
-  const int hc = tid >> 4, dl = (tid & 15) * 4;
-  const int hd = hg * 16 + hc;
+  // the softmax denominator: this lane's entries, then over the lane groups and the waves
+  l_part += __shfl_xor(l_part, 16, 64);
+  l_part += __shfl_xor(l_part, 32, 64);
+  if (g == 0) wsum[16 * wave + c] = l_part;
   __syncthreads();
-  if (g == 0) { wm[c] = m_run; wl[c] = l_run; }
-  float fw[4], inv = 0.f, lse = -INFINITY;
+  float L = 0.f;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int w = 0; w < 8; ++w) L += wsum[16 * w + c];
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float lse = L > 0.f ? (m_run + log2f(L)) * kLn2 : -INFINITY;
+  const int64_t hrow = (int64_t)qi * H + head;
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt)
-      *reinterpret_cast<f32x4*>(wo + c * kMergeRow + 16 * dt + 4 * g) = O[half * (kD / 32) + dt];
-    __syncthreads();
-    if (half == 0) {
-      float mw[4], M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        mw[w] = reinterpret_cast<const float*>(smem + w * kWaveF8)[hc];
-        M = fmaxf(M, mw[w]);
-      }
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        fw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
-        L += fw[w] * reinterpret_cast<const float*>(smem + w * kWaveF8)[16 + hc];
-      }
-      inv = L > 0.f ? 1.f / L : 0.f;
-      lse = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-    }
-#pragma unroll
-    for (int k = 0; k < kD / 128; ++k) {
-      const int dh = dl + 64 * k;           // dim within the half
-      const int d = half * (kD / 2) + dh;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        acc += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(smem + w * kWaveF8) + 32 + hc * kMergeRow + dh) *
-               fw[w];
-      acc *= inv;
-      if (a.n_split == 1) {
-        const int64_t oi = ((int64_t)qi * H + hd) * kD + d;
-        if (a.o_dtype == HCA_BF16) {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + oi) =
-              make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + oi) = acc;
-        }
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 64 * wave + 16 * dt + 4 * g;
+    const f32x4 acc = O[dt] * inv;
+    if (a.n_split == 1) {
+      if (a.o_dtype == HCA_BF16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + hrow * kD + d) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
       } else {
-        const int64_t pi = ((int64_t)qi * a.n_split + s) * H + hd;
-        *reinterpret_cast<f32x4*>(a.part_o + pi * kD + d) = acc;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + hrow * kD + d) = acc;
       }
+    } else {
+      const int64_t pi = ((int64_t)qi * a.n_split + s) * H + head;
+      *reinterpret_cast<f32x4*>(a.part_o + pi * kD + d) = acc;
     }
-    __syncthreads();
   }
-  if ((tid & 15) == 0) {
-    if (a.n_split == 1) a.lse[(int64_t)qi * H + hd] = lse;
-    else a.part_lse[((int64_t)qi * a.n_split + s) * H + hd] = lse;
+  if (wave == 0 && g == 0) {
+    if (a.n_split == 1) a.lse[hrow] = lse;
+    else a.part_lse[((int64_t)qi * a.n_split + s) * H + head] = lse;
   }
 }
 
@@ -792,7 +828,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(256), kFp8Lds, s, a, n_hg, total);
+    hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(512), kF8Lds, s, a, n_hg, total);
   } else if (mfma) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
@@ -814,7 +850,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 hipError_t attention_init() {
   hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)attn_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kFp8Lds);
+  return hipFuncSetAttribute((const void*)attn_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
 }
 
 }  // namespace hca

@@ -30,7 +30,8 @@
 //    [T, thr_b); such blocks are rescanned from their stored keys and the selection
 //    is repeated once, after which every key >= the new T is a candidate, so the
 //    result is exact for any input (ties included). The k indices are emitted in
-//    ascending order through an LDS bitmap over the visible entries.
+//    ascending order by bucketing them per score block and ranking each inside its
+//    bucket.
 #include "common.h"
 #include "internal.h"
 
@@ -38,10 +39,10 @@ namespace hca {
 namespace {
 
 constexpr int kBlockKeys = 1024;        // entries per score block
-constexpr int kFinThreads = 1024;       // finalize block
-constexpr int64_t kBitmapBits = 1 << 19;
-constexpr int kCandCap = 16384;         // candidates held in LDS by finalize (128 KB)
+constexpr int kFinThreads = 512;        // finalize block
+constexpr int kCandCap = 8192;          // candidates finalize holds in registers
 constexpr int kMaxBlk = 2048;           // score blocks per query (max_visible <= 2^21)
+constexpr int kBpt = kMaxBlk / kFinThreads;  // score blocks per finalize thread
 
 __device__ __forceinline__ int64_t visible_keys(const IndexArgs& a, int qi, int64_t* row0) {
   const int b = a.q_seq[qi];
@@ -62,12 +63,7 @@ __device__ __forceinline__ int64_t visible_keys(const IndexArgs& a, int qi, int6
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds_tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(x, off, 64);
-    if (lane >= off) x += t;
-  }
+  const uint32_t x = wave_incl_scan_add(v);
   if (lane == 63) lds_tmp[wave] = x;
   __syncthreads();
   uint32_t wbase = 0, tot = 0;
@@ -91,19 +87,19 @@ __device__ __forceinline__ void find_crossing(const uint32_t* c, uint32_t rem, i
   constexpr int G = 4 * PER;  // counters per lane
   uint32_t v[G];
   uint32_t own = 0;
+  const uint4* c4 = reinterpret_cast<const uint4*>(c);
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    v[i] = c[G * lane + i];
-    own += v[i];
+  for (int i = 0; i < G / 4; ++i) {
+    const uint4 q = c4[(G / 4) * lane + i];
+    v[4 * i] = q.x;
+    v[4 * i + 1] = q.y;
+    v[4 * i + 2] = q.z;
+    v[4 * i + 3] = q.w;
+    own += q.x + q.y + q.z + q.w;
   }
-  uint32_t suf = own;  // inclusive suffix sum over lanes lane..63
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_down(suf, off, 64);
-    if (lane + off < 64) suf += t;
-  }
-  uint32_t nxt = __shfl_down(suf, 1, 64);
-  if (lane == 63) nxt = 0;
+  const uint32_t pre = wave_incl_scan_add(own);
+  const uint32_t nxt = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre;  // sum over lanes > lane
+  const uint32_t suf = nxt + own;                                                 // sum over lanes >= lane
   if (suf >= rem && nxt < rem) {
     uint32_t acc = nxt;
     int d = G * lane;
@@ -117,40 +113,57 @@ __device__ __forceinline__ void find_crossing(const uint32_t* c, uint32_t rem, i
   }
 }
 
+struct CrossLds {
+  int dc, d;
+  uint32_t ac, above;
+};
+
+// Over 2048 counters h in LDS with NT threads: *d = the largest bin with
+// sum_{i >= d} h[i] >= rem and *above = sum_{i > d} h[i]. Requires sum >= rem >= 1; part is
+// NT words of LDS. Reads are 16-byte vectors so that the threads hit distinct LDS banks.
+// Ends with the block synchronised.
+template <int NT>
+__device__ __forceinline__ void crossing2048(const uint32_t* h, uint32_t* part, uint32_t rem, CrossLds& x, int* d,
+                                             uint32_t* above) {
+  constexpr int B = kHistBins / NT;  // bins per thread
+  const int tid = threadIdx.x;
+  const uint4* h4 = reinterpret_cast<const uint4*>(h);
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < B / 4; ++i) {
+    const uint4 q = h4[(B / 4) * tid + i];
+    s += q.x + q.y + q.z + q.w;
+  }
+  part[tid] = s;
+  __syncthreads();
+  if (tid < 64) find_crossing<NT / 256>(part, rem, &x.dc, &x.ac);
+  __syncthreads();
+  if (tid == x.dc) {
+    uint32_t acc = x.ac;
+    int b = B * tid + B - 1;
+    for (; b > B * tid; --b) {
+      if (acc + h[b] >= rem) break;
+      acc += h[b];
+    }
+    x.d = b;
+    x.above = acc;
+  }
+  __syncthreads();
+  *d = x.d;
+  *above = x.above;
+}
+
 struct BlockLds {
   uint32_t hist[kHistBins];
   uint32_t key[kBlockKeys];
   uint32_t part[256];
   uint32_t tmp[8];
-  int d, bin;
-  uint32_t above, above_bin;
+  CrossLds cx;
   uint64_t thr;
 };
 
-// Over the 2048 counters lds.hist (256 threads): the largest bin d with sum_{i >= d} >= rem
-// and above = sum_{i > d}. Requires sum >= rem >= 1. Ends with the block synchronised.
 __device__ __forceinline__ void block_crossing(BlockLds& lds, uint32_t rem, int* d, uint32_t* above) {
-  const int tid = threadIdx.x;
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sum += lds.hist[8 * tid + i];
-  lds.part[tid] = sum;
-  __syncthreads();
-  if (tid < 64) find_crossing<1>(lds.part, rem, &lds.d, &lds.above);
-  __syncthreads();
-  if (tid == lds.d) {
-    uint32_t acc = lds.above;
-    int b = 8 * tid + 7;
-    for (; b > 8 * tid; --b) {
-      if (acc + lds.hist[b] >= rem) break;
-      acc += lds.hist[b];
-    }
-    lds.bin = b;
-    lds.above_bin = acc;
-  }
-  __syncthreads();
-  *d = lds.bin;
-  *above = lds.above_bin;
+  crossing2048<256>(lds.hist, lds.part, rem, lds.cx, d, above);
 }
 
 // Candidates of a block: L = max(16, ceil(2 k 1024 / n_vis)), about twice the block's share of
@@ -158,6 +171,8 @@ __device__ __forceinline__ void block_crossing(BlockLds& lds, uint32_t rem, int*
 __device__ __forceinline__ uint32_t block_quota(int k, int64_t nv) {
   return (uint32_t)max<int64_t>(16, (2 * (int64_t)k * kBlockKeys + nv - 1) / nv);
 }
+// Candidate slots per block: a block emits at most 2L keys (and at most its 1024 entries).
+__device__ __forceinline__ uint32_t region_slots(uint32_t L) { return min(2 * L, (uint32_t)kBlockKeys); }
 
 // Candidate emission of one score block (all 256 threads; lds.key / lds.hist complete).
 // Thread tid owns block positions 4 tid .. 4 tid + 3.
@@ -230,10 +245,12 @@ __device__ void emit_candidates(const IndexArgs& a, int qi, int64_t jb, int64_t 
   uint32_t tot;
   uint32_t off = block_exclusive_scan<256>(n, lds.tmp, &tot);
   const int64_t slot = (int64_t)qi * a.nblk + blockIdx.x;
-  uint64_t* dst = a.cand + slot * kBlockKeys;
+  const uint32_t R = region_slots(L);
+  uint64_t* dst = a.cand + (int64_t)qi * a.nblk * kBlockKeys + (int64_t)blockIdx.x * R;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (t0 + i < nvalid && k64[i] >= thr) dst[off++] = k64[i];
+  for (uint32_t i = tot + tid; i < R; i += 256) dst[i] = 0;
   uint32_t* sk = a.scores + (int64_t)qi * a.nblk * kBlockKeys + jb;
   if (t0 + 3 < nvalid) {
     *reinterpret_cast<uint4*>(sk + t0) = kv;
@@ -242,10 +259,7 @@ __device__ void emit_candidates(const IndexArgs& a, int qi, int64_t jb, int64_t 
     for (int i = 0; i < 4; ++i)
       if (t0 + i < nvalid) sk[t0 + i] = kk[i];
   }
-  if (tid == 0) {
-    a.blk_cnt[slot] = tot;
-    a.blk_thr[slot] = thr;
-  }
+  if (tid == 0) a.blk_thr[slot] = thr;
 }
 
 // MXFP4 scores via the scaled MFMA. grid = (nblk, nq), 256 threads, 1024 keys per block.
@@ -259,7 +273,7 @@ __global__ __launch_bounds__(256) void score_mxfp4_kernel(IndexArgs a) {
   if (jb >= nv) return;
   for (int i = threadIdx.x; i < kHistBins; i += 256) lds.hist[i] = 0;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 31, blk = lane >> 5;
   const uint8_t* qb = static_cast<const uint8_t*>(a.q);
   const uint8_t* kb = static_cast<const uint8_t*>(a.keys);
@@ -376,36 +390,43 @@ __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Finalisation: one block of 1024 threads per query.
+// Finalisation: one block of kFinThreads threads per query.
+
+constexpr int kListCap = kHistBins / 2;         // keys of one bin ranked exactly (the histogram's LDS)
+constexpr int kPer = kCandCap / kFinThreads;    // candidates per thread, held in registers
 
 struct FinLds {
-  uint32_t h[kHistBins];        // radix histogram; list of flagged blocks
-  int32_t sel[kMaxTopK];        // the selected entries
-  uint32_t pre[kMaxBlk + 1];    // exclusive prefix of the per-block candidate counts
+  uint32_t h[kHistBins];  // histogram; keys of the crossing bin (as u64); flagged blocks; output
+  int32_t sel[kMaxTopK];  // the selected entries
+  int32_t sel_sink[64];   // per-lane targets of writes that select nothing (branch-free code)
+  uint64_t list_sink[64];
+  uint32_t part[kFinThreads];
   uint32_t tmp[32];
-  uint64_t kmin, kmax;
-  int d;
-  uint32_t above, nsel, nflag;
+  CrossLds cx;
+  uint64_t kmin, kmax, T;
+  uint32_t smin, smax, nsel, nflag, novf;
+};
+
+// The candidates of one query: ns slots of the score blocks (0 = empty) and novf rescanned keys.
+struct CandSet {
+  const uint64_t* slots;
+  uint32_t ns;
+  const uint64_t* ovf;
+  uint32_t novf;
 };
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Calls f(key) once for every candidate: from LDS (lk[0..nc)) or from the per-block regions.
-template <bool kLds, class F>
-__device__ __forceinline__ void for_each_cand(const uint64_t* lk, uint32_t nc, const uint64_t* cq, const FinLds& f,
-                                              int nb, F fn) {
-  if (kLds) {
-    for (uint32_t i = threadIdx.x; i < nc; i += kFinThreads) fn(lk[i]);
-  } else {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int b = wave; b < nb; b += kFinThreads / 64) {
-      const uint32_t c = f.pre[b + 1] - f.pre[b];
-      for (uint32_t i = lane; i < c; i += 64) fn(cq[(int64_t)b * kBlockKeys + i]);
-    }
-  }
+__device__ __forceinline__ int32_t key_entry(uint64_t key) { return (int32_t)(0xFFFFFFFFu - (uint32_t)key); }
+
+// The score whose float_key is k (the top half of a candidate key).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
+
+
 
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
 #pragma unroll
@@ -426,99 +447,246 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// Per-block counts -> f.pre, then (if they fit) the candidates into lk; f.kmin / f.kmax get
-// the smallest and largest candidate key. Returns the candidate count.
-__device__ uint32_t gather_candidates(const uint32_t* cnt, const uint64_t* cq, int nb, uint64_t* lk, FinLds& f) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t c0 = 2 * tid < nb ? cnt[2 * tid] : 0u, c1 = 2 * tid + 1 < nb ? cnt[2 * tid + 1] : 0u;
-  uint32_t nc;
-  const uint32_t off = block_exclusive_scan<kFinThreads>(c0 + c1, f.tmp, &nc);
-  f.pre[2 * tid] = off;
-  f.pre[2 * tid + 1] = off + c0;
-  if (tid == 0) {
-    f.pre[nb] = nc;
+// f.kmin / f.kmax <- the smallest and largest of the per-thread extremes lo / hi.
+__device__ __forceinline__ void block_min_max(uint64_t lo, uint64_t hi, FinLds& f) {
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  if (threadIdx.x == 0) {
     f.kmin = ~0ull;
     f.kmax = 0;
   }
   __syncthreads();
-  uint64_t lo = ~0ull, hi = 0;
-  if (nc <= (uint32_t)kCandCap) {
-    constexpr int kBatch = 8, kStride = kFinThreads / 64;
-    for (int b0 = wave; b0 < nb; b0 += kStride * kBatch) {
-      uint64_t v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int b = b0 + kStride * u;
-        const uint32_t c = b < nb ? f.pre[b + 1] - f.pre[b] : 0u;
-        v[u] = (uint32_t)lane < c ? cq[(int64_t)b * kBlockKeys + lane] : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int b = b0 + kStride * u;
-        const uint32_t c = b < nb ? f.pre[b + 1] - f.pre[b] : 0u;
-        for (uint32_t i = lane; i < c; i += 64) {
-          const uint64_t x = i == (uint32_t)lane ? v[u] : cq[(int64_t)b * kBlockKeys + i];
-          lk[f.pre[b] + i] = x;
-          lo = x < lo ? x : lo;
-          hi = x > hi ? x : hi;
-        }
-      }
-    }
-  } else {
-    for_each_cand<false>(lk, nc, cq, f, nb, [&](uint64_t x) {
-      lo = x < lo ? x : lo;
-      hi = x > hi ? x : hi;
-    });
-  }
-  lo = wave_min_u64(lo);
-  hi = wave_max_u64(hi);
-  if (lane == 0) {
+  if ((threadIdx.x & 63) == 0) {
     atomicMin(reinterpret_cast<unsigned long long*>(&f.kmin), (unsigned long long)lo);
     atomicMax(reinterpret_cast<unsigned long long*>(&f.kmax), (unsigned long long)hi);
   }
   __syncthreads();
-  return nc;
 }
 
-// The K-th largest of the nc >= K unique candidate keys: returns T such that exactly K
-// candidates are >= T. Radix passes of 11 bits start below the bits every candidate shares
-// and stop once the bin holding the K-th key is taken whole.
-template <bool kLds>
-__device__ uint64_t select_kth(const uint64_t* lk, uint32_t nc, const uint64_t* cq, FinLds& f, int nb, uint32_t K) {
-  const int tid = threadIdx.x;
-  const uint64_t kmin = f.kmin, kmax = f.kmax;
-  if (kmin == kmax) return kmin;
-  int lo = 64 - __clzll((long long)(kmin ^ kmax));  // bits >= lo are common to all candidates
-  uint64_t prefix = lo >= 64 ? 0ull : (kmax >> lo) << lo;
-  uint32_t rem = K;
-  while (true) {
-    const int hi = lo, width = min(11, lo);
-    lo -= width;
-    for (int i = tid; i < kHistBins; i += kFinThreads) f.h[i] = 0;
-    __syncthreads();
-    const uint64_t want = hi >= 64 ? 0ull : prefix >> hi;
-    const uint32_t dmask = (1u << width) - 1u;
-    for_each_cand<kLds>(lk, nc, cq, f, nb, [&](uint64_t key) {
-      if (hi >= 64 || (key >> hi) == want) atomicAdd(&f.h[(uint32_t)(key >> lo) & dmask], 1u);
-    });
-    __syncthreads();
-    if (tid < 64) find_crossing<8>(f.h, rem, &f.d, &f.above);
-    __syncthreads();
-    const int d = f.d;
-    rem -= f.above;
-    prefix |= (uint64_t)d << lo;
-    const bool done = f.h[d] == rem || lo == 0;
-    __syncthreads();
-    if (done) return prefix;
+// Monotone map of a candidate key to one of 2048 equal-width bins of the score range between
+// the score keys k0 < k1.
+struct ScoreBins {
+  float s0, inv;
+  __device__ __forceinline__ ScoreBins(uint32_t k0, uint32_t k1) {
+    s0 = key_score(k0);
+    inv = 2047.0f / (key_score(k1) - s0);
   }
+  __device__ __forceinline__ int operator()(uint64_t key) const {
+    return (int)fminf(fmaxf(__fmul_rn(__fsub_rn(key_score((uint32_t)(key >> 32)), s0), inv), 0.f), 2047.f);
+  }
+};
+
+// Selection with the candidates in registers (v[i], 0 = empty; at least K non-empty, unique).
+// Returns T, the K-th largest key (exactly K keys are >= T), and writes those K entries to
+// f.sel (unordered). First pass: a histogram over 2048 equal-width bins of the candidates'
+// score range; the keys of the bin holding the K-th key are then ranked exactly among
+// themselves, and every selected key is placed by a block scan or by its rank, without
+// atomics. Equal scores throughout, or a crossing bin with more than kListCap keys (heavy
+// ties), are resolved by 11-bit radix passes below the bits all candidates share.
+__device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint32_t K, FinLds& f) {
+  const int tid = threadIdx.x;
+  // Elementwise steps below are written without branches (selects, sink addresses): in this
+  // one-pass kernel every taken branch is a likely instruction-cache miss.
+  const int lane = tid & 63;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint32_t k = (uint32_t)(v[i] >> 32);  // 0 for an empty slot
+    lo = min(lo, v[i] ? k : 0xFFFFFFFFu);
+    hi = max(hi, k);
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (tid == 0) {
+    f.smin = 0xFFFFFFFFu;
+    f.smax = 0;
+  }
+  for (int i = tid; i < kHistBins; i += kFinThreads) f.h[i] = 0;
+  __syncthreads();
+  if ((tid & 63) == 0) {
+    atomicMin(&f.smin, lo);
+    atomicMax(&f.smax, hi);
+  }
+  __syncthreads();
+  if (f.smin != f.smax) {
+    const ScoreBins bin(f.smin, f.smax);
+    int bn[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int b = bin(v[i]);
+      bn[i] = v[i] ? b : -1;
+      atomicAdd(v[i] ? &f.h[b] : &f.part[tid], 1u);  // part[] is rewritten by the crossing search
+    }
+    __syncthreads();
+    int d;
+    uint32_t above;
+    crossing2048<kFinThreads>(f.h, f.part, K, f.cx, &d, &above);
+    const uint32_t rem = K - above, cd = f.h[d];
+    __syncthreads();
+    if (cd <= (uint32_t)kListCap) {
+      uint64_t* list = reinterpret_cast<uint64_t*>(f.h);
+      uint32_t na = 0, nl = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        na += bn[i] > d;
+        nl += bn[i] == d;
+      }
+      uint32_t tot;
+      const uint32_t off = block_exclusive_scan<kFinThreads>(na | (nl << 16), f.tmp, &tot);
+      uint32_t oa = off & 0xFFFFu, ol = off >> 16;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const bool a = bn[i] > d, l = bn[i] == d;
+        *(a ? &f.sel[min(oa, K - 1)] : &f.sel_sink[lane]) = key_entry(v[i]);
+        *(l ? &list[min(ol, (uint32_t)kListCap - 1)] : &f.list_sink[lane]) = v[i];
+        oa += a;
+        ol += l;
+      }
+      __syncthreads();
+      // rank within the bin: a key with g larger keys is selected iff g < rem
+      for (uint32_t i = tid; i < cd; i += kFinThreads) {
+        const uint64_t x = list[i];
+        uint32_t g = 0;
+        for (uint32_t j = 0; j < cd; ++j) g += list[j] > x;
+        if (g < rem) f.sel[above + g] = key_entry(x);
+        if (g == rem - 1) f.T = x;
+      }
+      __syncthreads();
+      return f.T;
+    }
+  }
+  // radix passes (heavy ties, or a single candidate)
+  uint64_t klo = ~0ull, khi = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (v[i]) klo = v[i] < klo ? v[i] : klo;
+    khi = v[i] > khi ? v[i] : khi;
+  }
+  block_min_max(klo, khi, f);
+  const uint64_t kmin = f.kmin, kmax = f.kmax;
+  uint64_t T = kmin;
+  if (kmin != kmax) {
+    int lb = 64 - __clzll((long long)(kmin ^ kmax));  // bits >= lb are common to all candidates
+    uint64_t prefix = lb >= 64 ? 0ull : (kmax >> lb) << lb;
+    uint32_t rem = K;
+    while (true) {
+      const int hb = lb, width = min(11, lb);
+      lb -= width;
+      for (int i = tid; i < kHistBins; i += kFinThreads) f.h[i] = 0;
+      __syncthreads();
+      const uint64_t want = hb >= 64 ? 0ull : prefix >> hb;
+      const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const bool m = v[i] && (hb >= 64 || (v[i] >> hb) == want);
+        atomicAdd(m ? &f.h[(uint32_t)(v[i] >> lb) & dmask] : &f.part[tid], 1u);
+      }
+      __syncthreads();
+      int d;
+      uint32_t above;
+      crossing2048<kFinThreads>(f.h, f.part, rem, f.cx, &d, &above);
+      rem -= above;
+      prefix |= (uint64_t)d << lb;
+      const bool done = f.h[d] == rem || lb == 0;
+      __syncthreads();
+      if (done) break;
+    }
+    T = prefix;
+  }
+  uint32_t n = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) n += v[i] >= T;  // T > 0, so empty slots never count
+  uint32_t tot;
+  uint32_t o = block_exclusive_scan<kFinThreads>(n, f.tmp, &tot);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool s = v[i] >= T;
+    *(s ? &f.sel[min(o, K - 1)] : &f.sel_sink[tid & 63]) = key_entry(v[i]);
+    o += s;
+  }
+  __syncthreads();
+  return T;
 }
 
-__host__ __device__ __forceinline__ int64_t bitmap_words(int64_t nv) { return (nv + 31) >> 5; }
+// Appends x to list[] (counter *n) with one LDS atomic per wave; p says whether this lane appends.
+template <class Tv>
+__device__ __forceinline__ void wave_append(bool p, Tv x, Tv* list, uint32_t* n, uint32_t cap) {
+  const uint64_t m = __ballot(p);
+  if (m == 0) return;
+  const int lane = threadIdx.x & 63, leader = __ffsll((long long)m) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(n, (uint32_t)__popcll(m));
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+  const uint32_t slot = base + lanes_below(m);
+  if (p && slot < cap) list[slot] = x;
+}
+
+// Calls fn(key) for every candidate held in global memory (empty slots skipped).
+template <class F>
+__device__ __forceinline__ void for_each_global(const CandSet& cs, F fn) {
+  for (uint32_t i = threadIdx.x; i < cs.ns; i += kFinThreads) {
+    const uint64_t key = cs.slots[i];
+    if (key) fn(key);
+  }
+  for (uint32_t i = threadIdx.x; i < cs.novf; i += kFinThreads) fn(cs.ovf[i]);
+}
+
+// Selection over more candidates than the registers hold: the same steps as select_regs, with
+// every pass reading the candidates from global memory and LDS atomics for the appends.
+__device__ uint64_t select_global(const CandSet& cs, uint32_t K, FinLds& f) {
+  const int tid = threadIdx.x;
+  uint64_t lo = ~0ull, hi = 0;
+  for_each_global(cs, [&](uint64_t x) {
+    lo = x < lo ? x : lo;
+    hi = x > hi ? x : hi;
+  });
+  block_min_max(lo, hi, f);
+  const uint64_t kmin = f.kmin, kmax = f.kmax;
+  if (tid == 0) f.nsel = 0;
+  uint64_t T = kmin;
+  if (kmin != kmax) {
+    int lb = 64 - __clzll((long long)(kmin ^ kmax));
+    uint64_t prefix = lb >= 64 ? 0ull : (kmax >> lb) << lb;
+    uint32_t rem = K;
+    while (true) {
+      const int hb = lb, width = min(11, lb);
+      lb -= width;
+      for (int i = tid; i < kHistBins; i += kFinThreads) f.h[i] = 0;
+      __syncthreads();
+      const uint64_t want = hb >= 64 ? 0ull : prefix >> hb;
+      const uint32_t dmask = (1u << width) - 1u;
+      for_each_global(cs, [&](uint64_t key) {
+        if (hb >= 64 || (key >> hb) == want) atomicAdd(&f.h[(uint32_t)(key >> lb) & dmask], 1u);
+      });
+      __syncthreads();
+      int d;
+      uint32_t above;
+      crossing2048<kFinThreads>(f.h, f.part, rem, f.cx, &d, &above);
+      rem -= above;
+      prefix |= (uint64_t)d << lb;
+      const bool done = f.h[d] == rem || lb == 0;
+      __syncthreads();
+      if (done) break;
+    }
+    T = prefix;
+  }
+  __syncthreads();
+  for_each_global(cs, [&](uint64_t key) { wave_append<int32_t>(key >= T, key_entry(key), f.sel, &f.nsel, K); });
+  __syncthreads();
+  return T;
+}
+
+// Output LDS: per-block counts (then their prefix), per-block cursors, entries bucketed by block.
+struct OutLds {
+  uint32_t pre[kMaxBlk + 1];
+  uint32_t cur[kMaxBlk];
+  int32_t bucket[kMaxTopK];
+};
 
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
-  extern __shared__ uint64_t lk[];  // kCandCap candidate keys, later the output bitmap
   __shared__ FinLds f;
-  const int qi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ OutLds ol;
+  const int qi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.k;
   int64_t rb;
   const int64_t nv = visible_keys(a, qi, &rb);
@@ -529,112 +697,113 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
   }
   const int nb = (int)((nv + kBlockKeys - 1) / kBlockKeys);
   const int64_t q_blk = (int64_t)qi * a.nblk;
-  uint32_t* cnt = a.blk_cnt + q_blk;
   const uint64_t* thr = a.blk_thr + q_blk;
-  uint64_t* cq = a.cand + q_blk * kBlockKeys;
   const uint32_t* sk = a.scores + q_blk * kBlockKeys;
-  uint32_t nc = gather_candidates(cnt, cq, nb, lk, f);
-  bool in_lds = nc <= (uint32_t)kCandCap;
-  uint64_t T = in_lds ? select_kth<true>(lk, nc, cq, f, nb, (uint32_t)K) : select_kth<false>(lk, nc, cq, f, nb, (uint32_t)K);
-  // blocks whose unemitted keys (all below their threshold) may reach T
-  if (tid == 0) f.nflag = 0;
-  __syncthreads();
-  for (int b = tid; b < nb; b += kFinThreads)
-    if (thr[b] > T) f.h[atomicAdd(&f.nflag, 1u)] = (uint32_t)b;
-  __syncthreads();
-  const uint32_t nflag = f.nflag;
-  if (nflag > 0) {
-    // append their unemitted keys >= T to their own regions, one wave per block
+  uint64_t* ovf = a.ovf + q_blk * kBlockKeys;
+  CandSet cs;
+  cs.slots = a.cand + q_blk * kBlockKeys;
+  cs.ns = (uint32_t)nb * region_slots(block_quota(K, nv));
+  cs.ovf = ovf;
+  cs.novf = 0;
+  // thresholds of blocks kBpt * tid + i
+  uint64_t tq[kBpt];
+#pragma unroll
+  for (int i = 0; i < kBpt; ++i) {
+    const int b = kBpt * tid + i;
+    const uint64_t tv = thr[min(b, nb - 1)];
+    tq[i] = b < nb ? tv : 0ull;
+  }
+  if (tid == 0) f.novf = 0;
+  for (int round = 0;; ++round) {
+    const uint32_t n = cs.ns + cs.novf;
+    uint64_t T;
+    if (n <= (uint32_t)kCandCap) {
+      uint64_t v[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {  // unconditional loads from clamped slots stay in flight together
+        const uint32_t s = min((uint32_t)(tid + kFinThreads * i), n - 1);
+        v[i] = *(s < cs.ns ? cs.slots + s : cs.ovf + (s - cs.ns));
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (tid + kFinThreads * i >= (int)n) v[i] = 0;
+      T = select_regs(v, (uint32_t)K, f);
+    } else {
+      T = select_global(cs, (uint32_t)K, f);
+    }
+    if (round == 1) break;
+    // blocks whose unemitted keys (all below their threshold) may reach T
+    if (tid == 0) f.nflag = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kBpt; ++i)
+      if (tq[i] > T) f.h[atomicAdd(&f.nflag, 1u)] = (uint32_t)(kBpt * tid + i);
+    __syncthreads();
+    const uint32_t nflag = f.nflag;
+    if (nflag == 0) break;
+    // add their unemitted keys >= T to the overflow list (one wave per block), select again
     for (uint32_t fi = wave; fi < nflag; fi += kFinThreads / 64) {
       const int b = (int)f.h[fi];
       const int64_t jb = (int64_t)b * kBlockKeys;
       const uint64_t tb = thr[b];
-      uint32_t c = cnt[b];
       uint32_t kv[kBlockKeys / 64];
 #pragma unroll
-      for (int r = 0; r < kBlockKeys / 64; ++r) {
-        const int64_t j = jb + lane + 64 * r;
-        kv[r] = j < nv ? sk[j] : 0u;
-      }
+      for (int r = 0; r < kBlockKeys / 64; ++r) kv[r] = sk[min<int64_t>(jb + lane + 64 * r, nv - 1)];
 #pragma unroll
       for (int r = 0; r < kBlockKeys / 64; ++r) {
         const int64_t j = jb + lane + 64 * r;
         const uint64_t k64 = ((uint64_t)kv[r] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-        const bool p = j < nv && k64 < tb && k64 >= T;
-        const uint64_t m = __ballot(p);
-        if (p) cq[jb + c + lanes_below(m)] = k64;
-        c += (uint32_t)__popcll(m);
+        wave_append<uint64_t>(j < nv && k64 < tb && k64 >= T, k64, ovf, &f.novf, (uint32_t)(a.nblk * kBlockKeys));
       }
-      if (lane == 0) cnt[b] = c;
     }
     __threadfence_block();
     __syncthreads();
-    nc = gather_candidates(cnt, cq, nb, lk, f);
-    in_lds = nc <= (uint32_t)kCandCap;
-    T = in_lds ? select_kth<true>(lk, nc, cq, f, nb, (uint32_t)K) : select_kth<false>(lk, nc, cq, f, nb, (uint32_t)K);
+    cs.novf = f.novf;
+    __syncthreads();
   }
-  // the K selected entries: candidate keys >= T (one LDS atomic per wave and pass)
-  if (tid == 0) f.nsel = 0;
+  // ascending order: bucket the K entries by score block, then rank each within its bucket
+  const int32_t* sel = f.sel;
+  for (int b = tid; b < nb; b += kFinThreads) ol.pre[b] = 0;
   __syncthreads();
-  auto collect = [&](uint64_t key) {
-    const bool p = key >= T;
-    const uint64_t m = __ballot(p);
-    if (m == 0) return;
-    const int leader = __ffsll((long long)m) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(&f.nsel, (uint32_t)__popcll(m));
-    base = __shfl(base, leader, 64);
-    const uint32_t slot = base + lanes_below(m);
-    if (p && slot < (uint32_t)K) f.sel[slot] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
-  };
-  if (in_lds) for_each_cand<true>(lk, nc, cq, f, nb, collect);
-  else for_each_cand<false>(lk, nc, cq, f, nb, collect);
+  const uint32_t last = (uint32_t)nb - 1;
+  for (int i = tid; i < K; i += kFinThreads) atomicAdd(&ol.pre[min((uint32_t)sel[i] >> 10, last)], 1u);
   __syncthreads();
-  int32_t* sel = f.sel;
-  if (nv <= kBitmapBits) {
-    // ascending order through a bitmap over the visible entries (reusing the candidate LDS)
-    uint32_t* bm = reinterpret_cast<uint32_t*>(lk);
-    const int64_t nw = bitmap_words(nv);
-    for (int64_t i = tid; i < nw; i += kFinThreads) bm[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < K; i += kFinThreads) atomicOr(&bm[sel[i] >> 5], 1u << (sel[i] & 31));
-    __syncthreads();
-    const int64_t per = (nw + kFinThreads - 1) / kFinThreads;
-    const int64_t w0 = tid * per, w1 = min<int64_t>(nw, w0 + per);
-    uint32_t pc = 0;
-    for (int64_t w = w0; w < w1; ++w) pc += __popc(bm[w]);
+  {
+    uint32_t c[kBpt], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kBpt; ++i) {
+      const int b = kBpt * tid + i;
+      c[i] = b < nb ? ol.pre[b] : 0u;
+      sum += c[i];
+    }
     uint32_t tot;
-    uint32_t pos = block_exclusive_scan<kFinThreads>(pc, f.tmp, &tot);
-    for (int64_t w = w0; w < w1; ++w) {
-      uint32_t bits = bm[w];
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (pos < (uint32_t)K) out[pos] = (int32_t)(w * 32 + b);
-        ++pos;
-      }
+    uint32_t off = block_exclusive_scan<kFinThreads>(sum, f.tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < kBpt; ++i) {
+      const int b = kBpt * tid + i;
+      if (b <= nb) ol.pre[b] = off;  // b == nb receives the total K
+      if (b < nb) ol.cur[b] = off;
+      off += c[i];
     }
-    return;
+    if (tid == 0) ol.pre[nb] = tot;
   }
-  // very long sequences: bitonic sort of the K indices in LDS
-  int N = 1;
-  while (N < K) N <<= 1;
-  for (int i = K + tid; i < N; i += kFinThreads) sel[i] = 0x7FFFFFFF;
   __syncthreads();
-  for (int k2 = 2; k2 <= N; k2 <<= 1) {
-    for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < N; i += kFinThreads) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          const int32_t x = sel[i], y = sel[ixj];
-          const bool asc = (i & k2) == 0;
-          if ((x > y) == asc) { sel[i] = y; sel[ixj] = x; }
-        }
-      }
-      __syncthreads();
-    }
+  for (int i = tid; i < K; i += kFinThreads) {
+    const int32_t j = sel[i];
+    ol.bucket[min(atomicAdd(&ol.cur[min((uint32_t)j >> 10, last)], 1u), (uint32_t)K - 1)] = j;
   }
-  for (int i = tid; i < K; i += kFinThreads) out[i] = sel[i];
+  __syncthreads();
+  int32_t* sorted = reinterpret_cast<int32_t*>(f.h);
+  for (int i = tid; i < K; i += kFinThreads) {
+    const int32_t j = ol.bucket[i];
+    const uint32_t b = min((uint32_t)j >> 10, last);
+    const uint32_t s0 = ol.pre[b], s1 = ol.pre[b + 1];
+    uint32_t r = 0;
+    for (uint32_t s = s0; s < s1; ++s) r += ol.bucket[s] < j;
+    sorted[min(s0 + r, (uint32_t)K - 1)] = j;
+  }
+  __syncthreads();
+  for (int i = tid; i < K; i += kFinThreads) out[i] = sorted[i];
 }
 
 }  // namespace
@@ -650,21 +819,20 @@ size_t index_ws_layout(int64_t nq, int64_t max_visible, void* ws, IndexArgs* a) 
   };
   void* scores = take((size_t)nq * nblk * kBlockKeys * 4);
   void* cand = take((size_t)nq * nblk * kBlockKeys * 8);
-  void* cnt = take((size_t)nq * nblk * 4);
+  void* ovf = take((size_t)nq * nblk * kBlockKeys * 8);
   void* thr = take((size_t)nq * nblk * 8);
   if (a) {
     a->nblk = (int)nblk;
     a->scores = static_cast<uint32_t*>(scores);
     a->cand = static_cast<uint64_t*>(cand);
-    a->blk_cnt = static_cast<uint32_t*>(cnt);
+    a->ovf = static_cast<uint64_t*>(ovf);
     a->blk_thr = static_cast<uint64_t*>(thr);
   }
   return (size_t)(p - p0) + 256;
 }
 
 hipError_t index_init() {
-  return hipFuncSetAttribute((const void*)finalize_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             kCandCap * 8);
+  return hipSuccess;
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
@@ -674,7 +842,7 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
     else if (a.dtype == HCA_F32) hipLaunchKernelGGL(score_valu_kernel<float>, g, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(score_valu_kernel<uint16_t>, g, dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.nq), dim3(kFinThreads), (size_t)kCandCap * 8, s, a);
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.nq), dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -46,8 +46,9 @@ struct IndexArgs {
   // workspace views for the batch (set by index_ws_layout)
   int nblk;             // score blocks per query: ceil(max_visible / 1024)
   uint32_t* scores;     // [nq, max_visible] order-preserving score keys
-  uint64_t* cand;       // [nq, nblk * 1024] per-block candidate keys (score key << 32 | ~j)
-  uint32_t* blk_cnt;    // [nq, nblk] candidates held by each score block's region
+  uint64_t* cand;       // [nq, nblk * 1024] candidate keys (score key << 32 | ~j), a fixed slot
+                        // range per score block, 0 = empty slot
+  uint64_t* ovf;        // [nq, nblk * 1024] keys added by rescans
   uint64_t* blk_thr;    // [nq, nblk] a block emitted exactly its keys >= this threshold
 };
 constexpr int kHistBins = 2048;
