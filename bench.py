@@ -34,6 +34,103 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class KernelGraphs:
+    """Per-kernel timing through the HIP graph API (the HIP runtime that torch has loaded).
+
+    capture(fn) records the kernels fn launches on the current stream and returns their launch
+    parameters; chain(params) builds one executable graph that launches the given kernels back
+    to back. Timing such a graph of K launches between two events on the same stream gives the
+    kernel's average duration without per-launch submission overhead."""
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+        self.ct = ctypes
+        lib = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.hip = ctypes.CDLL(lib)
+        self.torch = torch
+        self.keep = []  # captured graphs own the argument buffers the parameters point to
+
+        class Dim3(ctypes.Structure):
+            _fields_ = [("x", ctypes.c_uint32), ("y", ctypes.c_uint32), ("z", ctypes.c_uint32)]
+
+        class KernelNodeParams(ctypes.Structure):
+            _fields_ = [("blockDim", Dim3), ("extra", ctypes.c_void_p), ("func", ctypes.c_void_p),
+                        ("gridDim", Dim3), ("kernelParams", ctypes.c_void_p), ("sharedMemBytes", ctypes.c_uint)]
+        self.KNP = KernelNodeParams
+
+    def _ok(self, e, what):
+        if e != 0:
+            raise RuntimeError(f"{what} failed with hipError {e}")
+
+    def _stream(self):
+        return self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+
+    def capture(self, fn):
+        ct, hip = self.ct, self.hip
+        graph = ct.c_void_p()
+        self._ok(hip.hipStreamBeginCapture(self._stream(), 1), "hipStreamBeginCapture")
+        fn()
+        self._ok(hip.hipStreamEndCapture(self._stream(), ct.byref(graph)), "hipStreamEndCapture")
+        self.keep.append(graph)
+        n = ct.c_size_t(0)
+        self._ok(hip.hipGraphGetNodes(graph, None, ct.byref(n)), "hipGraphGetNodes")
+        nodes = (ct.c_void_p * n.value)()
+        self._ok(hip.hipGraphGetNodes(graph, nodes, ct.byref(n)), "hipGraphGetNodes")
+        out = []
+        for nd in nodes:
+            t = ct.c_int(-1)
+            self._ok(hip.hipGraphNodeGetType(ct.c_void_p(nd), ct.byref(t)), "hipGraphNodeGetType")
+            if t.value != 0:  # kernel nodes only
+                continue
+            prm = self.KNP()
+            self._ok(hip.hipGraphKernelNodeGetParams(ct.c_void_p(nd), ct.byref(prm)), "hipGraphKernelNodeGetParams")
+            out.append(prm)
+        return out
+
+    def chain(self, params):
+        ct, hip = self.ct, self.hip
+        graph = ct.c_void_p()
+        self._ok(hip.hipGraphCreate(ct.byref(graph), 0), "hipGraphCreate")
+        prev = None
+        for prm in params:
+            node = ct.c_void_p()
+            deps = (ct.c_void_p * 1)(prev) if prev is not None else None
+            self._ok(hip.hipGraphAddKernelNode(ct.byref(node), graph, deps, ct.c_size_t(1 if deps else 0),
+                                               ct.byref(prm)), "hipGraphAddKernelNode")
+            prev = node
+        ex = ct.c_void_p()
+        self._ok(hip.hipGraphInstantiate(ct.byref(ex), graph, None, None, ct.c_size_t(0)), "hipGraphInstantiate")
+        self.keep.append(graph)
+        return ex
+
+    def launch(self, ex):
+        self._ok(self.hip.hipGraphLaunch(ex, self._stream()), "hipGraphLaunch")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None when
+    there is none or the kernel's source file has changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and line.startswith("- "):
+                    key, val = line[2:].split(":", 1)
+                    fields[key.strip()] = val.strip()
+        if fields.get("kernel") != kernel:
+            continue
+        src, want = fields.get("source", " ").split()[:2]
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != want:
+                return None
+        return int(fields["traffic_bytes_per_launch"])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +229,59 @@ def main():
     t_csa = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     t_hca = sum(e[2].elapsed_time(e[3]) for e in ev) / K
 
+    # per-kernel durations: one-kernel graphs cloned from each entry point, rotating over the
+    # copies, each launch between two events on the stream it runs on
+    kg = KernelGraphs()
+    kstream = torch.cuda.Stream()  # stream capture needs a stream other than the default one
+    names = {"lightning_index_topk": ["score_mxfp4_kernel", "finalize_kernel"],
+             "csa_sparse_mqa_attn": ["attn_fp8_kernel<true>", "combine_kernel (csa)"],
+             "hca_dense_mqa_attn": ["attn_fp8_kernel<false>", "combine_kernel (hca)"]}
+    per_copy = []
+    torch.cuda.synchronize()
+    kctx = torch.cuda.stream(kstream)
+    kctx.__enter__()
+    for r in runs:
+        ks = {}
+        for ep, fn in (("lightning_index_topk", r.index), ("csa_sparse_mqa_attn", r.csa_attention),
+                       ("hca_dense_mqa_attn", r.hca_attention)):
+            got = kg.capture(fn)
+            assert len(got) == len(names[ep]), f"{ep}: {len(got)} kernels captured"
+            ks.update(zip(names[ep], got))
+        per_copy.append(ks)
+    def chain_ms(kernel_names):
+        ex = kg.chain([per_copy[i % R][nm] for i in range(K) for nm in kernel_names])
+        kg.launch(ex)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(50_000_000)
+        e0.record()
+        kg.launch(ex)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    # the first kernel of an entry point is timed alone; the second one consumes the first's
+    # workspace output, so it is timed as (both, copy after copy) minus (first alone)
+    kern_ms = {}
+    for ep, (k1, k2) in names.items():
+        kern_ms[k1] = chain_ms([k1])
+        kern_ms[k2] = max(0.0, chain_ms([k1, k2]) - kern_ms[k1])
+    kctx.__exit__(None, None, None)
+    # a plain copy of known size: the second bandwidth denominator, and the reference that
+    # scales the HBM traffic counters
+    copy_n = 512 << 20
+    src = torch.empty(copy_n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record()
+    for _ in range(10):
+        dst.copy_(src)
+    ce[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * copy_n * 10 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src, dst
+
     # algorithmic bytes / flops (what the method must move or compute)
     entry = 448 + 4 + 64 * 2
     by_idx = B * n_c * 34 + B * HI * 34 + B * HI * 4 + B * k * 4
@@ -140,6 +290,18 @@ def main():
     fl_idx = B * n_c * HI * 64 * 2
     fl_csa = B * (k + W_) * H * D * 4
     fl_hca = B * (n_h + W_) * H * D * 4
+    # per kernel launch: the score kernel reads the keys (and the query operands); the attention
+    # kernels read their entries, the index list (CSA) and the queries; finalize and combine
+    # move only workspace data and the final index list / output
+    kern_bytes = {"score_mxfp4_kernel": B * n_c * 34 + B * HI * 34 + B * HI * 4,
+                  "finalize_kernel": B * k * 4,
+                  "attn_fp8_kernel<true>": B * (k + W_) * entry + B * k * 4 + B * H * D * 2,
+                  "combine_kernel (csa)": B * H * D * 2 + B * H * 4,
+                  "attn_fp8_kernel<false>": B * (n_h + W_) * entry + B * H * D * 2,
+                  "combine_kernel (hca)": B * H * D * 2 + B * H * 4}
+    dom = max(kern_ms, key=kern_ms.get)
+    dom_gbs = kern_bytes[dom] / (kern_ms[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(dom)
     step_bytes = by_idx + by_csa + by_hca
     step_flops = fl_idx + fl_csa + fl_hca
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
@@ -223,10 +385,11 @@ def main():
         "step_bytes": step_bytes, "step_flops": step_flops,
         "breakdown_ms": {"lightning_index_topk": round(t_idx, 5), "csa_sparse_mqa_attn": round(t_csa, 5),
                          "hca_dense_mqa_attn": round(t_hca, 5)},
-        "roofline": {"kernel": "lightning_index_topk (score + select kernels)", "bound": "hbm",
-                     "achieved": round(by_idx / (t_idx * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(by_idx / (t_idx * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes": by_idx},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": kern_bytes[dom], "ms_per_launch": round(kern_ms[dom], 5)},
+        "kernels_ms": {nm: round(v, 5) for nm, v in kern_ms.items()},
+        "copy_gbs": round(copy_gbs, 1),
         "rooflines": {
             "csa_sparse_mqa_attn": {"bound": "hbm", "achieved": round(by_csa / (t_csa * 1e-3) / 1e9, 1),
                                     "frac": round(by_csa / (t_csa * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -483,6 +483,8 @@ __device__ __forceinline__ void stage_rows(const WaveRows& w, uint8_t* dst, int 
   }
 }
 
+// kSparse: CSA (entries listed by idx) or HCA (dense); the same code, two names in profiles.
+template <bool kSparse>
 __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, int total) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
@@ -828,7 +830,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(512), kF8Lds, s, a, n_hg, total);
+    if (a.idx) hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(grid), dim3(512), kF8Lds, s, a, n_hg, total);
+    else hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(grid), dim3(512), kF8Lds, s, a, n_hg, total);
   } else if (mfma) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
@@ -850,7 +853,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 hipError_t attention_init() {
   hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)attn_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
+  e = hipFuncSetAttribute((const void*)attn_fp8_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)attn_fp8_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
 }
 
 }  // namespace hca

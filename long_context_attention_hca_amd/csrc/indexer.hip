@@ -397,8 +397,8 @@ constexpr int kPer = kCandCap / kFinThreads;    // candidates per thread, held i
 
 struct FinLds {
   uint32_t h[kHistBins];  // histogram; keys of the crossing bin (as u64); flagged blocks; output
-  int32_t sel[kMaxTopK];  // the selected entries
-  int32_t sel_sink[64];   // per-lane targets of writes that select nothing (branch-free code)
+  uint64_t sel[kMaxTopK];  // keys of the selected entries
+  uint64_t sel_sink[64];   // per-lane targets of writes that select nothing (branch-free code)
   uint64_t list_sink[64];
   uint32_t part[kFinThreads];
   uint32_t tmp[32];
@@ -478,7 +478,7 @@ struct ScoreBins {
 
 // Selection with the candidates in registers (v[i], 0 = empty; at least K non-empty, unique).
 // Returns T, the K-th largest key (exactly K keys are >= T), and writes those K entries to
-// f.sel (unordered). First pass: a histogram over 2048 equal-width bins of the candidates'
+// f.sel as keys (unordered). First pass: a histogram over 2048 equal-width bins of the candidates'
 // score range; the keys of the bin holding the K-th key are then ranked exactly among
 // themselves, and every selected key is placed by a block scan or by its rank, without
 // atomics. Equal scores throughout, or a crossing bin with more than kListCap keys (heavy
@@ -537,7 +537,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const bool a = bn[i] > d, l = bn[i] == d;
-        *(a ? &f.sel[min(oa, K - 1)] : &f.sel_sink[lane]) = key_entry(v[i]);
+        *(a ? &f.sel[min(oa, K - 1)] : &f.sel_sink[lane]) = v[i];
         *(l ? &list[min(ol, (uint32_t)kListCap - 1)] : &f.list_sink[lane]) = v[i];
         oa += a;
         ol += l;
@@ -548,7 +548,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
         const uint64_t x = list[i];
         uint32_t g = 0;
         for (uint32_t j = 0; j < cd; ++j) g += list[j] > x;
-        if (g < rem) f.sel[above + g] = key_entry(x);
+        if (g < rem) f.sel[above + g] = x;
         if (g == rem - 1) f.T = x;
       }
       __syncthreads();
@@ -601,7 +601,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const bool s = v[i] >= T;
-    *(s ? &f.sel[min(o, K - 1)] : &f.sel_sink[tid & 63]) = key_entry(v[i]);
+    *(s ? &f.sel[min(o, K - 1)] : &f.sel_sink[tid & 63]) = v[i];
     o += s;
   }
   __syncthreads();
@@ -671,7 +671,7 @@ __device__ uint64_t select_global(const CandSet& cs, uint32_t K, FinLds& f) {
     T = prefix;
   }
   __syncthreads();
-  for_each_global(cs, [&](uint64_t key) { wave_append<int32_t>(key >= T, key_entry(key), f.sel, &f.nsel, K); });
+  for_each_global(cs, [&](uint64_t key) { wave_append<uint64_t>(key >= T, key, f.sel, &f.nsel, K); });
   __syncthreads();
   return T;
 }
@@ -699,7 +699,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
   const int64_t q_blk = (int64_t)qi * a.nblk;
   const uint64_t* thr = a.blk_thr + q_blk;
   const uint32_t* sk = a.scores + q_blk * kBlockKeys;
-  uint64_t* ovf = a.ovf + q_blk * kBlockKeys;
+  const int64_t ovf_cap = (int64_t)a.nblk * kBlockKeys + kMaxTopK;  // >= k + n_vis
+  uint64_t* ovf = a.ovf + (int64_t)qi * ovf_cap;
   CandSet cs;
   cs.slots = a.cand + q_blk * kBlockKeys;
   cs.ns = (uint32_t)nb * region_slots(block_quota(K, nv));
@@ -741,7 +742,12 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     __syncthreads();
     const uint32_t nflag = f.nflag;
     if (nflag == 0) break;
-    // add their unemitted keys >= T to the overflow list (one wave per block), select again
+    // round 2 selects among the round-1 winners (every candidate >= T) and the unemitted keys
+    // >= T of the flagged blocks (one wave per block), all gathered in the overflow list:
+    // together they hold every key >= T, hence the whole top-k
+    for (int i = tid; i < K; i += kFinThreads) ovf[i] = f.sel[i];
+    if (tid == 0) f.novf = (uint32_t)K;
+    __syncthreads();
     for (uint32_t fi = wave; fi < nflag; fi += kFinThreads / 64) {
       const int b = (int)f.h[fi];
       const int64_t jb = (int64_t)b * kBlockKeys;
@@ -753,20 +759,21 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
       for (int r = 0; r < kBlockKeys / 64; ++r) {
         const int64_t j = jb + lane + 64 * r;
         const uint64_t k64 = ((uint64_t)kv[r] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-        wave_append<uint64_t>(j < nv && k64 < tb && k64 >= T, k64, ovf, &f.novf, (uint32_t)(a.nblk * kBlockKeys));
+        wave_append<uint64_t>(j < nv && k64 < tb && k64 >= T, k64, ovf, &f.novf, (uint32_t)ovf_cap);
       }
     }
     __threadfence_block();
     __syncthreads();
+    cs.ns = 0;
     cs.novf = f.novf;
     __syncthreads();
   }
   // ascending order: bucket the K entries by score block, then rank each within its bucket
-  const int32_t* sel = f.sel;
+  const uint64_t* sel = f.sel;
   for (int b = tid; b < nb; b += kFinThreads) ol.pre[b] = 0;
   __syncthreads();
   const uint32_t last = (uint32_t)nb - 1;
-  for (int i = tid; i < K; i += kFinThreads) atomicAdd(&ol.pre[min((uint32_t)sel[i] >> 10, last)], 1u);
+  for (int i = tid; i < K; i += kFinThreads) atomicAdd(&ol.pre[min((uint32_t)key_entry(sel[i]) >> 10, last)], 1u);
   __syncthreads();
   {
     uint32_t c[kBpt], sum = 0;
@@ -789,7 +796,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
   }
   __syncthreads();
   for (int i = tid; i < K; i += kFinThreads) {
-    const int32_t j = sel[i];
+    const int32_t j = key_entry(sel[i]);
     ol.bucket[min(atomicAdd(&ol.cur[min((uint32_t)j >> 10, last)], 1u), (uint32_t)K - 1)] = j;
   }
   __syncthreads();
@@ -819,7 +826,7 @@ size_t index_ws_layout(int64_t nq, int64_t max_visible, void* ws, IndexArgs* a) 
   };
   void* scores = take((size_t)nq * nblk * kBlockKeys * 4);
   void* cand = take((size_t)nq * nblk * kBlockKeys * 8);
-  void* ovf = take((size_t)nq * nblk * kBlockKeys * 8);
+  void* ovf = take((size_t)nq * (nblk * kBlockKeys + kMaxTopK) * 8);
   void* thr = take((size_t)nq * nblk * 8);
   if (a) {
     a->nblk = (int)nblk;

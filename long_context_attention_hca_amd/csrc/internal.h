@@ -48,7 +48,7 @@ struct IndexArgs {
   uint32_t* scores;     // [nq, max_visible] order-preserving score keys
   uint64_t* cand;       // [nq, nblk * 1024] candidate keys (score key << 32 | ~j), a fixed slot
                         // range per score block, 0 = empty slot
-  uint64_t* ovf;        // [nq, nblk * 1024] keys added by rescans
+  uint64_t* ovf;        // [nq, nblk * 1024 + kMaxTopK] second-round candidates
   uint64_t* blk_thr;    // [nq, nblk] a block emitted exactly its keys >= this threshold
 };
 constexpr int kHistBins = 2048;
