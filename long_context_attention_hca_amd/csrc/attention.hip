@@ -451,42 +451,231 @@ struct WaveRows {
   uint32_t vmask;   // valid entries
 };
 
-__device__ __forceinline__ WaveRows wave_rows(const AttnArgs& a, const QueryCtx& ctx, int qi, int64_t base,
-                                              int64_t hi, int lane) {
+// The top-k slot value of list position base + (lane & 15) (CSA), loaded one chunk before its
+// rows are computed so that no wait on it sits behind row loads in flight. Positions past the
+// top-k list are clamped to a valid slot; their value is not used.
+template <bool kSparse>
+__device__ __forceinline__ int32_t prefetch_slot(const AttnArgs& a, int qi, int64_t base, int lane) {
+  if (!kSparse) return 0;
+  const int64_t r = min<int64_t>(base + (lane & 15), (int64_t)a.k - 1);
+  return a.idx[(int64_t)qi * a.k + r];
+}
+
+// The rows of positions base .. base + 15 from their prefetched slot values (no dependent
+// loads; the entry-scale load is issued and left in flight). Store fields are selected one by
+// one so that they stay in scalar registers.
+template <bool kSparse>
+__device__ __forceinline__ WaveRows wave_rows(const AttnArgs& a, const QueryCtx& ctx, int64_t base, int64_t hi,
+                                              int32_t slot, int lane) {
   WaveRows w;
-  bool win = false;
+  const int64_t r = base + lane;
+  const bool win = r >= ctx.n_c;
   int64_t row = -1;
-  if (lane < 16 && base + lane < hi) row = list_row(a, ctx, qi, base + lane, &win);
-  const StoreView& v = win ? a.win : a.cache;
-  w.np = reinterpret_cast<uint64_t>(v.data) + (uint64_t)(row * v.row_stride);
-  w.rp = reinterpret_cast<uint64_t>(v.rope) + (uint64_t)(row * v.rope_stride * 2) - kNope;
-  w.esc = row >= 0 ? v.scale[row] : 0.f;
+  if (lane < 16 && r < hi) {
+    if (!win) {
+      const int64_t j = kSparse ? (int64_t)slot : r;
+      const int64_t cr = ctx.cache_rb + j;
+      row = (j >= 0 && cr >= 0 && cr < a.cache.n_rows) ? cr : -1;
+    } else if (r < ctx.n_c + ctx.n_w) {
+      const int64_t pos = ctx.t - ctx.n_w + 1 + (r - ctx.n_c);
+      const int64_t wr = ctx.win_rb + (pos - ctx.win_p0);
+      row = (wr >= 0 && wr < a.win.n_rows) ? wr : -1;
+    }
+  }
+  const uint64_t data = win ? reinterpret_cast<uint64_t>(a.win.data) : reinterpret_cast<uint64_t>(a.cache.data);
+  const uint64_t rope = win ? reinterpret_cast<uint64_t>(a.win.rope) : reinterpret_cast<uint64_t>(a.cache.rope);
+  const int64_t rs = win ? a.win.row_stride : a.cache.row_stride;
+  const int64_t ps = win ? a.win.rope_stride : a.cache.rope_stride;
+  const float* scale = win ? a.win.scale : a.cache.scale;
+  w.np = data + (uint64_t)(row * rs);
+  w.rp = rope + (uint64_t)(row * ps * 2) - kNope;
+  w.esc = row >= 0 ? scale[row] : 0.f;
   w.vmask = (uint32_t)__ballot(lane < 16 && row >= 0);
   return w;
 }
 
-// One global_load_lds per valid row (lanes 0-27: FP8 bytes, 28-35: RoPE bytes); invalid rows
-// are zeroed so that their (masked) P = 0 never meets a NaN.
+// Invalid rows of a wave's 16 are zeroed so that their (masked) P = 0 never meets a NaN; this
+// precedes the row loads into the same buffer.
+__device__ __forceinline__ void zero_invalid_rows(const WaveRows& w, uint8_t* dst, int lane) {
+  uint32_t inval = ~w.vmask & 0xFFFFu;
+  while (inval) {
+    const int e = __builtin_ctz(inval);
+    inval &= inval - 1;
+    if (lane < kRowF8 / 16) *reinterpret_cast<uint4*>(dst + e * kRowF8 + 16 * lane) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// One global_load_lds per valid row e in [E0, E0 + kN) (lanes 0-27: FP8 bytes, 28-35: RoPE
+// bytes).
+template <int E0, int kN>
 __device__ __forceinline__ void stage_rows(const WaveRows& w, uint8_t* dst, int lane) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    uint8_t* rowp = dst + e * kRowF8;
+  for (int e = E0; e < E0 + kN; ++e) {
     if ((w.vmask >> e) & 1) {
       const uint64_t n = readlane64(w.np, e), r = readlane64(w.rp, e);
       const uint64_t src = (lane < 28 ? n : r) + 16 * (uint64_t)lane;
       if (lane < 36)
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                         (__attribute__((address_space(3))) void*)rowp, 16, 0, 0);
-    } else if (lane < kRowF8 / 16) {
-      *reinterpret_cast<uint4*>(rowp + 16 * lane) = make_uint4(0, 0, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(dst + e * kRowF8), 16, 0, 0);
     }
   }
 }
 
-// kSparse: CSA (entries listed by idx) or HCA (dense); the same code, two names in profiles.
+// Workgroup barrier that waits for this wave's LDS accesses only: row loads into the other
+// chunk buffer stay in flight across it. The signal fences stop the compiler from moving LDS
+// accesses over the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+struct F8Query {
+  i32x8 qh[4], ql[4];  // FP8 hi / lo parts of the 448 non-RoPE dims, per K step
+  bf16x8 qr[2];        // RoPE dims
+  uint32_t sh, sl;     // per K step scale byte (E8M0) of the hi / lo parts
+};
+
+struct F8State {
+  f32x4 O[4];
+  float m_run, l_part;
+  WaveRows cur, nxt;  // rows of this chunk (staged) and of the next one (known)
+  int32_t slot2;      // prefetched slot values of the chunk after next
+};
+
+// One 128-entry chunk in buf, whose rows this wave has requested: wait for all of them, request
+// the next chunk's rows into nbuf (spread over this chunk's phases), then scores, softmax and
+// PV. The chunk buffers are distinct LDS objects, so the compiler knows that reads of buf need
+// not wait for the loads into nbuf.
+template <bool kSparse>
+__device__ __forceinline__ void f8_chunk(const AttnArgs& a, const QueryCtx& ctx, int qi, int64_t base, int64_t hi,
+                                         const uint8_t* buf, uint8_t* nbuf, const F8Query& q, F8State& st,
+                                         uint16_t* pbs, uint16_t* pb, float* wmax, float sl2, int wave, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  __builtin_amdgcn_s_waitcnt(0);  // this chunk's rows staged by this wave; next rows' loads done
+  __syncthreads();                // all rows of the chunk; the other buffer is free
+  const bool more = base + kCh < hi;
+  const WaveRows cur = st.cur, nxt = st.nxt;
+  uint8_t* ndst = nbuf + 16 * wave * kRowF8;
+  if (more) {
+    zero_invalid_rows(nxt, ndst, lane);
+    stage_rows<0, 4>(nxt, ndst, lane);
+  }
+  // rows of the chunk after next from their prefetched slots; slots one further ahead
+  const int64_t b2 = base + 2 * kCh + 16 * wave;
+  st.cur = nxt;
+  st.nxt = wave_rows<kSparse>(a, ctx, b2, hi, st.slot2, lane);
+  st.slot2 = prefetch_slot<kSparse>(a, qi, b2 + kCh, lane);
+
+  // scores of this wave's 16 entries (lane: entries 4g + i, head c)
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, sr = s0;
+  {
+    const uint8_t* rowp = buf + (16 * wave + c) * kRowF8 + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(rowp + 128 * ks);
+      uint4 x1 = make_uint4(0, 0, 0, 0);  // dims 448.. (K step 3, bytes 16-31) are RoPE bytes: zero
+      if (ks < 3) x1 = *reinterpret_cast<const uint4*>(rowp + 128 * ks + 64);
+      const i32x8 A = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.qh[ks], s0, 0, 0, 0, 127, 0,
+                                                             (int)((q.sh >> (8 * ks)) & 255u));
+      s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.ql[ks], s1, 0, 0, 0, 127, 0,
+                                                             (int)((q.sl >> (8 * ks)) & 255u));
+    }
+    const uint8_t* ropep = buf + (16 * wave + c) * kRowF8 + kNope + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ropep + 64 * ks));
+      sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q.qr[ks], sr, 0, 0, 0);
+    }
+  }
+  if (more) stage_rows<4, 4>(nxt, ndst, lane);
+  float sv[4], escl[4];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * g + i;
+    escl[i] = __shfl(cur.esc, e, 64);
+    const float st_ = fmaf(escl[i], s0[i] + s1[i], sr[i]);
+    sv[i] = ((cur.vmask >> e) & 1) ? st_ * sl2 : -INFINITY;
+    cmax = fmaxf(cmax, sv[i]);
+  }
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  if (g == 0) wmax[16 * wave + c] = cmax;
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < 8; ++w) cmax = fmaxf(cmax, wmax[16 * w + c]);
+  // lazy rescaling: the reference max moves only when a score exceeds it by more than 2^8
+  // (log2 units), so p <= 256 and O is rescaled rarely instead of every chunk
+  const bool grow = cmax > st.m_run + 8.f;
+  const float m_ref = grow ? cmax : st.m_run;
+  const bool none = m_ref == -INFINITY;
+  const float corr = grow ? exp2f(st.m_run - cmax) : 1.f;
+  float p[4], psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = none ? 0.f : exp2f(sv[i] - m_ref);
+    psum += p[i];
+  }
+  st.l_part = st.l_part * corr + psum;
+  st.m_run = m_ref;
+  if (__ballot(grow)) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.O[dt] *= corr;
+  }
+  {
+    const int pe = c * kPRow + 16 * wave + 4 * g;
+    *reinterpret_cast<uint2*>(pbs + pe) =
+        make_uint2(pack_bf16x2(p[0] * escl[0], p[1] * escl[1]), pack_bf16x2(p[2] * escl[2], p[3] * escl[3]));
+    *reinterpret_cast<uint2*>(pb + pe) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+  }
+  if (more) stage_rows<8, 4>(nxt, ndst, lane);
+  lds_barrier();
+  // O^T (this wave's 64 dims x 16 heads) += V^T P^T over the chunk's 128 entries
+  if (wave < 7) {
+    const int r = c >> 1, hsel = c & 1;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pbs + c * kPRow + 32 * kk + 8 * g));
+      const uint8_t* vp = buf + (32 * kk + 8 * g + r) * kRowF8 + 64 * wave + 8 * hsel;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * dt));
+        st.O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]), B,
+                                                           st.O[dt], 0, 0, 0);
+      }
+    }
+  } else {
+    const int rs = c >> 2, qd = c & 3;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + c * kPRow + 32 * kk + 8 * g));
+      const uint8_t* v0 = buf + (32 * kk + 8 * g + rs) * kRowF8 + kNope + 8 * qd;
+      const uint8_t* v1 = v0 + 4 * kRowF8;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * dt));
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * dt));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), B, st.O[dt], 0, 0, 0);
+      }
+    }
+  }
+  if (more) stage_rows<12, 4>(nxt, ndst, lane);
+}
+
+// kSparse: CSA (entries listed by idx, a.idx set) or HCA (dense, a.idx null).
 template <bool kSparse>
 __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, int total) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // two chunk buffers as separate LDS objects (see f8_chunk), then the P tiles and maxima
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBufF8];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[kBufF8];
+  __shared__ __attribute__((aligned(16))) uint16_t pbs[16 * kPRow];  // [16][kPRow] P x entry scale
+  __shared__ __attribute__((aligned(16))) uint16_t pb[16 * kPRow];   // [16][kPRow] P
+  __shared__ float wmax[8 * 16], wsum[8 * 16];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= total) return;
   const int hg = id % n_hg;
@@ -497,10 +686,6 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const int head = hg * 16 + c;
-  uint16_t* pbs = reinterpret_cast<uint16_t*>(smem + 2 * kBufF8);  // [16][kPRow] P x entry scale
-  uint16_t* pb = pbs + 16 * kPRow;                                  // [16][kPRow] P
-  float* wmax = reinterpret_cast<float*>(pb + 16 * kPRow);          // [8][16]
-  float* wsum = wmax + 8 * 16;                                      // [8][16]
 
   // query: FP8 hi/lo parts of the 448 non-RoPE dims. Operand layout of the 16x16x128 FP8
   // MFMA: in K step ks, lane (g, c) holds dims 128ks + 16g .. +16 in bytes 0-15 and dims
@@ -510,7 +695,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   // the second chunk buffer (unused until the first chunk is staged); every wave then loads
   // all four steps.
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * H + head) * kD;
-  uint8_t* qbuf = smem + kBufF8;  // [4 ks][64 lanes][32 hi + 32 lo bytes], then [4][64] scale words
+  uint8_t* qbuf = buf1;  // [4 ks][64 lanes][32 hi + 32 lo bytes], then [4][64] scale words
   uint32_t* qsc = reinterpret_cast<uint32_t*>(qbuf + 4 * 64 * 64);
   uint4 qraw[4];
   if (wave < 4) {
@@ -531,8 +716,16 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   const int64_t N = ctx.n_c + ctx.n_w;
   const int64_t lo = (int64_t)s * a.per_split;
   const int64_t hi = min<int64_t>(N, lo + a.per_split);
-  // first chunk's rows in flight while the query is prepared
-  WaveRows cur = wave_rows(a, ctx, qi, lo + 16 * wave, hi, lane);
+  // first chunk's rows in flight while the query is prepared; the next two chunks' row
+  // sources follow one chunk ahead of their use
+  F8State st;
+  {
+    const int64_t b0 = lo + 16 * wave;
+    const int32_t s0 = prefetch_slot<kSparse>(a, qi, b0, lane), s1 = prefetch_slot<kSparse>(a, qi, b0 + kCh, lane);
+    st.slot2 = prefetch_slot<kSparse>(a, qi, b0 + 2 * kCh, lane);
+    st.cur = wave_rows<kSparse>(a, ctx, b0, hi, s0, lane);
+    st.nxt = wave_rows<kSparse>(a, ctx, b0 + kCh, hi, s1, lane);
+  }
 
   if (wave < 4) {
     float x[32];
@@ -585,147 +778,55 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
     const int eop = g == 0 ? eb[0] : g == 1 ? from_lo2 : g == 2 ? from_hi0 : eb[1];
     qsc[64 * wave + lane] = (uint32_t)(eop + 127) | ((uint32_t)(eop - 4 + 127) << 8);
   }
-  if (lo < hi) stage_rows(cur, smem + 16 * wave * kRowF8, lane);
-  __syncthreads();
-  i32x8 qh[4], ql[4];
-  uint32_t sh = 0, sl = 0;
+  if (lo < hi) {
+    uint8_t* dst = buf0 + 16 * wave * kRowF8;
+    zero_invalid_rows(st.cur, dst, lane);
+    stage_rows<0, 16>(st.cur, dst, lane);
+  }
+  lds_barrier();
+  F8Query q;
+  q.sh = q.sl = 0;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const uint4* src = reinterpret_cast<const uint4*>(qbuf + (64 * ks + lane) * 64);
     const uint4 h0 = src[0], h1 = src[1], l0 = src[2], l1 = src[3];
-    qh[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
-    ql[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+    q.qh[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+    q.ql[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
     const uint32_t sw = qsc[64 * ks + lane];
-    sh |= (sw & 255u) << (8 * ks);
-    sl |= ((sw >> 8) & 255u) << (8 * ks);
+    q.sh |= (sw & 255u) << (8 * ks);
+    q.sl |= ((sw >> 8) & 255u) << (8 * ks);
   }
+  q.qr[0] = qr[0];
+  q.qr[1] = qr[1];
 
-  f32x4 O[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
+  for (int i = 0; i < 4; ++i) st.O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
   const float sl2 = a.scale * kLog2e;
-
-  for (int it = 0; lo + (int64_t)it * kCh < hi; ++it) {
-    const int64_t base = lo + (int64_t)it * kCh;
-    uint8_t* buf = smem + (it & 1) * kBufF8;
-    const bool more = base + kCh < hi;
-    WaveRows nxt = wave_rows(a, ctx, qi, base + kCh + 16 * wave, hi, lane);
-    __builtin_amdgcn_s_waitcnt(0);  // this chunk's rows staged by this wave; next rows known
-    __syncthreads();                // all rows of the chunk; the other buffer is free
-    if (more) stage_rows(nxt, smem + ((it + 1) & 1) * kBufF8 + 16 * wave * kRowF8, lane);
-
-    // scores of this wave's 16 entries (lane: entries 4g + i, head c)
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, sr = s0;
-    {
-      const uint8_t* rowp = buf + (16 * wave + c) * kRowF8 + 16 * g;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(rowp + 128 * ks);
-        uint4 x1 = make_uint4(0, 0, 0, 0);  // dims 448.. (K step 3, bytes 16-31) are RoPE bytes: zero
-        if (ks < 3) x1 = *reinterpret_cast<const uint4*>(rowp + 128 * ks + 64);
-        const i32x8 A = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qh[ks], s0, 0, 0, 0, 127, 0, (int)((sh >> (8 * ks)) & 255u));
-        s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, ql[ks], s1, 0, 0, 0, 127, 0, (int)((sl >> (8 * ks)) & 255u));
-      }
-      const uint8_t* ropep = buf + (16 * wave + c) * kRowF8 + kNope + 16 * g;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ropep + 64 * ks));
-        sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qr[ks], sr, 0, 0, 0);
-      }
-    }
-    float sv[4], escl[4];
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * g + i;
-      escl[i] = __shfl(cur.esc, e, 64);
-      const float st = fmaf(escl[i], s0[i] + s1[i], sr[i]);
-      sv[i] = ((cur.vmask >> e) & 1) ? st * sl2 : -INFINITY;
-      cmax = fmaxf(cmax, sv[i]);
-    }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    if (g == 0) wmax[16 * wave + c] = cmax;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < 8; ++w) cmax = fmaxf(cmax, wmax[16 * w + c]);
-    // lazy rescaling: the reference max moves only when a score exceeds it by more than 2^8
-    // (log2 units), so p <= 256 and O is rescaled rarely instead of every chunk
-    const bool grow = cmax > m_run + 8.f;
-    const float m_ref = grow ? cmax : m_run;
-    const bool none = m_ref == -INFINITY;
-    const float corr = grow ? exp2f(m_run - cmax) : 1.f;
-    float p[4], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = none ? 0.f : exp2f(sv[i] - m_ref);
-      psum += p[i];
-    }
-    l_part = l_part * corr + psum;
-    m_run = m_ref;
-    if (__ballot(grow)) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) O[dt] *= corr;
-    }
-    {
-      const int pe = c * kPRow + 16 * wave + 4 * g;
-      *reinterpret_cast<uint2*>(pbs + pe) =
-          make_uint2(pack_bf16x2(p[0] * escl[0], p[1] * escl[1]), pack_bf16x2(p[2] * escl[2], p[3] * escl[3]));
-      *reinterpret_cast<uint2*>(pb + pe) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-    }
-    __syncthreads();
-    // O^T (this wave's 64 dims x 16 heads) += V^T P^T over the chunk's 128 entries
-    if (wave < 7) {
-      const int r = c >> 1, hsel = c & 1;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pbs + c * kPRow + 32 * kk + 8 * g));
-        const uint8_t* vp = buf + (32 * kk + 8 * g + r) * kRowF8 + 64 * wave + 8 * hsel;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * dt));
-          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]), B, O[dt],
-                                                          0, 0, 0);
-        }
-      }
-    } else {
-      const int rs = c >> 2, qd = c & 3;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + c * kPRow + 32 * kk + 8 * g));
-        const uint8_t* v0 = buf + (32 * kk + 8 * g + rs) * kRowF8 + kNope + 8 * qd;
-        const uint8_t* v1 = v0 + 4 * kRowF8;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * dt));
-          const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * dt));
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
-          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), B, O[dt], 0, 0, 0);
-        }
-      }
-    }
-    cur = nxt;
+  // unrolled by two so that each call names its chunk buffers statically
+  for (int64_t base = lo; base < hi; base += 2 * kCh) {
+    f8_chunk<kSparse>(a, ctx, qi, base, hi, buf0, buf1, q, st, pbs, pb, wmax, sl2, wave, lane);
+    if (base + kCh >= hi) break;
+    f8_chunk<kSparse>(a, ctx, qi, base + kCh, hi, buf1, buf0, q, st, pbs, pb, wmax, sl2, wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
   // the softmax denominator: this lane's entries, then over the lane groups and the waves
-  l_part += __shfl_xor(l_part, 16, 64);
-  l_part += __shfl_xor(l_part, 32, 64);
-  if (g == 0) wsum[16 * wave + c] = l_part;
+  st.l_part += __shfl_xor(st.l_part, 16, 64);
+  st.l_part += __shfl_xor(st.l_part, 32, 64);
+  if (g == 0) wsum[16 * wave + c] = st.l_part;
   __syncthreads();
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < 8; ++w) L += wsum[16 * w + c];
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  const float lse = L > 0.f ? (m_run + log2f(L)) * kLn2 : -INFINITY;
+  const float lse = L > 0.f ? (st.m_run + log2f(L)) * kLn2 : -INFINITY;
   const int64_t hrow = (int64_t)qi * H + head;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     const int d = 64 * wave + 16 * dt + 4 * g;
-    const f32x4 acc = O[dt] * inv;
+    const f32x4 acc = st.O[dt] * inv;
     if (a.n_split == 1) {
       if (a.o_dtype == HCA_BF16) {
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + hrow * kD + d) =
@@ -830,8 +931,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;
-    if (a.idx) hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(grid), dim3(512), kF8Lds, s, a, n_hg, total);
-    else hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(grid), dim3(512), kF8Lds, s, a, n_hg, total);
+    if (a.idx) hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(grid), dim3(512), 0, s, a, n_hg, total);
+    else hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(grid), dim3(512), 0, s, a, n_hg, total);
   } else if (mfma) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
@@ -851,11 +952,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t attention_init() {
-  hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)attn_fp8_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)attn_fp8_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
+  return hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
 }
 
 }  // namespace hca
