@@ -444,11 +444,12 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Row sources of one wave's 16 entries of a chunk: lane e < 16 holds list position base + e.
+// Row sources of one wave's 16 entries of a chunk (list positions base + e, e < 16).
 struct WaveRows {
-  uint64_t np, rp;  // FP8-row and RoPE-row addresses (lane e)
-  float esc;        // entry scale (lane e; its load is left in flight)
-  uint32_t vmask;   // valid entries
+  uint64_t src;    // lane e < 16: FP8-row address of entry e; lane 16 + e: its RoPE-row address
+                   // minus 448, so that LDS row byte o >= 448 comes from src + o
+  float esc;       // lane e < 16: entry scale (its load is left in flight)
+  uint32_t vmask;  // valid entries
 };
 
 // The top-k slot value of list position base + (lane & 15) (CSA), loaded one chunk before its
@@ -468,10 +469,11 @@ template <bool kSparse>
 __device__ __forceinline__ WaveRows wave_rows(const AttnArgs& a, const QueryCtx& ctx, int64_t base, int64_t hi,
                                               int32_t slot, int lane) {
   WaveRows w;
-  const int64_t r = base + lane;
+  const int e = lane & 15;
+  const int64_t r = base + e;
   const bool win = r >= ctx.n_c;
   int64_t row = -1;
-  if (lane < 16 && r < hi) {
+  if (lane < 32 && r < hi) {
     if (!win) {
       const int64_t j = kSparse ? (int64_t)slot : r;
       const int64_t cr = ctx.cache_rb + j;
@@ -487,9 +489,8 @@ __device__ __forceinline__ WaveRows wave_rows(const AttnArgs& a, const QueryCtx&
   const int64_t rs = win ? a.win.row_stride : a.cache.row_stride;
   const int64_t ps = win ? a.win.rope_stride : a.cache.rope_stride;
   const float* scale = win ? a.win.scale : a.cache.scale;
-  w.np = data + (uint64_t)(row * rs);
-  w.rp = rope + (uint64_t)(row * ps * 2) - kNope;
-  w.esc = row >= 0 ? scale[row] : 0.f;
+  w.src = lane < 16 ? data + (uint64_t)(row * rs) : rope + (uint64_t)(row * ps * 2) - kNope;
+  w.esc = (lane < 16 && row >= 0) ? scale[row] : 0.f;
   w.vmask = (uint32_t)__ballot(lane < 16 && row >= 0);
   return w;
 }
@@ -505,19 +506,23 @@ __device__ __forceinline__ void zero_invalid_rows(const WaveRows& w, uint8_t* ds
   }
 }
 
-// One global_load_lds per valid row e in [E0, E0 + kN) (lanes 0-27: FP8 bytes, 28-35: RoPE
-// bytes).
-template <int E0, int kN>
+// A wave's 16 rows fill 16 * 592 = 9,472 LDS bytes, loaded by 10 lane-linear DMAs of up to
+// 1 KiB (16 bytes a lane); DMAs I0 .. I0 + kN - 1 here. The cost of a DMA is per instruction,
+// not per byte, so full 64-lane DMAs beat one 36-lane DMA per row. Lanes that fall on a row's
+// 16 padding bytes, past the 16 rows, or on an invalid row stay idle.
+template <int I0, int kN>
 __device__ __forceinline__ void stage_rows(const WaveRows& w, uint8_t* dst, int lane) {
 #pragma unroll
-  for (int e = E0; e < E0 + kN; ++e) {
-    if ((w.vmask >> e) & 1) {
-      const uint64_t n = readlane64(w.np, e), r = readlane64(w.rp, e);
-      const uint64_t src = (lane < 28 ? n : r) + 16 * (uint64_t)lane;
-      if (lane < 36)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                         (__attribute__((address_space(3))) void*)(dst + e * kRowF8), 16, 0, 0);
-    }
+  for (int i = I0; i < I0 + kN; ++i) {
+    const int b = 1024 * i + 16 * lane;  // LDS byte within the wave's rows
+    const int e = b / kRowF8, o = b - e * kRowF8;
+    const int sl = o < kNope ? e : 16 + e;
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)w.src, sl, 64);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(w.src >> 32), sl, 64);
+    const uint64_t src = (((uint64_t)hi << 32) | lo) + (uint64_t)o;
+    if (e < 16 && o < kNope + 2 * kRope && ((w.vmask >> (e & 15)) & 1))
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
   }
 }
 
@@ -560,7 +565,7 @@ __device__ __forceinline__ void f8_chunk(const AttnArgs& a, const QueryCtx& ctx,
   uint8_t* ndst = nbuf + 16 * wave * kRowF8;
   if (more) {
     zero_invalid_rows(nxt, ndst, lane);
-    stage_rows<0, 4>(nxt, ndst, lane);
+    stage_rows<0, 3>(nxt, ndst, lane);
   }
   // rows of the chunk after next from their prefetched slots; slots one further ahead
   const int64_t b2 = base + 2 * kCh + 16 * wave;
@@ -590,7 +595,7 @@ __device__ __forceinline__ void f8_chunk(const AttnArgs& a, const QueryCtx& ctx,
       sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q.qr[ks], sr, 0, 0, 0);
     }
   }
-  if (more) stage_rows<4, 4>(nxt, ndst, lane);
+  if (more) stage_rows<3, 3>(nxt, ndst, lane);
   float sv[4], escl[4];
   float cmax = -INFINITY;
 #pragma unroll
@@ -631,7 +636,7 @@ __device__ __forceinline__ void f8_chunk(const AttnArgs& a, const QueryCtx& ctx,
         make_uint2(pack_bf16x2(p[0] * escl[0], p[1] * escl[1]), pack_bf16x2(p[2] * escl[2], p[3] * escl[3]));
     *reinterpret_cast<uint2*>(pb + pe) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
   }
-  if (more) stage_rows<8, 4>(nxt, ndst, lane);
+  if (more) stage_rows<6, 2>(nxt, ndst, lane);
   lds_barrier();
   // O^T (this wave's 64 dims x 16 heads) += V^T P^T over the chunk's 128 entries
   if (wave < 7) {
@@ -664,7 +669,7 @@ __device__ __forceinline__ void f8_chunk(const AttnArgs& a, const QueryCtx& ctx,
       }
     }
   }
-  if (more) stage_rows<12, 4>(nxt, ndst, lane);
+  if (more) stage_rows<8, 2>(nxt, ndst, lane);
 }
 
 // kSparse: CSA (entries listed by idx, a.idx set) or HCA (dense, a.idx null).
@@ -781,7 +786,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   if (lo < hi) {
     uint8_t* dst = buf0 + 16 * wave * kRowF8;
     zero_invalid_rows(st.cur, dst, lane);
-    stage_rows<0, 16>(st.cur, dst, lane);
+    stage_rows<0, 10>(st.cur, dst, lane);
   }
   lds_barrier();
   F8Query q;
