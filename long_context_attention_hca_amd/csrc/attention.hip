@@ -851,48 +851,75 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
 }
 
 // ---------------------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials. grid = (H, nq), 128 threads; D % 4 == 0.
+// Log-sum-exp merge of the split partials of one (query, head) over the dims held by a lane
+// (V = f32x4 for 4 dims at po + d, float for one). The lse values and partial outputs of kG
+// splits are loaded at once (positions past S clamp to the last split and get weight 0), so a
+// merge of up to kG splits is one memory round trip. Returns the merged sum and, through *M and
+// *L, the max and the scaled denominator.
+template <typename V>
+__device__ __forceinline__ V merge_splits(const float* pl, const float* po, int S, int H, int64_t sstride, float* M,
+                                          float* L) {
+  constexpr int kG = 16;
+  V acc = V{};
+  float m = -INFINITY, l_sum = 0.f;
+  for (int s0 = 0; s0 < S; s0 += kG) {
+    float l[kG];
+    V v[kG];
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      const int s = min(s0 + i, S - 1);
+      l[i] = pl[(int64_t)s * H];
+      v[i] = *reinterpret_cast<const V*>(po + s * sstride);
+    }
+    float gm = m;
+#pragma unroll
+    for (int i = 0; i < kG; ++i)
+      if (s0 + i < S) gm = fmaxf(gm, l[i]);
+    if (gm == -INFINITY) continue;  // nothing visible so far
+    const float corr = expf(m - gm);  // 0 while m is -inf
+    acc *= corr;
+    l_sum *= corr;
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      const float w = (s0 + i < S && l[i] != -INFINITY) ? expf(l[i] - gm) : 0.f;
+      acc += w * v[i];
+      l_sum += w;
+    }
+    m = gm;
+  }
+  *M = m;
+  *L = l_sum;
+  return acc;
+}
+
+// Merge of the split partials. grid = (H, nq), 128 threads; a thread takes 4 dims (a vector
+// pass over D & ~3 dims, then single dims).
 __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
-  __shared__ float wts[1024];
-  __shared__ float s_inv, s_lse;
   const int h = blockIdx.x, qi = blockIdx.y, tid = threadIdx.x;
   const int S = a.n_split, H = a.H, D = a.D;
-  if (tid < 64) {
-    const float* pl = a.part_lse + (int64_t)qi * S * H + h;
-    float M = -INFINITY;
-    for (int s = tid; s < S; s += 64) M = fmaxf(M, pl[(int64_t)s * H]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int s = tid; s < S; s += 64) {
-      const float l = pl[(int64_t)s * H];
-      const float wv = (M == -INFINITY || l == -INFINITY) ? 0.f : expf(l - M);
-      wts[s] = wv;
-      L += wv;
-    }
-    L = wave_sum(L);
-    if (tid == 0) {
-      s_inv = L > 0.f ? 1.f / L : 0.f;
-      s_lse = L > 0.f ? M + logf(L) : -INFINITY;
-    }
-  }
-  __syncthreads();
-  const float inv = s_inv;
+  const float* pl = a.part_lse + (int64_t)qi * S * H + h;
   const float* po = a.part_o + ((int64_t)qi * S * H + h) * D;
-  const int64_t sstride = (int64_t)H * D;
-  for (int d = tid * 4; d < D; d += 512) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int s = 0; s < S; ++s) acc += wts[s] * *reinterpret_cast<const f32x4*>(po + s * sstride + d);
-    acc *= inv;
-    const int64_t oi = ((int64_t)qi * H + h) * D + d;
+  const int64_t sstride = (int64_t)H * D, orow = ((int64_t)qi * H + h) * D;
+  const int D4 = D & ~3;
+  float M = -INFINITY, L = 0.f;
+  for (int d = tid * 4; d < D4; d += 512) {
+    f32x4 acc = merge_splits<f32x4>(pl, po + d, S, H, sstride, &M, &L);
+    acc *= L > 0.f ? 1.f / L : 0.f;
     if (a.o_dtype == HCA_BF16) {
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + oi) =
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + orow + d) =
           make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
     } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + oi) = acc;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d) = acc;
     }
   }
-  if (tid == 0) a.lse[(int64_t)qi * H + h] = s_lse;
+  for (int d = D4 + tid; d < D; d += 128) {
+    float acc = merge_splits<float>(pl, po + d, S, H, sstride, &M, &L);
+    acc *= L > 0.f ? 1.f / L : 0.f;
+    if (a.o_dtype == HCA_BF16) static_cast<uint16_t*>(a.o)[orow + d] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
+    else static_cast<float*>(a.o)[orow + d] = acc;
+  }
+  // thread 0 merged dim 0 (vector or single pass), so it holds the (dim-independent) M and L
+  if (tid == 0) a.lse[(int64_t)qi * H + h] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
 }  // namespace

@@ -127,3 +127,36 @@ def test_empty_sets_give_zero_and_neg_inf(hca):
     torch.cuda.synchronize()
     assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
     assert torch.all(o2.float() == 0) and torch.all(torch.isneginf(lse2))
+
+
+def test_many_splits_and_unaligned_width(hca):
+    """fp32 path with D = 27 (rows padded to 28 floats) and about 1000 visible HCA entries:
+    more than 16 split-K partials per (query, head) and a width that is not a multiple of 4,
+    so the merge runs several load groups and a single-dim tail."""
+    m, W_ = hca
+    dn, dr, n, H = 21, 6, 1500, 4
+    D = dn + dr
+    g = synth.generator(91)
+    dec = synth.normal(g, (n, D))
+    full = torch.zeros(n, D + 1)
+    full[:, :D] = dec
+    dev = "cuda"
+    cache = m.Store.dense(full.to(dev)[:, :D], dn, dr)  # row stride 28 floats
+    nq, W, mp, max_vis = 3, 20, 1, 1000
+    q_pos = np.array([1199, 1499, 400], np.int64)
+    q = synth.normal(synth.generator(92), (nq, H, D))
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=dev)
+    ws = W_.Workspace(dev)
+    scale = 1.0 / math.sqrt(D)
+    seq = torch.zeros(nq, dtype=torch.int32, device=dev)
+    o, lse = W_.hca_attn(q.to(dev), cache, i64([0]), mp, max_vis, cache, i64([0]), i64([0]), W, seq,
+                         torch.tensor(q_pos, device=dev), scale, ws)
+    torch.cuda.synchronize()
+    o, lse = np_(o), np_(lse)
+    ent = dec.double().numpy()
+    for i in range(nq):
+        t = int(q_pos[i])
+        nv = min((t + 1) // mp, max_vis)
+        rows = np.concatenate([ent[:nv], ent[OA.window_positions(t, W)]])
+        ro, rl = OA.attend(q[i].double().numpy(), rows, scale)
+        check_attention(o[i], lse[i], ro, rl, "fp32", f"q{i} nv={nv}")
