@@ -483,6 +483,7 @@ struct ScoreBins {
 // themselves, and every selected key is placed by a block scan or by its rank, without
 // atomics. Equal scores throughout, or a crossing bin with more than kListCap keys (heavy
 // ties), are resolved by 11-bit radix passes below the bits all candidates share.
+template <bool kSel>
 __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint32_t K, FinLds& f) {
   const int tid = threadIdx.x;
   // Elementwise steps below are written without branches (selects, sink addresses): in this
@@ -537,7 +538,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const bool a = bn[i] > d, l = bn[i] == d;
-        *(a ? &f.sel[min(oa, K - 1)] : &f.sel_sink[lane]) = v[i];
+        if (kSel) *(a ? &f.sel[min(oa, K - 1)] : &f.sel_sink[lane]) = v[i];
         *(l ? &list[min(ol, (uint32_t)kListCap - 1)] : &f.list_sink[lane]) = v[i];
         oa += a;
         ol += l;
@@ -548,7 +549,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
         const uint64_t x = list[i];
         uint32_t g = 0;
         for (uint32_t j = 0; j < cd; ++j) g += list[j] > x;
-        if (g < rem) f.sel[above + g] = x;
+        if (kSel && g < rem) f.sel[above + g] = x;
         if (g == rem - 1) f.T = x;
       }
       __syncthreads();
@@ -593,6 +594,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
     }
     T = prefix;
   }
+  if (!kSel) return T;
   uint32_t n = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) n += v[i] >= T;  // T > 0, so empty slots never count
@@ -676,6 +678,63 @@ __device__ uint64_t select_global(const CandSet& cs, uint32_t K, FinLds& f) {
   return T;
 }
 
+// Candidates tid + kFinThreads * i of cs into registers (0 past the end). Unconditional loads
+// from clamped slots stay in flight together.
+__device__ __forceinline__ void load_candidates(const CandSet& cs, uint64_t (&v)[kPer]) {
+  const int tid = threadIdx.x;
+  const uint32_t n = cs.ns + cs.novf;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint32_t s = min((uint32_t)(tid + kFinThreads * i), n - 1);
+    v[i] = *(s < cs.ns ? cs.slots + s : cs.ovf + (s - cs.ns));
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (tid + kFinThreads * i >= (int)n) v[i] = 0;
+}
+
+// Score blocks whose unemitted keys (all below the block's threshold) may reach T; their
+// numbers go to f.h. Returns how many.
+__device__ __forceinline__ uint32_t flag_blocks(const uint64_t (&tq)[kBpt], uint64_t T, FinLds& f) {
+  const int tid = threadIdx.x;
+  if (tid == 0) f.nflag = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kBpt; ++i)
+    if (tq[i] > T) f.h[atomicAdd(&f.nflag, 1u)] = (uint32_t)(kBpt * tid + i);
+  __syncthreads();
+  return f.nflag;
+}
+
+// Output of the K keys >= T when they are all among the emitted candidates. The candidate slots
+// are in ascending entry order (score blocks in order, each block's keys ascending, empty slots
+// 0 < T), so compacting the selected slots in slot order gives the ascending answer. Slot
+// tid + kFinThreads * i is position (i, wave, lane) in row-major order: per-wave ballots give
+// the lane offsets, a scan of the kPer x 8 wave counts the rest.
+__device__ __forceinline__ void ordered_output(const uint64_t (&v)[kPer], uint64_t T, int K, int32_t* out, FinLds& f) {
+  static_assert(kPer * (kFinThreads / 64) == 128, "two counts per lane of one wave");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* cnt = f.h;  // [kPer][8] wave counts, then their exclusive prefix
+  uint32_t mb[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint64_t bal = __ballot(v[i] >= T);
+    mb[i] = lanes_below(bal);
+    if (lane == 0) cnt[i * 8 + wave] = (uint32_t)__popcll(bal);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t c0 = cnt[2 * lane], c1 = cnt[2 * lane + 1];
+    const uint32_t incl = wave_incl_scan_add(c0 + c1);
+    cnt[2 * lane] = incl - c0 - c1;
+    cnt[2 * lane + 1] = incl - c1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (v[i] >= T) out[min(cnt[i * 8 + wave] + mb[i], (uint32_t)K - 1)] = key_entry(v[i]);
+}
+
 // Output LDS: per-block counts (then their prefix), per-block cursors, entries bucketed by block.
 struct OutLds {
   uint32_t pre[kMaxBlk + 1];
@@ -715,37 +774,37 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     tq[i] = b < nb ? tv : 0ull;
   }
   if (tid == 0) f.novf = 0;
-  for (int round = 0;; ++round) {
-    const uint32_t n = cs.ns + cs.novf;
-    uint64_t T;
-    if (n <= (uint32_t)kCandCap) {
-      uint64_t v[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {  // unconditional loads from clamped slots stay in flight together
-        const uint32_t s = min((uint32_t)(tid + kFinThreads * i), n - 1);
-        v[i] = *(s < cs.ns ? cs.slots + s : cs.ovf + (s - cs.ns));
-      }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (tid + kFinThreads * i >= (int)n) v[i] = 0;
-      T = select_regs(v, (uint32_t)K, f);
-    } else {
-      T = select_global(cs, (uint32_t)K, f);
+  // round 1 over the emitted candidates
+  uint64_t T;
+  uint32_t nflag;
+  if (cs.ns <= (uint32_t)kCandCap) {
+    uint64_t v[kPer];
+    load_candidates(cs, v);
+    T = select_regs<false>(v, (uint32_t)K, f);
+    nflag = flag_blocks(tq, T, f);
+    if (nflag == 0) {
+      ordered_output(v, T, K, out, f);
+      return;
     }
-    if (round == 1) break;
-    // blocks whose unemitted keys (all below their threshold) may reach T
-    if (tid == 0) f.nflag = 0;
-    __syncthreads();
+    // the round-1 winners (the K keys >= T) seed the overflow list of round 2
+    uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < kBpt; ++i)
-      if (tq[i] > T) f.h[atomicAdd(&f.nflag, 1u)] = (uint32_t)(kBpt * tid + i);
-    __syncthreads();
-    const uint32_t nflag = f.nflag;
-    if (nflag == 0) break;
+    for (int i = 0; i < kPer; ++i) c += v[i] >= T;
+    uint32_t tot;
+    uint32_t o = block_exclusive_scan<kFinThreads>(c, f.tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (v[i] >= T) ovf[min(o++, (uint32_t)K - 1)] = v[i];
+  } else {
+    T = select_global(cs, (uint32_t)K, f);
+    nflag = flag_blocks(tq, T, f);
+    if (nflag > 0)
+      for (int i = tid; i < K; i += kFinThreads) ovf[i] = f.sel[i];
+  }
+  if (nflag > 0) {
     // round 2 selects among the round-1 winners (every candidate >= T) and the unemitted keys
     // >= T of the flagged blocks (one wave per block), all gathered in the overflow list:
     // together they hold every key >= T, hence the whole top-k
-    for (int i = tid; i < K; i += kFinThreads) ovf[i] = f.sel[i];
     if (tid == 0) f.novf = (uint32_t)K;
     __syncthreads();
     for (uint32_t fi = wave; fi < nflag; fi += kFinThreads / 64) {
@@ -767,6 +826,13 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     cs.ns = 0;
     cs.novf = f.novf;
     __syncthreads();
+    if (cs.novf <= (uint32_t)kCandCap) {
+      uint64_t v[kPer];
+      load_candidates(cs, v);
+      T = select_regs<true>(v, (uint32_t)K, f);
+    } else {
+      T = select_global(cs, (uint32_t)K, f);
+    }
   }
   // ascending order: bucket the K entries by score block, then rank each within its bucket
   const uint64_t* sel = f.sel;
