@@ -476,13 +476,27 @@ struct ScoreBins {
   }
 };
 
+// Appends x to list[] (counter *n) with one LDS atomic per wave; p says whether this lane appends.
+template <class Tv>
+__device__ __forceinline__ void wave_append(bool p, Tv x, Tv* list, uint32_t* n, uint32_t cap) {
+  const uint64_t m = __ballot(p);
+  if (m == 0) return;
+  const int lane = threadIdx.x & 63, leader = __ffsll((long long)m) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(n, (uint32_t)__popcll(m));
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+  const uint32_t slot = base + lanes_below(m);
+  if (p && slot < cap) list[slot] = x;
+}
+
 // Selection with the candidates in registers (v[i], 0 = empty; at least K non-empty, unique).
-// Returns T, the K-th largest key (exactly K keys are >= T), and writes those K entries to
-// f.sel as keys (unordered). First pass: a histogram over 2048 equal-width bins of the candidates'
-// score range; the keys of the bin holding the K-th key are then ranked exactly among
-// themselves, and every selected key is placed by a block scan or by its rank, without
-// atomics. Equal scores throughout, or a crossing bin with more than kListCap keys (heavy
-// ties), are resolved by 11-bit radix passes below the bits all candidates share.
+// Returns T, the K-th largest key (exactly K keys are >= T); with kSel it also writes those K
+// keys to f.sel (unordered). First pass: a histogram over 2048 equal-width bins of the
+// candidates' score range; the keys of the bin holding the K-th key are then ranked exactly
+// among themselves (gathered by per-wave appends when only T is wanted; with kSel every
+// selected key is placed by a block scan or by its rank). Equal scores throughout, or a
+// crossing bin with more than kListCap keys (heavy ties), are resolved by 11-bit radix passes
+// below the bits all candidates share.
 template <bool kSel>
 __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint32_t K, FinLds& f) {
   const int tid = threadIdx.x;
@@ -523,7 +537,23 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
     uint32_t above;
     crossing2048<kFinThreads>(f.h, f.part, K, f.cx, &d, &above);
     const uint32_t rem = K - above, cd = f.h[d];
+    if (tid == 0) f.nsel = 0;
     __syncthreads();
+    if (cd <= (uint32_t)kListCap && !kSel) {
+      // the crossing bin's keys, in any order (one LDS atomic per wave and slot)
+      uint64_t* list = reinterpret_cast<uint64_t*>(f.h);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) wave_append<uint64_t>(bn[i] == d, v[i], list, &f.nsel, (uint32_t)kListCap);
+      __syncthreads();
+      for (uint32_t i = tid; i < cd; i += kFinThreads) {
+        const uint64_t x = list[i];
+        uint32_t g = 0;
+        for (uint32_t j = 0; j < cd; ++j) g += list[j] > x;
+        if (g == rem - 1) f.T = x;
+      }
+      __syncthreads();
+      return f.T;
+    }
     if (cd <= (uint32_t)kListCap) {
       uint64_t* list = reinterpret_cast<uint64_t*>(f.h);
       uint32_t na = 0, nl = 0;
@@ -608,19 +638,6 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
   }
   __syncthreads();
   return T;
-}
-
-// Appends x to list[] (counter *n) with one LDS atomic per wave; p says whether this lane appends.
-template <class Tv>
-__device__ __forceinline__ void wave_append(bool p, Tv x, Tv* list, uint32_t* n, uint32_t cap) {
-  const uint64_t m = __ballot(p);
-  if (m == 0) return;
-  const int lane = threadIdx.x & 63, leader = __ffsll((long long)m) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(n, (uint32_t)__popcll(m));
-  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
-  const uint32_t slot = base + lanes_below(m);
-  if (p && slot < cap) list[slot] = x;
 }
 
 // Calls fn(key) for every candidate held in global memory (empty slots skipped).
@@ -747,6 +764,19 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
   __shared__ OutLds ol;
   const int qi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.k;
+  const int64_t q_blk = (int64_t)qi * a.nblk;
+  const uint64_t* thr = a.blk_thr + q_blk;
+  const uint64_t* slots = a.cand + q_blk * kBlockKeys;
+  // The candidate slots and block thresholds lie in this query's workspace region, so their
+  // loads go out first (clamped to the region) and are masked once the visible count is known.
+  uint64_t v[kPer], tq[kBpt];
+  {
+    const uint32_t region = (uint32_t)a.nblk * kBlockKeys;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = slots[min((uint32_t)(tid + kFinThreads * i), region - 1)];
+#pragma unroll
+    for (int i = 0; i < kBpt; ++i) tq[i] = thr[min(kBpt * tid + i, a.nblk - 1)];
+  }
   int64_t rb;
   const int64_t nv = visible_keys(a, qi, &rb);
   int32_t* out = a.out + (int64_t)qi * K;
@@ -755,31 +785,26 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     return;
   }
   const int nb = (int)((nv + kBlockKeys - 1) / kBlockKeys);
-  const int64_t q_blk = (int64_t)qi * a.nblk;
-  const uint64_t* thr = a.blk_thr + q_blk;
   const uint32_t* sk = a.scores + q_blk * kBlockKeys;
   const int64_t ovf_cap = (int64_t)a.nblk * kBlockKeys + kMaxTopK;  // >= k + n_vis
   uint64_t* ovf = a.ovf + (int64_t)qi * ovf_cap;
   CandSet cs;
-  cs.slots = a.cand + q_blk * kBlockKeys;
+  cs.slots = slots;
   cs.ns = (uint32_t)nb * region_slots(block_quota(K, nv));
   cs.ovf = ovf;
   cs.novf = 0;
   // thresholds of blocks kBpt * tid + i
-  uint64_t tq[kBpt];
 #pragma unroll
-  for (int i = 0; i < kBpt; ++i) {
-    const int b = kBpt * tid + i;
-    const uint64_t tv = thr[min(b, nb - 1)];
-    tq[i] = b < nb ? tv : 0ull;
-  }
+  for (int i = 0; i < kBpt; ++i)
+    if (kBpt * tid + i >= nb) tq[i] = 0ull;
   if (tid == 0) f.novf = 0;
   // round 1 over the emitted candidates
   uint64_t T;
   uint32_t nflag;
   if (cs.ns <= (uint32_t)kCandCap) {
-    uint64_t v[kPer];
-    load_candidates(cs, v);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if ((uint32_t)(tid + kFinThreads * i) >= cs.ns) v[i] = 0;
     T = select_regs<false>(v, (uint32_t)K, f);
     nflag = flag_blocks(tq, T, f);
     if (nflag == 0) {
