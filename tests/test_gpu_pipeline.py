@@ -187,3 +187,43 @@ def test_chunked_prefill(W, prefixes, chunk, nsample):
         check_idx(idx[qi], r["idx"], f"top-k query {qi}")
         check_attention(o_c[n], l_c[n], r["o_csa"], r["lse_csa"], "low", f"csa attention query {qi}")
         check_attention(o_h[n], l_h[n], r["o_hca"], r["lse_hca"], "low", f"hca attention query {qi}")
+
+
+@pytest.mark.parametrize("raw_dt,layout,scalar", [("bf16", "split", False), ("bf16", "split", True),
+                                                  ("bf16", "bf16", True), ("f32", "f32", False), ("f32", "f32", True)])
+def test_csa_compress_runs_and_scalar_logits(W, raw_dt, layout, scalar):
+    """csa_compress of entries 37 .. 239 from raw rows that begin at entry 37's window (runs of
+    consecutive entries end mid-run), with per-channel or one-per-token logits, against the
+    oracle on every entry."""
+    import long_context_attention_hca_amd as H
+    from oracle.codecs import decode_bf16
+    _say(f"csa compress {raw_dt} {layout} scalar={scalar}")
+    m, w = 4, 8
+    dn, dr = (448, 64) if raw_dt == "bf16" else (128, 64)
+    D = dn + dr
+    e0, n = 37, 203
+    first_pos = e0 * m - (w - m)
+    rows = (e0 + n) * m - first_pos  # through the last entry's window
+    g = synth.generator(1006)
+    x = synth.normal(g, (rows, D))
+    z = synth.normal(g, (rows, 1 if scalar else D), std=2.0)
+    bias = synth.normal(g, (w, D), std=0.5)
+    if raw_dt == "bf16":
+        xin, zin = synth.bf16_bits(x), synth.bf16_bits(z)
+        xd, zd = decode_bf16(np_(xin).view(np.uint16)), decode_bf16(np_(zin).view(np.uint16))
+    else:
+        xin, zin = x, z
+        xd, zd = x.double().numpy(), z.double().numpy()
+    code = {"split": H.LAYOUT_SPLIT, "bf16": H.LAYOUT_BF16, "f32": H.LAYOUT_F32}[layout]
+    out = W.empty_store(code, n, dn, dr, "cuda")
+    H.csa_compress(xin.cuda(), first_pos, zin.cuda(), bias.cuda(), m, w, e0, n, out, scalar_logits=scalar)
+    torch.cuda.synchronize()
+    b = bias.double().numpy()
+    y = OC.compress(xd, zd, b, m, w, e0, n, first_pos=first_pos)
+    ya = OC.compress(np.abs(xd), zd, b, m, w, e0, n, first_pos=first_pos)
+    if layout == "split":
+        check_split_entries(np_(out.data), np_(out.scale), np_(out.rope), y, dn, "csa entries", ya)
+    elif layout == "bf16":
+        check_bf16_entries(np_(out.data), y, "csa entries", ya)
+    else:
+        check_f32_entries(np_(out.data), y, ya, "csa entries")
