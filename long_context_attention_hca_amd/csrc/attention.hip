@@ -717,20 +717,15 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   for (int ks = 0; ks < 2; ++ks)
     qr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + kNope + 32 * ks + 8 * g));
 
-  const QueryCtx ctx = query_ctx(a, qi);
-  const int64_t N = ctx.n_c + ctx.n_w;
   const int64_t lo = (int64_t)s * a.per_split;
-  const int64_t hi = min<int64_t>(N, lo + a.per_split);
-  // first chunk's rows in flight while the query is prepared; the next two chunks' row
-  // sources follow one chunk ahead of their use
+  const int64_t b0 = lo + 16 * wave;
+  const int32_t s0 = prefetch_slot<kSparse>(a, qi, b0, lane), s1 = prefetch_slot<kSparse>(a, qi, b0 + kCh, lane);
+  // Top-k slots of the first three chunks (CSA) need only the query and the split; the
+  // sequence-offset loads follow. The query is prepared while both are in flight, and the first
+  // chunk's rows are requested once they are known.
   F8State st;
-  {
-    const int64_t b0 = lo + 16 * wave;
-    const int32_t s0 = prefetch_slot<kSparse>(a, qi, b0, lane), s1 = prefetch_slot<kSparse>(a, qi, b0 + kCh, lane);
-    st.slot2 = prefetch_slot<kSparse>(a, qi, b0 + 2 * kCh, lane);
-    st.cur = wave_rows<kSparse>(a, ctx, b0, hi, s0, lane);
-    st.nxt = wave_rows<kSparse>(a, ctx, b0 + kCh, hi, s1, lane);
-  }
+  st.slot2 = prefetch_slot<kSparse>(a, qi, b0 + 2 * kCh, lane);
+  const QueryCtx ctx = query_ctx(a, qi);
 
   if (wave < 4) {
     float x[32];
@@ -783,6 +778,10 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
     const int eop = g == 0 ? eb[0] : g == 1 ? from_lo2 : g == 2 ? from_hi0 : eb[1];
     qsc[64 * wave + lane] = (uint32_t)(eop + 127) | ((uint32_t)(eop - 4 + 127) << 8);
   }
+  const int64_t N = ctx.n_c + ctx.n_w;
+  const int64_t hi = min<int64_t>(N, lo + a.per_split);
+  st.cur = wave_rows<kSparse>(a, ctx, b0, hi, s0, lane);
+  st.nxt = wave_rows<kSparse>(a, ctx, b0 + kCh, hi, s1, lane);
   if (lo < hi) {
     uint8_t* dst = buf0 + 16 * wave * kRowF8;
     zero_invalid_rows(st.cur, dst, lane);
