@@ -832,19 +832,34 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     // together they hold every key >= T, hence the whole top-k
     if (tid == 0) f.novf = (uint32_t)K;
     __syncthreads();
-    for (uint32_t fi = wave; fi < nflag; fi += kFinThreads / 64) {
-      const int b = (int)f.h[fi];
+    // one wave per flagged block; the next block's keys are loaded before this block's are
+    // appended, so each block's load time overlaps the previous block's appends
+    constexpr int kR = kBlockKeys / 64;
+    uint32_t fi = wave;
+    int b = fi < nflag ? (int)f.h[fi] : 0;
+    uint32_t kv[kR];
+    uint64_t tb = thr[b];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) kv[r] = sk[min<int64_t>((int64_t)b * kBlockKeys + lane + 64 * r, nv - 1)];
+    while (fi < nflag) {
+      const uint32_t fn = fi + kFinThreads / 64;
+      const int bn = fn < nflag ? (int)f.h[fn] : b;
+      uint32_t kn[kR];
+      const uint64_t tbn = thr[bn];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) kn[r] = sk[min<int64_t>((int64_t)bn * kBlockKeys + lane + 64 * r, nv - 1)];
       const int64_t jb = (int64_t)b * kBlockKeys;
-      const uint64_t tb = thr[b];
-      uint32_t kv[kBlockKeys / 64];
 #pragma unroll
-      for (int r = 0; r < kBlockKeys / 64; ++r) kv[r] = sk[min<int64_t>(jb + lane + 64 * r, nv - 1)];
-#pragma unroll
-      for (int r = 0; r < kBlockKeys / 64; ++r) {
+      for (int r = 0; r < kR; ++r) {
         const int64_t j = jb + lane + 64 * r;
         const uint64_t k64 = ((uint64_t)kv[r] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
         wave_append<uint64_t>(j < nv && k64 < tb && k64 >= T, k64, ovf, &f.novf, (uint32_t)ovf_cap);
       }
+      fi = fn;
+      b = bn;
+      tb = tbn;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) kv[r] = kn[r];
     }
     __threadfence_block();
     __syncthreads();
