@@ -160,3 +160,47 @@ def test_many_splits_and_unaligned_width(hca):
         rows = np.concatenate([ent[:nv], ent[OA.window_positions(t, W)]])
         ro, rl = OA.attend(q[i].double().numpy(), rows, scale)
         check_attention(o[i], lse[i], ro, rl, "fp32", f"q{i} nv={nv}")
+
+
+def test_long_entry_lists(hca):
+    """CSA with k = 65536 selected entries (the largest k the call accepts; a quarter of the slots
+    padded with -1) and HCA over 70000 visible entries, split FP8 stores, 16 heads: long lists
+    give many split-K partials per head (more than one merge group)."""
+    m, W_ = hca
+    n_cache, n_win, H, W, k = 70000, 256, 16, 128, 65536
+    dn, dr = 448, 64
+    D = dn + dr
+    cache_st, cache_dec = make_store("split", n_cache, 31, dn, dr)
+    win_st, win_dec = make_store("split", n_win, 32, dn, dr)
+    dev = "cuda"
+    cache, win = to_store(m, cache_st, dn, dr), to_store(m, win_st, dn, dr)
+    rng = np.random.default_rng(33)
+    nq = 2
+    q_pos = np.array([n_cache - 1, n_cache - 50], np.int64)  # the window store holds positions 69744 .. 69999
+    q_seq = np.zeros(nq, np.int32)
+    idx = np.full((nq, k), -1, np.int32)
+    for i in range(nq):
+        sel = rng.choice(n_cache, size=3 * k // 4, replace=False)
+        idx[i, rng.choice(k, size=sel.size, replace=False)] = sel
+    g = synth.generator(34)
+    q = synth.normal(g, (nq, H, D)).bfloat16()
+    qdec = q.double().numpy()
+    scale = 1.0 / math.sqrt(D)
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=dev)
+    wp0 = n_cache - n_win
+    ws = W_.Workspace(dev)
+    o, lse = W_.csa_attn(q.to(dev), cache, i64([0]), torch.tensor(idx, device=dev), win, i64([0]), i64([wp0]), W,
+                         torch.tensor(q_seq, device=dev), torch.tensor(q_pos, device=dev), scale, ws,
+                         o_dtype=torch.float32)
+    o2, lse2 = W_.hca_attn(q.to(dev), cache, i64([0]), 1, n_cache, win, i64([0]), i64([wp0]), W,
+                           torch.tensor(q_seq, device=dev), torch.tensor(q_pos, device=dev), scale, ws,
+                           o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o, lse, o2, lse2 = np_(o), np_(lse), np_(o2), np_(lse2)
+    raw = lambda pos: win_dec[np.asarray(pos) - wp0]
+    for i in range(nq):
+        t = int(q_pos[i])
+        ro, rl = OA.csa(qdec[i], t, cache_dec, idx[i], raw, W, scale)
+        check_attention(o[i], lse[i], ro, rl, "low", f"csa k=65536 q{i}")
+        ro, rl = OA.attend(qdec[i], np.concatenate([cache_dec[:t + 1], raw(OA.window_positions(t, W))]), scale)
+        check_attention(o2[i], lse2[i], ro, rl, "low", f"hca {t + 1} visible q{i}")

@@ -1,7 +1,8 @@
 """GPU parity of lightning_index_topk against the oracle on edge cases: exact
 ties (all-equal keys, all-zero scores), fewer visible entries than k, no visible
 entry, several sequences, batching forced by a small workspace, 1 and 8 indexer
-heads, k = 1 and k = 2048, and the path for more than 2^19 visible entries."""
+heads, k = 1 and k = 2048, the path for more than 2^19 visible entries, and the maximum of
+2^21 visible entries with k = 2048."""
 import numpy as np
 import pytest
 import torch
@@ -110,6 +111,16 @@ def test_more_than_2_19_visible_entries(hca):
     q, qs, w, kp, ks = mx_case(7, n, 2)
     got = run(hca, q, w, kp, [0], [0, 0], [n - 1, n - 5000], n, 1, 1000, qs, ks)
     check_idx(got, oracle_mxfp4(q, qs, w, kp, ks, [0], [0, 0], [n - 1, n - 5000], 1, 1000), "fallback path")
+
+
+def test_maximum_visible_entries_and_k(hca):
+    """The documented maximum: 2^21 visible entries (2048 score blocks) with k = 2048, beside a
+    query that sees fewer entries in the same launch."""
+    n = 1 << 21
+    q, qs, w, kp, ks = mx_case(8, n, 2)
+    q_pos = [n - 1, n - 700001]
+    got = run(hca, q, w, kp, [0], [0, 0], q_pos, n, 1, 2048, qs, ks)
+    check_idx(got, oracle_mxfp4(q, qs, w, kp, ks, [0], [0, 0], q_pos, 1, 2048), "2^21 visible, k = 2048")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
