@@ -137,3 +137,46 @@ def decode_mxfp4(packed, scales, block=32):
     sc = decode_e8m0(scales)
     assert sc.shape[-1] * block == d
     return vals * np.repeat(sc, block, axis=-1)
+
+
+def mx_shared_exp(amax, emax_elem=2):
+    """Shared exponent of an MX block (OCP Microscaling Formats v1.0, the
+    conversion of a block of values: the scale is 2**(floor(log2(amax)) -
+    emax_elem), with emax_elem = 2 for E2M1, whose largest normal is 1.5 * 2**2).
+
+    Readings of what the spec leaves to the implementation: the exponent is
+    clamped below at -127 (the smallest E8M0 scale), and a block of zeros gets
+    -127 too. floor(log2(amax)) is taken from frexp, so it is exact."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(amax)                  # amax = mant * 2**ex, mant in [0.5, 1)
+    e = np.maximum(ex - 1 - emax_elem, -127)
+    return np.where(amax == 0, -127, e).astype(np.int64)
+
+
+_E2M1_POS = E2M1_VALUES[:8]                 # codes 0..7, increasing
+
+
+def encode_e2m1(values):
+    """float64 -> E2M1 codes (uint8 nibbles), nearest with ties to the even
+    code, saturating at +-6. A value that rounds to zero magnitude encodes as
+    +0 (code 0), whatever its sign."""
+    v = np.asarray(values, dtype=np.float64)
+    assert np.all(np.isfinite(v)), "non-finite input"
+    code = _round_to_grid(np.abs(v), _E2M1_POS).astype(np.uint8)
+    sign = (np.signbit(v) & (code != 0)).astype(np.uint8) << 3
+    return code | sign
+
+
+def encode_mxfp4(values, block=32):
+    """float64 [..., d] -> (packed uint8 [..., d/2], E8M0 scales uint8
+    [..., d/block]): per block of `block` consecutive values the shared
+    exponent of mx_shared_exp, elements encode_e2m1(v / 2**exp), two per
+    byte with element 2i in the low nibble of byte i."""
+    v = np.asarray(values, dtype=np.float64)
+    d = v.shape[-1]
+    assert d % block == 0 and d % 2 == 0
+    blocks = v.reshape(*v.shape[:-1], d // block, block)
+    e = mx_shared_exp(np.abs(blocks).max(axis=-1))
+    nib = encode_e2m1(blocks / np.ldexp(1.0, e)[..., None]).reshape(v.shape)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)

@@ -162,12 +162,14 @@ def test_many_splits_and_unaligned_width(hca):
         check_attention(o[i], lse[i], ro, rl, "fp32", f"q{i} nv={nv}")
 
 
-def test_long_entry_lists(hca):
+@pytest.mark.parametrize("H", [16, 32])
+def test_long_entry_lists(hca, H):
     """CSA with k = 65536 selected entries (the largest k the call accepts; a quarter of the slots
-    padded with -1) and HCA over 70000 visible entries, split FP8 stores, 16 heads: long lists
-    give many split-K partials per head (more than one merge group)."""
+    padded with -1) and HCA over 70000 visible entries, split FP8 stores, 16 heads (one head
+    group per block) and 32 (two): long lists give many split-K partials per head (more than one
+    merge group)."""
     m, W_ = hca
-    n_cache, n_win, H, W, k = 70000, 256, 16, 128, 65536
+    n_cache, n_win, W, k = 70000, 256, 128, 65536
     dn, dr = 448, 64
     D = dn + dr
     cache_st, cache_dec = make_store("split", n_cache, 31, dn, dr)
