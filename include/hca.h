@@ -68,6 +68,11 @@ extern "C" {
                               two scale (value = code * scale), d_rope bf16
                               (the efficiency paragraph: FP8 for the non-RoPE
                               dims, BF16 for the RoPE dims)                   */
+#define HCA_LAYOUT_MXFP4 3 /* per row: D/2 bytes of E2M1 codes (element 2i in
+                              the low nibble of byte i) and D/32 E8M0 block
+                              scales (the efficiency paragraph: FP4 indexer;
+                              OCP MX blocks of 32). Written by the
+                              compressors only: the indexer-key layout.       */
 
 /*
  * A view of n_rows KV rows of width D = d_nope + d_rope. The first d_nope
@@ -77,6 +82,13 @@ extern "C" {
  *  split layout:  row r's FP8 codes are `data + r * row_stride` (bytes), its
  *                 scale is `scale[r]`, its RoPE dims are
  *                 `rope + r * rope_stride` (bf16 elements).
+ *  MXFP4 layout:  d_nope = D (a multiple of 32), d_rope = 0; row r's codes
+ *                 are `data + r * row_stride` (bytes), its E8M0 scales are
+ *                 the bytes `(uint8_t*)rope + r * rope_stride`; `scale` is
+ *                 unused. The scale rows are byte-addressed (no 16-byte
+ *                 alignment needed); k_idx / k_idx_scale of
+ *                 lightning_index_topk are such a store with row_stride
+ *                 d/2 and rope_stride d/32.
  */
 typedef struct hca_store {
   int32_t layout;
@@ -106,7 +118,11 @@ const char* hca_last_error(void);
  * Entries first_entry .. first_entry + n_entries - 1 are written to rows
  * out_row0 .. of `out`; a split output gets a per-row scale
  * 2^e, e the smallest integer (>= -126) with max|y[j, :d_nope]| <= 448 * 2^e,
- * and E4M3 codes RNE(y / 2^e); bf16 outputs round to nearest even.
+ * and E4M3 codes RNE(y / 2^e); bf16 outputs round to nearest even. An MXFP4
+ * output (OCP MX conversion) takes per block of 32 channels the scale 2^e,
+ * e = floor(log2 max|y|) - 2 clamped below at -127 (-127 for a zero block),
+ * and E2M1 codes of y / 2^e rounded to nearest, ties to the even code,
+ * saturating at 6; zero magnitudes encode as +0.
  *
  * raw:     [n_rows, D] of raw_dtype (HCA_F32 or HCA_BF16), row stride
  *          raw_row_stride elements; row r holds absolute position first_pos+r.
@@ -118,7 +134,9 @@ const char* hca_last_error(void);
  * requested entries read (HCA_ERR_INVALID_ARG otherwise); D <= 1024 (bf16)
  * or 512 (f32), D a multiple of 8 (bf16) or 4 (f32), d_nope likewise;
  * out_row0 + n_entries <= out->n_rows.
- * Output layouts: HCA_LAYOUT_F32, HCA_LAYOUT_BF16, HCA_LAYOUT_SPLIT.
+ * Output layouts: HCA_LAYOUT_F32, HCA_LAYOUT_BF16, HCA_LAYOUT_SPLIT,
+ * HCA_LAYOUT_MXFP4 (the indexer keys: the efficiency paragraph's FP4
+ * indexer applied to compressed 64-dim keys).
  */
 int csa_compress(const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int64_t n_rows,
                  int64_t first_pos, const void* logits, int64_t logit_row_stride,
@@ -136,6 +154,75 @@ int hca_compress(const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int
                  int64_t logit_col_stride, const float* pos_bias, int32_t m_prime,
                  int64_t first_entry, int64_t n_entries, const hca_store* out, int64_t out_row0,
                  void* stream);
+
+/*
+ * One layer's decode-time state (CSA paragraph: an entry per m tokens and a
+ * lightning indexer over the entries; HCA paragraph: an entry per m' tokens,
+ * no overlap; both: a sliding window of the last W raw tokens).
+ *
+ * Raw ring: per sequence b, R rows (R >= w and R >= m_prime) of the raw
+ * inputs of its last R tokens, the token at position p in row b * R + p % R
+ * of each ring array (bf16, row-contiguous: D elements per row for x and the
+ * two logit rings, d_idx for the indexer-key rings).
+ * Window store: the last W raw tokens in the store's layout (F32, BF16 or
+ * SPLIT), the token at position p written to rows win_row_begin[b] + p % W
+ * and win_row_begin[b] + p % W + W, with win_pos0[b] kept at
+ * W * floor(max(0, t - W + 1) / W) once the token at t is in: position p of
+ * the window is then row win_row_begin[b] + p - win_pos0[b], which is how
+ * csa_sparse_mqa_attn / hca_dense_mqa_attn read the window.
+ * Entry stores: CSA entry j of sequence b goes to row csa_row_begin[b] + j
+ * of `csa`, HCA entry j to hca_row_begin[b] + j of `hca`, the indexer key of
+ * CSA entry j (the CSA compressor with w, m on d_idx channels, then encoded
+ * in `idx`'s layout, normally MXFP4) to idx_row_begin[b] + j of `idx`.
+ * All pointers are device pointers; the struct lives in host memory.
+ */
+typedef struct hca_decode_layer {
+  int32_t m, w, m_prime, W;
+  int32_t R;             /* ring rows per sequence */
+  int32_t d_idx;         /* indexer key width; 0 = no indexer keys */
+  const float* bias_csa; /* [w, D] */
+  const float* bias_hca; /* [m_prime, D] */
+  const float* bias_idx; /* [w, d_idx] */
+  void* ring_x;          /* bf16 [B * R, D]: raw KV */
+  void* ring_z_csa;      /* bf16 [B * R, D]: CSA compression logits */
+  void* ring_z_hca;      /* bf16 [B * R, D]: HCA compression logits */
+  void* ring_k_idx;      /* bf16 [B * R, d_idx]: raw indexer keys */
+  void* ring_z_idx;      /* bf16 [B * R, d_idx]: indexer-key compression logits */
+  hca_store window;
+  const int64_t* win_row_begin; /* [B] */
+  int64_t* win_pos0;            /* [B], written */
+  hca_store csa;
+  const int64_t* csa_row_begin; /* [B] */
+  hca_store hca;
+  const int64_t* hca_row_begin; /* [B] */
+  hca_store idx;
+  const int64_t* idx_row_begin; /* [B] */
+} hca_decode_layer;
+
+/*
+ * decode_append — one decode step of the layer's compression state: for
+ * every sequence b with pos[b] >= 0, the token at t = pos[b] (row b of x,
+ * z_csa, z_hca [B, D] and of k_idx, z_idx [B, d_idx], bf16, contiguous) goes
+ * into the raw ring and the window store (win_pos0[b] updated); if
+ * (t+1) % m == 0 it emits CSA entry j = (t+1)/m - 1 and its indexer key,
+ * and if (t+1) % m_prime == 0 HCA entry (t+1)/m_prime - 1, each equal to
+ * what csa_compress / hca_compress write for that entry from the whole
+ * sequence (same arithmetic in the same order). Sequences with pos[b] < 0
+ * are left untouched (an idle slot of the batch).
+ * Preconditions (device contents): tokens of a sequence arrive in order,
+ * one per call, starting at position 0 or with the ring already holding the
+ * previous R - 1 positions. Rows past a store's n_rows are not written (an
+ * entry or window row beyond it is dropped).
+ * Requires B >= 1; the window, csa and hca stores of one width D (a multiple
+ * of 8, <= 1024), window layout F32, BF16 or SPLIT, entry stores in any
+ * layout csa_compress writes; d_idx == 0 or a multiple of 8 (of 32 for an
+ * MXFP4 idx store) <= 1024; 1 <= m <= w; 1 <= m_prime; R >= max(w, m_prime);
+ * W >= 1. k_idx, z_idx, bias_idx, the indexer rings and idx are unused when
+ * d_idx == 0.
+ */
+int decode_append(const hca_decode_layer* layer, int32_t B, const int64_t* pos, const void* x,
+                  const void* z_csa, const void* z_hca, const void* k_idx, const void* z_idx,
+                  void* stream);
 
 /*
  * lightning_index_topk — the lightning indexer (CSA paragraph: it selects

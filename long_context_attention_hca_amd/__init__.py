@@ -15,14 +15,14 @@ import os
 import torch
 
 __all__ = [
-    "F32", "BF16", "FP8_E4M3", "MXFP4", "LAYOUT_F32", "LAYOUT_BF16", "LAYOUT_SPLIT",
-    "HcaError", "Store", "abi_version", "csa_compress", "hca_compress",
+    "F32", "BF16", "FP8_E4M3", "MXFP4", "LAYOUT_F32", "LAYOUT_BF16", "LAYOUT_SPLIT", "LAYOUT_MXFP4",
+    "HcaError", "Store", "DecodeLayer", "abi_version", "csa_compress", "hca_compress", "decode_append",
     "lightning_index_topk_workspace", "lightning_index_topk", "mqa_attn_workspace",
     "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "library_path",
 ]
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
-LAYOUT_F32, LAYOUT_BF16, LAYOUT_SPLIT = 0, 1, 2
+LAYOUT_F32, LAYOUT_BF16, LAYOUT_SPLIT, LAYOUT_MXFP4 = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libhca.so")
@@ -38,6 +38,18 @@ class _StoreC(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("n_rows", ctypes.c_int64), ("data", ctypes.c_void_p),
                 ("row_stride", ctypes.c_int64), ("scale", ctypes.c_void_p), ("rope", ctypes.c_void_p),
                 ("rope_stride", ctypes.c_int64)]
+
+
+class _DecodeLayerC(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("w", ctypes.c_int32), ("m_prime", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("R", ctypes.c_int32), ("d_idx", ctypes.c_int32),
+                ("bias_csa", ctypes.c_void_p), ("bias_hca", ctypes.c_void_p), ("bias_idx", ctypes.c_void_p),
+                ("ring_x", ctypes.c_void_p), ("ring_z_csa", ctypes.c_void_p), ("ring_z_hca", ctypes.c_void_p),
+                ("ring_k_idx", ctypes.c_void_p), ("ring_z_idx", ctypes.c_void_p),
+                ("window", _StoreC), ("win_row_begin", ctypes.c_void_p), ("win_pos0", ctypes.c_void_p),
+                ("csa", _StoreC), ("csa_row_begin", ctypes.c_void_p),
+                ("hca", _StoreC), ("hca_row_begin", ctypes.c_void_p),
+                ("idx", _StoreC), ("idx_row_begin", ctypes.c_void_p)]
 
 
 _P, _I32, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -57,6 +69,8 @@ _last_error = _sig("hca_last_error", ctypes.c_char_p, [])
 _compress_args = [_P, _I32, _I64, _I64, _I64, _P, _I64, _I64, _P]
 _csa_compress = _sig("csa_compress", ctypes.c_int, _compress_args + [_I32, _I32, _I64, _I64, _SP, _I64, _P])
 _hca_compress = _sig("hca_compress", ctypes.c_int, _compress_args + [_I32, _I64, _I64, _SP, _I64, _P])
+_decode_append = _sig("decode_append", ctypes.c_int,
+                      [ctypes.POINTER(_DecodeLayerC), _I32, _P, _P, _P, _P, _P, _P, _P])
 _index_ws = _sig("lightning_index_topk_workspace", _SZ, [_I32, _I64, _I32])
 _index = _sig("lightning_index_topk", ctypes.c_int,
               [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P])
@@ -107,6 +121,8 @@ class Store:
     dense: `data` [n_rows, >=D] float32 or bf16 (torch.bfloat16 / int16 bits).
     split: `data` uint8 E4M3 codes [n_rows, >=d_nope], `scale` float32 [n_rows],
            `rope` bf16 bits [n_rows, >=d_rope].
+    mxfp4: `data` uint8 E2M1 codes [n_rows, >=D/2], the E8M0 scales uint8
+           [n_rows, >=D/32] in the `rope` slot (d_nope = D, d_rope = 0).
     Tensors are kept referenced by the Store.
     """
 
@@ -126,6 +142,10 @@ class Store:
     @classmethod
     def split(cls, nope, scale, rope):
         return cls(LAYOUT_SPLIT, nope.shape[1], rope.shape[1], nope, scale, rope)
+
+    @classmethod
+    def mxfp4(cls, codes, scales):
+        return cls(LAYOUT_MXFP4, codes.shape[1] * 2, 0, codes, None, scales)
 
     @property
     def n_rows(self):
@@ -147,6 +167,38 @@ def hca_compress(raw, first_pos, logits, pos_bias, m_prime, first_entry, n_entri
     _check(_hca_compress(_ptr(raw), _dtype_code(raw), raw.stride(0), raw.shape[0], first_pos, _ptr(logits),
                          logits.stride(0), 0 if scalar_logits else 1, _ptr(pos_bias), m_prime, first_entry,
                          n_entries, out.c(), out_row0, _stream(stream)))
+
+
+class DecodeLayer:
+    """One layer's decode-time state for decode_append (the hca_decode_layer of include/hca.h).
+
+    rings: dict of bf16 tensors "x", "z_csa", "z_hca" [B * R, D] and, with indexer keys,
+    "k_idx", "z_idx" [B * R, d_idx]; window / csa / hca / idx: Stores; *_row_begin: int64 [B]
+    device tensors; win_pos0: int64 [B] (written by decode_append). Tensors are kept referenced.
+    """
+
+    def __init__(self, m, w, m_prime, W, R, bias_csa, bias_hca, rings, window, win_row_begin, win_pos0, csa,
+                 csa_row_begin, hca, hca_row_begin, idx=None, idx_row_begin=None, bias_idx=None):
+        self.keep = (bias_csa, bias_hca, bias_idx, rings, window, win_row_begin, win_pos0, csa, csa_row_begin, hca,
+                     hca_row_begin, idx, idx_row_begin)
+        d_idx = 0 if idx is None else idx.d_nope + idx.d_rope
+        p = lambda t: None if t is None else t.data_ptr()
+        self._c = _DecodeLayerC(m, w, m_prime, W, R, d_idx, p(bias_csa), p(bias_hca), p(bias_idx),
+                                p(rings["x"]), p(rings["z_csa"]), p(rings["z_hca"]),
+                                p(rings.get("k_idx")), p(rings.get("z_idx")),
+                                window._c, p(win_row_begin), p(win_pos0), csa._c, p(csa_row_begin), hca._c,
+                                p(hca_row_begin), idx._c if idx is not None else _StoreC(),
+                                p(idx_row_begin))
+
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def decode_append(layer, pos, x, z_csa, z_hca, k_idx=None, z_idx=None, stream=None):
+    """One decode step: pos int64 [B] (negative = idle slot), x / z_csa / z_hca bf16 [B, D],
+    k_idx / z_idx bf16 [B, d_idx] (with indexer keys)."""
+    _check(_decode_append(layer.c(), pos.shape[0], _ptr(pos), _ptr(x), _ptr(z_csa), _ptr(z_hca), _ptr(k_idx),
+                          _ptr(z_idx), _stream(stream)))
 
 
 def lightning_index_topk_workspace(nq, max_visible, k):

@@ -78,6 +78,13 @@ int check_store(const char* fn, const hca_store* s, const char* what, std::strin
       if (s->rope_stride < s->d_rope || (s->rope_stride * 2) % 16) return bad("bad rope_stride");
       if (s->d_nope % 8 || s->d_rope % 8) return bad("d_nope and d_rope must be multiples of 8");
       return HCA_OK;
+    case HCA_LAYOUT_MXFP4:
+      if (s->d_rope != 0 || s->d_nope % 32) return bad("MXFP4 rows need d_rope == 0 and d_nope a multiple of 32");
+      if (s->n_rows > 0 && (!s->data || !s->rope)) return bad("NULL data/scales (rope)");
+      if (!aligned16(s->data)) return bad("data not 16-byte aligned");
+      if (s->row_stride < s->d_nope / 2 || s->row_stride % 16) return bad("bad MXFP4 row_stride");
+      if (s->rope_stride < s->d_nope / 32) return bad("bad MXFP4 scale stride (rope_stride)");
+      return HCA_OK;
     default:
       return bad("unknown layout");
   }
@@ -141,6 +148,69 @@ int compress_impl(const char* fn, const void* raw, int32_t raw_dtype, int64_t ra
   return launched(fn, hca::launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 
+
+int decode_impl(const char* fn, const hca_decode_layer* L, int32_t B, const int64_t* pos, const void* x,
+                const void* z_csa, const void* z_hca, const void* k_idx, const void* z_idx, void* stream) {
+  if (!L || !pos || !x || !z_csa || !z_hca) return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
+  if (B < 1) return fail(HCA_ERR_INVALID_ARG, fn, "B < 1");
+  if (L->m < 1 || L->w < L->m || L->m_prime < 1 || L->W < 1)
+    return fail(HCA_ERR_INVALID_ARG, fn, "need 1 <= m <= w, m_prime >= 1, W >= 1");
+  if (L->R < L->w || L->R < L->m_prime) return fail(HCA_ERR_INVALID_ARG, fn, "ring rows R < max(w, m_prime)");
+  if (L->w > 1024 || L->m_prime > 1024) return fail(HCA_ERR_INVALID_ARG, fn, "window longer than 1024");
+  std::string msg;
+  if (check_store(fn, &L->window, "window", &msg) != HCA_OK || check_store(fn, &L->csa, "csa", &msg) != HCA_OK ||
+      check_store(fn, &L->hca, "hca", &msg) != HCA_OK)
+    return fail(HCA_ERR_INVALID_ARG, fn, msg.c_str());
+  if (L->window.layout == HCA_LAYOUT_MXFP4) return fail(HCA_ERR_UNSUPPORTED, fn, "window layout must be F32, BF16 or SPLIT");
+  const int64_t D = (int64_t)L->csa.d_nope + L->csa.d_rope;
+  if ((int64_t)L->window.d_nope + L->window.d_rope != D || (int64_t)L->hca.d_nope + L->hca.d_rope != D)
+    return fail(HCA_ERR_INVALID_ARG, fn, "window, csa and hca widths differ");
+  for (const hca_store* s : {&L->window, &L->csa, &L->hca})
+    if (s->d_nope % 8) return fail(HCA_ERR_UNSUPPORTED, fn, "d_nope must be a multiple of 8");
+  if (D % 8 || D > 1024) return fail(HCA_ERR_UNSUPPORTED, fn, "D must be a multiple of 8, at most 1024");
+  const int64_t di = L->d_idx;
+  if (di < 0 || di % 8 || di > 1024) return fail(HCA_ERR_UNSUPPORTED, fn, "d_idx must be 0 or a multiple of 8 <= 1024");
+  if (!L->bias_csa || !L->bias_hca || !L->ring_x || !L->ring_z_csa || !L->ring_z_hca || !L->win_row_begin ||
+      !L->win_pos0 || !L->csa_row_begin || !L->hca_row_begin)
+    return fail(HCA_ERR_INVALID_ARG, fn, "NULL field of the layer");
+  for (const void* p : {(const void*)L->bias_csa, (const void*)L->bias_hca, (const void*)L->ring_x,
+                        (const void*)L->ring_z_csa, (const void*)L->ring_z_hca, x, z_csa, z_hca})
+    if (!aligned16(p)) return fail(HCA_ERR_INVALID_ARG, fn, "inputs, rings and biases must be 16-byte aligned");
+  if (di > 0) {
+    if (!k_idx || !z_idx || !L->bias_idx || !L->ring_k_idx || !L->ring_z_idx || !L->idx_row_begin)
+      return fail(HCA_ERR_INVALID_ARG, fn, "NULL indexer-key argument");
+    if (check_store(fn, &L->idx, "idx", &msg) != HCA_OK) return fail(HCA_ERR_INVALID_ARG, fn, msg.c_str());
+    if ((int64_t)L->idx.d_nope + L->idx.d_rope != di) return fail(HCA_ERR_INVALID_ARG, fn, "idx width != d_idx");
+    if (L->idx.d_nope % 8) return fail(HCA_ERR_UNSUPPORTED, fn, "idx d_nope must be a multiple of 8");
+    for (const void* p : {(const void*)L->bias_idx, (const void*)L->ring_k_idx, (const void*)L->ring_z_idx, k_idx, z_idx})
+      if (!aligned16(p)) return fail(HCA_ERR_INVALID_ARG, fn, "indexer inputs, rings and bias must be 16-byte aligned");
+  }
+  hca::DecodeArgs a;
+  a.B = B;
+  a.pos = pos;
+  a.x = static_cast<const uint16_t*>(x);
+  a.zc = static_cast<const uint16_t*>(z_csa);
+  a.zh = static_cast<const uint16_t*>(z_hca);
+  a.ki = static_cast<const uint16_t*>(k_idx);
+  a.zi = static_cast<const uint16_t*>(z_idx);
+  a.m = L->m; a.w = L->w; a.m_prime = L->m_prime; a.W = L->W; a.R = L->R; a.D = (int)D; a.d_idx = (int)di;
+  a.bias_csa = L->bias_csa; a.bias_hca = L->bias_hca; a.bias_idx = L->bias_idx;
+  a.ring_x = static_cast<uint16_t*>(L->ring_x);
+  a.ring_zc = static_cast<uint16_t*>(L->ring_z_csa);
+  a.ring_zh = static_cast<uint16_t*>(L->ring_z_hca);
+  a.ring_ki = static_cast<uint16_t*>(L->ring_k_idx);
+  a.ring_zi = static_cast<uint16_t*>(L->ring_z_idx);
+  a.win = view_of(&L->window);
+  a.csa = view_of(&L->csa);
+  a.hca = view_of(&L->hca);
+  a.idx = di > 0 ? view_of(&L->idx) : a.csa;
+  a.win_rb = L->win_row_begin;
+  a.win_pos0 = L->win_pos0;
+  a.csa_rb = L->csa_row_begin;
+  a.hca_rb = L->hca_row_begin;
+  a.idx_rb = di > 0 ? L->idx_row_begin : L->csa_row_begin;
+  return launched(fn, hca::launch_decode_append(a, static_cast<hipStream_t>(stream)));
+}
 
 size_t index_ws(int64_t nq, int64_t max_visible) { return hca::index_ws_layout(nq, max_visible, nullptr, nullptr); }
 
@@ -213,6 +283,12 @@ extern "C" {
 #define HCA_EXPORT __attribute__((visibility("default")))
 
 HCA_EXPORT int hca_abi_version(void) { return HCA_ABI_VERSION; }
+
+HCA_EXPORT int decode_append(const hca_decode_layer* layer, int32_t B, const int64_t* pos, const void* x,
+                             const void* z_csa, const void* z_hca, const void* k_idx, const void* z_idx,
+                             void* stream) {
+  return decode_impl("decode_append", layer, B, pos, x, z_csa, z_hca, k_idx, z_idx, stream);
+}
 
 HCA_EXPORT const char* hca_status_string(int status) {
   switch (status) {

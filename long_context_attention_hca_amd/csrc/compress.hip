@@ -14,7 +14,13 @@
 // per lane) with an online softmax across blocks, so HCA's 128-row windows need
 // one exp per element plus one per block. The output encoding (float32, bf16,
 // or FP8 E4M3 + per-entry power-of-two scale + bf16 RoPE dims) is fused into
-// the store; the FP8 scale needs one wave-wide max.
+// the store; the FP8 scale needs one wave-wide max. MXFP4 outputs (the indexer keys) take one
+// max per 32-channel block across the lanes that hold it.
+//
+// Decode: decode_append_kernel runs one sequence per block and one wave per task (CSA entry,
+// HCA entry, indexer key, window row, ring write). The entry tasks call the same per-entry
+// reduction as compress_kernel, reading the raw ring and the step's own token through a
+// row-source functor, so an entry emitted at decode time equals the bulk one bit for bit.
 #include "common.h"
 #include "internal.h"
 
@@ -97,6 +103,42 @@ __device__ __forceinline__ void store_entry(const CompressArgs& a, int64_t orow,
         *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(y[g][0], y[g][1]), pack_bf16x2(y[g][2], y[g][3]));
       }
     }
+  } else if (LAYOUT == HCA_LAYOUT_MXFP4) {
+    // blocks of 32 channels = LPB consecutive lanes: shared exponent floor(log2 amax) - 2
+    // (>= -127; -127 for a zero block), E2M1 codes of y * 2^-e, nearest with ties to the even
+    // code (the thresholds below: strict at ties that fall to the lower, even code), saturating
+    // at 6; zero magnitudes are +0. Two codes per byte, channel 2i in the low nibble of byte i.
+    constexpr int LPB = 32 / VEC;
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      const int c0 = (g * 64 + lane) * VEC;
+      float amax = 0.f;
+      if (c0 < a.D) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) amax = fmaxf(amax, fabsf(y[g][v]));
+      }
+#pragma unroll
+      for (int off = 1; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      if (c0 >= a.D) continue;
+      const uint32_t ef = (__float_as_uint(amax) >> 23) & 0xFFu;
+      const int ex = ef == 0 ? -127 : max((int)ef - 129, -127);
+      const float inv = __builtin_ldexpf(1.0f, -ex);
+      uint32_t word = 0;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const float q = y[g][v] * inv;  // exact: a power-of-two scaling within range
+        const float m = fabsf(q);
+        uint32_t code = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                        (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
+        if (code != 0 && (__float_as_uint(q) >> 31)) code |= 8u;
+        word |= code << (4 * v);
+      }
+      uint8_t* op = static_cast<uint8_t*>(a.out) + orow * a.out_stride + c0 / 2;
+      if (VEC == 8) *reinterpret_cast<uint32_t*>(op) = word;
+      else *reinterpret_cast<uint16_t*>(op) = (uint16_t)word;
+      if ((lane & (LPB - 1)) == 0)
+        static_cast<uint8_t*>(a.out_rope)[orow * a.out_rope_stride + c0 / 32] = (uint8_t)(ex + 127);
+    }
   } else {  // split: FP8 E4M3 non-RoPE dims with a per-entry power-of-two scale, bf16 RoPE dims
     float amax = 0.f;
 #pragma unroll
@@ -141,23 +183,30 @@ __device__ __forceinline__ void store_entry(const CompressArgs& a, int64_t orow,
   }
 }
 
-template <typename T, int LAYOUT, bool SCALAR>
-__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+// Raw and logit rows of a contiguous input: position p is row p - first_pos.
+template <typename T>
+struct LinearRows {
+  const T* raw;
+  const T* lg;
+  int64_t raw_stride, lg_stride, first_pos;
+  __device__ const T* x(int64_t p) const { return raw + (p - first_pos) * raw_stride; }
+  __device__ const T* z(int64_t p) const { return lg + (p - first_pos) * lg_stride; }
+};
+
+constexpr int kGMax = 2;  // column groups of 64*VEC channels: D <= 1024 (bf16) / 512 (f32)
+
+// Entry j into y (lane's channels (g * 64 + lane) * VEC + v): per channel the softmax over the
+// window's positions of logit + bias, weighting the raw values. Window positions are taken in
+// blocks of 8 rows held in registers, with an online softmax across blocks.
+template <typename T, bool SCALAR, class Rows>
+__device__ __forceinline__ void compress_entry(const CompressArgs& a, const Rows& rows, int64_t j,
+                                               float (&y)[kGMax][Raw<T>::VEC], int lane) {
   constexpr int VEC = Raw<T>::VEC;
-  constexpr int GMAX = 2;  // column groups of 64*VEC channels: D <= 1024 (bf16) / 512 (f32)
-  constexpr int PB = 8;    // window positions per register block
-  const int lane = threadIdx.x & 63;
-  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= a.n_entries) return;
-  const int64_t j = a.first_entry + e;
+  constexpr int PB = 8;  // window positions per register block
   const int64_t start = j * a.m - (a.w - a.m);  // absolute position of window position 0
   const int p0 = start < 0 ? (int)(-start) : 0;
-  const T* raw = static_cast<const T*>(a.raw);
-  const T* lg = static_cast<const T*>(a.logits);
-
-  float y[GMAX][VEC];
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g) {
+  for (int g = 0; g < kGMax; ++g) {
     const int c0 = (g * 64 + lane) * VEC;
 #pragma unroll
     for (int v = 0; v < VEC; ++v) y[g][v] = 0.f;
@@ -171,14 +220,14 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
       for (int i = 0; i < PB; ++i) {
         if (i < nb) {
-          const int64_t r = start + pb + i - a.first_pos;
-          Raw<T>::load(raw + r * a.raw_stride + c0, xv[i]);
+          const int64_t pos = start + pb + i;
+          Raw<T>::load(rows.x(pos) + c0, xv[i]);
           if (SCALAR) {
-            const float zz = Raw<T>::scalar(lg + r * a.logit_row_stride);
+            const float zz = Raw<T>::scalar(rows.z(pos));
 #pragma unroll
             for (int v = 0; v < VEC; ++v) zv[i][v] = zz;
           } else {
-            Raw<T>::load(lg + r * a.logit_row_stride + c0, zv[i]);
+            Raw<T>::load(rows.z(pos) + c0, zv[i]);
           }
           const float* bp = a.bias + (int64_t)(pb + i) * a.D + c0;
 #pragma unroll
@@ -211,8 +260,18 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) y[g][v] = A[v] / S[v];
   }
+}
 
-  store_entry<VEC, GMAX, LAYOUT>(a, a.out_row0 + e, y, lane);
+template <typename T, int LAYOUT, bool SCALAR>
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= a.n_entries) return;
+  const LinearRows<T> rows{static_cast<const T*>(a.raw), static_cast<const T*>(a.logits), a.raw_stride,
+                           a.logit_row_stride, a.first_pos};
+  float y[kGMax][Raw<T>::VEC];
+  compress_entry<T, SCALAR>(a, rows, a.first_entry + e, y, lane);
+  store_entry<Raw<T>::VEC, kGMax, LAYOUT>(a, a.out_row0 + e, y, lane);
 }
 
 // CSA-shaped windows (w = 2m = 8) with D <= 64 VEC: one wave takes kRun consecutive entries
@@ -320,11 +379,123 @@ hipError_t launch_layout(const CompressArgs& a, hipStream_t s) {
   switch (a.out_layout) {
     case HCA_LAYOUT_F32: return launch_t<T, HCA_LAYOUT_F32>(a, s);
     case HCA_LAYOUT_BF16: return launch_t<T, HCA_LAYOUT_BF16>(a, s);
+    case HCA_LAYOUT_MXFP4: return launch_t<T, HCA_LAYOUT_MXFP4>(a, s);
     default: return launch_t<T, HCA_LAYOUT_SPLIT>(a, s);
   }
 }
 
+// Rows of one sequence at a decode step: the token at position t from the step's inputs, older
+// positions from the raw ring (row p mod R).
+struct RingRows {
+  const uint16_t* ring_x;
+  const uint16_t* ring_z;
+  const uint16_t* in_x;
+  const uint16_t* in_z;
+  int64_t t;
+  int R, stride;
+  __device__ const uint16_t* x(int64_t p) const { return p == t ? in_x : ring_x + (p % R) * stride; }
+  __device__ const uint16_t* z(int64_t p) const { return p == t ? in_z : ring_z + (p % R) * stride; }
+};
+
+// store_entry for a layout known at run time (uniform across the wave).
+template <int VEC, int G>
+__device__ __forceinline__ void store_any(const CompressArgs& a, int layout, int64_t orow, const float (&y)[G][VEC],
+                                          int lane) {
+  switch (layout) {
+    case HCA_LAYOUT_F32: store_entry<VEC, G, HCA_LAYOUT_F32>(a, orow, y, lane); break;
+    case HCA_LAYOUT_BF16: store_entry<VEC, G, HCA_LAYOUT_BF16>(a, orow, y, lane); break;
+    case HCA_LAYOUT_MXFP4: store_entry<VEC, G, HCA_LAYOUT_MXFP4>(a, orow, y, lane); break;
+    default: store_entry<VEC, G, HCA_LAYOUT_SPLIT>(a, orow, y, lane); break;
+  }
+}
+
+// Output fields of a store view for store_entry.
+__device__ __forceinline__ void set_out(CompressArgs& c, const StoreView& v, int D) {
+  c.D = D;
+  c.d_nope = v.d_nope;
+  c.out_layout = v.layout;
+  c.out = const_cast<void*>(v.data);
+  c.out_stride = v.row_stride;
+  c.out_scale = const_cast<float*>(v.scale);
+  c.out_rope = const_cast<void*>(v.rope);
+  c.out_rope_stride = v.rope_stride;
+}
+
+// One block per sequence, wave k runs task k: 0 CSA entry, 1 HCA entry, 2 indexer key,
+// 3 window rows, 4 ring row. The entry tasks read positions t - w + 1 .. t - 1 (t - m' + 1 ..)
+// from the ring, none of which is the ring row that task 4 overwrites (R >= w, m').
+__global__ __launch_bounds__(320) void decode_append_kernel(DecodeArgs a) {
+  constexpr int VEC = 8;
+  const int b = blockIdx.x;
+  const int task = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t t = a.pos[b];
+  if (t < 0) return;
+  const int D = a.D, di = a.d_idx;
+  const uint16_t* xin = a.x + (int64_t)b * D;
+  const size_t ring_row = (size_t)b * a.R + (size_t)(t % a.R);
+  if (task <= 2) {
+    const bool idx = task == 2;
+    const int mm = task == 1 ? a.m_prime : a.m, ww = task == 1 ? a.m_prime : a.w;
+    if (idx && di == 0) return;
+    if ((t + 1) % mm != 0) return;
+    const int64_t j = (t + 1) / mm - 1;
+    const StoreView& st = task == 0 ? a.csa : task == 1 ? a.hca : a.idx;
+    const int64_t rb = (task == 0 ? a.csa_rb : task == 1 ? a.hca_rb : a.idx_rb)[b];
+    const int64_t orow = rb + j;
+    if (orow < 0 || orow >= st.n_rows) return;
+    const int width = idx ? di : D;
+    CompressArgs c;
+    c.m = mm;
+    c.w = ww;
+    c.bias = task == 0 ? a.bias_csa : task == 1 ? a.bias_hca : a.bias_idx;
+    set_out(c, st, width);
+    const RingRows rows{idx ? a.ring_ki + (size_t)b * a.R * di : a.ring_x + (size_t)b * a.R * D,
+                        (task == 0 ? a.ring_zc : task == 1 ? a.ring_zh : a.ring_zi) + (size_t)b * a.R * width,
+                        idx ? a.ki + (int64_t)b * di : xin,
+                        (task == 0 ? a.zc : task == 1 ? a.zh : a.zi) + (int64_t)b * width,
+                        t, a.R, width};
+    float y[kGMax][VEC];
+    compress_entry<uint16_t, false>(c, rows, j, y, lane);
+    store_any<VEC, kGMax>(c, st.layout, orow, y, lane);
+  } else if (task == 3) {
+    // the token into both window rows of its position; the window's base position
+    CompressArgs c;
+    set_out(c, a.win, D);
+    float y[kGMax][VEC];
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) {
+      const int c0 = (g * 64 + lane) * VEC;
+      if (c0 < D) Raw<uint16_t>::load(xin + c0, y[g]);
+      else
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) y[g][v] = 0.f;
+    }
+    const int64_t r0 = a.win_rb[b] + t % a.W;
+    if (r0 >= 0 && r0 < a.win.n_rows) store_any<VEC, kGMax>(c, a.win.layout, r0, y, lane);
+    if (r0 + a.W >= 0 && r0 + a.W < a.win.n_rows) store_any<VEC, kGMax>(c, a.win.layout, r0 + a.W, y, lane);
+    if (lane == 0) a.win_pos0[b] = (int64_t)a.W * (max<int64_t>(0, t - a.W + 1) / a.W);
+  } else {
+    // ring row of position t: raw KV, both logit rows, the indexer-key pair
+    auto copy = [&](uint16_t* dst, const uint16_t* src, int n) {
+      for (int c0 = lane * VEC; c0 < n; c0 += 64 * VEC)
+        *reinterpret_cast<uint4*>(dst + c0) = *reinterpret_cast<const uint4*>(src + c0);
+    };
+    copy(a.ring_x + ring_row * D, xin, D);
+    copy(a.ring_zc + ring_row * D, a.zc + (int64_t)b * D, D);
+    copy(a.ring_zh + ring_row * D, a.zh + (int64_t)b * D, D);
+    if (di > 0) {
+      copy(a.ring_ki + ring_row * di, a.ki + (int64_t)b * di, di);
+      copy(a.ring_zi + ring_row * di, a.zi + (int64_t)b * di, di);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(decode_append_kernel, dim3((unsigned)a.B), dim3(320), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n_entries <= 0) return hipSuccess;

@@ -68,6 +68,21 @@ struct StoreView {
   int64_t rope_stride;
 };
 
+// One decode step (decode_append): inputs [B, D] / [B, d_idx] bf16, rings [B * R, .] bf16.
+struct DecodeArgs {
+  int B;
+  const int64_t* pos;
+  const uint16_t *x, *zc, *zh, *ki, *zi;
+  int m, w, m_prime, W, R, D, d_idx;
+  const float *bias_csa, *bias_hca, *bias_idx;
+  uint16_t *ring_x, *ring_zc, *ring_zh, *ring_ki, *ring_zi;
+  StoreView win, csa, hca, idx;
+  const int64_t* win_rb;
+  int64_t* win_pos0;
+  const int64_t *csa_rb, *hca_rb, *idx_rb;
+};
+hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   int q_dtype;

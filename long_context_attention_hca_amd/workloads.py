@@ -12,9 +12,9 @@ import math
 
 import torch
 
-from . import (BF16, F32, LAYOUT_BF16, LAYOUT_F32, LAYOUT_SPLIT, Store, csa_compress, csa_sparse_mqa_attn,
-               hca_compress, hca_dense_mqa_attn, lightning_index_topk, lightning_index_topk_workspace,
-               mqa_attn_workspace)
+from . import (BF16, F32, LAYOUT_BF16, LAYOUT_F32, LAYOUT_MXFP4, LAYOUT_SPLIT, DecodeLayer, Store, csa_compress,
+               csa_sparse_mqa_attn, decode_append, hca_compress, hca_dense_mqa_attn, lightning_index_topk,
+               lightning_index_topk_workspace, mqa_attn_workspace)
 
 
 def _i64(vals, dev):
@@ -27,6 +27,10 @@ def empty_store(layout, n, d_nope, d_rope, dev):
         return Store.dense(torch.zeros(n, d_nope + d_rope, dtype=torch.float32, device=dev), d_nope, d_rope)
     if layout == LAYOUT_BF16:
         return Store.dense(torch.zeros(n, d_nope + d_rope, dtype=torch.int16, device=dev), d_nope, d_rope)
+    if layout == LAYOUT_MXFP4:
+        assert d_rope == 0 and d_nope % 32 == 0
+        return Store.mxfp4(torch.zeros(n, d_nope // 2, dtype=torch.uint8, device=dev),
+                           torch.zeros(n, d_nope // 32, dtype=torch.uint8, device=dev))
     return Store.split(torch.zeros(n, d_nope, dtype=torch.uint8, device=dev),
                        torch.zeros(n, dtype=torch.float32, device=dev),
                        torch.zeros(n, d_rope, dtype=torch.int16, device=dev))
@@ -91,6 +95,42 @@ def hca_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_be
     hca_dense_mqa_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq,
                        q_pos, scale, o, lse, buf, stream=stream)
     return o, lse
+
+
+class DecodeState:
+    """Decode-time compression state of one layer for B sequences of up to max_len positions:
+    raw rings of R = max(w, m_prime) rows, the window store (2W rows per sequence), CSA and HCA
+    entry stores in `layout` and MXFP4 indexer keys (d_idx > 0). step() appends one token per
+    sequence with decode_append; the stores are then what the attention and indexer calls read
+    (window through win_row_begin / win_pos0)."""
+
+    def __init__(self, B, max_len, bias_csa, bias_hca, bias_idx=None, d_nope=448, d_rope=64, d_idx=64, m=4, w=8,
+                 m_prime=128, W=128, layout=LAYOUT_SPLIT, dev="cuda"):
+        D = d_nope + d_rope
+        R = max(w, m_prime)
+        self.B, self.D, self.d_idx, self.m, self.w, self.m_prime, self.W, self.R = B, D, d_idx, m, w, m_prime, W, R
+        self.n_c, self.n_h = max_len // m, max_len // m_prime
+        z = lambda n, d: torch.zeros(n, d, dtype=torch.int16, device=dev)
+        self.rings = {"x": z(B * R, D), "z_csa": z(B * R, D), "z_hca": z(B * R, D)}
+        if d_idx:
+            self.rings.update({"k_idx": z(B * R, d_idx), "z_idx": z(B * R, d_idx)})
+        self.window = empty_store(layout, B * 2 * W, d_nope, d_rope, dev)
+        self.win_row_begin = _i64([b * 2 * W for b in range(B)], dev)
+        self.win_pos0 = torch.zeros(B, dtype=torch.int64, device=dev)
+        self.csa = empty_store(layout, B * max(self.n_c, 1), d_nope, d_rope, dev)
+        self.csa_row_begin = _i64([b * max(self.n_c, 1) for b in range(B)], dev)
+        self.hca = empty_store(layout, B * max(self.n_h, 1), d_nope, d_rope, dev)
+        self.hca_row_begin = _i64([b * max(self.n_h, 1) for b in range(B)], dev)
+        self.idx = self.idx_row_begin = None
+        if d_idx:
+            self.idx = empty_store(LAYOUT_MXFP4, B * max(self.n_c, 1), d_idx, 0, dev)
+            self.idx_row_begin = self.csa_row_begin
+        self.layer = DecodeLayer(m, w, m_prime, W, R, bias_csa, bias_hca, self.rings, self.window,
+                                 self.win_row_begin, self.win_pos0, self.csa, self.csa_row_begin, self.hca,
+                                 self.hca_row_begin, self.idx, self.idx_row_begin, bias_idx)
+
+    def step(self, pos, x, z_csa, z_hca, k_idx=None, z_idx=None, stream=None):
+        decode_append(self.layer, pos, x, z_csa, z_hca, k_idx, z_idx, stream=stream)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -15,14 +15,13 @@ at position t is in:
 * the window store holds the last W raw tokens.
 
 Layout readings (the pages describe no storage layout):
-* Raw ring: the last R raw tokens of a sequence, each token at position p
-  written twice, to ring rows p mod R and p mod R + R. Any R consecutive
-  positions then sit in consecutive rows, so a compression window of up to R
-  positions is one contiguous run of rows.
-* Window store: the same double mapping with R = W, and a per-sequence
-  base position win_pos0 = W * floor(max(0, t-W+1) / W) such that position p
-  of the window lives in row p - win_pos0. The attention calls read the
-  window through exactly this linear map.
+* Raw ring: the last R raw tokens of a sequence (R at least the longest
+  compression window), the token at position p in ring row p mod R.
+* Window store: each token at position p is written twice, to rows p mod W
+  and p mod W + W, and a per-sequence base position
+  win_pos0 = W * floor(max(0, t-W+1) / W) makes position p of the window live
+  in row p - win_pos0: the last W positions are one contiguous run of rows,
+  which the attention calls read through exactly this linear map.
 """
 
 import numpy as np
@@ -30,9 +29,14 @@ import numpy as np
 from . import compress as C
 
 
-def ring_rows(p, R):
-    """The two ring rows that hold position p."""
-    return p % R, p % R + R
+def ring_row(p, R):
+    """The raw-ring row that holds position p."""
+    return p % R
+
+
+def window_rows(p, W):
+    """The two window-store rows that the token at position p is written to."""
+    return p % W, p % W + W
 
 
 def window_pos0(t, W):
@@ -57,18 +61,16 @@ def run(x, z, beta, m, w, steps):
     x = np.asarray(x, dtype=np.float64)
     z = np.asarray(z, dtype=np.float64)
     R = w
-    ring_x = np.zeros((2 * R, x.shape[1]))
-    ring_z = np.zeros((2 * R, z.shape[1]))
+    ring_x = np.zeros((R, x.shape[1]))
+    ring_z = np.zeros((R, z.shape[1]))
     out = {}
     for t in range(steps):
-        for r in ring_rows(t, R):
-            ring_x[r] = x[t]
-            ring_z[r] = z[t]
+        ring_x[ring_row(t, R)] = x[t]
+        ring_z[ring_row(t, R)] = z[t]
         j = entries_due(t, m)
         if j is None:
             continue
         lo = max(0, t - R + 1)                 # first position the ring still holds
-        base = lo % R                          # its first row; the run is contiguous
-        rows = slice(base, base + (t - lo + 1))
+        rows = [ring_row(p, R) for p in range(lo, t + 1)]
         out[j] = C.compress(ring_x[rows], ring_z[rows], beta, m, w, j, 1, first_pos=lo)[0]
     return out

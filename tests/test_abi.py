@@ -142,3 +142,59 @@ def test_attention_workspace_policy():
     assert hca.mqa_attn_workspace(1, 4, 64, 512, 8192 + 128) > 0
     assert hca.mqa_attn_workspace(1, 24576, 64, 512, 2048 + 128) == 0
     assert hca.mqa_attn_workspace(0, 16, 16, 192, 64 + 128) > 0
+
+
+def test_mxfp4_output_store_validation():
+    mx = lambda **k: store(**{**dict(layout=3, d_nope=64, d_rope=0, row_stride=32, rope_stride=2), **k})
+    raw = dict(rs=64, lrs=64, out=mx())
+    assert compress_call(**raw) in (0, -4)               # passes validation; launching needs a GPU
+    for bad, msg in [(mx(d_rope=8), "d_rope == 0"), (mx(d_nope=48), "multiple of 32"),
+                     (mx(row_stride=24), "row_stride"), (mx(rope_stride=1), "scale stride")]:
+        assert compress_call(**{**raw, "out": bad}) == -1
+        assert msg in hca._last_error().decode()
+
+
+def test_decode_layer_struct_matches_the_header(tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "hca.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(hca_decode_layer),'
+                   ' offsetof(hca_decode_layer, window), offsetof(hca_decode_layer, csa),'
+                   ' offsetof(hca_decode_layer, idx), offsetof(hca_decode_layer, idx_row_begin));return 0;}\n')
+    exe = tmp_path / "sz"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    C = hca._DecodeLayerC
+    assert got == [ctypes.sizeof(C), C.window.offset, C.csa.offset, C.idx.offset, C.idx_row_begin.offset]
+
+
+def decode_call(B=2, d_idx=64, **kw):
+    D = 512
+    st = lambda layout=2: store(layout=layout, n_rows=1000)
+    L = hca._DecodeLayerC(4, 8, 128, 128, 128, d_idx, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7],
+                          st(), P[8], P[9], st(), P[10], st(), P[11],
+                          store(layout=3, d_nope=64, d_rope=0, row_stride=32, rope_stride=2), P[12])
+    for k, v in kw.items():
+        setattr(L, k, v)
+    return hca._decode_append(ctypes.byref(L), B, P[13], P[14], P[14], P[14], P[15], P[15], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(m=0), -1, "m <= w"), (dict(w=2), -1, "m <= w"), (dict(W=0), -1, "W >= 1"),
+    (dict(R=100), -1, "ring rows"), (dict(B=0), -1, "B < 1"),
+    (dict(window=store(layout=3, d_nope=64, d_rope=0, row_stride=32, rope_stride=2)), -2, "window layout"),
+    (dict(window=store(d_nope=384, d_rope=64, row_stride=384)), -1, "widths differ"),
+    (dict(hca=store(d_nope=384, d_rope=64, row_stride=384)), -1, "widths differ"),
+    (dict(d_idx=48), -1, "idx width"), (dict(d_idx=12), -2, "d_idx"),
+    (dict(bias_csa=None), -1, "NULL field"), (dict(ring_x=0x100004), -1, "aligned"),
+    (dict(idx_row_begin=None), -1, "NULL indexer"),
+])
+def test_decode_append_rejects_bad_arguments(kw, status, msg):
+    B = kw.pop("B", 2)
+    assert decode_call(B=B, **kw) == status
+    assert msg in hca._last_error().decode()
+
+
+def test_decode_append_valid_call_reaches_launch():
+    assert decode_call() in (0, -4)
+    assert decode_call(d_idx=0, idx_row_begin=None) in (0, -4)   # no indexer keys

@@ -82,7 +82,7 @@ def test_mxfp4_encode_round_trip_and_error_bound():
 def test_window_layout_holds_the_last_w_positions(W):
     rows = np.full(2 * W, -1)
     for t in range(6 * W + 3):
-        for r in DEC.ring_rows(t, W):
+        for r in DEC.window_rows(t, W):
             rows[r] = t
         lo = max(0, t - W + 1)
         for p in range(lo, t + 1):
