@@ -344,6 +344,64 @@ def main():
                 "hca_frac_hbm": round(by_h / (th * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
         del cc, csa_st, hca_st
 
+        log("indexer-key compression and decode_append")
+        # indexer keys: the CSA compressor on 2^20 raw 64-dim bf16 keys into MXFP4 rows
+        ck = synth.indexer_keys(seed=1014, L=L, device=dev).t
+        di = 64
+        idx_st = W.empty_store(3, n_c, di, 0, dev)
+        for _ in range(3):
+            csa_compress(ck["k"], 0, ck["z"], ck["bias"], m, 8, 0, n_c, idx_st)
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(n_rep):
+            csa_compress(ck["k"], 0, ck["z"], ck["bias"], m, 8, 0, n_c, idx_st)
+        e[1].record()
+        torch.cuda.synchronize()
+        tk = e[0].elapsed_time(e[1]) / n_rep
+        by_k = L * di * 2 * 2 + 8 * di * 4 + n_c * (di // 2 + di // 32)
+        comp.update({"idx_key_compress_ms": round(tk, 4), "idx_key_tokens_per_s": round(L / (tk * 1e-3)),
+                     "idx_key_gbs": round(by_k / (tk * 1e-3) / 1e9, 1),
+                     "idx_key_frac_hbm": round(by_k / (tk * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                     "idx_key_workload": "2^20 raw bf16 indexer keys, d=64, per-channel logits -> MXFP4 rows"})
+        del ck, idx_st
+        # decode_append: one HCA period (128 steps) of the batch at positions 2^20 - 128 .. 2^20 - 1
+        tok = synth.decode_tokens(seed=1015, B=B, D=D, device=dev).t
+        dst = W.DecodeState(B, L, tok["bias_csa"], tok["bias_hca"], tok["bias_idx"], d_idx=di, m=m, w=8,
+                            m_prime=mp, W=W_, dev=dev)
+        n_step = mp
+        pos = (torch.arange(n_step, device=dev, dtype=torch.int64)[:, None] + (L - n_step)).repeat(1, B).contiguous()
+        args_tok = (tok["x"], tok["z_csa"], tok["z_hca"], tok["k_idx"], tok["z_idx"])
+        for i in range(n_step):
+            dst.step(pos[i], *args_tok)
+        torch.cuda.synchronize()
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd):
+            for i in range(n_step):
+                dst.step(pos[i], *args_tok)
+        gd.replay()
+        torch.cuda.synchronize()
+        n_rd = 20
+        e[0].record()
+        for _ in range(n_rd):
+            gd.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        t_app = e[0].elapsed_time(e[1]) / (n_rd * n_step)
+        # algorithmic bytes per sequence over the period: every step reads its inputs, writes them
+        # to the ring and the token twice to the window; every m-th step reads w - 1 ring rows
+        # (raw + logits) and the bias for the CSA entry and its indexer key and writes both; the
+        # last step does the same for the HCA entry over m' - 1 rows
+        tok_b = (3 * D + 2 * di) * 2
+        csa_b = (8 - 1) * 2 * D * 2 + 8 * D * 4 + entry + (8 - 1) * 2 * di * 2 + 8 * di * 4 + di // 2 + di // 32
+        hca_b = (mp - 1) * 2 * D * 2 + mp * D * 4 + entry
+        by_app = B * (n_step * (2 * tok_b + 2 * entry) + (n_step // m) * csa_b + hca_b) / n_step
+        comp["decode_append"] = {
+            "workload": f"batch {B}, one step per token over {n_step} consecutive positions (one HCA entry, "
+                        f"{n_step // m} CSA entries and indexer keys per sequence), D=512 split stores, MXFP4 keys",
+            "us_per_step": round(t_app * 1e3, 3), "bytes_per_step": round(by_app),
+            "gbs": round(by_app / (t_app * 1e-3) / 1e9, 2), "bound": "latency"}
+        del dst, gd
+
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle on the host cores")

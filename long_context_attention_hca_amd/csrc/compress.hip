@@ -280,12 +280,16 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 // window's rows stay in registers in the input format; the next entry's four rows are
 // requested before the current entry is reduced. Per entry the reduction is the same
 // expression in the same order as compress_kernel's (positions before 0 weigh 0).
-template <typename T, int LAYOUT, bool SCALAR>
+// Narrow rows (D <= 64 VEC / NR, e.g. the 64-dim indexer keys) run NR runs side by side in a
+// wave, 64 / NR lanes each, so that every row load still spans the whole wave; this needs a
+// layout whose store reduces within a row's lanes only (not the split layout's wave-wide max).
+template <typename T, int LAYOUT, bool SCALAR, int NR>
 __global__ __launch_bounds__(256) void compress_slide_kernel(CompressArgs a) {
   constexpr int VEC = Raw<T>::VEC;
-  constexpr int W = 8, M = 4, kRun = 16;
-  const int lane = threadIdx.x & 63;
-  const int64_t e0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRun;
+  constexpr int W = 8, M = 4, kRun = 16, LPR = 64 / NR;
+  static_assert(NR == 1 || LAYOUT != HCA_LAYOUT_SPLIT, "the split store reduces across the wave");
+  const int lane = (threadIdx.x & 63) % LPR, sub = (threadIdx.x & 63) / LPR;
+  const int64_t e0 = (((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * NR + sub) * kRun;
   if (e0 >= a.n_entries) return;
   const int ne = (int)min<int64_t>(kRun, a.n_entries - e0);
   const int c0 = lane * VEC;
@@ -356,15 +360,24 @@ __global__ __launch_bounds__(256) void compress_slide_kernel(CompressArgs a) {
   }
 }
 
+template <typename T, int LAYOUT, int NR>
+hipError_t launch_slide(const CompressArgs& a, hipStream_t s) {
+  const int64_t per_block = 4 * NR * 16;  // 4 waves x NR runs x 16 entries
+  const dim3 grid((unsigned)((a.n_entries + per_block - 1) / per_block)), block(256);
+  if (a.logit_col_stride == 0)
+    hipLaunchKernelGGL((compress_slide_kernel<T, LAYOUT, true, NR>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((compress_slide_kernel<T, LAYOUT, false, NR>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int LAYOUT>
 hipError_t launch_t(const CompressArgs& a, hipStream_t s) {
-  if (a.m == 4 && a.w == 8 && a.D <= 64 * Raw<T>::VEC) {
-    const dim3 grid((unsigned)((a.n_entries + 63) / 64)), block(256);  // 4 waves x 16 entries
-    if (a.logit_col_stride == 0)
-      hipLaunchKernelGGL((compress_slide_kernel<T, LAYOUT, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((compress_slide_kernel<T, LAYOUT, false>), grid, block, 0, s, a);
-    return hipGetLastError();
+  constexpr int VEC = Raw<T>::VEC;
+  if (a.m == 4 && a.w == 8 && a.D <= 64 * VEC) {
+    if (LAYOUT != HCA_LAYOUT_SPLIT && a.D <= 8 * VEC) return launch_slide<T, LAYOUT, (LAYOUT != HCA_LAYOUT_SPLIT ? 8 : 1)>(a, s);
+    if (LAYOUT != HCA_LAYOUT_SPLIT && a.D <= 16 * VEC) return launch_slide<T, LAYOUT, (LAYOUT != HCA_LAYOUT_SPLIT ? 4 : 1)>(a, s);
+    return launch_slide<T, LAYOUT, 1>(a, s);
   }
   const dim3 grid((unsigned)((a.n_entries + 3) / 4)), block(256);
   if (a.logit_col_stride == 0)

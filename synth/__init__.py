@@ -175,6 +175,33 @@ def compression(seed=1004, device="cpu", L=1 << 20, d_nope=448, d_rope=64, m=4, 
     return c
 
 
+def indexer_keys(seed=1014, device="cpu", L=1 << 20, d_idx=64, w=8):
+    """Raw indexer keys of one long sequence for their compression: bf16 keys and
+    per-channel logits [L, d_idx], position bias [w, d_idx]."""
+    g = generator(seed, device)
+    c = Case(dict(L=L, d_idx=d_idx, w=w))
+    c.t["k"] = bf16_bits(normal(g, (L, d_idx)))
+    c.t["z"] = bf16_bits(normal(g, (L, d_idx), 0.5))
+    c.t["bias"] = normal(g, (w, d_idx), 0.1)
+    return c
+
+
+def decode_tokens(seed=1015, device="cpu", B=4, D=512, d_idx=64, m=4, w=8, m_prime=128):
+    """One decode step's new tokens (bf16 raw KV, both compression logits, raw indexer
+    key and its logits, [B, .]) and the compressors' position biases."""
+    g = generator(seed, device)
+    c = Case(dict(B=B, D=D, d_idx=d_idx, m=m, w=w, m_prime=m_prime))
+    c.t["x"] = bf16_bits(normal(g, (B, D)))
+    c.t["z_csa"] = bf16_bits(normal(g, (B, D), 0.5))
+    c.t["z_hca"] = bf16_bits(normal(g, (B, D), 0.5))
+    c.t["k_idx"] = bf16_bits(normal(g, (B, d_idx)))
+    c.t["z_idx"] = bf16_bits(normal(g, (B, d_idx), 0.5))
+    c.t["bias_csa"] = normal(g, (w, D), 0.1)
+    c.t["bias_hca"] = normal(g, (m_prime, D), 0.1)
+    c.t["bias_idx"] = normal(g, (w, d_idx), 0.1)
+    return c
+
+
 def chunked_prefill(seed=1005, device="cpu", prefixes=(32768, 131072, 262144), chunk=8192,
                     heads=64, d_nope=448, d_rope=64, m=4, w=8, topk=1024, n_idx_heads=4,
                     d_idx=64, m_prime=128, W=128):

@@ -12,7 +12,7 @@ import synth
 from oracle import codecs
 from oracle import compress as OC
 from oracle import decode as OD
-from tests._common import EVAL, check_split_entries, np_
+from tests._common import EVAL, check_bf16_entries, check_f32_entries, check_split_entries, np_
 
 pytestmark = pytest.mark.gpu
 
@@ -101,23 +101,39 @@ def _check_mxfp4_entries(codes, scales, y, yabs, what):
     assert ok.all(), f"{what}: {np.count_nonzero(~ok)} E2M1 codes outside the rounding of y"
 
 
-def test_indexer_key_compression_vs_oracle(mods):
-    """The CSA compressor (m = 4, w = 8) on 64-dim bf16 indexer keys into MXFP4 rows, against
-    the oracle's float64 entries encoded by its MXFP4 encoder."""
+@pytest.mark.parametrize("raw_dt,d,layout,scalar", [("bf16", 64, "mxfp4", False), ("bf16", 128, "mxfp4", False),
+                                                    ("bf16", 64, "mxfp4", True), ("bf16", 64, "bf16", False),
+                                                    ("f32", 64, "f32", False), ("f32", 32, "mxfp4", False)])
+def test_narrow_key_compression_vs_oracle(mods, raw_dt, d, layout, scalar):
+    """The CSA compressor (m = 4, w = 8) on narrow rows (64-dim indexer keys and neighbours:
+    several runs of entries share a wave) into MXFP4, bf16 or float32 rows, 1000 entries (a
+    ragged last block), against the oracle's float64 entries (MXFP4: encoded by its MXFP4
+    encoder)."""
     H, W = mods
-    _say("indexer keys mxfp4 m=4 w=8")
-    m, w, d, n = 4, 8, 64, 1000
+    _say(f"narrow keys {raw_dt} d={d} {layout} scalar={scalar}")
+    m, w, n = 4, 8, 1000
     g = synth.generator(1012)
-    x = synth.bf16_bits(synth.normal(g, (n * m, d)))
-    z = synth.bf16_bits(synth.normal(g, (n * m, d), std=0.5))
+    x = synth.normal(g, (n * m, d))
+    z = synth.normal(g, (n * m, 1 if scalar else d), std=0.5)
     bias = synth.normal(g, (w, d), std=0.1)
-    out = W.empty_store(H.LAYOUT_MXFP4, n, d, 0, "cuda")
-    H.csa_compress(x.cuda(), 0, z.cuda(), bias.cuda(), m, w, 0, n, out)
+    if raw_dt == "bf16":
+        x, z = synth.bf16_bits(x), synth.bf16_bits(z)
+        xd, zd = _bits_f64(x), _bits_f64(z)
+    else:
+        xd, zd = x.double().numpy(), z.double().numpy()
+    code = {"mxfp4": H.LAYOUT_MXFP4, "bf16": H.LAYOUT_BF16, "f32": H.LAYOUT_F32}[layout]
+    out = W.empty_store(code, n, d, 0, "cuda")
+    H.csa_compress(x.cuda(), 0, z.cuda(), bias.cuda(), m, w, 0, n, out, scalar_logits=scalar)
     torch.cuda.synchronize()
-    xd, zd, b = _bits_f64(x), _bits_f64(z), bias.double().numpy()
+    b = bias.double().numpy()
     y = OC.compress(xd, zd, b, m, w, 0, n)
     ya = OC.compress(np.abs(xd), zd, b, m, w, 0, n)
-    _check_mxfp4_entries(np_(out.data), np_(out.rope), y, ya, "indexer keys")
+    if layout == "mxfp4":
+        _check_mxfp4_entries(np_(out.data), np_(out.rope), y, ya, "narrow keys")
+    elif layout == "bf16":
+        check_bf16_entries(np_(out.data), y, "narrow keys", ya)
+    else:
+        check_f32_entries(np_(out.data), y, ya, "narrow keys")
 
 
 def test_decode_append_equals_bulk_and_oracle(mods):
