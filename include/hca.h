@@ -170,6 +170,10 @@ int hca_compress(const void* raw, int32_t raw_dtype, int64_t raw_row_stride, int
  * W * floor(max(0, t - W + 1) / W) once the token at t is in: position p of
  * the window is then row win_row_begin[b] + p - win_pos0[b], which is how
  * csa_sparse_mqa_attn / hca_dense_mqa_attn read the window.
+ * HCA state: the softmax over an HCA entry's window runs in blocks of 8
+ * positions; decode_append folds each block at the step that completes it
+ * into hca_state (per channel: running max, sum and weighted sum) and writes
+ * the entry at its last block, the same arithmetic as hca_compress.
  * Entry stores: CSA entry j of sequence b goes to row csa_row_begin[b] + j
  * of `csa`, HCA entry j to hca_row_begin[b] + j of `hca`, the indexer key of
  * CSA entry j (the CSA compressor with w, m on d_idx channels, then encoded
@@ -188,6 +192,8 @@ typedef struct hca_decode_layer {
   void* ring_z_hca;      /* bf16 [B * R, D]: HCA compression logits */
   void* ring_k_idx;      /* bf16 [B * R, d_idx]: raw indexer keys */
   void* ring_z_idx;      /* bf16 [B * R, d_idx]: indexer-key compression logits */
+  float* hca_state;      /* float32 [B, 3, D]: the HCA entry in progress (scratch; no
+                            initialisation needed) */
   hca_store window;
   const int64_t* win_row_begin; /* [B] */
   int64_t* win_pos0;            /* [B], written */
@@ -211,8 +217,9 @@ typedef struct hca_decode_layer {
  * are left untouched (an idle slot of the batch).
  * Preconditions (device contents): tokens of a sequence arrive in order,
  * one per call, starting at position 0 or with the ring already holding the
- * previous R - 1 positions. Rows past a store's n_rows are not written (an
- * entry or window row beyond it is dropped).
+ * previous R - 1 positions and hca_state the blocks of the HCA entry in
+ * progress (none when t is a multiple of m_prime). Rows past a store's
+ * n_rows are not written (an entry or window row beyond it is dropped).
  * Requires B >= 1; the window, csa and hca stores of one width D (a multiple
  * of 8, <= 1024), window layout F32, BF16 or SPLIT, entry stores in any
  * layout csa_compress writes; d_idx == 0 or a multiple of 8 (of 32 for an

@@ -45,7 +45,7 @@ class _DecodeLayerC(ctypes.Structure):
                 ("R", ctypes.c_int32), ("d_idx", ctypes.c_int32),
                 ("bias_csa", ctypes.c_void_p), ("bias_hca", ctypes.c_void_p), ("bias_idx", ctypes.c_void_p),
                 ("ring_x", ctypes.c_void_p), ("ring_z_csa", ctypes.c_void_p), ("ring_z_hca", ctypes.c_void_p),
-                ("ring_k_idx", ctypes.c_void_p), ("ring_z_idx", ctypes.c_void_p),
+                ("ring_k_idx", ctypes.c_void_p), ("ring_z_idx", ctypes.c_void_p), ("hca_state", ctypes.c_void_p),
                 ("window", _StoreC), ("win_row_begin", ctypes.c_void_p), ("win_pos0", ctypes.c_void_p),
                 ("csa", _StoreC), ("csa_row_begin", ctypes.c_void_p),
                 ("hca", _StoreC), ("hca_row_begin", ctypes.c_void_p),
@@ -173,19 +173,20 @@ class DecodeLayer:
     """One layer's decode-time state for decode_append (the hca_decode_layer of include/hca.h).
 
     rings: dict of bf16 tensors "x", "z_csa", "z_hca" [B * R, D] and, with indexer keys,
-    "k_idx", "z_idx" [B * R, d_idx]; window / csa / hca / idx: Stores; *_row_begin: int64 [B]
-    device tensors; win_pos0: int64 [B] (written by decode_append). Tensors are kept referenced.
+    "k_idx", "z_idx" [B * R, d_idx]; hca_state: float32 [B, 3, D]; window / csa / hca / idx:
+    Stores; *_row_begin: int64 [B] device tensors; win_pos0: int64 [B] (written by
+    decode_append). Tensors are kept referenced.
     """
 
-    def __init__(self, m, w, m_prime, W, R, bias_csa, bias_hca, rings, window, win_row_begin, win_pos0, csa,
-                 csa_row_begin, hca, hca_row_begin, idx=None, idx_row_begin=None, bias_idx=None):
-        self.keep = (bias_csa, bias_hca, bias_idx, rings, window, win_row_begin, win_pos0, csa, csa_row_begin, hca,
-                     hca_row_begin, idx, idx_row_begin)
+    def __init__(self, m, w, m_prime, W, R, bias_csa, bias_hca, rings, hca_state, window, win_row_begin, win_pos0,
+                 csa, csa_row_begin, hca, hca_row_begin, idx=None, idx_row_begin=None, bias_idx=None):
+        self.keep = (bias_csa, bias_hca, bias_idx, rings, hca_state, window, win_row_begin, win_pos0, csa,
+                     csa_row_begin, hca, hca_row_begin, idx, idx_row_begin)
         d_idx = 0 if idx is None else idx.d_nope + idx.d_rope
         p = lambda t: None if t is None else t.data_ptr()
         self._c = _DecodeLayerC(m, w, m_prime, W, R, d_idx, p(bias_csa), p(bias_hca), p(bias_idx),
                                 p(rings["x"]), p(rings["z_csa"]), p(rings["z_hca"]),
-                                p(rings.get("k_idx")), p(rings.get("z_idx")),
+                                p(rings.get("k_idx")), p(rings.get("z_idx")), p(hca_state),
                                 window._c, p(win_row_begin), p(win_pos0), csa._c, p(csa_row_begin), hca._c,
                                 p(hca_row_begin), idx._c if idx is not None else _StoreC(),
                                 p(idx_row_begin))

@@ -170,11 +170,12 @@ int decode_impl(const char* fn, const hca_decode_layer* L, int32_t B, const int6
   if (D % 8 || D > 1024) return fail(HCA_ERR_UNSUPPORTED, fn, "D must be a multiple of 8, at most 1024");
   const int64_t di = L->d_idx;
   if (di < 0 || di % 8 || di > 1024) return fail(HCA_ERR_UNSUPPORTED, fn, "d_idx must be 0 or a multiple of 8 <= 1024");
-  if (!L->bias_csa || !L->bias_hca || !L->ring_x || !L->ring_z_csa || !L->ring_z_hca || !L->win_row_begin ||
+  if (!L->bias_csa || !L->bias_hca || !L->ring_x || !L->ring_z_csa || !L->ring_z_hca || !L->hca_state || !L->win_row_begin ||
       !L->win_pos0 || !L->csa_row_begin || !L->hca_row_begin)
     return fail(HCA_ERR_INVALID_ARG, fn, "NULL field of the layer");
   for (const void* p : {(const void*)L->bias_csa, (const void*)L->bias_hca, (const void*)L->ring_x,
-                        (const void*)L->ring_z_csa, (const void*)L->ring_z_hca, x, z_csa, z_hca})
+                        (const void*)L->ring_z_csa, (const void*)L->ring_z_hca, (const void*)L->hca_state, x,
+                        z_csa, z_hca})
     if (!aligned16(p)) return fail(HCA_ERR_INVALID_ARG, fn, "inputs, rings and biases must be 16-byte aligned");
   if (di > 0) {
     if (!k_idx || !z_idx || !L->bias_idx || !L->ring_k_idx || !L->ring_z_idx || !L->idx_row_begin)
@@ -200,6 +201,7 @@ int decode_impl(const char* fn, const hca_decode_layer* L, int32_t B, const int6
   a.ring_zh = static_cast<uint16_t*>(L->ring_z_hca);
   a.ring_ki = static_cast<uint16_t*>(L->ring_k_idx);
   a.ring_zi = static_cast<uint16_t*>(L->ring_z_idx);
+  a.hca_state = L->hca_state;
   a.win = view_of(&L->window);
   a.csa = view_of(&L->csa);
   a.hca = view_of(&L->hca);

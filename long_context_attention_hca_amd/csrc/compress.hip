@@ -195,14 +195,65 @@ struct LinearRows {
 
 constexpr int kGMax = 2;  // column groups of 64*VEC channels: D <= 1024 (bf16) / 512 (f32)
 
+constexpr int kPB = 8;  // window positions per register block of the online softmax
+
+// Folds window positions pb .. pb + nb - 1 (nb <= kPB) of the entry whose window starts at
+// absolute position `start` into the lane's running softmax state (max M, sum S, weighted sum A)
+// of channels c0 .. c0 + VEC - 1.
+template <typename T, bool SCALAR, class Rows>
+__device__ __forceinline__ void fold_block(const CompressArgs& a, const Rows& rows, int64_t start, int pb, int nb,
+                                           int c0, float (&M)[Raw<T>::VEC], float (&S)[Raw<T>::VEC],
+                                           float (&A)[Raw<T>::VEC]) {
+  constexpr int VEC = Raw<T>::VEC;
+  float xv[kPB][VEC], zv[kPB][VEC];
+#pragma unroll
+  for (int i = 0; i < kPB; ++i) {
+    if (i < nb) {
+      const int64_t pos = start + pb + i;
+      Raw<T>::load(rows.x(pos) + c0, xv[i]);
+      if (SCALAR) {
+        const float zz = Raw<T>::scalar(rows.z(pos));
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) zv[i][v] = zz;
+      } else {
+        Raw<T>::load(rows.z(pos) + c0, zv[i]);
+      }
+      const float* bp = a.bias + (int64_t)(pb + i) * a.D + c0;
+#pragma unroll
+      for (int v = 0; v < VEC; v += 4) {
+        float4 bb = *reinterpret_cast<const float4*>(bp + v);
+        zv[i][v] += bb.x; zv[i][v + 1] += bb.y; zv[i][v + 2] += bb.z; zv[i][v + 3] += bb.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    float bm = zv[0][v];
+#pragma unroll
+    for (int i = 1; i < kPB; ++i)
+      if (i < nb) bm = fmaxf(bm, zv[i][v]);
+    const float mn = fmaxf(M[v], bm);
+    const float corr = __expf(M[v] - mn);  // 0 on the first block (M = -inf)
+    float s = S[v] * corr, acc = A[v] * corr;
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) {
+      if (i < nb) {
+        const float pe = __expf(zv[i][v] - mn);
+        s += pe;
+        acc = fmaf(pe, xv[i][v], acc);
+      }
+    }
+    M[v] = mn; S[v] = s; A[v] = acc;
+  }
+}
+
 // Entry j into y (lane's channels (g * 64 + lane) * VEC + v): per channel the softmax over the
 // window's positions of logit + bias, weighting the raw values. Window positions are taken in
-// blocks of 8 rows held in registers, with an online softmax across blocks.
+// blocks of kPB rows held in registers, with an online softmax across blocks.
 template <typename T, bool SCALAR, class Rows>
 __device__ __forceinline__ void compress_entry(const CompressArgs& a, const Rows& rows, int64_t j,
                                                float (&y)[kGMax][Raw<T>::VEC], int lane) {
   constexpr int VEC = Raw<T>::VEC;
-  constexpr int PB = 8;  // window positions per register block
   const int64_t start = j * a.m - (a.w - a.m);  // absolute position of window position 0
   const int p0 = start < 0 ? (int)(-start) : 0;
 #pragma unroll
@@ -214,49 +265,7 @@ __device__ __forceinline__ void compress_entry(const CompressArgs& a, const Rows
     float M[VEC], S[VEC], A[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) { M[v] = -INFINITY; S[v] = 0.f; A[v] = 0.f; }
-    for (int pb = p0; pb < a.w; pb += PB) {
-      const int nb = min(PB, a.w - pb);
-      float xv[PB][VEC], zv[PB][VEC];
-#pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        if (i < nb) {
-          const int64_t pos = start + pb + i;
-          Raw<T>::load(rows.x(pos) + c0, xv[i]);
-          if (SCALAR) {
-            const float zz = Raw<T>::scalar(rows.z(pos));
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) zv[i][v] = zz;
-          } else {
-            Raw<T>::load(rows.z(pos) + c0, zv[i]);
-          }
-          const float* bp = a.bias + (int64_t)(pb + i) * a.D + c0;
-#pragma unroll
-          for (int v = 0; v < VEC; v += 4) {
-            float4 bb = *reinterpret_cast<const float4*>(bp + v);
-            zv[i][v] += bb.x; zv[i][v + 1] += bb.y; zv[i][v + 2] += bb.z; zv[i][v + 3] += bb.w;
-          }
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        float bm = zv[0][v];
-#pragma unroll
-        for (int i = 1; i < PB; ++i)
-          if (i < nb) bm = fmaxf(bm, zv[i][v]);
-        const float mn = fmaxf(M[v], bm);
-        const float corr = __expf(M[v] - mn);  // 0 on the first block (M = -inf)
-        float s = S[v] * corr, acc = A[v] * corr;
-#pragma unroll
-        for (int i = 0; i < PB; ++i) {
-          if (i < nb) {
-            const float pe = __expf(zv[i][v] - mn);
-            s += pe;
-            acc = fmaf(pe, xv[i][v], acc);
-          }
-        }
-        M[v] = mn; S[v] = s; A[v] = acc;
-      }
-    }
+    for (int pb = p0; pb < a.w; pb += kPB) fold_block<T, SCALAR>(a, rows, start, pb, min(kPB, a.w - pb), c0, M, S, A);
 #pragma unroll
     for (int v = 0; v < VEC; ++v) y[g][v] = A[v] / S[v];
   }
@@ -398,16 +407,21 @@ hipError_t launch_layout(const CompressArgs& a, hipStream_t s) {
 }
 
 // Rows of one sequence at a decode step: the token at position t from the step's inputs, older
-// positions from the raw ring (row p mod R).
+// positions t - R < p < t from the raw ring, row p mod R = tr - d (+ R when d > tr) for
+// d = t - p and tr = t mod R.
 struct RingRows {
   const uint16_t* ring_x;
   const uint16_t* ring_z;
   const uint16_t* in_x;
   const uint16_t* in_z;
   int64_t t;
-  int R, stride;
-  __device__ const uint16_t* x(int64_t p) const { return p == t ? in_x : ring_x + (p % R) * stride; }
-  __device__ const uint16_t* z(int64_t p) const { return p == t ? in_z : ring_z + (p % R) * stride; }
+  int tr, R, stride;
+  __device__ int row(int64_t p) const {
+    const int d = (int)(t - p);
+    return tr - d + (d > tr ? R : 0);
+  }
+  __device__ const uint16_t* x(int64_t p) const { return p == t ? in_x : ring_x + (size_t)row(p) * stride; }
+  __device__ const uint16_t* z(int64_t p) const { return p == t ? in_z : ring_z + (size_t)row(p) * stride; }
 };
 
 // store_entry for a layout known at run time (uniform across the wave).
@@ -437,6 +451,10 @@ __device__ __forceinline__ void set_out(CompressArgs& c, const StoreView& v, int
 // One block per sequence, wave k runs task k: 0 CSA entry, 1 HCA entry, 2 indexer key,
 // 3 window rows, 4 ring row. The entry tasks read positions t - w + 1 .. t - 1 (t - m' + 1 ..)
 // from the ring, none of which is the ring row that task 4 overwrites (R >= w, m').
+// HCA: the entry's window starts at j m' >= 0, and compress_entry folds it in blocks of kPB
+// positions; each block is folded here at the step that completes it, into the sequence's
+// running state (M, S, A per channel, float32 [B, 3, D]), and the last block gives the entry,
+// so the arithmetic is compress_entry's, step for step, at one block's latency per step.
 __global__ __launch_bounds__(320) void decode_append_kernel(DecodeArgs a) {
   constexpr int VEC = 8;
   const int b = blockIdx.x;
@@ -444,32 +462,71 @@ __global__ __launch_bounds__(320) void decode_append_kernel(DecodeArgs a) {
   const int64_t t = a.pos[b];
   if (t < 0) return;
   const int D = a.D, di = a.d_idx;
+  const int tr = (int)(t % a.R);
   const uint16_t* xin = a.x + (int64_t)b * D;
-  const size_t ring_row = (size_t)b * a.R + (size_t)(t % a.R);
-  if (task <= 2) {
+  const size_t ring_row = (size_t)b * a.R + (size_t)tr;
+  if (task == 0 || task == 2) {
     const bool idx = task == 2;
-    const int mm = task == 1 ? a.m_prime : a.m, ww = task == 1 ? a.m_prime : a.w;
     if (idx && di == 0) return;
-    if ((t + 1) % mm != 0) return;
-    const int64_t j = (t + 1) / mm - 1;
-    const StoreView& st = task == 0 ? a.csa : task == 1 ? a.hca : a.idx;
-    const int64_t rb = (task == 0 ? a.csa_rb : task == 1 ? a.hca_rb : a.idx_rb)[b];
-    const int64_t orow = rb + j;
+    if ((t + 1) % a.m != 0) return;
+    const int64_t j = (t + 1) / a.m - 1;
+    const StoreView& st = idx ? a.idx : a.csa;
+    const int64_t orow = (idx ? a.idx_rb : a.csa_rb)[b] + j;
     if (orow < 0 || orow >= st.n_rows) return;
     const int width = idx ? di : D;
     CompressArgs c;
-    c.m = mm;
-    c.w = ww;
-    c.bias = task == 0 ? a.bias_csa : task == 1 ? a.bias_hca : a.bias_idx;
+    c.m = a.m;
+    c.w = a.w;
+    c.bias = idx ? a.bias_idx : a.bias_csa;
     set_out(c, st, width);
     const RingRows rows{idx ? a.ring_ki + (size_t)b * a.R * di : a.ring_x + (size_t)b * a.R * D,
-                        (task == 0 ? a.ring_zc : task == 1 ? a.ring_zh : a.ring_zi) + (size_t)b * a.R * width,
+                        (idx ? a.ring_zi : a.ring_zc) + (size_t)b * a.R * width,
                         idx ? a.ki + (int64_t)b * di : xin,
-                        (task == 0 ? a.zc : task == 1 ? a.zh : a.zi) + (int64_t)b * width,
-                        t, a.R, width};
+                        (idx ? a.zi : a.zc) + (int64_t)b * width, t, tr, a.R, width};
     float y[kGMax][VEC];
     compress_entry<uint16_t, false>(c, rows, j, y, lane);
     store_any<VEC, kGMax>(c, st.layout, orow, y, lane);
+  } else if (task == 1) {
+    const int mp = a.m_prime;
+    const int q = (int)((t + 1) % mp), seen = q == 0 ? mp : q;  // positions of the entry so far
+    if (q % kPB != 0 && q != 0) return;                          // no block completes here
+    const int pb = (seen - 1) / kPB * kPB, nb = seen - pb;
+    const int64_t j = (t + 1 - seen) / mp, start = j * mp;
+    CompressArgs c;
+    c.m = mp;
+    c.w = mp;
+    c.bias = a.bias_hca;
+    set_out(c, a.hca, D);
+    const RingRows rows{a.ring_x + (size_t)b * a.R * D, a.ring_zh + (size_t)b * a.R * D, xin,
+                        a.zh + (int64_t)b * D, t, tr, a.R, D};
+    float* state = a.hca_state + (size_t)b * 3 * D;
+    float y[kGMax][VEC];
+#pragma unroll
+    for (int g = 0; g < kGMax; ++g) {
+      const int c0 = (g * 64 + lane) * VEC;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) y[g][v] = 0.f;
+      if (c0 >= D) continue;
+      float M[VEC], S[VEC], A[VEC];
+      if (pb == 0) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { M[v] = -INFINITY; S[v] = 0.f; A[v] = 0.f; }
+      } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { M[v] = state[c0 + v]; S[v] = state[D + c0 + v]; A[v] = state[2 * D + c0 + v]; }
+      }
+      fold_block<uint16_t, false>(c, rows, start, pb, nb, c0, M, S, A);
+      if (q != 0) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { state[c0 + v] = M[v]; state[D + c0 + v] = S[v]; state[2 * D + c0 + v] = A[v]; }
+      } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) y[g][v] = A[v] / S[v];
+      }
+    }
+    if (q != 0) return;
+    const int64_t orow = a.hca_rb[b] + j;
+    if (orow >= 0 && orow < a.hca.n_rows) store_any<VEC, kGMax>(c, a.hca.layout, orow, y, lane);
   } else if (task == 3) {
     // the token into both window rows of its position; the window's base position
     CompressArgs c;

@@ -76,6 +76,7 @@ struct DecodeArgs {
   int m, w, m_prime, W, R, D, d_idx;
   const float *bias_csa, *bias_hca, *bias_idx;
   uint16_t *ring_x, *ring_zc, *ring_zh, *ring_ki, *ring_zi;
+  float* hca_state;  // [B, 3, D]
   StoreView win, csa, hca, idx;
   const int64_t* win_rb;
   int64_t* win_pos0;

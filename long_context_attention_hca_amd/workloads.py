@@ -114,6 +114,7 @@ class DecodeState:
         self.rings = {"x": z(B * R, D), "z_csa": z(B * R, D), "z_hca": z(B * R, D)}
         if d_idx:
             self.rings.update({"k_idx": z(B * R, d_idx), "z_idx": z(B * R, d_idx)})
+        self.hca_state = torch.zeros(B, 3, D, dtype=torch.float32, device=dev)
         self.window = empty_store(layout, B * 2 * W, d_nope, d_rope, dev)
         self.win_row_begin = _i64([b * 2 * W for b in range(B)], dev)
         self.win_pos0 = torch.zeros(B, dtype=torch.int64, device=dev)
@@ -125,7 +126,7 @@ class DecodeState:
         if d_idx:
             self.idx = empty_store(LAYOUT_MXFP4, B * max(self.n_c, 1), d_idx, 0, dev)
             self.idx_row_begin = self.csa_row_begin
-        self.layer = DecodeLayer(m, w, m_prime, W, R, bias_csa, bias_hca, self.rings, self.window,
+        self.layer = DecodeLayer(m, w, m_prime, W, R, bias_csa, bias_hca, self.rings, self.hca_state, self.window,
                                  self.win_row_begin, self.win_pos0, self.csa, self.csa_row_begin, self.hca,
                                  self.hca_row_begin, self.idx, self.idx_row_begin, bias_idx)
 

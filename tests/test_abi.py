@@ -171,7 +171,7 @@ def test_decode_layer_struct_matches_the_header(tmp_path):
 def decode_call(B=2, d_idx=64, **kw):
     D = 512
     st = lambda layout=2: store(layout=layout, n_rows=1000)
-    L = hca._DecodeLayerC(4, 8, 128, 128, 128, d_idx, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7],
+    L = hca._DecodeLayerC(4, 8, 128, 128, 128, d_idx, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[0],
                           st(), P[8], P[9], st(), P[10], st(), P[11],
                           store(layout=3, d_nope=64, d_rope=0, row_stride=32, rope_stride=2), P[12])
     for k, v in kw.items():
@@ -186,7 +186,8 @@ def decode_call(B=2, d_idx=64, **kw):
     (dict(window=store(d_nope=384, d_rope=64, row_stride=384)), -1, "widths differ"),
     (dict(hca=store(d_nope=384, d_rope=64, row_stride=384)), -1, "widths differ"),
     (dict(d_idx=48), -1, "idx width"), (dict(d_idx=12), -2, "d_idx"),
-    (dict(bias_csa=None), -1, "NULL field"), (dict(ring_x=0x100004), -1, "aligned"),
+    (dict(bias_csa=None), -1, "NULL field"), (dict(hca_state=None), -1, "NULL field"),
+    (dict(ring_x=0x100004), -1, "aligned"),
     (dict(idx_row_begin=None), -1, "NULL indexer"),
 ])
 def test_decode_append_rejects_bad_arguments(kw, status, msg):

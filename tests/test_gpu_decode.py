@@ -136,16 +136,24 @@ def test_narrow_key_compression_vs_oracle(mods, raw_dt, d, layout, scalar):
         check_f32_entries(np_(out.data), y, ya, "narrow keys")
 
 
-def test_decode_append_equals_bulk_and_oracle(mods):
-    """300 decode steps over a batch of three sequences: sequence 0 from step 0, sequence 1
-    from step 37, sequence 2 idle throughout (pos = -1). The CSA, HCA and MXFP4 indexer-key
+DECODE_CASES = [
+    # m, w, m', W, d_nope, d_rope, d_idx, steps, first step of each sequence (None: idle)
+    (4, 8, 128, 128, 448, 64, 64, 300, [0, 37, None]),
+    (3, 5, 20, 7, 48, 16, 32, 150, [0, 11, None]),      # m' not a multiple of 8: a short last block
+]
+
+
+@pytest.mark.parametrize("m,w,mp,Wn,dn,dr,di,T,start", DECODE_CASES)
+def test_decode_append_equals_bulk_and_oracle(mods, m, w, mp, Wn, dn, dr, di, T, start):
+    """Decode steps over a batch of three sequences: sequence 0 from the first step, sequence 1
+    from a later one, sequence 2 idle throughout (pos = -1). The CSA, HCA and MXFP4 indexer-key
     entries emitted along the way equal the bulk compressors' bit for bit and the oracle to
     the compression tolerances; the window store and win_pos0 hold the last W tokens (checked
-    mid-run and at the end); the idle sequence's rows stay untouched; HCA attention through
-    the decode-built window equals attention through a contiguous window bit for bit."""
+    mid-run and at the end); the idle sequence's rows stay untouched; at D = 512, HCA attention
+    through the decode-built window equals attention through a contiguous window bit for bit."""
     H, W = mods
-    B, T, start = 3, 300, [0, 37, None]
-    m, w, mp, Wn, dn, dr, di = 4, 8, 128, 128, 448, 64, 64
+    _say(f"decode m={m} w={w} m'={mp} W={Wn} D={dn}+{dr} d_idx={di}")
+    B = 3
     D = dn + dr
     g = synth.generator(1013)
     X = synth.bf16_bits(synth.normal(g, (B, T, D)))
@@ -172,9 +180,9 @@ def test_decode_append_equals_bulk_and_oracle(mods):
         pos = torch.tensor(p, dtype=torch.int64, device="cuda")
         pc = torch.tensor([max(v, 0) for v in p], device="cuda")
         st.step(pos, Xc[ar, pc], ZCc[ar, pc], ZHc[ar, pc], KIc[ar, pc], ZIc[ar, pc])
-        if step == 131:
+        if step == T // 2:
             torch.cuda.synchronize()
-            _check_window(H, W, st, 0, 131, X[0], Wn, dn, dr, "window mid-run")
+            _check_window(H, W, st, 0, T // 2, X[0], Wn, dn, dr, "window mid-run")
     torch.cuda.synchronize()
     _say("bulk comparisons")
     for b in range(2):
@@ -222,6 +230,8 @@ def test_decode_append_equals_bulk_and_oracle(mods):
     r0 = st.n_c
     _check_mxfp4_entries(np_(st.idx.data[r0:r0 + L // m]), np_(st.idx.rope[r0:r0 + L // m]), y, ya,
                          "decode indexer keys vs oracle")
+    if D != 512:
+        return
     # HCA attention for each sequence's last token: decode-built window vs a contiguous one
     _say("attention through the window")
     Hh = 16
