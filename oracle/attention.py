@@ -19,6 +19,10 @@ Readings of what the pages leave open:
 * The two branches are combined by log-sum-exp, i.e. one joint softmax over
   the union of compressed entries and window tokens.
 * HCA entry j is visible at t iff (j + 1) * m' - 1 <= t.
+* Document masks (packed sequences, a query's document starting at raw
+  position lo): the window starts at lo at the earliest, and an HCA entry is
+  visible only if its window [j m', (j+1) m') starts at or after lo; CSA's
+  entries are whatever the (masked) indexer selected. lo <= 0 is no mask.
 * An empty entry set gives o = 0 and lse = -inf.
 * lse is the natural log of the softmax denominator of the scaled logits.
 """
@@ -44,9 +48,10 @@ def attend(q, E, scale):
     return o, mx[:, 0] + np.log(den[:, 0])
 
 
-def window_positions(t, W):
-    """Raw positions of the sliding-window branch of a query at position t."""
-    return np.arange(max(0, t - W + 1), t + 1)
+def window_positions(t, W, lo=0):
+    """Raw positions of the sliding-window branch of a query at position t
+    (in a document starting at lo)."""
+    return np.arange(max(0, lo, t - W + 1), t + 1)
 
 
 def merge(o1, lse1, o2, lse2):
@@ -57,7 +62,7 @@ def merge(o1, lse1, o2, lse2):
     return w1[:, None] * o1 + w2[:, None] * o2, lse
 
 
-def csa(q, t, entries, idx, raw, W, scale):
+def csa(q, t, entries, idx, raw, W, scale, lo=0):
     """CSA core attention of one query.
 
     q [h, D]; t: absolute position; entries [n, D]: decoded compressed
@@ -68,19 +73,20 @@ def csa(q, t, entries, idx, raw, W, scale):
     idx = np.asarray(idx)
     sel = idx[idx >= 0]
     assert len(np.unique(sel)) == len(sel), "duplicate selection"
-    win = _rows(raw, window_positions(t, W))
+    win = _rows(raw, window_positions(t, W, lo))
     E = np.concatenate([np.asarray(entries, np.float64)[sel], win], axis=0)
     return attend(q, E, scale)
 
 
-def hca(q, t, entries, m_prime, raw, W, scale):
+def hca(q, t, entries, m_prime, raw, W, scale, lo=0):
     """HCA core attention of one query over all visible heavily compressed
     entries plus the window."""
     n_vis = (t + 1) // m_prime
     entries = np.asarray(entries, np.float64)
     assert n_vis <= entries.shape[0], "visible entries missing from the store"
-    win = _rows(raw, window_positions(t, W))
-    E = np.concatenate([entries[:n_vis], win], axis=0)
+    vis = [j for j in range(n_vis) if j * m_prime >= lo]
+    win = _rows(raw, window_positions(t, W, lo))
+    E = np.concatenate([entries[np.array(vis, dtype=np.int64)].reshape(len(vis), entries.shape[1]), win], axis=0)
     return attend(q, E, scale)
 
 

@@ -15,6 +15,10 @@ Readings of what the pages leave open:
 * Ties go to the lower entry index; when fewer than k entries are visible
   all of them are returned; the selection is returned in ascending entry
   order and padded with -1 up to k.
+* Document masks (packed sequences; the pages use sample-level masks in
+  pretraining): a query whose document starts at raw position lo sees an
+  entry only if every raw position of the entry's window (those >= 0) lies
+  in [lo, t]; lo <= 0 is no mask.
 * FP4 case: q and keys are MXFP4 (block 32 along the indexer dimension).
   Each per-head dot product is then exact in float32, and the score is
   defined bit-exactly as a float32 fold in head order with separate
@@ -61,6 +65,29 @@ def topk(s, n_vis, k):
     s = np.asarray(s)[:n_vis]
     order = np.lexsort((np.arange(n_vis), -s.astype(np.float64)))
     sel = np.sort(order[:min(k, n_vis)])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:len(sel)] = sel
+    return out
+
+
+def visible_entries(t, m, w, lo, n_entries):
+    """Entries a query at t in a document starting at lo may select: those
+    whose window's raw positions (the ones >= 0) all lie in [lo, t]."""
+    out = []
+    for j in range(n_entries):
+        pos = [p for p in range(j * m - (w - m), (j + 1) * m) if p >= 0]
+        if pos and min(pos) >= max(lo, 0) and max(pos) <= t:
+            out.append(j)
+    return np.array(out, dtype=np.int64)
+
+
+def topk_among(s, entries, k):
+    """The k entries of `entries` with the largest s (ties -> lower index),
+    ascending, padded with -1 to length k (int32)."""
+    entries = np.asarray(entries, dtype=np.int64)
+    s = np.asarray(s)
+    order = np.lexsort((entries, -s[entries].astype(np.float64))) if len(entries) else np.array([], np.int64)
+    sel = np.sort(entries[order[:min(k, len(entries))]])
     out = np.full(k, -1, dtype=np.int32)
     out[:len(sel)] = sel
     return out
