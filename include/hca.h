@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define HCA_ABI_VERSION 1
+#define HCA_ABI_VERSION 2
 
 /* Status codes. */
 #define HCA_OK 0
@@ -238,11 +238,14 @@ int decode_append(const hca_decode_layer* layer, int32_t B, const int64_t* pos, 
  *
  * For query i in sequence b = q_seq[i] at position t = q_pos[i], the
  * visible entries are j < n_vis = floor((t+1)/m) (entry j's last raw
- * position (j+1)m-1 must be <= t), and
+ * position (j+1)m-1 must be <= t) and, with a document mask (q_lo not NULL,
+ * lo = q_lo[i] > 0: packed sequences, the query's document starting at raw
+ * position lo), only entries whose window [j*m - (w-m), (j+1)*m) starts at or
+ * after lo, i.e. j >= j_lo = ceil((lo + w - m) / m); and
  *   s[j] = sum_h w_idx[i, h] * max(0, <q_idx[i, h, :], k_idx[k_row_begin[b] + j, :]>).
- * out_idx[i, :] receives the k entries with the largest s (ties to the
- * lower j; all n_vis entries if n_vis <= k) in ascending order of j,
- * padded with -1.
+ * out_idx[i, :] receives the k visible entries with the largest s (ties to
+ * the lower j; all of them if at most k are visible) in ascending order of
+ * j, padded with -1.
  *
  * idx_dtype HCA_F32 / HCA_BF16: q_idx [nq, H, d] and k_idx [k_rows, d]
  *   elements, contiguous; scores accumulate in float32.
@@ -254,8 +257,10 @@ int decode_append(const hca_decode_layer* layer, int32_t B, const int64_t* pos, 
  *   blocks; the score is defined bit-exactly as s = w0*r0, then
  *   s = s + w_h*r_h in head order, each product and sum rounded to float32
  *   (no fused multiply-add).
- * w_idx: float32 [nq, H]. Requires d == 64, 1 <= H <= 8, 1 <= k <= 2048,
- * m >= 1, 1 <= nq, max_visible <= 2^21 (HCA_ERR_UNSUPPORTED beyond).
+ * w_idx: float32 [nq, H]. q_lo: int64 [nq] or NULL (no document mask); w is
+ * the CSA window (used with q_lo only). Requires d == 64, 1 <= H <= 8,
+ * 1 <= k <= 2048, 1 <= m <= w, 1 <= nq, max_visible <= 2^21
+ * (HCA_ERR_UNSUPPORTED beyond).
  * Preconditions: q_seq[i] indexes k_row_begin; every
  * n_vis <= max_visible and k_row_begin[b] + n_vis <= k_rows (reads are
  * clamped to both bounds).
@@ -267,9 +272,9 @@ size_t lightning_index_topk_workspace(int32_t nq, int64_t max_visible, int32_t k
 int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx,
                          int32_t n_idx_heads, int32_t d_idx, int32_t idx_dtype, const void* k_idx,
                          const uint8_t* k_idx_scale, int64_t k_rows, const int64_t* k_row_begin,
-                         const int32_t* q_seq, const int64_t* q_pos, int32_t nq,
-                         int64_t max_visible, int32_t m, int32_t k, int32_t* out_idx, void* ws,
-                         size_t ws_bytes, void* stream);
+                         const int32_t* q_seq, const int64_t* q_pos, const int64_t* q_lo,
+                         int32_t nq, int64_t max_visible, int32_t m, int32_t w, int32_t k,
+                         int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa_sparse_mqa_attn — CSA core attention (CSA paragraph: MQA with shared
@@ -279,7 +284,9 @@ int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scale, const fl
  * For query i (sequence b, position t) and every head h, one softmax over
  * the set E = {cache row cache_row_begin[b] + idx[i, r] : r < k, idx >= 0}
  * U {window row win_row_begin[b] + (p - win_pos0[b]) :
- *     max(0, t-W+1) <= p <= t}, with K = V = the stored row (all D dims):
+ *     max(0, lo, t-W+1) <= p <= t}, with K = V = the stored row (all D dims);
+ * lo = q_lo[i] is the first raw position of the query's document in a packed
+ * sequence (q_lo NULL: no document mask, lo = 0):
  *   o[i, h] = sum_e softmax_e(scale * <q[i, h], e>) e,
  *   lse[i, h] = log sum_e exp(scale * <q[i, h], e>)  (natural log).
  * An empty set gives o = 0, lse = -inf.
@@ -300,14 +307,16 @@ int csa_sparse_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_he
                         const hca_store* cache, const int64_t* cache_row_begin,
                         const int32_t* idx, int32_t k, const hca_store* window,
                         const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W,
-                        const int32_t* q_seq, const int64_t* q_pos, float scale, void* o,
-                        int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+                        const int32_t* q_seq, const int64_t* q_pos, const int64_t* q_lo, float scale,
+                        void* o, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /*
  * hca_dense_mqa_attn — HCA core attention (HCA paragraph: dense attention
  * over all heavily compressed entries plus the sliding-window branch).
  * As csa_sparse_mqa_attn, with the compressed part of E being every visible
- * entry j < n_vis = min(floor((t+1)/m_prime), max_visible):
+ * entry j < n_vis = min(floor((t+1)/m_prime), max_visible) whose window
+ * [j*m_prime, (j+1)*m_prime) starts at or after lo (j >= ceil(lo / m_prime)):
  * cache rows cache_row_begin[b] + j.
  * Workspace: mqa_attn_workspace(q_dtype, nq, n_heads, D, max_visible + W) bytes.
  */
@@ -315,8 +324,8 @@ int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_hea
                        const hca_store* cache, const int64_t* cache_row_begin, int32_t m_prime,
                        int64_t max_visible, const hca_store* window, const int64_t* win_row_begin,
                        const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
-                       const int64_t* q_pos, float scale, void* o, int32_t o_dtype, float* lse,
-                       void* ws, size_t ws_bytes, void* stream);
+                       const int64_t* q_pos, const int64_t* q_lo, float scale, void* o,
+                       int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,9 +73,10 @@ _decode_append = _sig("decode_append", ctypes.c_int,
                       [ctypes.POINTER(_DecodeLayerC), _I32, _P, _P, _P, _P, _P, _P, _P])
 _index_ws = _sig("lightning_index_topk_workspace", _SZ, [_I32, _I64, _I32])
 _index = _sig("lightning_index_topk", ctypes.c_int,
-              [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P])
+              [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ,
+               _P])
 _attn_ws = _sig("mqa_attn_workspace", _SZ, [_I32, _I32, _I32, _I32, _I64])
-_attn_tail = [_SP, _P, _P, _I32, _P, _P, _F, _P, _I32, _P, _P, _SZ, _P]
+_attn_tail = [_SP, _P, _P, _I32, _P, _P, _P, _F, _P, _I32, _P, _P, _SZ, _P]
 _csa_attn = _sig("csa_sparse_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP, _P, _P, _I32] + _attn_tail)
 _hca_attn = _sig("hca_dense_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail)
 
@@ -207,14 +208,16 @@ def lightning_index_topk_workspace(nq, max_visible, k):
 
 
 def lightning_index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out_idx, ws,
-                         q_idx_scale=None, k_idx_scale=None, idx_dtype=None, stream=None):
-    """q_idx [nq, H, d] (f32/bf16) or [nq, H, d/2] uint8 (MXFP4, with scales)."""
+                         q_idx_scale=None, k_idx_scale=None, idx_dtype=None, q_lo=None, w=None, stream=None):
+    """q_idx [nq, H, d] (f32/bf16) or [nq, H, d/2] uint8 (MXFP4, with scales). q_lo: int64 [nq]
+    document starts (None: no document mask); w: the CSA window (default 2m)."""
     dt = _dtype_code(q_idx) if idx_dtype is None else idx_dtype
     nq, H = q_idx.shape[0], q_idx.shape[1]
     d = q_idx.shape[2] * (2 if dt == MXFP4 else 1)
     _check(_index(_ptr(q_idx), _ptr(q_idx_scale), _ptr(w_idx), H, d, dt, _ptr(k_idx), _ptr(k_idx_scale),
-                  k_idx.shape[0], _ptr(k_row_begin), _ptr(q_seq), _ptr(q_pos), nq, max_visible, m, k,
-                  _ptr(out_idx), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+                  k_idx.shape[0], _ptr(k_row_begin), _ptr(q_seq), _ptr(q_pos), _ptr(q_lo), nq, max_visible, m,
+                  2 * m if w is None else w, k, _ptr(out_idx), _ptr(ws), ws.numel() * ws.element_size(),
+                  _stream(stream)))
 
 
 def mqa_attn_workspace(q_dtype, nq, n_heads, d, max_entries):
@@ -228,16 +231,16 @@ def _ws_args(ws):
 
 
 def csa_sparse_mqa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale,
-                        o, lse, ws=None, stream=None):
+                        o, lse, ws=None, q_lo=None, stream=None):
     wp, wb = _ws_args(ws)
     _check(_csa_attn(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin),
                      _ptr(idx), idx.shape[1], window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq),
-                     _ptr(q_pos), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb, _stream(stream)))
+                     _ptr(q_pos), _ptr(q_lo), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb, _stream(stream)))
 
 
 def hca_dense_mqa_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq,
-                       q_pos, scale, o, lse, ws=None, stream=None):
+                       q_pos, scale, o, lse, ws=None, q_lo=None, stream=None):
     wp, wb = _ws_args(ws)
     _check(_hca_attn(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin), m_prime,
                      max_visible, window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq), _ptr(q_pos),
-                     scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb, _stream(stream)))
+                     _ptr(q_lo), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb, _stream(stream)))

@@ -227,7 +227,8 @@ size_t attn_ws(int q_dtype, int64_t nq, int H, int D, int64_t max_entries, int* 
 int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
               const hca_store* cache, const int64_t* cache_row_begin, const int32_t* idx, int32_t k,
               int32_t m_prime, int64_t max_visible, const hca_store* window, const int64_t* win_row_begin,
-              const int64_t* win_pos0, int32_t W, const int32_t* q_seq, const int64_t* q_pos, float scale,
+              const int64_t* win_pos0, int32_t W, const int32_t* q_seq, const int64_t* q_pos,
+              const int64_t* q_lo, float scale,
               void* o, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !cache_row_begin || !win_row_begin || !win_pos0 || !q_seq || !q_pos || !o || !lse)
     return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
@@ -267,7 +268,7 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
   a.m_prime = csa ? 1 : m_prime;
   a.max_visible = csa ? 0 : max_visible;
   a.win_row_begin = win_row_begin; a.win_pos0 = win_pos0; a.W = W;
-  a.q_seq = q_seq; a.q_pos = q_pos; a.scale = scale;
+  a.q_seq = q_seq; a.q_pos = q_pos; a.q_lo = q_lo; a.scale = scale;
   a.o = o; a.o_dtype = o_dtype; a.lse = lse;
   a.n_split = n_split; a.per_split = per;
   a.part_o = nullptr; a.part_lse = nullptr;
@@ -330,8 +331,8 @@ HCA_EXPORT size_t lightning_index_topk_workspace(int32_t nq, int64_t max_visible
 HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx, int32_t n_idx_heads,
                          int32_t d_idx, int32_t idx_dtype, const void* k_idx, const uint8_t* k_idx_scale,
                          int64_t k_rows, const int64_t* k_row_begin, const int32_t* q_seq, const int64_t* q_pos,
-                         int32_t nq, int64_t max_visible, int32_t m, int32_t k, int32_t* out_idx, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         const int64_t* q_lo, int32_t nq, int64_t max_visible, int32_t m, int32_t w, int32_t k,
+                         int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "lightning_index_topk";
   if (!q_idx || !w_idx || !k_idx || !k_row_begin || !q_seq || !q_pos || !out_idx)
     return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
@@ -342,6 +343,7 @@ HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scal
   if (n_idx_heads < 1 || n_idx_heads > 8) return fail(HCA_ERR_UNSUPPORTED, fn, "indexer heads must be 1..8");
   if (k < 1 || k > 2048) return fail(HCA_ERR_INVALID_ARG, fn, "k must be 1..2048");
   if (m < 1 || nq < 0 || max_visible < 0 || k_rows < 0) return fail(HCA_ERR_INVALID_ARG, fn, "bad m/nq/max_visible/k_rows");
+  if (w < m || w > (1 << 20)) return fail(HCA_ERR_INVALID_ARG, fn, "need m <= w <= 2^20");
   if (max_visible > ((int64_t)1 << 21)) return fail(HCA_ERR_UNSUPPORTED, fn, "max_visible above 2^21");
   if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(HCA_ERR_INVALID_ARG, fn, "q_idx/k_idx not 16-byte aligned");
   if (nq == 0) return HCA_OK;
@@ -368,6 +370,8 @@ HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scal
     a.k_row_begin = k_row_begin;
     a.q_seq = q_seq + q0;
     a.q_pos = q_pos + q0;
+    a.q_lo = q_lo ? q_lo + q0 : nullptr;
+    a.cw = w;
     a.nq = (int)nb;
     a.max_visible = max_visible;
     a.m = m;
@@ -388,20 +392,21 @@ HCA_EXPORT size_t mqa_attn_workspace(int32_t q_dtype, int32_t nq, int32_t n_head
 HCA_EXPORT int csa_sparse_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads, const hca_store* cache,
                         const int64_t* cache_row_begin, const int32_t* idx, int32_t k, const hca_store* window,
                         const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
-                        const int64_t* q_pos, float scale, void* o, int32_t o_dtype, float* lse, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        const int64_t* q_pos, const int64_t* q_lo, float scale, void* o, int32_t o_dtype, float* lse,
+                        void* ws, size_t ws_bytes, void* stream) {
   return attn_impl("csa_sparse_mqa_attn", true, q, q_dtype, nq, n_heads, cache, cache_row_begin, idx, k, 1, 0,
-                   window, win_row_begin, win_pos0, W, q_seq, q_pos, scale, o, o_dtype, lse, ws, ws_bytes, stream);
+                   window, win_row_begin, win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype, lse, ws, ws_bytes,
+                   stream);
 }
 
 HCA_EXPORT int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads, const hca_store* cache,
                        const int64_t* cache_row_begin, int32_t m_prime, int64_t max_visible, const hca_store* window,
                        const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
-                       const int64_t* q_pos, float scale, void* o, int32_t o_dtype, float* lse, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       const int64_t* q_pos, const int64_t* q_lo, float scale, void* o, int32_t o_dtype, float* lse,
+                       void* ws, size_t ws_bytes, void* stream) {
   return attn_impl("hca_dense_mqa_attn", false, q, q_dtype, nq, n_heads, cache, cache_row_begin, nullptr, 0,
-                   m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale, o, o_dtype, lse,
-                   ws, ws_bytes, stream);
+                   m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype,
+                   lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

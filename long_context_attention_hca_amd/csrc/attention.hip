@@ -43,18 +43,24 @@ struct QueryCtx {
   int64_t t, n_c, n_w, cache_rb, win_rb, win_p0;
 };
 
+// With a document mask (lo > 0) the window starts at lo at the earliest and HCA skips the
+// entries j < ceil(lo / m') whose window starts before lo: the cache rows then begin j_lo
+// rows later (CSA's selected entries come from the indexer, which applies the mask).
 __device__ __forceinline__ QueryCtx query_ctx(const AttnArgs& a, int qi) {
   QueryCtx c;
   const int b = a.q_seq[qi];
   c.t = a.q_pos[qi];
+  const int64_t lo = a.q_lo ? max<int64_t>(a.q_lo[qi], 0) : 0;
+  int64_t j_lo = 0;
   if (a.idx) {
     c.n_c = a.k;
   } else {
     int64_t nv = c.t >= 0 ? (c.t + 1) / a.m_prime : 0;
-    c.n_c = min(nv, a.max_visible);
+    j_lo = (lo + a.m_prime - 1) / a.m_prime;
+    c.n_c = max<int64_t>(min(nv, a.max_visible) - j_lo, 0);
   }
-  c.n_w = c.t >= 0 ? min<int64_t>(a.W, c.t + 1) : 0;
-  c.cache_rb = a.cache_row_begin[b];
+  c.n_w = c.t >= 0 ? max<int64_t>(min<int64_t>(min<int64_t>(a.W, c.t + 1), c.t - lo + 1), 0) : 0;
+  c.cache_rb = a.cache_row_begin[b] + j_lo;
   c.win_rb = a.win_row_begin[b];
   c.win_p0 = a.win_pos0[b];
   return c;

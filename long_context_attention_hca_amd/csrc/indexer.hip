@@ -44,15 +44,22 @@ constexpr int kCandCap = 8192;          // candidates finalize holds in register
 constexpr int kMaxBlk = 2048;           // score blocks per query (max_visible <= 2^21)
 constexpr int kBpt = kMaxBlk / kFinThreads;  // score blocks per finalize thread
 
-__device__ __forceinline__ int64_t visible_keys(const IndexArgs& a, int qi, int64_t* row0) {
+// The visible entries of query qi are the rows *row0 + j, j < the returned count, which are
+// entries *j0 + j of its sequence: with a document mask the entries before j_lo (their window
+// starts before the document) are cut off the front, so the kernels work on the shifted range
+// and add *j0 to the indices they output.
+__device__ __forceinline__ int64_t visible_keys(const IndexArgs& a, int qi, int64_t* row0, int64_t* j0 = nullptr) {
   const int b = a.q_seq[qi];
   const int64_t t = a.q_pos[qi];
-  const int64_t rb = a.k_row_begin[b];
+  const int64_t lo = a.q_lo ? a.q_lo[qi] : 0;
+  const int64_t j_lo = lo > 0 ? (lo + a.cw - 1) / a.m : 0;  // ceil((lo + cw - m) / m)
+  const int64_t rb = a.k_row_begin[b] + j_lo;
   int64_t nv = t >= 0 ? (t + 1) / a.m : 0;
-  nv = min(nv, a.max_visible);
+  nv = min(nv, a.max_visible) - j_lo;
   nv = min(nv, a.k_rows - rb);
   if (rb < 0 || nv < 0) nv = 0;
   *row0 = rb;
+  if (j0) *j0 = j_lo;
   return nv;
 }
 
@@ -728,7 +735,8 @@ __device__ __forceinline__ uint32_t flag_blocks(const uint64_t (&tq)[kBpt], uint
 // 0 < T), so compacting the selected slots in slot order gives the ascending answer. Slot
 // tid + kFinThreads * i is position (i, wave, lane) in row-major order: per-wave ballots give
 // the lane offsets, a scan of the kPer x 8 wave counts the rest.
-__device__ __forceinline__ void ordered_output(const uint64_t (&v)[kPer], uint64_t T, int K, int32_t* out, FinLds& f) {
+__device__ __forceinline__ void ordered_output(const uint64_t (&v)[kPer], uint64_t T, int K, int32_t* out, int32_t j0,
+                                               FinLds& f) {
   static_assert(kPer * (kFinThreads / 64) == 128, "two counts per lane of one wave");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* cnt = f.h;  // [kPer][8] wave counts, then their exclusive prefix
@@ -749,7 +757,7 @@ __device__ __forceinline__ void ordered_output(const uint64_t (&v)[kPer], uint64
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (v[i] >= T) out[min(cnt[i * 8 + wave] + mb[i], (uint32_t)K - 1)] = key_entry(v[i]);
+    if (v[i] >= T) out[min(cnt[i * 8 + wave] + mb[i], (uint32_t)K - 1)] = key_entry(v[i]) + j0;
 }
 
 // Output LDS: per-block counts (then their prefix), per-block cursors, entries bucketed by block.
@@ -777,11 +785,12 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
 #pragma unroll
     for (int i = 0; i < kBpt; ++i) tq[i] = thr[min(kBpt * tid + i, a.nblk - 1)];
   }
-  int64_t rb;
-  const int64_t nv = visible_keys(a, qi, &rb);
+  int64_t rb, j0;
+  const int64_t nv = visible_keys(a, qi, &rb, &j0);
+  const int32_t jo = (int32_t)j0;  // entry index of visible key 0
   int32_t* out = a.out + (int64_t)qi * K;
   if (nv <= K) {  // every visible entry is selected, ascending; pad with -1
-    for (int j = tid; j < K; j += kFinThreads) out[j] = j < nv ? j : -1;
+    for (int j = tid; j < K; j += kFinThreads) out[j] = j < nv ? j + jo : -1;
     return;
   }
   const int nb = (int)((nv + kBlockKeys - 1) / kBlockKeys);
@@ -808,7 +817,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     T = select_regs<false>(v, (uint32_t)K, f);
     nflag = flag_blocks(tq, T, f);
     if (nflag == 0) {
-      ordered_output(v, T, K, out, f);
+      ordered_output(v, T, K, out, jo, f);
       return;
     }
     // the round-1 winners (the K keys >= T) seed the overflow list of round 2
@@ -916,7 +925,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(IndexArgs a) {
     sorted[min(s0 + r, (uint32_t)K - 1)] = j;
   }
   __syncthreads();
-  for (int i = tid; i < K; i += kFinThreads) out[i] = sorted[i];
+  for (int i = tid; i < K; i += kFinThreads) out[i] = sorted[i] + jo;
 }
 
 }  // namespace

@@ -39,9 +39,10 @@ struct IndexArgs {
   const int64_t* k_row_begin;
   const int32_t* q_seq;
   const int64_t* q_pos;
+  const int64_t* q_lo;  // document starts or nullptr
   int nq;  // queries of this batch (pointers above already offset to the batch)
   int64_t max_visible;
-  int m, k;
+  int m, cw, k;  // cw: the CSA window (document masks)
   int32_t* out;  // [nq, k]
   // workspace views for the batch (set by index_ws_layout)
   int nblk;             // score blocks per query: ceil(max_visible / 1024)
@@ -99,6 +100,7 @@ struct AttnArgs {
   int W;
   const int32_t* q_seq;
   const int64_t* q_pos;
+  const int64_t* q_lo;  // document starts or nullptr
   float scale;
   void* o;
   int o_dtype;

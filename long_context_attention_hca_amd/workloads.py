@@ -56,7 +56,7 @@ class Workspace:
 
 
 def index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, ws, q_idx_scale=None,
-               k_idx_scale=None, out=None, stream=None):
+               k_idx_scale=None, out=None, q_lo=None, w=None, stream=None):
     nq = q_idx.shape[0]
     if out is None:
         out = torch.empty(nq, k, dtype=torch.int32, device=q_idx.device)
@@ -65,12 +65,12 @@ def index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k
     one = lightning_index_topk_workspace(1, max_visible, k)
     buf = ws.get("index", min(need, max(one, 4 << 30)))
     lightning_index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out, buf,
-                         q_idx_scale=q_idx_scale, k_idx_scale=k_idx_scale, stream=stream)
+                         q_idx_scale=q_idx_scale, k_idx_scale=k_idx_scale, q_lo=q_lo, w=w, stream=stream)
     return out
 
 
 def csa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale, ws,
-             o_dtype=None, o=None, lse=None, stream=None):
+             o_dtype=None, o=None, lse=None, q_lo=None, stream=None):
     nq, H, D = q.shape
     if o is None:
         o = torch.empty(nq, H, D, dtype=o_dtype or q.dtype, device=q.device)
@@ -79,12 +79,12 @@ def csa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W,
     qd = F32 if q.dtype == torch.float32 else BF16
     buf = ws.get("csa", mqa_attn_workspace(qd, nq, H, D, idx.shape[1] + W))
     csa_sparse_mqa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale,
-                        o, lse, buf, stream=stream)
+                        o, lse, buf, q_lo=q_lo, stream=stream)
     return o, lse
 
 
 def hca_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos,
-             scale, ws, o_dtype=None, o=None, lse=None, stream=None):
+             scale, ws, o_dtype=None, o=None, lse=None, q_lo=None, stream=None):
     nq, H, D = q.shape
     if o is None:
         o = torch.empty(nq, H, D, dtype=o_dtype or q.dtype, device=q.device)
@@ -93,7 +93,7 @@ def hca_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_be
     qd = F32 if q.dtype == torch.float32 else BF16
     buf = ws.get("hca", mqa_attn_workspace(qd, nq, H, D, max_visible + W))
     hca_dense_mqa_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq,
-                       q_pos, scale, o, lse, buf, stream=stream)
+                       q_pos, scale, o, lse, buf, q_lo=q_lo, stream=stream)
     return o, lse
 
 

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert hca.abi_version() == 1
+    assert hca.abi_version() == 2
     for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small")]:
         assert hca._status_string(code) == text
 
@@ -85,16 +85,18 @@ def test_compress_offsets_with_halo_pass_validation_then_need_a_gpu():
 
 def index_call(**kw):
     a = dict(q=P[0], qs=P[1], w=P[2], H=4, d=64, dt=3, k_idx=P[3], ks=P[4], k_rows=1000, krb=P[5], qseq=P[6],
-             qpos=P[7], nq=4, mv=1000, m=4, k=64, out=P[8], ws=P[9], wsb=1 << 30)
+             qpos=P[7], qlo=None, nq=4, mv=1000, m=4, cw=8, k=64, out=P[8], ws=P[9], wsb=1 << 30)
     a.update(kw)
     return hca._index(a["q"], a["qs"], a["w"], a["H"], a["d"], a["dt"], a["k_idx"], a["ks"], a["k_rows"], a["krb"],
-                      a["qseq"], a["qpos"], a["nq"], a["mv"], a["m"], a["k"], a["out"], a["ws"], a["wsb"], None)
+                      a["qseq"], a["qpos"], a["qlo"], a["nq"], a["mv"], a["m"], a["cw"], a["k"], a["out"], a["ws"],
+                      a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(qs=None), -1), (dict(d=128), -2), (dict(H=9), -2), (dict(H=0), -2),
     (dict(k=0), -1), (dict(k=4096), -1), (dict(m=0), -1), (dict(dt=2), -2), (dict(wsb=100), -3),
     (dict(ws=None), -3), (dict(k_idx=ctypes.c_void_p(0x100004)), -1), (dict(mv=(1 << 21) + 1), -2),
+    (dict(cw=3), -1),                                        # the CSA window shorter than m
 ])
 def test_index_rejects_bad_arguments(kw, status):
     assert index_call(**kw) == status
@@ -111,15 +113,15 @@ def test_index_workspace_is_monotone_and_batches():
 
 def attn_call(csa=True, **kw):
     a = dict(q=P[0], qdt=1, nq=4, H=64, cache=store(), crb=P[1], idx=P[2], k=64, mp=128, mv=100,
-             win=store(), wrb=P[3], wp0=P[4], W=128, qseq=P[5], qpos=P[6], scale=0.04, o=P[7], odt=1, lse=P[8],
-             ws=P[9], wsb=1 << 30)
+             win=store(), wrb=P[3], wp0=P[4], W=128, qseq=P[5], qpos=P[6], qlo=None, scale=0.04, o=P[7], odt=1,
+             lse=P[8], ws=P[9], wsb=1 << 30)
     a.update(kw)
     if csa:
         return hca._csa_attn(a["q"], a["qdt"], a["nq"], a["H"], ctypes.byref(a["cache"]), a["crb"], a["idx"], a["k"],
-                             ctypes.byref(a["win"]), a["wrb"], a["wp0"], a["W"], a["qseq"], a["qpos"], a["scale"],
-                             a["o"], a["odt"], a["lse"], a["ws"], a["wsb"], None)
+                             ctypes.byref(a["win"]), a["wrb"], a["wp0"], a["W"], a["qseq"], a["qpos"], a["qlo"],
+                             a["scale"], a["o"], a["odt"], a["lse"], a["ws"], a["wsb"], None)
     return hca._hca_attn(a["q"], a["qdt"], a["nq"], a["H"], ctypes.byref(a["cache"]), a["crb"], a["mp"], a["mv"],
-                         ctypes.byref(a["win"]), a["wrb"], a["wp0"], a["W"], a["qseq"], a["qpos"], a["scale"],
+                         ctypes.byref(a["win"]), a["wrb"], a["wp0"], a["W"], a["qseq"], a["qpos"], a["qlo"], a["scale"],
                          a["o"], a["odt"], a["lse"], a["ws"], a["wsb"], None)
 
 
