@@ -402,6 +402,55 @@ def main():
             "gbs": round(by_app / (t_app * 1e-3) / 1e9, 2), "bound": "latency"}
         del dst, gd
 
+        log("packed prefill with document masks")
+        # one packed sequence of 2^17 raw tokens (precompressed: 32768 CSA entries with MXFP4
+        # keys, 1024 HCA entries), a chunk of its last 2048 positions as queries, documents
+        # starting at 0, 50000, 100123 and 130072 (the chunk spans the last two); index + CSA +
+        # HCA attention with and without the document mask
+        Lp, nqp, k_p = 1 << 17, 2048, 1024
+        ncp, nhp = Lp // m, Lp // mp
+        gp = synth.generator(1017, dev)
+        kp, ks = synth.mxfp4_rows(gp, ncp, 64)
+        qp, qs = synth.mxfp4_rows(gp, nqp * 4, 64)
+        wp = synth.normal(gp, (nqp, 4), std=0.125)
+        cs_p = W.split_store({f"c_{x}": v for x, v in synth.split_entries(gp, ncp, 448, 64).items()}, "c")
+        hs_p = W.split_store({f"h_{x}": v for x, v in synth.split_entries(gp, nhp, 448, 64).items()}, "h")
+        first = Lp - nqp - W_ + 1
+        win_p = W.split_store({f"w_{x}": v for x, v in synth.split_entries(gp, nqp + W_, 448, 64).items()}, "w")
+        qv = synth.bf16_bits(synth.normal(gp, (nqp, H, D))).view(torch.bfloat16)
+        pos_p = torch.arange(Lp - nqp, Lp, dtype=torch.int64, device=dev)
+        starts = torch.tensor([0, 50000, 100123, 130072], dtype=torch.int64, device=dev)
+        lo_p = starts[torch.searchsorted(starts, pos_p, right=True) - 1].contiguous()
+        zero_p = torch.zeros(1, dtype=torch.int64, device=dev)
+        seq_p = torch.zeros(nqp, dtype=torch.int32, device=dev)
+        wp0 = torch.tensor([first], dtype=torch.int64, device=dev)
+        wsp = W.Workspace(dev)
+        idx_p = torch.empty(nqp, k_p, dtype=torch.int32, device=dev)
+
+        def prefill(lo):
+            W.index_topk(qp.view(nqp, 4, 32), wp, kp, zero_p, seq_p, pos_p, ncp, m, k_p, wsp, q_idx_scale=qs.view(nqp, 4, 2),
+                         k_idx_scale=ks, out=idx_p, q_lo=lo, w=8)
+            W.csa_attn(qv, cs_p, zero_p, idx_p, win_p, zero_p, wp0, W_, seq_p, pos_p, 1.0 / D ** 0.5, wsp, q_lo=lo)
+            W.hca_attn(qv, hs_p, zero_p, mp, nhp, win_p, zero_p, wp0, W_, seq_p, pos_p, 1.0 / D ** 0.5, wsp, q_lo=lo)
+
+        res = {}
+        for name, lo in (("masked", lo_p), ("unmasked", None)):
+            prefill(lo)
+            torch.cuda.synchronize()
+            e[0].record()
+            for _ in range(5):
+                prefill(lo)
+            e[1].record()
+            torch.cuda.synchronize()
+            res[name] = e[0].elapsed_time(e[1]) / 5
+        comp["packed_prefill"] = {
+            "workload": f"one packed sequence of 2^17 tokens (4 documents), a chunk of its last {nqp} positions as "
+                        f"queries: index (MXFP4, k={k_p}) + CSA + HCA attention, {H} heads, split stores",
+            "masked_ms": round(res["masked"], 4), "unmasked_ms": round(res["unmasked"], 4),
+            "masked_query_tokens_per_s": round(nqp / (res["masked"] * 1e-3)),
+            "unmasked_query_tokens_per_s": round(nqp / (res["unmasked"] * 1e-3))}
+        del kp, ks, qp, qs, cs_p, hs_p, win_p, qv, wsp
+
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle on the host cores")
