@@ -277,6 +277,33 @@ int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scale, const fl
                          int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * lightning_index_scores + lightning_index_select — lightning_index_topk in
+ * two calls, for callers that run independent work between the scoring and
+ * the selection (HCA attention, say, beside the selection and CSA attention
+ * on another stream: the selection kernel runs one block per query and
+ * leaves most of the GPU free). The two calls take exactly the arguments of
+ * lightning_index_topk; lightning_index_scores enqueues the scores and
+ * leaves every query's candidates in `ws`, and lightning_index_select,
+ * enqueued after it on `stream` with the same arguments and workspace,
+ * writes out_idx. Together they equal lightning_index_topk. The workspace
+ * must hold all nq queries at once (lightning_index_topk_workspace(nq,
+ * max_visible, k) bytes; HCA_ERR_WORKSPACE otherwise), and nothing else may
+ * write it between the two calls.
+ */
+int lightning_index_scores(const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx,
+                           int32_t n_idx_heads, int32_t d_idx, int32_t idx_dtype, const void* k_idx,
+                           const uint8_t* k_idx_scale, int64_t k_rows, const int64_t* k_row_begin,
+                           const int32_t* q_seq, const int64_t* q_pos, const int64_t* q_lo,
+                           int32_t nq, int64_t max_visible, int32_t m, int32_t w, int32_t k,
+                           int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
+int lightning_index_select(const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx,
+                           int32_t n_idx_heads, int32_t d_idx, int32_t idx_dtype, const void* k_idx,
+                           const uint8_t* k_idx_scale, int64_t k_rows, const int64_t* k_row_begin,
+                           const int32_t* q_seq, const int64_t* q_pos, const int64_t* q_lo,
+                           int32_t nq, int64_t max_visible, int32_t m, int32_t w, int32_t k,
+                           int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * csa_sparse_mqa_attn — CSA core attention (CSA paragraph: MQA with shared
  * keys and values over the selected entries; HCA paragraph: plus a
  * sliding-window branch).

@@ -28,7 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libhca.so")
 
 if not os.path.exists(library_path):
-    raise ImportError(f"{library_path} is not built; run `python -m long_context_attention_hca_amd.build` "
+    raise ImportError(f"{library_path} is not built; run `python long_context_attention_hca_amd/build.py` "
                       "(or __graft_entry__.build())")
 _lib = ctypes.CDLL(library_path)
 
@@ -72,9 +72,11 @@ _hca_compress = _sig("hca_compress", ctypes.c_int, _compress_args + [_I32, _I64,
 _decode_append = _sig("decode_append", ctypes.c_int,
                       [ctypes.POINTER(_DecodeLayerC), _I32, _P, _P, _P, _P, _P, _P, _P])
 _index_ws = _sig("lightning_index_topk_workspace", _SZ, [_I32, _I64, _I32])
-_index = _sig("lightning_index_topk", ctypes.c_int,
-              [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P, _SZ,
-               _P])
+_index_argtypes = [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _P, _P,
+                   _SZ, _P]
+_index = _sig("lightning_index_topk", ctypes.c_int, _index_argtypes)
+_index_phase = {"both": _index, "scores": _sig("lightning_index_scores", ctypes.c_int, _index_argtypes),
+                "select": _sig("lightning_index_select", ctypes.c_int, _index_argtypes)}
 _attn_ws = _sig("mqa_attn_workspace", _SZ, [_I32, _I32, _I32, _I32, _I64])
 _attn_tail = [_SP, _P, _P, _I32, _P, _P, _P, _F, _P, _I32, _P, _P, _SZ, _P]
 _csa_attn = _sig("csa_sparse_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP, _P, _P, _I32] + _attn_tail)
@@ -208,13 +210,15 @@ def lightning_index_topk_workspace(nq, max_visible, k):
 
 
 def lightning_index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out_idx, ws,
-                         q_idx_scale=None, k_idx_scale=None, idx_dtype=None, q_lo=None, w=None, stream=None):
+                         q_idx_scale=None, k_idx_scale=None, idx_dtype=None, q_lo=None, w=None, phase="both",
+                         stream=None):
     """q_idx [nq, H, d] (f32/bf16) or [nq, H, d/2] uint8 (MXFP4, with scales). q_lo: int64 [nq]
-    document starts (None: no document mask); w: the CSA window (default 2m)."""
+    document starts (None: no document mask); w: the CSA window (default 2m). phase "scores" /
+    "select" calls lightning_index_scores / lightning_index_select (the two halves)."""
     dt = _dtype_code(q_idx) if idx_dtype is None else idx_dtype
     nq, H = q_idx.shape[0], q_idx.shape[1]
     d = q_idx.shape[2] * (2 if dt == MXFP4 else 1)
-    _check(_index(_ptr(q_idx), _ptr(q_idx_scale), _ptr(w_idx), H, d, dt, _ptr(k_idx), _ptr(k_idx_scale),
+    _check(_index_phase[phase](_ptr(q_idx), _ptr(q_idx_scale), _ptr(w_idx), H, d, dt, _ptr(k_idx), _ptr(k_idx_scale),
                   k_idx.shape[0], _ptr(k_row_begin), _ptr(q_seq), _ptr(q_pos), _ptr(q_lo), nq, max_visible, m,
                   2 * m if w is None else w, k, _ptr(out_idx), _ptr(ws), ws.numel() * ws.element_size(),
                   _stream(stream)))

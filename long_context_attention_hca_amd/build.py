@@ -1,6 +1,7 @@
 """Builds libhca.so (the HIP library) in-tree for gfx950 with hipcc.
 
-Usage: python -m long_context_attention_hca_amd.build
+Usage: python long_context_attention_hca_amd/build.py (run by path: importing the package
+needs the library already built)
 """
 import os
 import subprocess

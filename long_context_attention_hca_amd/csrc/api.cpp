@@ -328,12 +328,20 @@ HCA_EXPORT size_t lightning_index_topk_workspace(int32_t nq, int64_t max_visible
   return index_ws(nq, max_visible);
 }
 
-HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx, int32_t n_idx_heads,
-                         int32_t d_idx, int32_t idx_dtype, const void* k_idx, const uint8_t* k_idx_scale,
-                         int64_t k_rows, const int64_t* k_row_begin, const int32_t* q_seq, const int64_t* q_pos,
-                         const int64_t* q_lo, int32_t nq, int64_t max_visible, int32_t m, int32_t w, int32_t k,
-                         int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "lightning_index_topk";
+}  // extern "C"
+
+namespace {
+
+// The indexer's two phases: kIndexBoth (lightning_index_topk), kIndexScores or kIndexSelect
+// (the split calls, which keep every query's intermediate state in the workspace in between
+// and so need the workspace of all nq queries at once).
+enum IndexPhase { kIndexBoth = 0, kIndexScores = 1, kIndexSelect = 2 };
+
+int index_impl(const char* fn, int phase, const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx,
+               int32_t n_idx_heads, int32_t d_idx, int32_t idx_dtype, const void* k_idx,
+               const uint8_t* k_idx_scale, int64_t k_rows, const int64_t* k_row_begin, const int32_t* q_seq,
+               const int64_t* q_pos, const int64_t* q_lo, int32_t nq, int64_t max_visible, int32_t m, int32_t w,
+               int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
   if (!q_idx || !w_idx || !k_idx || !k_row_begin || !q_seq || !q_pos || !out_idx)
     return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
   if (idx_dtype != HCA_F32 && idx_dtype != HCA_BF16 && idx_dtype != HCA_MXFP4)
@@ -348,6 +356,8 @@ HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scal
   if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(HCA_ERR_INVALID_ARG, fn, "q_idx/k_idx not 16-byte aligned");
   if (nq == 0) return HCA_OK;
   if (!ws || ws_bytes < index_ws(1, max_visible)) return fail(HCA_ERR_WORKSPACE, fn, "workspace too small");
+  if (phase != kIndexBoth && ws_bytes < index_ws(nq, max_visible))
+    return fail(HCA_ERR_WORKSPACE, fn, "the split calls need the workspace of all nq queries");
   int64_t batch = nq;
   while (batch > 1 && index_ws(batch, max_visible) > ws_bytes) batch = std::max<int64_t>(1, batch / 2);
   const int64_t q_row = idx_dtype == HCA_MXFP4 ? (int64_t)n_idx_heads * d_idx / 2
@@ -377,10 +387,37 @@ HCA_EXPORT int lightning_index_topk(const void* q_idx, const uint8_t* q_idx_scal
     a.m = m;
     a.k = k;
     a.out = out_idx + q0 * k;
-    hipError_t e = hca::launch_index_topk(a, static_cast<hipStream_t>(stream));
+    hipError_t e = hca::launch_index_topk(a, phase != kIndexSelect, phase != kIndexScores,
+                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return launched(fn, e);
   }
   return HCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+#define HCA_INDEX_ARGS                                                                                           \
+  const void *q_idx, const uint8_t *q_idx_scale, const float *w_idx, int32_t n_idx_heads, int32_t d_idx,         \
+      int32_t idx_dtype, const void *k_idx, const uint8_t *k_idx_scale, int64_t k_rows,                          \
+      const int64_t *k_row_begin, const int32_t *q_seq, const int64_t *q_pos, const int64_t *q_lo, int32_t nq,   \
+      int64_t max_visible, int32_t m, int32_t w, int32_t k, int32_t *out_idx, void *ws, size_t ws_bytes,         \
+      void *stream
+#define HCA_INDEX_PASS                                                                                           \
+  q_idx, q_idx_scale, w_idx, n_idx_heads, d_idx, idx_dtype, k_idx, k_idx_scale, k_rows, k_row_begin, q_seq,      \
+      q_pos, q_lo, nq, max_visible, m, w, k, out_idx, ws, ws_bytes, stream
+
+HCA_EXPORT int lightning_index_topk(HCA_INDEX_ARGS) {
+  return index_impl("lightning_index_topk", kIndexBoth, HCA_INDEX_PASS);
+}
+
+HCA_EXPORT int lightning_index_scores(HCA_INDEX_ARGS) {
+  return index_impl("lightning_index_scores", kIndexScores, HCA_INDEX_PASS);
+}
+
+HCA_EXPORT int lightning_index_select(HCA_INDEX_ARGS) {
+  return index_impl("lightning_index_select", kIndexSelect, HCA_INDEX_PASS);
 }
 
 HCA_EXPORT size_t mqa_attn_workspace(int32_t q_dtype, int32_t nq, int32_t n_heads, int32_t d, int64_t max_entries) {

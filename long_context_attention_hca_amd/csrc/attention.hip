@@ -56,10 +56,10 @@ __device__ __forceinline__ QueryCtx query_ctx(const AttnArgs& a, int qi) {
     c.n_c = a.k;
   } else {
     int64_t nv = c.t >= 0 ? (c.t + 1) / a.m_prime : 0;
-    j_lo = (lo + a.m_prime - 1) / a.m_prime;
+    if (lo > 0) j_lo = (lo + a.m_prime - 1) / a.m_prime;  // no division on the common path
     c.n_c = max<int64_t>(min(nv, a.max_visible) - j_lo, 0);
   }
-  c.n_w = c.t >= 0 ? max<int64_t>(min<int64_t>(min<int64_t>(a.W, c.t + 1), c.t - lo + 1), 0) : 0;
+  c.n_w = c.t >= 0 ? max<int64_t>(min<int64_t>(a.W, c.t + 1 - lo), 0) : 0;  // positions max(lo, t-W+1) .. t
   c.cache_rb = a.cache_row_begin[b] + j_lo;
   c.win_rb = a.win_row_begin[b];
   c.win_p0 = a.win_pos0[b];

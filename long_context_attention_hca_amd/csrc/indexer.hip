@@ -957,14 +957,14 @@ hipError_t index_init() {
   return hipSuccess;
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
-  if (a.max_visible > a.k) {
+hipError_t launch_index_topk(const IndexArgs& a, bool scores, bool select, hipStream_t s) {
+  if (scores && a.max_visible > a.k) {
     const dim3 g((unsigned)a.nblk, (unsigned)a.nq);
     if (a.dtype == HCA_MXFP4) hipLaunchKernelGGL(score_mxfp4_kernel, g, dim3(256), 0, s, a);
     else if (a.dtype == HCA_F32) hipLaunchKernelGGL(score_valu_kernel<float>, g, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(score_valu_kernel<uint16_t>, g, dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.nq), dim3(kFinThreads), 0, s, a);
+  if (select) hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.nq), dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
 }
 

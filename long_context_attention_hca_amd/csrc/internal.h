@@ -56,7 +56,9 @@ constexpr int kHistBins = 2048;
 constexpr int kMaxTopK = 2048;
 // Lays out the workspace of a batch of nq queries at `ws` (nullptr: only size it); returns bytes.
 size_t index_ws_layout(int64_t nq, int64_t max_visible, void* ws, IndexArgs* a);
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
+// scores: the score kernel (the candidates and block thresholds it leaves in the workspace);
+// select: the selection kernel that reads them
+hipError_t launch_index_topk(const IndexArgs& a, bool scores, bool select, hipStream_t stream);
 hipError_t index_init();
 
 struct StoreView {

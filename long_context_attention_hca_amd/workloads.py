@@ -56,16 +56,18 @@ class Workspace:
 
 
 def index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, ws, q_idx_scale=None,
-               k_idx_scale=None, out=None, q_lo=None, w=None, stream=None):
+               k_idx_scale=None, out=None, q_lo=None, w=None, phase="both", stream=None):
     nq = q_idx.shape[0]
     if out is None:
         out = torch.empty(nq, k, dtype=torch.int32, device=q_idx.device)
-    # all queries at once up to 4 GiB of workspace; beyond that the library batches queries
+    # all queries at once up to 4 GiB of workspace (always for the split phases); beyond that
+    # the library batches queries
     need = lightning_index_topk_workspace(nq, max_visible, k)
     one = lightning_index_topk_workspace(1, max_visible, k)
-    buf = ws.get("index", min(need, max(one, 4 << 30)))
+    buf = ws.get("index", need if phase != "both" else min(need, max(one, 4 << 30)))
     lightning_index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out, buf,
-                         q_idx_scale=q_idx_scale, k_idx_scale=k_idx_scale, q_lo=q_lo, w=w, stream=stream)
+                         q_idx_scale=q_idx_scale, k_idx_scale=k_idx_scale, q_lo=q_lo, w=w, phase=phase,
+                         stream=stream)
     return out
 
 
@@ -193,9 +195,11 @@ class Decode1M:
     (index + CSA attention for one layer, HCA attention for another), with all
     outputs and workspaces preallocated so that `step()` only enqueues kernels.
 
-    HCA attention does not depend on the indexer, so `step()` forks it onto a side
-    stream (default priority) and joins it back: it runs concurrently with
-    index -> CSA attention, on the GPU and inside a captured graph alike."""
+    HCA attention does not depend on the indexer. `step()` runs the indexer's scores,
+    then forks HCA attention onto a side stream (default priority), where it runs beside
+    the top-k selection (one block per query) and CSA attention, and joins it back; on
+    the GPU and inside a captured graph alike. Beside the scores instead, HCA attention
+    and the bandwidth-bound scoring slow each other down about as much as they overlap."""
 
     def __init__(self, case, ws=None, overlap=True):
         p, t = case.params, case.t
@@ -228,11 +232,11 @@ class Decode1M:
         self.ws.get("hca", mqa_attn_workspace(BF16, B, H, D, self.n_h + W))
         self.side = torch.cuda.Stream(device=dev) if overlap else None
 
-    def index(self, stream=None):
+    def index(self, stream=None, phase="both"):
         t = self.case.t
         return index_topk(t["q_idx"], t["w_idx"], t["k_idx"], self.crb, t["q_seq"], t["q_pos"], self.n_c, self.m,
                           self.k, self.ws, q_idx_scale=t["q_idx_scale"], k_idx_scale=t["k_idx_scale"], out=self.idx,
-                          stream=stream)
+                          phase=phase, stream=stream)
 
     def csa_attention(self, stream=None):
         t = self.case.t
@@ -251,10 +255,11 @@ class Decode1M:
             self.hca_attention()
             return
         main = torch.cuda.current_stream()
+        self.index(phase="scores")
         self.side.wait_stream(main)
         with torch.cuda.stream(self.side):
             self.hca_attention()
-        self.index()
+        self.index(phase="select")
         self.csa_attention()
         main.wait_stream(self.side)
 

@@ -201,3 +201,17 @@ def test_decode_append_rejects_bad_arguments(kw, status, msg):
 def test_decode_append_valid_call_reaches_launch():
     assert decode_call() in (0, -4)
     assert decode_call(d_idx=0, idx_row_begin=None) in (0, -4)   # no indexer keys
+
+
+@pytest.mark.parametrize("phase", ["scores", "select"])
+def test_split_index_calls_need_the_whole_workspace(phase):
+    one = hca.lightning_index_topk_workspace(1, 1000, 64)
+    four = hca.lightning_index_topk_workspace(4, 1000, 64)
+    a = dict(q=P[0], qs=P[1], w=P[2], H=4, d=64, dt=3, k_idx=P[3], ks=P[4], k_rows=1000, krb=P[5], qseq=P[6],
+             qpos=P[7], qlo=None, nq=4, mv=1000, m=4, cw=8, k=64, out=P[8], ws=P[9])
+    f = hca._index_phase[phase]
+    call = lambda wsb: f(*[a[x] for x in ("q", "qs", "w", "H", "d", "dt", "k_idx", "ks", "k_rows", "krb", "qseq",
+                                          "qpos", "qlo", "nq", "mv", "m", "cw", "k", "out", "ws")], wsb, None)
+    assert call(one) == -3 and "all nq queries" in hca._last_error().decode()
+    assert call(four) in (0, -4)
+    assert index_call(wsb=one) in (0, -4)            # the one-call version batches instead

@@ -142,3 +142,39 @@ def test_float_indexer(hca, dtype):
     ref = np.stack([OI.topk(OI.scores(qd[i], w[i].double().numpy(), kd[:(q_pos[i] + 1) // 4]),
                             (q_pos[i] + 1) // 4, 300) for i in range(3)])
     check_idx(got, ref, dtype)
+
+
+@pytest.mark.parametrize("dt", ["mxfp4", "f32"])
+def test_split_calls_equal_one_call(hca, dt):
+    """lightning_index_scores then lightning_index_select (with other GPU work queued between
+    them) give the same indices as lightning_index_topk, bit for bit: MXFP4 keys at the
+    decode-1M size, and fp32 keys with some queries seeing at most k entries."""
+    dev = "cuda"
+    g = synth.generator(1018)
+    if dt == "mxfp4":
+        n, nq, k, m = 1 << 18, 4, 1024, 4
+        kp, ks = synth.mxfp4_rows(g, n, 64)
+        qp, qs = synth.mxfp4_rows(g, nq * 4, 64)
+        q, keys, qsc, ksc = qp.view(nq, 4, 32), kp, qs.view(nq, 4, 2), ks
+        q_pos = [4 * n - 1, 4 * n - 1000, 100000, 37]
+    else:
+        n, nq, k, m = 5000, 6, 64, 4
+        q, keys, qsc, ksc = synth.normal(g, (nq, 4, 64)), synth.normal(g, (n, 64)), None, None
+        q_pos = [4 * n - 1, 200, 255, 256, 3, 12345]
+    w = synth.normal(g, (nq, 4), std=0.125)
+    args = lambda: (q.to(dev), w.to(dev), keys.to(dev), torch.zeros(1, dtype=torch.int64, device=dev),
+                    torch.zeros(nq, dtype=torch.int32, device=dev), torch.tensor(q_pos, dtype=torch.int64, device=dev),
+                    n, m, k)
+    ws = torch.empty(hca.lightning_index_topk_workspace(nq, n, k), dtype=torch.uint8, device=dev)
+    kw = dict(q_idx_scale=None if qsc is None else qsc.to(dev), k_idx_scale=None if ksc is None else ksc.to(dev))
+    one = torch.full((nq, k), -7, dtype=torch.int32, device=dev)
+    hca.lightning_index_topk(*args(), one, ws, **kw)
+    two = torch.full((nq, k), -7, dtype=torch.int32, device=dev)
+    a = args()
+    hca.lightning_index_topk(*a, two, ws, phase="scores", **kw)
+    junk = torch.randn(1 << 20, device=dev)
+    junk.mul_(2.0).add_(1.0)                                # unrelated work between the two halves
+    hca.lightning_index_topk(*a, two, ws, phase="select", **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+    assert bool((one >= -1).all())
