@@ -832,7 +832,11 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
   for (int w = 0; w < 8; ++w) L += wsum[16 * w + c];
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const float lse = L > 0.f ? (st.m_run + log2f(L)) * kLn2 : -INFINITY;
-  const int64_t hrow = (int64_t)qi * H + head;
+  // the output row is recomputed here from an opaque copy of the head index: otherwise the
+  // compiler keeps the prologue's 64-bit query-row products live across the chunk loop
+  int head_o = head;
+  asm volatile("" : "+v"(head_o));
+  const int64_t hrow = (int64_t)qi * H + head_o;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     const int d = 64 * wave + 16 * dt + 4 * g;
@@ -845,13 +849,13 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
         *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + hrow * kD + d) = acc;
       }
     } else {
-      const int64_t pi = ((int64_t)qi * a.n_split + s) * H + head;
+      const int64_t pi = ((int64_t)qi * a.n_split + s) * H + head_o;
       *reinterpret_cast<f32x4*>(a.part_o + pi * kD + d) = acc;
     }
   }
   if (wave == 0 && g == 0) {
     if (a.n_split == 1) a.lse[hrow] = lse;
-    else a.part_lse[((int64_t)qi * a.n_split + s) * H + head] = lse;
+    else a.part_lse[((int64_t)qi * a.n_split + s) * H + head_o] = lse;
   }
 }
 
