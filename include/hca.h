@@ -354,6 +354,26 @@ int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_hea
                        const int64_t* q_pos, const int64_t* q_lo, float scale, void* o,
                        int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * grouped_out_proj — the grouped output projection after core attention
+ * (CSA paragraph: core attention is followed by a grouped output projection
+ * to manage the computational cost). The heads are split into `groups`
+ * equal groups of consecutive heads; group g's concatenated head outputs are
+ * the k_group = (h / groups) * D values x[r, g*k_group .. (g+1)*k_group - 1]
+ * (the attention output [n, h, D] is such an x with ldx = h * D), and
+ *   y[r, g*n_group + c] = sum_k x[r, g*k_group + k] * w[g, c, k]
+ * with w bf16 [groups, n_group, k_group] (out-features by in-features, per
+ * group, contiguous), float32 accumulation, y of y_dtype (HCA_BF16, rounded
+ * to nearest even, or HCA_F32) with row stride ldy. x: bf16, row stride ldx
+ * (elements). The result is deterministic (fixed summation order).
+ * Requires n >= 0, n <= 2^22, 1 <= groups <= 65535, k_group a multiple of 32,
+ * n_group a multiple of 16, ldx >= groups * k_group and ldx a multiple of 8,
+ * ldy >= groups * n_group, x and w 16-byte aligned, y aligned to its element.
+ */
+int grouped_out_proj(const void* x, int64_t n, int64_t ldx, int32_t groups, int32_t k_group,
+                     const void* w, int32_t n_group, void* y, int32_t y_dtype, int64_t ldy,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ __all__ = [
     "F32", "BF16", "FP8_E4M3", "MXFP4", "LAYOUT_F32", "LAYOUT_BF16", "LAYOUT_SPLIT", "LAYOUT_MXFP4",
     "HcaError", "Store", "DecodeLayer", "abi_version", "csa_compress", "hca_compress", "decode_append",
     "lightning_index_topk_workspace", "lightning_index_topk", "mqa_attn_workspace",
-    "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "library_path",
+    "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "grouped_out_proj", "library_path",
 ]
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
@@ -69,6 +69,7 @@ _last_error = _sig("hca_last_error", ctypes.c_char_p, [])
 _compress_args = [_P, _I32, _I64, _I64, _I64, _P, _I64, _I64, _P]
 _csa_compress = _sig("csa_compress", ctypes.c_int, _compress_args + [_I32, _I32, _I64, _I64, _SP, _I64, _P])
 _hca_compress = _sig("hca_compress", ctypes.c_int, _compress_args + [_I32, _I64, _I64, _SP, _I64, _P])
+_proj = _sig("grouped_out_proj", ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _I32, _P, _I32, _I64, _P])
 _decode_append = _sig("decode_append", ctypes.c_int,
                       [ctypes.POINTER(_DecodeLayerC), _I32, _P, _P, _P, _P, _P, _P, _P])
 _index_ws = _sig("lightning_index_topk_workspace", _SZ, [_I32, _I64, _I32])
@@ -203,6 +204,14 @@ def decode_append(layer, pos, x, z_csa, z_hca, k_idx=None, z_idx=None, stream=No
     k_idx / z_idx bf16 [B, d_idx] (with indexer keys)."""
     _check(_decode_append(layer.c(), pos.shape[0], _ptr(pos), _ptr(x), _ptr(z_csa), _ptr(z_hca), _ptr(k_idx),
                           _ptr(z_idx), _stream(stream)))
+
+
+def grouped_out_proj(x, w, y, stream=None):
+    """x: bf16 [n, G * K] (e.g. the attention output [n, h, D] viewed as [n, h * D]); w: bf16
+    [G, N, K]; y: bf16 or float32 [n, G * N] (row strides from the tensors)."""
+    G, N, K = w.shape
+    _check(_proj(_ptr(x), x.shape[0], x.stride(0), G, K, _ptr(w), N, _ptr(y), _dtype_code(y), y.stride(0),
+                 _stream(stream)))
 
 
 def lightning_index_topk_workspace(nq, max_visible, k):

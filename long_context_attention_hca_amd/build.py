@@ -9,7 +9,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = ["compress.hip", "indexer.hip", "attention.hip", "api.cpp"]
+SOURCES = ["compress.hip", "indexer.hip", "attention.hip", "proj.hip", "api.cpp"]
 LIB = os.path.join(PKG, "libhca.so")
 
 FLAGS = [

@@ -287,6 +287,34 @@ extern "C" {
 
 HCA_EXPORT int hca_abi_version(void) { return HCA_ABI_VERSION; }
 
+HCA_EXPORT int grouped_out_proj(const void* x, int64_t n, int64_t ldx, int32_t groups, int32_t k_group, const void* w,
+                                int32_t n_group, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  const char* fn = "grouped_out_proj";
+  if (!x || !w || !y) return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
+  if (n < 0 || n > ((int64_t)1 << 22)) return fail(HCA_ERR_INVALID_ARG, fn, "n out of range");
+  if (groups < 1 || groups > 65535) return fail(HCA_ERR_INVALID_ARG, fn, "groups out of range");
+  if (k_group < 32 || k_group % 32) return fail(HCA_ERR_UNSUPPORTED, fn, "k_group must be a multiple of 32");
+  if (n_group < 16 || n_group % 16) return fail(HCA_ERR_UNSUPPORTED, fn, "n_group must be a multiple of 16");
+  if (y_dtype != HCA_BF16 && y_dtype != HCA_F32) return fail(HCA_ERR_UNSUPPORTED, fn, "y dtype must be BF16 or F32");
+  if (ldx < (int64_t)groups * k_group || ldx % 8) return fail(HCA_ERR_INVALID_ARG, fn, "bad ldx");
+  if (ldy < (int64_t)groups * n_group) return fail(HCA_ERR_INVALID_ARG, fn, "bad ldy");
+  if (!aligned16(x) || !aligned16(w)) return fail(HCA_ERR_INVALID_ARG, fn, "x/w not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(y) % (y_dtype == HCA_F32 ? 4 : 2)) return fail(HCA_ERR_INVALID_ARG, fn, "y misaligned");
+  if (n == 0) return HCA_OK;
+  hca::ProjArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.ldx = ldx;
+  a.w = static_cast<const uint16_t*>(w);
+  a.y = y;
+  a.ldy = ldy;
+  a.n = n;
+  a.G = groups;
+  a.Kg = k_group;
+  a.Ng = n_group;
+  a.y_dtype = y_dtype;
+  return launched(fn, hca::launch_proj(a, static_cast<hipStream_t>(stream)));
+}
+
 HCA_EXPORT int decode_append(const hca_decode_layer* layer, int32_t B, const int64_t* pos, const void* x,
                              const void* z_csa, const void* z_hca, const void* k_idx, const void* z_idx,
                              void* stream) {

@@ -87,6 +87,19 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t stream);
 
+// Grouped output projection: x [n, G Kg] (row stride ldx), w [G, Ng, Kg] bf16, y [n, G Ng] (row
+// stride ldy) of y_dtype (HCA_F32 / HCA_BF16).
+struct ProjArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  const uint16_t* w;
+  void* y;
+  int64_t ldy;
+  int64_t n;
+  int G, Kg, Ng, y_dtype;
+};
+hipError_t launch_proj(const ProjArgs& a, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   int q_dtype;

@@ -215,3 +215,25 @@ def test_split_index_calls_need_the_whole_workspace(phase):
     assert call(one) == -3 and "all nq queries" in hca._last_error().decode()
     assert call(four) in (0, -4)
     assert index_call(wsb=one) in (0, -4)            # the one-call version batches instead
+
+
+def proj_call(**kw):
+    a = dict(x=P[0], n=4, ldx=32768, G=8, K=4096, w=P[1], N=1024, y=P[2], ydt=1, ldy=8192)
+    a.update(kw)
+    return hca._proj(a["x"], a["n"], a["ldx"], a["G"], a["K"], a["w"], a["N"], a["y"], a["ydt"], a["ldy"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(x=None), -1, "NULL"), (dict(n=-1), -1, "n out of range"), (dict(G=0), -1, "groups"),
+    (dict(K=100), -2, "k_group"), (dict(N=40), -2, "n_group"), (dict(ydt=3), -2, "dtype"),
+    (dict(ldx=1000), -1, "ldx"), (dict(ldx=32772), -1, "ldx"), (dict(ldy=100), -1, "ldy"),
+    (dict(w=ctypes.c_void_p(0x100008)), -1, "aligned"),
+])
+def test_grouped_projection_rejects_bad_arguments(kw, status, msg):
+    assert proj_call(**kw) == status
+    assert msg in hca._last_error().decode()
+
+
+def test_grouped_projection_valid_call_reaches_launch():
+    assert proj_call() in (0, -4)
+    assert proj_call(n=0) == 0
