@@ -451,6 +451,48 @@ def main():
             "unmasked_query_tokens_per_s": round(nqp / (res["unmasked"] * 1e-3))}
         del kp, ks, qp, qs, cs_p, hs_p, win_p, qv, wsp
 
+        log("grouped output projection")
+        # the decode step's attention output (batch 4, 64 heads x 512) through 8 groups of 8 heads
+        # into 1024 features per group (bf16 weights, 64 MB per copy, 5 copies rotated so that
+        # the Infinity Cache cannot serve them), and an 8192-row prefill chunk
+        from long_context_attention_hca_amd import grouped_out_proj
+        Gp, Kg, Ng = 8, 8 * D, 1024
+        gw = synth.generator(1020, dev)
+        wcopies = [synth.normal(gw, (Gp, Ng, Kg), std=Kg ** -0.5).to(torch.bfloat16) for _ in range(5)]
+        xo = synth.normal(gw, (B, H * D)).to(torch.bfloat16)
+        yo = torch.empty(B, Gp * Ng, dtype=torch.bfloat16, device=dev)
+        for wc in wcopies:
+            grouped_out_proj(xo, wc, yo)
+        torch.cuda.synchronize()
+        n_rep = 40
+        e[0].record()
+        for i in range(n_rep):
+            grouped_out_proj(xo, wcopies[i % 5], yo)
+        e[1].record()
+        torch.cuda.synchronize()
+        t_dec = e[0].elapsed_time(e[1]) / n_rep
+        by_dec = Gp * Ng * Kg * 2 + B * H * D * 2 + B * Gp * Ng * 2
+        n_pf = 8192
+        xp_ = synth.normal(gw, (n_pf, H * D)).to(torch.bfloat16)
+        yp_ = torch.empty(n_pf, Gp * Ng, dtype=torch.bfloat16, device=dev)
+        grouped_out_proj(xp_, wcopies[0], yp_)
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(5):
+            grouped_out_proj(xp_, wcopies[0], yp_)
+        e[1].record()
+        torch.cuda.synchronize()
+        t_pf = e[0].elapsed_time(e[1]) / 5
+        fl_pf = 2.0 * n_pf * Gp * Ng * Kg
+        comp["grouped_out_proj"] = {
+            "workload": f"8 groups of 8 heads x {D} -> {Ng} features per group, bf16 weights (64 MB); decode: "
+                        f"{B} rows, 5 rotating weight copies; prefill: {n_pf} rows",
+            "decode_us": round(t_dec * 1e3, 2), "decode_gbs": round(by_dec / (t_dec * 1e-3) / 1e9, 1),
+            "decode_frac_hbm": round(by_dec / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+            "prefill_ms": round(t_pf, 4), "prefill_tflops": round(fl_pf / (t_pf * 1e-3) / 1e12, 1),
+            "prefill_frac_mfma_bf16": round(fl_pf / (t_pf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 3)}
+        del wcopies, xo, yo, xp_, yp_
+
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle on the host cores")
