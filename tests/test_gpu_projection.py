@@ -31,7 +31,8 @@ def _f64(t):
 @pytest.mark.parametrize("n,G,K,N,extra_x,extra_y,ydt", [
     (4, 8, 4096, 1024, 0, 0, "bf16"),        # decode: o [4, 64, 512] -> 8 groups of 4096 -> 1024
     (4, 8, 4096, 1024, 0, 0, "f32"),
-    (300, 4, 512, 256, 64, 16, "bf16"),      # many rows (ragged last 64-row block), 4 x 4 tiles per wave
+    (300, 4, 512, 256, 64, 16, "bf16"),      # many rows (ragged last 128-row block): LDS-tiled blocks
+    (270, 2, 64, 192, 0, 0, "f32"),          # many rows, features not a multiple of 128: 4 x 4 tiles per wave
     (37, 3, 96, 48, 8, 3, "f32"),            # odd widths: K tail steps, one 16-wide tile per wave
     (1, 1, 4096, 16, 0, 0, "f32"),           # one tile: K split over 8 waves
 ])
