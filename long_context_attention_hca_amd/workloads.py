@@ -279,10 +279,16 @@ def compress_1m(case, out_csa=None, out_hca=None, stream=None):
     return out_csa, out_hca
 
 
-def chunked_prefill(case, ws=None):
+def chunked_prefill(case, ws=None, window="split"):
     """Chunked prefill for S sequences: compress each chunk into the sequence's
     caches (CSA with a w-m row halo from the prefix), index every chunk query,
-    then CSA and HCA attention for all queries."""
+    then CSA and HCA attention for all queries.
+
+    window="split": the window rows (the last W prefix rows and the chunk) are
+    first written into a split-layout store, the layout the caches and the
+    decode window use, by csa_compress with m = w = 1 (a softmax over one
+    position is exactly 1, so each entry is its raw row, encoded).
+    window="bf16": the attention calls read the raw bf16 rows directly."""
     p, t = case.params, case.t
     dev = t["raw"].device
     ws = ws or Workspace(dev)
@@ -307,9 +313,35 @@ def chunked_prefill(case, ws=None):
     max_h = max((P + chunk) // mp for P in p["prefixes"])
     idx = index_topk(t["q_idx"], t["w_idx"], t["k_idx"], crb, t["q_seq"], t["q_pos"], max_c, m, k, ws,
                      q_idx_scale=t["q_idx_scale"], k_idx_scale=t["k_idx_scale"])
-    win = Store.dense(t["raw"], dn, dr)
+    if window == "split":
+        win = prefill_window(case, ws)
+    elif window == "bf16":
+        win = Store.dense(t["raw"], dn, dr)
+    else:
+        raise ValueError(f"window layout {window!r}")
     scale = 1.0 / math.sqrt(dn + dr)
     q = t["q"].view(torch.bfloat16)
     o_c, l_c = csa_attn(q, csa, crb, idx, win, wrb, wp0, W, t["q_seq"], t["q_pos"], scale, ws)
     o_h, l_h = hca_attn(q, hca, hrb, mp, max_h, win, wrb, wp0, W, t["q_seq"], t["q_pos"], scale, ws)
-    return dict(csa=csa, hca=hca, idx=idx, o_csa=o_c, lse_csa=l_c, o_hca=o_h, lse_hca=l_h)
+    return dict(csa=csa, hca=hca, win=win, idx=idx, o_csa=o_c, lse_csa=l_c, o_hca=o_h, lse_hca=l_h)
+
+
+def prefill_window(case, ws, stream=None):
+    """The chunked-prefill window rows of every sequence (positions P - W .. P + chunk - 1, the
+    rows of the raw input) written into a split-layout store by csa_compress with m = w = 1:
+    zero logits and bias, so every entry is its own raw row, encoded as the caches are."""
+    p, t = case.params, case.t
+    dev = t["raw"].device
+    S, W, chunk = p["S"], p["W"], p["chunk"]
+    dn, dr = p["d_nope"], p["d_rope"]
+    rows = W + chunk
+    raw = t["raw"].view(S, rows, -1)
+    win = Store.split(ws.get("win_nope", S * rows * dn).view(torch.uint8)[:S * rows * dn].view(S * rows, dn),
+                      ws.get("win_scale", S * rows * 4)[:S * rows * 4].view(torch.float32),
+                      ws.get("win_rope", S * rows * dr * 2)[:S * rows * dr * 2].view(torch.int16).view(S * rows, dr))
+    zero_logits = torch.zeros(rows, 1, dtype=raw.dtype, device=dev)
+    zero_bias = torch.zeros(1, dn + dr, dtype=torch.float32, device=dev)
+    for b, P in enumerate(p["prefixes"]):
+        csa_compress(raw[b], P - W, zero_logits, zero_bias, 1, 1, P - W, rows, win, out_row0=b * rows,
+                     scalar_logits=True, stream=stream)
+    return win

@@ -121,9 +121,12 @@ def decode_1m_query(p, a, b):
     return dict(idx=idx, scores=s, o_csa=o_c, lse_csa=l_c, o_hca=o_h, lse_hca=l_h)
 
 
-def prefill_query(p, a, qi, chunk_csa, chunk_hca):
+def prefill_query(p, a, qi, chunk_csa, chunk_hca, split_window=False):
     """One chunked-prefill query. chunk_csa/chunk_hca: callables (b) -> the oracle's own decoded
-    entries of sequence b's chunk (compressed from the raw chunk rows)."""
+    entries of sequence b's chunk (compressed from the raw chunk rows). split_window: the window
+    rows are held in the cache layout (DeepSeek-V4 page, efficiency section: FP8 for the
+    non-RoPE dims, BF16 for the RoPE dims), so attention sees each raw row after the oracle's
+    own split encoding and decoding; otherwise it sees the raw bf16 rows."""
     m, mp, W, k, chunk = p["m"], p["m_prime"], p["W"], p["topk"], p["chunk"]
     dn, dr = p["d_nope"], p["d_rope"]
     b = int(a["q_seq"][qi])
@@ -138,6 +141,8 @@ def prefill_query(p, a, qi, chunk_csa, chunk_hca):
     hca_ent = np.concatenate([split_rows(a, "hca", np.arange(hrb, hrb + P // mp)), chunk_hca(b)])
     rows = W + chunk
     raw = _f64(a["raw"][b * rows:(b + 1) * rows], "bf16")
+    if split_window:
+        raw = compress.decode(compress.encode(raw, "split", dn, dr), "split")
     win = lambda pos: raw[np.asarray(pos) - (P - W)]
     scale = 1.0 / np.sqrt(dn + dr)
     q = _f64(a["q"][qi], "bf16")

@@ -144,17 +144,29 @@ def test_compression_split(W, L):
         check_split_entries(np_(st.data)[js], np_(st.scale)[js], np_(st.rope)[js], ys, dn, f"{name} entries", ya)
 
 
-@pytest.mark.parametrize("prefixes,chunk,nsample", [((4096, 8192, 16384), 512, 24), ((32768, 131072, 262144), 8192, 6)])
-def test_chunked_prefill(W, prefixes, chunk, nsample):
-    _say(f"prefill prefixes={prefixes} chunk={chunk}")
+@pytest.mark.parametrize("prefixes,chunk,nsample,window", [((4096, 8192, 16384), 512, 24, "bf16"),
+                                                            ((4096, 8192, 16384), 512, 24, "split"),
+                                                            ((32768, 131072, 262144), 8192, 6, "split")])
+def test_chunked_prefill(W, prefixes, chunk, nsample, window):
+    _say(f"prefill prefixes={prefixes} chunk={chunk} window={window}")
     c = synth.chunked_prefill(seed=1005, prefixes=prefixes, chunk=chunk, device="cuda")
     a_in = case_numpy(c, keys={"raw", "logits_csa", "logits_hca", "bias_csa", "bias_hca", "csa_nope", "csa_scale",
                                "csa_rope", "hca_nope", "hca_scale", "hca_rope", "k_idx", "k_idx_scale", "q_seq",
                                "q_pos"})
-    got = W.chunked_prefill(c)
+    got = W.chunked_prefill(c, window=window)
     torch.cuda.synchronize()
     p = c.params
     S = p["S"]
+    if window == "split":
+        # window rows: each entry is its raw row (softmax over one position), so the store must
+        # equal the oracle's own split encoding of the raw rows bit for bit
+        rows = p["W"] + chunk
+        ref = OC.encode(OC.decode({"data": a_in["raw"]}, "bf16"), "split", p["d_nope"], p["d_rope"])
+        st = got["win"]
+        assert np.array_equal(np_(st.data), ref["nope"]), "window FP8 codes"
+        assert np.array_equal(np_(st.scale), ref["scale"]), "window scales"
+        assert np.array_equal(np_(st.rope).view(np.uint16), ref["rope"]), "window RoPE bits"
+        assert np_(st.data).shape[0] == S * rows
     rng = np.random.default_rng(1)
     picks = []
     for b in range(S):
@@ -183,7 +195,8 @@ def test_chunked_prefill(W, prefixes, chunk, nsample):
     o_c, l_c = np_(got["o_csa"][picks].float()), np_(got["lse_csa"][picks])
     o_h, l_h = np_(got["o_hca"][picks].float()), np_(got["lse_hca"][picks])
     for n, qi in enumerate(picks):
-        r = OP.prefill_query(p, a, qi, lambda b: chunk_ent[b][1], lambda b: chunk_ent[b][3])
+        r = OP.prefill_query(p, a, qi, lambda b: chunk_ent[b][1], lambda b: chunk_ent[b][3],
+                             split_window=window == "split")
         check_idx(idx[qi], r["idx"], f"top-k query {qi}")
         check_attention(o_c[n], l_c[n], r["o_csa"], r["lse_csa"], "low", f"csa attention query {qi}")
         check_attention(o_h[n], l_h[n], r["o_hca"], r["lse_hca"], "low", f"hca attention query {qi}")
