@@ -493,6 +493,81 @@ def main():
             "prefill_frac_mfma_bf16": round(fl_pf / (t_pf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 3)}
         del wcopies, xo, yo, xp_, yp_
 
+        log("chunked prefill")
+        # three sequences with prefixes of 32K, 128K and 256K tokens, each appending a chunk of
+        # 8192 query tokens: chunk compression, index (MXFP4 scores over every visible entry,
+        # top-1024), CSA and HCA attention for all 24,576 queries
+        cpf = synth.chunked_prefill(seed=1005, device=dev)
+        pp, tp = cpf.params, cpf.t
+        wsf = W.Workspace(dev)
+        nq_pf = tp["q_pos"].shape[0]
+        m_, mp_, W_pf, k_pf, HI_pf = pp["m"], pp["m_prime"], pp["W"], pp["topk"], pp["n_idx_heads"]
+        crb_pf = torch.tensor(pp["csa_row_begin"], dtype=torch.int64, device=dev)
+        hrb_pf = torch.tensor(pp["hca_row_begin"], dtype=torch.int64, device=dev)
+        wrb_pf = torch.tensor(pp["win_row_begin"], dtype=torch.int64, device=dev)
+        wp0_pf = torch.tensor(pp["win_pos0"], dtype=torch.int64, device=dev)
+        max_c_pf = max((P + pp["chunk"]) // m_ for P in pp["prefixes"])
+        max_h_pf = max((P + pp["chunk"]) // mp_ for P in pp["prefixes"])
+        # compresses the chunks into the caches and writes the split-layout window store that the
+        # attention calls below read
+        win_pf = W.chunked_prefill(cpf, wsf)["win"]
+        torch.cuda.synchronize()
+
+        def timed(fn, reps=3):
+            fn()
+            torch.cuda.synchronize()
+            e[0].record()
+            for _ in range(reps):
+                fn()
+            e[1].record()
+            torch.cuda.synchronize()
+            return e[0].elapsed_time(e[1]) / reps
+
+        def idx_call(phase):
+            return W.index_topk(tp["q_idx"], tp["w_idx"], tp["k_idx"], crb_pf, tp["q_seq"], tp["q_pos"], max_c_pf,
+                                m_, k_pf, wsf, q_idx_scale=tp["q_idx_scale"], k_idx_scale=tp["k_idx_scale"],
+                                phase=phase)
+
+        # the scoring phase alone needs the whole-batch workspace (about 31 GiB); once it has grown,
+        # every call below indexes all queries in one pass
+        t_sc = timed(lambda: idx_call("scores"))
+        idx_pf = idx_call("both")
+        t_ix = timed(lambda: idx_call("both"))
+        t_all = timed(lambda: W.chunked_prefill(cpf, wsf))
+        q_pf = tp["q"].view(torch.bfloat16)
+        sc_pf = 1.0 / math.sqrt(pp["d_nope"] + pp["d_rope"])
+        cs_pf = W.split_store(tp, "csa")
+        hs_pf = W.split_store(tp, "hca")
+        t_ca = timed(lambda: W.csa_attn(q_pf, cs_pf, crb_pf, idx_pf, win_pf, wrb_pf, wp0_pf, W_pf, tp["q_seq"],
+                                        tp["q_pos"], sc_pf, wsf))
+        t_ha = timed(lambda: W.hca_attn(q_pf, hs_pf, hrb_pf, mp_, max_h_pf, win_pf, wrb_pf, wp0_pf, W_pf,
+                                        tp["q_seq"], tp["q_pos"], sc_pf, wsf))
+        # flops from the visibility rules: n_vis = floor((t+1)/m) CSA entries scored, min(k, n_vis)
+        # selected plus min(W, t+1) window positions; floor((t+1)/m') HCA entries plus the window;
+        # per head and attended entry 2*D for QK^T and 2*D for PV
+        tq = tp["q_pos"].cpu().double()
+        nv_c = torch.clamp(torch.floor((tq + 1) / m_), max=max_c_pf)
+        nv_h = torch.floor((tq + 1) / mp_)
+        n_w = torch.clamp(tq + 1, max=W_pf)
+        Dpf, Hpf = pp["D"], pp["heads"]
+        fl_sc = float(nv_c.sum()) * HI_pf * pp["d_idx"] * 2
+        fl_ca = float((torch.clamp(nv_c, max=k_pf) + n_w).sum()) * Hpf * Dpf * 4
+        fl_ha = float((nv_h + n_w).sum()) * Hpf * Dpf * 4
+        comp["chunked_prefill"] = {
+            "workload": f"3 sequences with prefixes {tuple(pp['prefixes'])} each appending {pp['chunk']} query tokens "
+                        f"({nq_pf} queries): chunk compression and window rows into split stores, MXFP4 index "
+                        f"(k={k_pf}), CSA + HCA attention, {Hpf} heads",
+            "total_ms": round(t_all, 3), "query_tokens_per_s": round(nq_pf / (t_all * 1e-3)),
+            "index_ms": round(t_ix, 3),
+            "index_scores_ms": round(t_sc, 3), "index_scores_tflops": round(fl_sc / (t_sc * 1e-3) / 1e12, 1),
+            "index_scores_frac_mfma_mxfp4": round(fl_sc / (t_sc * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4),
+            "index_select_ms": round(t_ix - t_sc, 3),
+            "csa_attn_ms": round(t_ca, 3), "csa_attn_tflops": round(fl_ca / (t_ca * 1e-3) / 1e12, 1),
+            "csa_attn_frac_mfma_bf16": round(fl_ca / (t_ca * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "hca_attn_ms": round(t_ha, 3), "hca_attn_tflops": round(fl_ha / (t_ha * 1e-3) / 1e12, 1),
+            "hca_attn_frac_mfma_bf16": round(fl_ha / (t_ha * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del cpf, wsf, idx_pf, q_pf
+
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle on the host cores")
