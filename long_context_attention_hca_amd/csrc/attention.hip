@@ -860,6 +860,416 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
 }
 
 // ---------------------------------------------------------------------------------------
+// Row-owning FP8 kernel for calls with many queries (prefill). block = (query, split), 4 waves
+// (one per SIMD) for H = 64; wave w owns heads 16w .. 16w+15 over every entry of the split and
+// all 512 dims, so one staged chunk serves all 64 heads (the kernel above stages it once per
+// group of 16 heads, in four blocks).
+//  * staging through registers: wave w brings entries 32w .. 32w+31 of the next chunk (18,944
+//    LDS bytes) with 19 lane-linear 16-byte loads issued a chunk ahead, and writes them to LDS
+//    at the end of the current chunk; invalid rows are written as zeros;
+//  * S^T = K Q^T as above (scaled FP8 MFMA for the 448 dims, bf16 MFMA for RoPE) over the
+//    chunk's 8 tiles of 16 entries. Tile 2kk + u row r holds entry 32kk + 8(r/4) + 4u + r%4, so
+//    a lane's accumulators of tiles 2kk and 2kk + 1 are entries 32kk + 8g .. 32kk + 8g + 7 of
+//    its head: the B operand of the PV MFMA over that 32-entry step, without going through LDS;
+//  * the online softmax is per head inside the wave (two cross-lane maxima), lazy rescale;
+//  * O^T (512 dims x 16 heads: 28 FP8-dim tiles and 4 RoPE tiles) += V^T P^T, V^T from the
+//    same transpose reads as above.
+constexpr int kRowsWaves = 4;
+constexpr int kRowsEnt = kCh / kRowsWaves;                     // 32 entries staged per wave
+constexpr int kRowsBytes = kRowsEnt * kRowF8;                  // 18,944 bytes
+constexpr int kRowsLoads = (kRowsBytes + 1023) / 1024;         // 19 loads of 16 bytes a lane
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct RowsSrc {
+  uint64_t src;    // lane e < 32: FP8-row address of entry e; lane 32 + e: RoPE-row address - 448
+  float esc;       // lane e < 32: entry scale (load left in flight)
+  uint32_t vmask;  // valid entries
+};
+
+
+// Slot value of list position base + (lane & 31) (CSA); positions past the top-k list are
+// clamped to a valid slot whose value is not used.
+template <bool kSparse>
+__device__ __forceinline__ int32_t rows_slot(const AttnArgs& a, int qi, int64_t base, int lane) {
+  if (!kSparse) return 0;
+  const int64_t r = min<int64_t>(base + (lane & 31), (int64_t)a.k - 1);
+  return a.idx[(int64_t)qi * a.k + r];
+}
+
+template <bool kSparse>
+__device__ __forceinline__ RowsSrc rows_src(const AttnArgs& a, const QueryCtx& ctx, int64_t base, int64_t hi,
+                                            int32_t slot, int lane) {
+  RowsSrc w;
+  const int64_t r = base + (lane & 31);
+  const bool win = r >= ctx.n_c;
+  int64_t row = -1;
+  if (r < hi) {
+    if (!win) {
+      const int64_t j = kSparse ? (int64_t)slot : r;
+      const int64_t cr = ctx.cache_rb + j;
+      row = (j >= 0 && cr >= 0 && cr < a.cache.n_rows) ? cr : -1;
+    } else if (r < ctx.n_c + ctx.n_w) {
+      const int64_t pos = ctx.t - ctx.n_w + 1 + (r - ctx.n_c);
+      const int64_t wr = ctx.win_rb + (pos - ctx.win_p0);
+      row = (wr >= 0 && wr < a.win.n_rows) ? wr : -1;
+    }
+  }
+  const uint64_t data = win ? reinterpret_cast<uint64_t>(a.win.data) : reinterpret_cast<uint64_t>(a.cache.data);
+  const uint64_t rope = win ? reinterpret_cast<uint64_t>(a.win.rope) : reinterpret_cast<uint64_t>(a.cache.rope);
+  const int64_t rs = win ? a.win.row_stride : a.cache.row_stride;
+  const int64_t ps = win ? a.win.rope_stride : a.cache.rope_stride;
+  const float* scale = win ? a.win.scale : a.cache.scale;
+  const int64_t rr = row >= 0 ? row : 0;  // invalid entries are never loaded
+  w.src = lane < 32 ? data + (uint64_t)(rr * rs) : rope + (uint64_t)(rr * ps * 2) - kNope;
+  w.esc = (lane < 32 && row >= 0) ? scale[row] : 0.f;
+  w.vmask = (uint32_t)__ballot(lane < 32 && row >= 0);
+  return w;
+}
+
+// Loads I0 .. I0 + kN - 1 of a wave's 32 rows: LDS byte b = 1024 i + 16 lane of the wave's
+// region is entry b / 592, byte b % 592 (FP8 bytes, then RoPE bytes, then 16 pad bytes). Lanes on
+// padding, past the 32 rows or on an invalid row load nothing and hold zeros.
+// The per-lane offsets depend on the lane only; they are derived from an opaque copy of the lane
+// index so that the compiler recomputes them at each call instead of keeping all of them live
+// across the chunk loop.
+template <int I0, int kN>
+__device__ __forceinline__ void rows_load(const RowsSrc& w, uint4 (&v)[kN], int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+#pragma unroll
+  for (int j = 0; j < kN; ++j) {
+    const int b = 1024 * (I0 + j) + 16 * ln;
+    const int e = b / kRowF8, o = b - e * kRowF8;
+    const int sl = (o < kNope ? e : 32 + e) & 63;
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)w.src, sl, 64);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(w.src >> 32), sl, 64);
+    const uint64_t src = (((uint64_t)hi << 32) | lo) + (uint64_t)o;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    // a global (not generic) load: a flat load would also count against the LDS wait counter,
+    // so every LDS wait of the chunk would wait for these loads too
+    if (e < kRowsEnt && o < kNope + 2 * kRope && ((w.vmask >> (e & 31)) & 1))
+      x = __builtin_bit_cast(uint4, *reinterpret_cast<const __attribute__((address_space(1))) u32x4_t*>(src));
+    v[j] = x;
+  }
+}
+
+template <int I0, int kN>
+__device__ __forceinline__ void rows_store(const uint4 (&v)[kN], uint8_t* dst, int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+#pragma unroll
+  for (int j = 0; j < kN; ++j) {
+    const int b = 1024 * (I0 + j) + 16 * ln;
+    if (b < kRowsBytes) *reinterpret_cast<uint4*>(dst + b) = v[j];
+  }
+}
+
+constexpr int kRowsHalfA = 10, kRowsHalfB = kRowsLoads - kRowsHalfA;
+
+struct RowsState {
+  f32x4 O[32];
+  float m_run, l_part;
+};
+
+// Scores and softmax of one chunk in buf (scales sc, validity masks vm): O^T is rescaled if the
+// reference maximum moved, and the PV B operands of the four 32-entry steps are returned packed:
+// P times the entry scale (bs, for the FP8 dims) and P (br, for the RoPE dims).
+__device__ __forceinline__ void rows_scores(const uint8_t* buf, const float* sc, const uint32_t* vm, const F8Query& q,
+                                            RowsState& st, float sl2, int lane, uint4 (&bs)[4], uint4 (&br)[4]) {
+  asm volatile("" : "+v"(lane));  // lane-only addresses are recomputed per chunk, not kept live
+  const int g = lane >> 4, c = lane & 15;
+  const uint4 vmk = *reinterpret_cast<const uint4*>(vm);
+  const uint32_t vmw[4] = {vmk.x, vmk.y, vmk.z, vmk.w};
+  float sv[8][4];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int kk = t >> 1, u = t & 1;
+    const int ent = 32 * kk + 8 * (c >> 2) + 4 * u + (c & 3);  // entry of A row c
+    const uint8_t* rowp = buf + ent * kRowF8 + 16 * g;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, sr = s0;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(rowp + 128 * ks);
+      uint4 x1 = make_uint4(0, 0, 0, 0);
+      if (ks < 3) x1 = *reinterpret_cast<const uint4*>(rowp + 128 * ks + 64);
+      const i32x8 A = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.qh[ks], s0, 0, 0, 0, 127, 0,
+                                                             (int)((q.sh >> (8 * ks)) & 255u));
+      s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.ql[ks], s1, 0, 0, 0, 127, 0,
+                                                             (int)((q.sl >> (8 * ks)) & 255u));
+    }
+    const uint8_t* ropep = buf + ent * kRowF8 + kNope + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ropep + 64 * ks));
+      sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q.qr[ks], sr, 0, 0, 0);
+    }
+    // lane (g, c): entries 32kk + 8g + 4u + i of head c
+    const int e0 = 32 * kk + 8 * g + 4 * u;
+    const float4 e4 = *reinterpret_cast<const float4*>(sc + e0);
+    const float esc[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + i;
+      const float v = fmaf(esc[i], s0[i] + s1[i], sr[i]);
+      sv[t][i] = ((vmw[e >> 5] >> (e & 31)) & 1) ? v * sl2 : -INFINITY;
+      cmax = fmaxf(cmax, sv[t][i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one tile's operands live at a time
+  }
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  // lazy rescaling: the reference max moves only when a score exceeds it by more than 2^8
+  const bool grow = cmax > st.m_run + 8.f;
+  const float m_ref = grow ? cmax : st.m_run;
+  const bool none = m_ref == -INFINITY;
+  const float corr = grow ? exp2f(st.m_run - cmax) : 1.f;
+  float psum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[t][i] = none ? 0.f : exp2f(sv[t][i] - m_ref);
+      psum += sv[t][i];
+    }
+  st.l_part = st.l_part * corr + psum;
+  st.m_run = m_ref;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const float* p0 = sv[2 * kk];
+    const float* p1 = sv[2 * kk + 1];
+    const float4 x0 = *reinterpret_cast<const float4*>(sc + 32 * kk + 8 * g);
+    const float4 x1 = *reinterpret_cast<const float4*>(sc + 32 * kk + 8 * g + 4);
+    bs[kk].x = pack_bf16x2(p0[0] * x0.x, p0[1] * x0.y); bs[kk].y = pack_bf16x2(p0[2] * x0.z, p0[3] * x0.w);
+    bs[kk].z = pack_bf16x2(p1[0] * x1.x, p1[1] * x1.y); bs[kk].w = pack_bf16x2(p1[2] * x1.z, p1[3] * x1.w);
+    br[kk].x = pack_bf16x2(p0[0], p0[1]); br[kk].y = pack_bf16x2(p0[2], p0[3]);
+    br[kk].z = pack_bf16x2(p1[0], p1[1]); br[kk].w = pack_bf16x2(p1[2], p1[3]);
+  }
+  if (__ballot(grow)) {
+#pragma unroll
+    for (int d = 0; d < 32; ++d) st.O[d] *= corr;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// O^T += V^T P^T over the chunk's four 32-entry steps.
+__device__ __forceinline__ void rows_pv(const uint8_t* buf, const uint4 (&bs)[4], const uint4 (&br)[4], RowsState& st,
+                                        int lane) {
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 4, c = lane & 15;
+  const int r = c >> 1, hsel = c & 1, rs = c >> 2, qd = c & 3;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const bf16x8 Bs = __builtin_bit_cast(bf16x8, bs[kk]), Br = __builtin_bit_cast(bf16x8, br[kk]);
+    const uint8_t* vp = buf + (32 * kk + 8 * g + r) * kRowF8 + 8 * hsel;
+#pragma unroll
+    for (int d = 0; d < 28; ++d) {
+      const i32x2_t tv = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * d));
+      st.O[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8((uint32_t)tv[0], (uint32_t)tv[1]), Bs,
+                                                         st.O[d], 0, 0, 0);
+      if ((d & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // eight tiles' reads in flight at most
+    }
+    const uint8_t* v0 = buf + (32 * kk + 8 * g + rs) * kRowF8 + kNope + 8 * qd;
+    const uint8_t* v1 = v0 + 4 * kRowF8;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * d));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * d));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+      st.O[28 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), Br, st.O[28 + d], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The FP8 hi / lo query operands of the wave's 16 heads (lane (g, c): head 16 wave + c), built
+// in registers: K step ks takes dims 128ks + 16g .. +16 (bytes 0-15) and 128ks + 64 + 16g .. +16
+// (bytes 16-31), each 32-dim block with a power-of-two scale, laid out as the kernel above does
+// through LDS.
+__device__ __forceinline__ F8Query rows_query(const uint16_t* qp, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  F8Query q;
+  q.sh = q.sl = 0;
+  uint4 qraw[4][4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int d0 = 128 * ks + 64 * half + 16 * g;
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+        qraw[ks][2 * half + v] = d0 < kNope ? *reinterpret_cast<const uint4*>(qp + d0 + 8 * v) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    q.qr[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + kNope + 32 * ks + 8 * g));
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    float x[32];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t w4[4] = {qraw[ks][v].x, qraw[ks][v].y, qraw[ks][v].z, qraw[ks][v].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * v + 2 * k] = __uint_as_float(w4[k] << 16);
+        x[8 * v + 2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+      }
+    }
+    float am[2] = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) am[j >> 4] = fmaxf(am[j >> 4], fabsf(x[j]));
+    int eb[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const float m = fmaxf(am[half], __shfl_xor(am[half], 16, 64));  // the other half row of the block
+      int E = 0;
+      if (m > 0.f) (void)frexpf(m, &E);
+      eb[half] = m > 0.f ? min(max(E - 8, -120), 120) : 0;
+    }
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = eb[j >> 2];
+      const float inv_hi = __builtin_ldexpf(1.f, -e), inv_lo = __builtin_ldexpf(1.f, 4 - e);
+      const float sc_hi = __builtin_ldexpf(1.f, e);
+      const float* xj = x + 4 * j;
+      int h2 = __builtin_amdgcn_cvt_pk_fp8_f32(xj[0] * inv_hi, xj[1] * inv_hi, 0, false);
+      h2 = __builtin_amdgcn_cvt_pk_fp8_f32(xj[2] * inv_hi, xj[3] * inv_hi, h2, true);
+      const float r0 = xj[0] - __builtin_amdgcn_cvt_f32_fp8(h2, 0) * sc_hi;
+      const float r1 = xj[1] - __builtin_amdgcn_cvt_f32_fp8(h2, 1) * sc_hi;
+      const float r2 = xj[2] - __builtin_amdgcn_cvt_f32_fp8(h2, 2) * sc_hi;
+      const float r3 = xj[3] - __builtin_amdgcn_cvt_f32_fp8(h2, 3) * sc_hi;
+      int l2 = __builtin_amdgcn_cvt_pk_fp8_f32(r0 * inv_lo, r1 * inv_lo, 0, false);
+      l2 = __builtin_amdgcn_cvt_pk_fp8_f32(r2 * inv_lo, r3 * inv_lo, l2, true);
+      hw[j] = (uint32_t)h2;
+      lw[j] = (uint32_t)l2;
+    }
+    q.qh[ks] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+    q.ql[ks] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+    // block g's exponent: g0 its low half, g1 the low half of g2 (block 1), g2 the high half of
+    // g0 (block 2), g3 its high half (block 3)
+    const int from_lo2 = __shfl(eb[0], 32 + c, 64), from_hi0 = __shfl(eb[1], c, 64);
+    const int eop = g == 0 ? eb[0] : g == 1 ? from_lo2 : g == 2 ? from_hi0 : eb[1];
+    q.sh |= (uint32_t)(eop + 127) << (8 * ks);
+    q.sl |= (uint32_t)(eop - 4 + 127) << (8 * ks);
+  }
+  return q;
+}
+
+template <bool kSparse>
+__global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs a, int total) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBufF8];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[kBufF8];
+  __shared__ __attribute__((aligned(16))) float sc0[kCh];
+  __shared__ __attribute__((aligned(16))) float sc1[kCh];
+  __shared__ __attribute__((aligned(16))) uint32_t vm0[kRowsWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t vm1[kRowsWaves];
+  __shared__ float wsum[kRowsWaves * 16];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= total) return;
+  const int s = id % a.n_split;
+  const int qi = id / a.n_split;
+  const int H = a.H;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int head = 16 * wave + c;
+  (void)wsum;
+
+  const int64_t lo = (int64_t)s * a.per_split;
+  const int64_t b0 = lo + kRowsEnt * wave;
+  const int32_t s0 = rows_slot<kSparse>(a, qi, b0, lane), s1 = rows_slot<kSparse>(a, qi, b0 + kCh, lane);
+  int32_t slot2 = rows_slot<kSparse>(a, qi, b0 + 2 * kCh, lane);
+  const QueryCtx ctx = query_ctx(a, qi);
+  const int64_t N = ctx.n_c + ctx.n_w;
+  const int64_t hi = min<int64_t>(N, lo + a.per_split);
+  const RowsSrc cur = rows_src<kSparse>(a, ctx, b0, hi, s0, lane);
+  RowsSrc nxt = rows_src<kSparse>(a, ctx, b0 + kCh, hi, s1, lane);
+  // the first chunk's rows are requested before the query is quantized, which hides their latency
+  uint4 va0[kRowsHalfA], vb0[kRowsHalfB];
+  rows_load<0, kRowsHalfA>(cur, va0, lane);
+  rows_load<kRowsHalfA, kRowsHalfB>(cur, vb0, lane);
+  const F8Query q = rows_query(static_cast<const uint16_t*>(a.q) + ((int64_t)qi * H + head) * kD, lane);
+  rows_store<0, kRowsHalfA>(va0, buf0 + kRowsBytes * wave, lane);
+  rows_store<kRowsHalfA, kRowsHalfB>(vb0, buf0 + kRowsBytes * wave, lane);
+  if (lane < 32) sc0[kRowsEnt * wave + lane] = cur.esc;
+  if (lane == 0) vm0[wave] = cur.vmask;
+  __syncthreads();
+
+  RowsState st;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) st.O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
+  const float sl2 = a.scale * kLog2e;
+  // one chunk in buf; the next chunk's rows go to the other buffer in two halves (loaded at the
+  // start and written after the softmax, loaded then and written after PV), so that at most
+  // half of them sit in registers; one LDS barrier then publishes them and frees buf
+  auto chunk = [&](int64_t base, const uint8_t* buf, const float* sc, const uint32_t* vm, uint8_t* nbuf, float* nsc,
+                   uint32_t* nvm) {
+    const bool more = base + kCh < hi;
+    uint8_t* ndst = nbuf + kRowsBytes * wave;
+    uint4 va[kRowsHalfA], vb[kRowsHalfB];
+    if (more) rows_load<0, kRowsHalfA>(nxt, va, lane);
+    uint4 bs[4], br[4];
+    rows_scores(buf, sc, vm, q, st, sl2, lane, bs, br);
+    if (more) {
+      rows_store<0, kRowsHalfA>(va, ndst, lane);
+      rows_load<kRowsHalfA, kRowsHalfB>(nxt, vb, lane);
+    }
+    rows_pv(buf, bs, br, st, lane);
+    if (more) {
+      rows_store<kRowsHalfA, kRowsHalfB>(vb, ndst, lane);
+      if (lane < 32) nsc[kRowsEnt * wave + lane] = nxt.esc;
+      if (lane == 0) nvm[wave] = nxt.vmask;
+      const int64_t b2 = base + 2 * kCh + kRowsEnt * wave;
+      nxt = rows_src<kSparse>(a, ctx, b2, hi, slot2, lane);
+      slot2 = rows_slot<kSparse>(a, qi, b2 + kCh, lane);
+    }
+    // LDS only: the scale and slot loads just issued stay in flight across the barrier
+    lds_barrier();
+  };
+  // unrolled by two so that each call names its buffers statically
+  for (int64_t base = lo; base < hi; base += 2 * kCh) {
+    chunk(base, buf0, sc0, vm0, buf1, sc1, vm1);
+    if (base + kCh >= hi) break;
+    chunk(base + kCh, buf1, sc1, vm1, buf0, sc0, vm0);
+  }
+
+  // the softmax denominator of head c: this lane's entries, then over the lane groups
+  float L = st.l_part;
+  L += __shfl_xor(L, 16, 64);
+  L += __shfl_xor(L, 32, 64);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float lse = L > 0.f ? (st.m_run + log2f(L)) * kLn2 : -INFINITY;
+  int head_o = head;
+  asm volatile("" : "+v"(head_o));
+  const int64_t hrow = (int64_t)qi * H + head_o;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    const int dd = 16 * d + 4 * g;  // FP8 dims for d < 28, then RoPE dims 448 + 16 (d - 28) + 4 g
+    const f32x4 acc = st.O[d] * inv;
+    if (a.n_split == 1) {
+      if (a.o_dtype == HCA_BF16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + hrow * kD + dd) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + hrow * kD + dd) = acc;
+      }
+    } else {
+      const int64_t pi = ((int64_t)qi * a.n_split + s) * H + head_o;
+      *reinterpret_cast<f32x4*>(a.part_o + pi * kD + dd) = acc;
+    }
+  }
+  if (g == 0) {
+    if (a.n_split == 1) a.lse[hrow] = lse;
+    else a.part_lse[((int64_t)qi * a.n_split + s) * H + head_o] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Log-sum-exp merge of the split partials of one (query, head) over the dims held by a lane
 // (V = f32x4 for 4 dims at po + d, float for one). The lse values and partial outputs of kG
 // splits are loaded at once (positions past S clamp to the last split and get weight 0), so a
@@ -965,10 +1375,22 @@ void attn_split_policy(int nq, int H, int D, int64_t max_entries, bool mfma, int
   *per_split = (int)per;
 }
 
+// The row-owning kernel serves all 64 heads of a query per block. It is chosen when there are
+// enough (query, split) blocks to fill the chip on their own (many queries, as in prefill);
+// with few queries the per-head-group kernel's four blocks per split range fill it better.
+bool attn_rows_eligible(const AttnArgs& a) {
+  return a.H == 16 * kRowsWaves && (int64_t)a.nq * a.n_split >= 256;
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const bool mfma = a.q_dtype == HCA_BF16;
   const bool fp8 = mfma && attn_fp8_supported(a.cache, a.win);
-  if (fp8) {
+  if (fp8 && attn_rows_eligible(a)) {
+    const int total = a.nq * a.n_split;
+    const int grid = (total + 7) / 8 * 8;
+    if (a.idx) hipLaunchKernelGGL(attn_rows_kernel<true>, dim3(grid), dim3(64 * kRowsWaves), 0, s, a, total);
+    else hipLaunchKernelGGL(attn_rows_kernel<false>, dim3(grid), dim3(64 * kRowsWaves), 0, s, a, total);
+  } else if (fp8) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;
