@@ -269,10 +269,8 @@ __device__ void emit_candidates(const IndexArgs& a, int qi, int64_t jb, int64_t 
   if (tid == 0) a.blk_thr[slot] = thr;
 }
 
-// MXFP4 scores via the scaled MFMA. grid = (nblk, nq), 256 threads, 1024 keys per block.
-__global__ __launch_bounds__(256) void score_mxfp4_kernel(IndexArgs a) {
-  __shared__ BlockLds lds;
-  const int qi = blockIdx.y;
+// MXFP4 scores of query qi for the keys of score block blockIdx.x (all 256 threads).
+__device__ __forceinline__ void score_mxfp4_one(const IndexArgs& a, int qi, BlockLds& lds) {
   int64_t rb;
   const int64_t nv = visible_keys(a, qi, &rb);
   if (nv <= a.k) return;  // every visible entry is selected; no scores needed
@@ -333,6 +331,122 @@ __global__ __launch_bounds__(256) void score_mxfp4_kernel(IndexArgs a) {
   }
   __syncthreads();
   emit_candidates(a, qi, jb, nv, lds);
+}
+
+// MXFP4 scores via the scaled MFMA. grid = (nblk, nq), 256 threads, 1024 keys per block.
+__global__ __launch_bounds__(256) void score_mxfp4_kernel(IndexArgs a) {
+  __shared__ BlockLds lds;
+  score_mxfp4_one(a, blockIdx.y, lds);
+}
+
+// Many queries with 4 indexer heads (prefill): grid = (nblk, ceil(nq / 4)); a block scores the
+// keys of score block blockIdx.x for the 4 consecutive queries 4 blockIdx.y .. +3. When their
+// visible keys start at the same row (one sequence, one document), the keys are loaded once
+// and one MFMA per 32 keys scores all of them: its A rows are the 16 (query, head) pairs
+// 4 q + h. Lanes 0-31 then hold queries 0 and 2 of their key column (accumulators 0-3 and
+// 4-7), lanes 32-63 queries 1 and 3. Each query keeps its own LDS keys and histogram and emits
+// its candidates as score_mxfp4_one does; every score is the same float32 value, folded in
+// the same order. Otherwise the block scores its queries one after another.
+constexpr int kScoreQ = 4;
+
+__global__ __launch_bounds__(256) void score_mxfp4_q4_kernel(IndexArgs a) {
+  __shared__ BlockLds lds[kScoreQ];
+  const int q0 = (int)blockIdx.y * kScoreQ;
+  const int nqb = min(kScoreQ, a.nq - q0);
+  int64_t rb[kScoreQ], nv[kScoreQ];
+  bool same = true;
+#pragma unroll
+  for (int i = 0; i < kScoreQ; ++i) {
+    nv[i] = 0;
+    rb[i] = 0;
+    if (i < nqb) nv[i] = visible_keys(a, q0 + i, &rb[i]);
+    if (i > 0 && i < nqb) same = same && rb[i] == rb[0];
+  }
+  if (!same) {
+    for (int i = 0; i < nqb; ++i) {
+      score_mxfp4_one(a, q0 + i, lds[0]);
+      __syncthreads();
+    }
+    return;
+  }
+  const int64_t jb = (int64_t)blockIdx.x * kBlockKeys;
+  bool act[kScoreQ];
+  bool any = false;
+  int64_t nvmax = 0;
+#pragma unroll
+  for (int i = 0; i < kScoreQ; ++i) {
+    act[i] = i < nqb && nv[i] > a.k && jb < nv[i];
+    any = any || act[i];
+    if (act[i]) nvmax = max(nvmax, nv[i]);
+  }
+  if (!any) return;
+#pragma unroll
+  for (int i = 0; i < kScoreQ; ++i)
+    for (int j = threadIdx.x; j < kHistBins; j += 256) lds[i].hist[j] = 0;
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 31, blk = lane >> 5;
+  const uint8_t* qb = static_cast<const uint8_t*>(a.q);
+  const uint8_t* kb = static_cast<const uint8_t*>(a.keys);
+  i32x8 A = {0, 0, 0, 0, 0, 0, 0, 0};
+  int sa = 127;
+  if ((row >> 2) < nqb) {  // row 4 q + h: query q0 + q, head h
+    const int64_t qr = (int64_t)(q0 + (row >> 2)) * 4 + (row & 3);
+    const uint4 v = *reinterpret_cast<const uint4*>(qb + qr * 32 + blk * 16);
+    A[0] = (int)v.x; A[1] = (int)v.y; A[2] = (int)v.z; A[3] = (int)v.w;
+    sa = a.q_scale[qr * 2 + blk];
+  }
+  // this lane's two queries: 0 and 2 (lanes 0-31) or 1 and 3 (lanes 32-63)
+  const int qa = blk, qc = blk + 2;
+  float wa[4], wc[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    wa[h] = qa < nqb ? a.w[(int64_t)(q0 + qa) * 4 + h] : 0.f;
+    wc[h] = qc < nqb ? a.w[(int64_t)(q0 + qc) * 4 + h] : 0.f;
+  }
+  const bool act_a = blk == 0 ? act[0] : act[1], act_c = blk == 0 ? act[2] : act[3];
+  const int64_t nv_a = blk == 0 ? nv[0] : nv[1], nv_c = blk == 0 ? nv[2] : nv[3];
+
+  constexpr int U = 8;
+  i32x8 B[U];
+  int sb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t j = jb + (int64_t)(wave * U + u) * 32 + row;
+    const int64_t jc = rb[0] + (j < nvmax ? j : nvmax - 1);
+    const uint4 v = *reinterpret_cast<const uint4*>(kb + jc * 32 + blk * 16);
+    B[u] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    sb[u] = a.key_scale[jc * 2 + blk];
+  }
+  __syncthreads();
+  BlockLds& la = lds[qa];
+  BlockLds& lc = lds[qc];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const f32x16 zero = {};
+    const f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B[u], zero, 4, 4, 0, sa, 0, sb[u]);
+    const int pos = (wave * U + u) * 32 + row;
+    if (act_a && jb + pos < nv_a) {
+      float s = __fmul_rn(wa[0], fmaxf(acc[0], 0.f));
+#pragma unroll
+      for (int h = 1; h < 4; ++h) s = __fadd_rn(s, __fmul_rn(wa[h], fmaxf(acc[h], 0.f)));
+      const uint32_t key = float_key(s);
+      la.key[pos] = key;
+      atomicAdd(&la.hist[key >> 21], 1u);
+    }
+    if (act_c && jb + pos < nv_c) {
+      float s = __fmul_rn(wc[0], fmaxf(acc[4], 0.f));
+#pragma unroll
+      for (int h = 1; h < 4; ++h) s = __fadd_rn(s, __fmul_rn(wc[h], fmaxf(acc[4 + h], 0.f)));
+      const uint32_t key = float_key(s);
+      lc.key[pos] = key;
+      atomicAdd(&lc.hist[key >> 21], 1u);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kScoreQ; ++i)
+    if (act[i]) emit_candidates(a, q0 + i, jb, nv[i], lds[i]);
 }
 
 // fp32 / bf16 scores on the vector ALUs (4 keys per thread). grid = (nblk, nq).
@@ -960,7 +1074,10 @@ hipError_t index_init() {
 hipError_t launch_index_topk(const IndexArgs& a, bool scores, bool select, hipStream_t s) {
   if (scores && a.max_visible > a.k) {
     const dim3 g((unsigned)a.nblk, (unsigned)a.nq);
-    if (a.dtype == HCA_MXFP4) hipLaunchKernelGGL(score_mxfp4_kernel, g, dim3(256), 0, s, a);
+    if (a.dtype == HCA_MXFP4 && a.H == 4 && a.nq >= 256) {
+      const dim3 g4((unsigned)a.nblk, (unsigned)((a.nq + kScoreQ - 1) / kScoreQ));
+      hipLaunchKernelGGL(score_mxfp4_q4_kernel, g4, dim3(256), 0, s, a);
+    } else if (a.dtype == HCA_MXFP4) hipLaunchKernelGGL(score_mxfp4_kernel, g, dim3(256), 0, s, a);
     else if (a.dtype == HCA_F32) hipLaunchKernelGGL(score_valu_kernel<float>, g, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(score_valu_kernel<uint16_t>, g, dim3(256), 0, s, a);
   }

@@ -70,6 +70,30 @@ def test_mxfp4_random(hca, H, k):
     check_idx(got, ref, f"mxfp4 H={H} k={k}")
 
 
+@pytest.mark.parametrize("k", [64, 1024])
+def test_mxfp4_many_queries_grouped_and_mixed(hca, k):
+    """At least 256 queries with 4 indexer heads take the scorer that serves 4 consecutive
+    queries per block: their keys are loaded once and scored by one MFMA when the queries' visible
+    keys start at the same row, and one query at a time otherwise. Queries 0 .. 199 alternate
+    between two sequences in runs of 3 (most blocks mixed), queries 200 .. 300 all belong to
+    sequence 0 (uniform blocks) at random positions, some of which see fewer than k entries or
+    none; nq = 301 leaves a partial last block."""
+    nq = 301
+    q, qs, w, kp, ks = mx_case(31, 20000, nq, 4)
+    rng = np.random.default_rng(5)
+    q_seq = [(i // 3) % 2 if i < 200 else 0 for i in range(nq)]
+    q_pos = [int(rng.integers(0, 80000)) for _ in range(nq)]
+    for i in (200, 201, 250, 300):
+        q_pos[i] = int(rng.integers(0, 4 * k))  # at most k visible entries
+    q_pos[202] = 2                               # no visible entry
+    rb = [0, 10000]
+    keys = torch.cat([kp, kp[:10000]])
+    kss = torch.cat([ks, ks[:10000]])
+    got = run(hca, q, w, keys, rb, q_seq, q_pos, 20000, 4, k, qs, kss)
+    ref = oracle_mxfp4(q, qs, w, keys, kss, rb, q_seq, q_pos, 4, k)
+    check_idx(got, ref, f"mxfp4 many queries k={k}")
+
+
 def test_mxfp4_all_equal_keys(hca):
     q, qs, w, kp, ks = mx_case(3, 9000, 2)
     kp[:] = kp[0]
