@@ -615,6 +615,17 @@ def main():
         "kernels_ms": {nm: round(v, 5) for nm, v in kern_ms.items()},
         "copy_gbs": round(copy_gbs, 1),
         "rooflines": {
+            "lightning_index_scores": {"kernel": "score_mxfp4_kernel", "bound": "hbm",
+                                       "achieved": round(kern_bytes["score_mxfp4_kernel"]
+                                                         / (kern_ms["score_mxfp4_kernel"] * 1e-3) / 1e9, 1),
+                                       "frac": round(kern_bytes["score_mxfp4_kernel"]
+                                                     / (kern_ms["score_mxfp4_kernel"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                       "tflops": round(fl_idx / (kern_ms["score_mxfp4_kernel"] * 1e-3) / 1e12, 2),
+                                       "frac_mfma_mxfp4": round(fl_idx / (kern_ms["score_mxfp4_kernel"] * 1e-3) / 1e12
+                                                                / MXFP4_PEAK_TFLOPS, 5)},
+            "lightning_index_select": {"kernel": "finalize_kernel", "bound": "latency",
+                                       "us_per_launch": round(kern_ms["finalize_kernel"] * 1e3, 2),
+                                       "note": "one block per query; moves only 4 k bytes of output per query"},
             "csa_sparse_mqa_attn": {"bound": "hbm", "achieved": round(by_csa / (t_csa * 1e-3) / 1e9, 1),
                                     "frac": round(by_csa / (t_csa * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                     "tflops": round(fl_csa / (t_csa * 1e-3) / 1e12, 2)},
