@@ -237,3 +237,15 @@ def test_grouped_projection_rejects_bad_arguments(kw, status, msg):
 def test_grouped_projection_valid_call_reaches_launch():
     assert proj_call() in (0, -4)
     assert proj_call(n=0) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: any --gpus other than 1 exits with status 2 and says why,
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
