@@ -249,3 +249,21 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """The binding has no CPU fallback: importing it from a folder without libhca.so raises
+    ImportError naming the missing library."""
+    import importlib.util
+    import shutil
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = tmp_path / "hca_without_lib"
+    pkg.mkdir()
+    shutil.copy(os.path.join(root, "long_context_attention_hca_amd", "__init__.py"), pkg / "__init__.py")
+    spec = importlib.util.spec_from_file_location("hca_without_lib", pkg / "__init__.py",
+                                                  submodule_search_locations=[str(pkg)])
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="libhca.so"):
+        spec.loader.exec_module(mod)
+    sys.modules.pop("hca_without_lib", None)
