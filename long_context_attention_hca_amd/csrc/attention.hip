@@ -1167,7 +1167,6 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs a, int total
   __shared__ __attribute__((aligned(16))) float sc1[kCh];
   __shared__ __attribute__((aligned(16))) uint32_t vm0[kRowsWaves];
   __shared__ __attribute__((aligned(16))) uint32_t vm1[kRowsWaves];
-  __shared__ float wsum[kRowsWaves * 16];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= total) return;
   const int s = id % a.n_split;
@@ -1176,7 +1175,6 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs a, int total
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const int head = 16 * wave + c;
-  (void)wsum;
 
   const int64_t lo = (int64_t)s * a.per_split;
   const int64_t b0 = lo + kRowsEnt * wave;
