@@ -245,6 +245,8 @@ def _ws_args(ws):
 
 def csa_sparse_mqa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale,
                         o, lse, ws=None, q_lo=None, stream=None):
+    if not idx.is_contiguous():
+        raise ValueError("idx must be contiguous [nq, k] (rows of k slots)")
     wp, wb = _ws_args(ws)
     _check(_csa_attn(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin),
                      _ptr(idx), idx.shape[1], window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq),

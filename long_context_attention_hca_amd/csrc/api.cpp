@@ -249,7 +249,8 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
   const bool mfma = hca::attn_mfma_supported(q_dtype, o_dtype, cv, wv, n_heads, D);
   if (!mfma) {
     const bool valu = q_dtype == HCA_F32 && o_dtype == HCA_F32 && cache->layout == HCA_LAYOUT_F32 &&
-                      window->layout == HCA_LAYOUT_F32 && D <= 512 && (int64_t)n_heads * D <= 8192;
+                      window->layout == HCA_LAYOUT_F32 && D <= 512 && (int64_t)n_heads * D <= 8192 &&
+                      hca::attn_valu_lds_bytes(n_heads, D) <= hca::kAttnValuMaxLds;
     if (!valu) return fail(HCA_ERR_UNSUPPORTED, fn, "unsupported dtype/layout/shape combination");
   }
   if (nq == 0) return HCA_OK;
@@ -263,8 +264,10 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
   a.q = q; a.q_dtype = q_dtype; a.nq = nq; a.H = n_heads; a.D = D;
   a.cache = cv; a.win = wv;
   a.cache_row_begin = cache_row_begin;
-  a.idx = csa ? idx : nullptr;
-  a.k = csa ? k : 0;
+  // k == 0 selects nothing: the call runs as the dense path over no compressed entries (the
+  // window only), so no kernel ever reads idx, whatever the pointer
+  a.idx = (csa && k > 0) ? idx : nullptr;
+  a.k = (csa && k > 0) ? k : 0;
   a.m_prime = csa ? 1 : m_prime;
   a.max_visible = csa ? 0 : max_visible;
   a.win_row_begin = win_row_begin; a.win_pos0 = win_pos0; a.W = W;

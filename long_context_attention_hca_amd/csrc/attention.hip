@@ -1400,8 +1400,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL(attn_mfma_kernel, dim3(grid), dim3(256), kMfmaLds, s, a, n_hg, total);
   } else {
-    const size_t lds = sizeof(float) * ((size_t)a.H * a.D + (size_t)kValuChunk * a.D + (size_t)a.H * kValuChunk + 3 * a.H);
-    hipLaunchKernelGGL(attn_valu_kernel, dim3(a.n_split, a.nq), dim3(256), lds, s, a);
+    static_assert(kValuChunk == 16, "attn_valu_lds_bytes assumes 16-entry chunks");
+    hipLaunchKernelGGL(attn_valu_kernel, dim3(a.n_split, a.nq), dim3(256), attn_valu_lds_bytes(a.H, a.D), s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1413,7 +1413,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t attention_init() {
-  return hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
+  hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
+  if (e != hipSuccess) return e;
+  // the float32 kernel's LDS grows with H * D (66,752 bytes at 16 heads of 512)
+  return hipFuncSetAttribute((const void*)attn_valu_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)kAttnValuMaxLds);
 }
 
 }  // namespace hca

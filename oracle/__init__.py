@@ -27,7 +27,14 @@ Readings of points the pages leave open are stated in each module.
 
 Pins: every function here is checked by the CPU test suite against closed
 forms, special cases that reduce to library routines, invariants and brute
-force (tests/test_oracle_*.py). No function is "parity unpinned".
+force (tests/test_oracle_*.py). The whole-workload compositions of
+pipeline.py are pinned by rebuilding queries from whole raw sequences
+(tests/test_oracle_pipeline.py): with k >= n_vis they equal textbook
+attention over the explicitly listed rows, a chunk's entries equal those of
+the whole sequence, and with one entry per token and no window they reduce
+to causal MQA through torch's scaled_dot_product_attention. The golden
+fixture under tests/golden is a regression record written by this oracle,
+not a pin.
 """
 
 from . import codecs, compress, indexer, attention  # noqa: F401

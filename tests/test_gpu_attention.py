@@ -206,3 +206,63 @@ def test_long_entry_lists(hca, H):
         check_attention(o[i], lse[i], ro, rl, "low", f"csa k=65536 q{i}")
         ro, rl = OA.attend(qdec[i], np.concatenate([cache_dec[:t + 1], raw(OA.window_positions(t, W))]), scale)
         check_attention(o2[i], lse2[i], ro, rl, "low", f"hca {t + 1} visible q{i}")
+
+
+def test_k_zero_reads_no_index(hca):
+    """k == 0 with idx a zero-width view into the middle of a larger int32 tensor (a non-NULL
+    pointer, a row stride of 0 slots): CSA attention is the window-only attention, for split and
+    bf16 stores."""
+    m, W_ = hca
+    dev = "cuda"
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=dev)
+    for layout in ("split", "bf16"):
+        st, dec = make_store(layout, 300, 41)
+        cache = to_store(m, st, 448, 64)
+        nq, H, W = 3, 64, 50
+        q = synth.normal(synth.generator(42), (nq, H, 512)).bfloat16()
+        big = torch.full((nq, 64), 7, dtype=torch.int32, device=dev)
+        idx = big[:, 20:20]
+        assert idx.data_ptr() != 0 and idx.shape == (nq, 0)
+        seq = torch.zeros(nq, dtype=torch.int32, device=dev)
+        pos = torch.tensor([60, 299, 10], dtype=torch.int64, device=dev)
+        ws = W_.Workspace(dev)
+        o, lse = W_.csa_attn(q.to(dev), cache, i64([0]), idx, cache, i64([0]), i64([0]), W, seq, pos, 0.05, ws)
+        torch.cuda.synchronize()
+        o, lse = np_(o.float()), np_(lse)
+        for i, t in enumerate(pos.tolist()):
+            ro, rl = OA.attend(q[i].double().numpy(), dec[OA.window_positions(t, W)], 0.05)
+            check_attention(o[i], lse[i], ro, rl, "low", f"{layout} k=0 q{i}")
+
+
+def test_fp32_sixteen_heads_of_512(hca):
+    """The float32 path at its largest documented shape (16 heads of 512: 66,752 bytes of LDS per
+    block) with split-K partials (about 2000 visible HCA entries for 2 queries) and a CSA call."""
+    m, W_ = hca
+    dn, dr, n, H = 448, 64, 2200, 16
+    D = dn + dr
+    st, dec = make_store("f32", n, 51, dn, dr)
+    dev = "cuda"
+    cache = to_store(m, st, dn, dr)
+    nq, W, mp = 2, 64, 1
+    q_pos = np.array([2199, 1500], np.int64)
+    q = synth.normal(synth.generator(52), (nq, H, D))
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=dev)
+    ws = W_.Workspace(dev)
+    scale = 1.0 / math.sqrt(D)
+    seq = torch.zeros(nq, dtype=torch.int32, device=dev)
+    pos = torch.tensor(q_pos, device=dev)
+    assert m.mqa_attn_workspace(m.F32, nq, H, D, 2000 + W) > 0  # split-K
+    o, lse = W_.hca_attn(q.to(dev), cache, i64([0]), mp, 2000, cache, i64([0]), i64([0]), W, seq, pos, scale, ws)
+    rng = np.random.default_rng(53)
+    idx = np.stack([np.sort(rng.choice(1400, size=300, replace=False)) for _ in range(nq)]).astype(np.int32)
+    o2, lse2 = W_.csa_attn(q.to(dev), cache, i64([0]), torch.tensor(idx, device=dev), cache, i64([0]), i64([0]), W,
+                           seq, pos, scale, ws)
+    torch.cuda.synchronize()
+    o, lse, o2, lse2 = np_(o), np_(lse), np_(o2), np_(lse2)
+    for i in range(nq):
+        t = int(q_pos[i])
+        qd = q[i].double().numpy()
+        ro, rl = OA.attend(qd, np.concatenate([dec[:min(t + 1, 2000)], dec[OA.window_positions(t, W)]]), scale)
+        check_attention(o[i], lse[i], ro, rl, "fp32", f"hca q{i}")
+        ro, rl = OA.csa(qd, t, dec, idx[i], dec, W, scale)
+        check_attention(o2[i], lse2[i], ro, rl, "fp32", f"csa q{i}")
