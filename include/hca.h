@@ -321,7 +321,7 @@ int lightning_index_select(const void* q_idx, const uint8_t* q_idx_scale, const 
  * q: [nq, n_heads, D] of q_dtype, contiguous. o: [nq, n_heads, D] of o_dtype,
  * contiguous. lse: float32 [nq, n_heads].
  * Supported: q, o, cache, window all F32 with D <= 512, n_heads * D <= 8192
- * and 4 * (n_heads * D + 16 * D + 19 * n_heads) <= 163840 (the vector path's
+ * and 4 * (n_heads * D + 16 * D + 19 * n_heads) <= 162816 (the vector path's
  * LDS; e.g. 16 heads of 512); or q BF16, o BF16 or F32, cache and window
  * BF16 or SPLIT with D = 512, n_heads a multiple of 16. Anything else:
  * HCA_ERR_UNSUPPORTED. k == 0 selects no compressed entry (idx is not read).

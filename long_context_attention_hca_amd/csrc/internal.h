@@ -133,7 +133,7 @@ bool attn_mfma_supported(int q_dtype, int o_dtype, const StoreView& c, const Sto
                          int D);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 // Dynamic LDS of the float32 attention kernel for H heads of width D, and its ceiling.
-constexpr size_t kAttnValuMaxLds = 160 * 1024;
+constexpr size_t kAttnValuMaxLds = 159 * 1024;  // 160 KiB less room for the static LDS
 inline size_t attn_valu_lds_bytes(int H, int D) {
   return sizeof(float) * ((size_t)H * D + 16 * (size_t)D + 16 * (size_t)H + 3 * (size_t)H);
 }

@@ -221,8 +221,19 @@ def test_k_zero_reads_no_index(hca):
         nq, H, W = 3, 64, 50
         q = synth.normal(synth.generator(42), (nq, H, 512)).bfloat16()
         big = torch.full((nq, 64), 7, dtype=torch.int32, device=dev)
-        idx = big[:, 20:20]
-        assert idx.data_ptr() != 0 and idx.shape == (nq, 0)
+
+        class ZeroWidthView:
+            """idx[:, 20:20] of `big` as the C ABI sees it: k = 0 and a non-NULL pointer into the
+            middle of the tensor (torch itself reports NULL for an empty view)."""
+            shape = (nq, 0)
+
+            def data_ptr(self):
+                return big.data_ptr() + 20 * 4
+
+            def is_contiguous(self):
+                return True
+
+        idx = ZeroWidthView()
         seq = torch.zeros(nq, dtype=torch.int32, device=dev)
         pos = torch.tensor([60, 299, 10], dtype=torch.int64, device=dev)
         ws = W_.Workspace(dev)
