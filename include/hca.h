@@ -357,6 +357,26 @@ int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_hea
                        int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * hca_dense_mqa_attn_noalloc — hca_dense_mqa_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments and results as
+ * hca_dense_mqa_attn without the workspace: the split-K partials go to a
+ * static device array of 16 MiB that the library holds on every GPU it runs
+ * on until the process ends. Calls needing more than that
+ * (mqa_attn_workspace(q_dtype, nq, n_heads, D, max_visible + W) > 16 MiB)
+ * return HCA_ERR_WORKSPACE before anything is enqueued. The call allocates
+ * nothing. Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race and give unspecified
+ * results; calls ordered on one stream do not.
+ */
+int hca_dense_mqa_attn_noalloc(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                               const hca_store* cache, const int64_t* cache_row_begin,
+                               int32_t m_prime, int64_t max_visible, const hca_store* window,
+                               const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W,
+                               const int32_t* q_seq, const int64_t* q_pos, const int64_t* q_lo,
+                               float scale, void* o, int32_t o_dtype, float* lse, void* stream);
+
+/*
  * grouped_out_proj — the grouped output projection after core attention
  * (CSA paragraph: core attention is followed by a grouped output projection
  * to manage the computational cost). The heads are split into `groups`

@@ -18,7 +18,8 @@ __all__ = [
     "F32", "BF16", "FP8_E4M3", "MXFP4", "LAYOUT_F32", "LAYOUT_BF16", "LAYOUT_SPLIT", "LAYOUT_MXFP4",
     "HcaError", "Store", "DecodeLayer", "abi_version", "csa_compress", "hca_compress", "decode_append",
     "lightning_index_topk_workspace", "lightning_index_topk", "mqa_attn_workspace",
-    "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "grouped_out_proj", "library_path",
+    "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "hca_dense_mqa_attn_noalloc", "grouped_out_proj",
+    "library_path",
 ]
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
@@ -82,6 +83,8 @@ _attn_ws = _sig("mqa_attn_workspace", _SZ, [_I32, _I32, _I32, _I32, _I64])
 _attn_tail = [_SP, _P, _P, _I32, _P, _P, _P, _F, _P, _I32, _P, _P, _SZ, _P]
 _csa_attn = _sig("csa_sparse_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP, _P, _P, _I32] + _attn_tail)
 _hca_attn = _sig("hca_dense_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail)
+_hca_attn_noalloc = _sig("hca_dense_mqa_attn_noalloc", ctypes.c_int,
+                         [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail[:-3] + [_P])
 
 
 class HcaError(RuntimeError):
@@ -259,3 +262,11 @@ def hca_dense_mqa_attn(q, cache, cache_row_begin, m_prime, max_visible, window, 
     _check(_hca_attn(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin), m_prime,
                      max_visible, window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq), _ptr(q_pos),
                      _ptr(q_lo), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb, _stream(stream)))
+
+
+def hca_dense_mqa_attn_noalloc(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W,
+                               q_seq, q_pos, scale, o, lse, q_lo=None, stream=None):
+    """hca_dense_mqa_attn without a workspace (the library's static 16 MiB scratch; allocates nothing)."""
+    _check(_hca_attn_noalloc(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin),
+                             m_prime, max_visible, window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq),
+                             _ptr(q_pos), _ptr(q_lo), scale, _ptr(o), _dtype_code(o), _ptr(lse), _stream(stream)))

@@ -229,7 +229,8 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
               int32_t m_prime, int64_t max_visible, const hca_store* window, const int64_t* win_row_begin,
               const int64_t* win_pos0, int32_t W, const int32_t* q_seq, const int64_t* q_pos,
               const int64_t* q_lo, float scale,
-              void* o, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+              void* o, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream,
+              bool static_scratch = false) {
   if (!q || !cache_row_begin || !win_row_begin || !win_pos0 || !q_seq || !q_pos || !o || !lse)
     return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
   if (csa && k > 0 && !idx) return fail(HCA_ERR_INVALID_ARG, fn, "NULL idx");
@@ -257,6 +258,21 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
   const int64_t max_entries = (csa ? (int64_t)k : max_visible) + W;
   int n_split = 1, per = 1;
   const size_t need = attn_ws(q_dtype, nq, n_heads, D, max_entries, &n_split, &per);
+  if (static_scratch) {
+    // the library's static device scratch stands in for the workspace (no allocation)
+    if (need > hca::kNoallocScratchBytes)
+      return fail(HCA_ERR_WORKSPACE, fn, "the call needs more than the 16 MiB static scratch (mqa_attn_workspace)");
+    ws = nullptr;
+    ws_bytes = 0;
+    if (need > 0) {
+      const hipError_t e = hca::noalloc_scratch(&ws);
+      if (e != hipSuccess) {
+        g_last_error = std::string(fn) + ": static scratch lookup failed: " + hipGetErrorString(e);
+        return HCA_ERR_HIP;
+      }
+      ws_bytes = hca::kNoallocScratchBytes;
+    }
+  }
   if (need > 0 && (!ws || ws_bytes < need)) return fail(HCA_ERR_WORKSPACE, fn, "workspace too small");
   int st = ensure_init(fn);
   if (st != HCA_OK) return st;
@@ -465,6 +481,17 @@ HCA_EXPORT int csa_sparse_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, i
   return attn_impl("csa_sparse_mqa_attn", true, q, q_dtype, nq, n_heads, cache, cache_row_begin, idx, k, 1, 0,
                    window, win_row_begin, win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype, lse, ws, ws_bytes,
                    stream);
+}
+
+HCA_EXPORT int hca_dense_mqa_attn_noalloc(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                                          const hca_store* cache, const int64_t* cache_row_begin, int32_t m_prime,
+                                          int64_t max_visible, const hca_store* window, const int64_t* win_row_begin,
+                                          const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
+                                          const int64_t* q_pos, const int64_t* q_lo, float scale, void* o,
+                                          int32_t o_dtype, float* lse, void* stream) {
+  return attn_impl("hca_dense_mqa_attn_noalloc", false, q, q_dtype, nq, n_heads, cache, cache_row_begin, nullptr, 0,
+                   m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype,
+                   lse, nullptr, 0, stream, /*static_scratch=*/true);
 }
 
 HCA_EXPORT int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads, const hca_store* cache,

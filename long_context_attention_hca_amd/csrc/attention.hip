@@ -29,6 +29,7 @@
 //    operands), and V^T tiles come from ds_read_b64_tr_b16 transpose reads of the
 //    row-major chunk.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -1410,6 +1411,35 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     e = hipGetLastError();
   }
   return e;
+}
+
+// Scratch of hca_dense_mqa_attn_noalloc (its split-K partials): a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends. Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device with that device current, and is
+// what the kernels receive.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t attention_init() {

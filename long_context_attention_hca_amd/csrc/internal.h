@@ -132,6 +132,10 @@ void attn_split_policy(int nq, int H, int D, int64_t max_entries, bool mfma, int
 bool attn_mfma_supported(int q_dtype, int o_dtype, const StoreView& c, const StoreView& w, int H,
                          int D);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+// The static scratch of hca_dense_mqa_attn_noalloc: its size, and its device address on the
+// current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = 16u << 20;
+hipError_t noalloc_scratch(void** ptr);
 // Dynamic LDS of the float32 attention kernel for H heads of width D, and its ceiling.
 constexpr size_t kAttnValuMaxLds = 159 * 1024;  // 160 KiB less room for the static LDS
 inline size_t attn_valu_lds_bytes(int H, int D) {

@@ -267,3 +267,18 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     with pytest.raises(ImportError, match="libhca.so"):
         spec.loader.exec_module(mod)
     sys.modules.pop("hca_without_lib", None)
+
+
+def test_noalloc_attention_rejects_calls_beyond_its_scratch():
+    """hca_dense_mqa_attn_noalloc checks on the host that the split-K partials fit its 16 MiB static
+    scratch: 16 fp32 heads of 512 over a million entries need 512 splits of 16 x 513 floats."""
+    f32 = store(layout=0, d_nope=448, d_rope=64, row_stride=512)
+    args = lambda nq, mv: (P[0], 0, nq, 16, ctypes.byref(f32), P[1], 1, mv, ctypes.byref(f32), P[3], P[4], 0, P[5],
+                           P[6], None, 0.04, P[7], 0, P[8], None)
+    assert hca.mqa_attn_workspace(0, 1, 16, 512, 1 << 20) > 16 << 20
+    assert hca._hca_attn_noalloc(*args(1, 1 << 20)) == -3
+    assert "16 MiB" in hca._last_error().decode()
+    assert hca._hca_attn_noalloc(*args(0, 1 << 20)) == 0          # nothing to do
+    bad = hca._StoreC(7, 448, 64, 0, 100, 0x9000000, 512, 0, 0, 0)
+    assert hca._hca_attn_noalloc(P[0], 0, 1, 16, ctypes.byref(bad), P[1], 1, 100, ctypes.byref(f32), P[3], P[4], 0,
+                                 P[5], P[6], None, 0.04, P[7], 0, P[8], None) == -1
