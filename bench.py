@@ -134,8 +134,8 @@ def measured_traffic(kernel):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=320)
-    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -155,8 +155,8 @@ def main():
     B, L, H, D, k, W_, m, mp, HI = 4, 1 << 20, 64, 512, 1024, 128, 4, 128, 4
     n_c, n_h = L // m, L // mp
     R = args.copies
-    K = max(R, (args.steps + R - 1) // R * R)
-    Wm = max(R, (args.warmup + R - 1) // R * R)
+    K = max(1, args.steps)
+    Wm = max(0, args.warmup)
 
     log(f"generating {R} input copies (B={B}, L={L})")
     base = synth.decode_1m(seed=1003, B=B, L=L, device=dev)
@@ -170,11 +170,19 @@ def main():
     torch.cuda.synchronize()
     eager = [(r.idx.clone(), r.o_csa.clone(), r.lse_csa.clone(), r.o_hca.clone(), r.lse_hca.clone()) for r in runs]
 
-    log("capturing the step graph")
+    # one graph of exactly K steps (step i on input copy i mod R) for the timed region, and one of
+    # the W warm-up steps
+    log(f"capturing the step graphs ({K} timed steps, {Wm} warm-up steps)")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for r in runs:
-            r.step()
+        for i in range(K):
+            runs[i % R].step()
+    gw = None
+    if Wm > 0:
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw):
+            for i in range(Wm):
+                runs[i % R].step()
     # per-entry-point graphs (for the kernel breakdown)
     parts = []
     for r in runs:
@@ -188,16 +196,20 @@ def main():
         parts.append((gi, gc, gh))
     torch.cuda.synchronize()
 
-    # graph replays must reproduce the eager results, replay after replay
+    # graph replays must reproduce the eager results, replay after replay (every copy that the
+    # timed graph touches)
     for rep in range(2):
+        for r in runs[:min(K, R)]:
+            r.o_csa.zero_()
+            r.o_hca.zero_()
         g.replay()
         torch.cuda.synchronize()
-        for r, e in zip(runs, eager):
+        for r, e in zip(runs[:min(K, R)], eager):
             got = (r.idx, r.o_csa, r.lse_csa, r.o_hca, r.lse_hca)
             assert all(torch.equal(x, y) for x, y in zip(got, e)), "graph replay differs from eager"
 
-    for _ in range(Wm // R):
-        g.replay()
+    if gw is not None:
+        gw.replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -205,16 +217,16 @@ def main():
     # host launch latency never shows up between the events
     torch.cuda._sleep(50_000_000)
     t0.record()
-    for _ in range(K // R):
-        g.replay()
+    g.replay()
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / K
 
     # breakdown: events around each entry point's graph, rotating over the copies
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    KB = 4 * R
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(KB)]
     torch.cuda._sleep(200_000_000)
-    for i in range(K):
+    for i in range(KB):
         gi, gc, gh = parts[i % R]
         e = ev[i]
         e[0].record()
@@ -225,9 +237,9 @@ def main():
         gh.replay()
         e[3].record()
     torch.cuda.synchronize()
-    t_idx = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    t_csa = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    t_hca = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    t_idx = sum(e[0].elapsed_time(e[1]) for e in ev) / KB
+    t_csa = sum(e[1].elapsed_time(e[2]) for e in ev) / KB
+    t_hca = sum(e[2].elapsed_time(e[3]) for e in ev) / KB
 
     # per-kernel durations: one-kernel graphs cloned from each entry point, rotating over the
     # copies, each launch between two events on the stream it runs on
@@ -249,7 +261,7 @@ def main():
             ks.update(zip(names[ep], got))
         per_copy.append(ks)
     def chain_ms(kernel_names):
-        ex = kg.chain([per_copy[i % R][nm] for i in range(K) for nm in kernel_names])
+        ex = kg.chain([per_copy[i % R][nm] for i in range(KB) for nm in kernel_names])
         kg.launch(ex)  # warm-up
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda._sleep(50_000_000)
@@ -257,14 +269,15 @@ def main():
         kg.launch(ex)
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
+        return e0.elapsed_time(e1) / KB
 
-    # the first kernel of an entry point is timed alone; the second one consumes the first's
+    # the first kernel of an entry point is timed alone; a second one consumes the first's
     # workspace output, so it is timed as (both, copy after copy) minus (first alone)
     kern_ms = {}
-    for ep, (k1, k2) in names.items():
-        kern_ms[k1] = chain_ms([k1])
-        kern_ms[k2] = max(0.0, chain_ms([k1, k2]) - kern_ms[k1])
+    for ep, ks_ in names.items():
+        kern_ms[ks_[0]] = chain_ms([ks_[0]])
+        if len(ks_) > 1:
+            kern_ms[ks_[1]] = max(0.0, chain_ms(ks_) - kern_ms[ks_[0]])
     kctx.__exit__(None, None, None)
     # a plain copy of known size: the second bandwidth denominator, and the reference that
     # scales the HBM traffic counters
@@ -311,7 +324,7 @@ def main():
     comp = None
     if not args.no_compress:
         log("compression throughput")
-        del g, parts
+        del g, gw, parts
         cc = synth.compression(seed=1004, L=L, device=dev)
         csa_st = W.empty_store(2, n_c, 448, 64, dev)
         hca_st = W.empty_store(2, n_h, 448, 64, dev)
@@ -343,6 +356,75 @@ def main():
                 "hca_gbs": round(by_h / (th * 1e-3) / 1e9, 1),
                 "hca_frac_hbm": round(by_h / (th * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
         del cc, csa_st, hca_st
+
+        log("decode at the bf16 configuration (8 x 128K)")
+        # 8 sequences of 131072 tokens, bf16 stores generated already compressed, bf16 indexer keys
+        # (k = 512), 64 heads of 512, window 128; 8 input copies (about 48 MB each, the CSA store
+        # shared) rotated so that the Infinity Cache cannot serve a step from earlier ones
+        B2, L2, k2, R2 = 8, 1 << 17, 512, 8
+        base2 = synth.decode_bf16_caches(seed=1012, B=B2, L=L2, topk=k2, device=dev)
+        cases2 = [base2] + [synth.decode_bf16_caches(seed=1012 + 7919 * i, B=B2, L=L2, topk=k2, device=dev,
+                                                     csa_store=base2.t["csa_data"]) for i in range(1, R2)]
+        ws2 = W.Workspace(dev)
+        runs2 = [W.DecodeBf16(c2, ws=ws2) for c2 in cases2]
+        for r2 in runs2:
+            r2.step()
+        torch.cuda.synchronize()
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            for r2 in runs2:
+                r2.step()
+        parts2 = []
+        for r2 in runs2:
+            gi2, gc2, gh2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gi2):
+                r2.index()
+            with torch.cuda.graph(gc2):
+                r2.csa_attention()
+            with torch.cuda.graph(gh2):
+                r2.hca_attention()
+            parts2.append((gi2, gc2, gh2))
+        g2.replay()
+        torch.cuda.synchronize()
+        n2 = 8
+        torch.cuda._sleep(50_000_000)
+        e[0].record()
+        for _ in range(n2):
+            g2.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        t2 = e[0].elapsed_time(e[1]) / (n2 * R2)
+        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(2 * R2)]
+        torch.cuda._sleep(100_000_000)
+        for i in range(2 * R2):
+            gi2, gc2, gh2 = parts2[i % R2]
+            ev2[i][0].record()
+            gi2.replay()
+            ev2[i][1].record()
+            gc2.replay()
+            ev2[i][2].record()
+            gh2.replay()
+            ev2[i][3].record()
+        torch.cuda.synchronize()
+        tb2 = [sum(x[j].elapsed_time(x[j + 1]) for x in ev2) / (2 * R2) for j in range(3)]
+        n_c2, n_h2 = L2 // m, L2 // mp
+        row2 = D * 2
+        by2 = {"lightning_index_topk": B2 * n_c2 * 64 * 2 + B2 * HI * 64 * 2 + B2 * HI * 4 + B2 * k2 * 4,
+               "csa_sparse_mqa_attn": B2 * (k2 + W_) * row2 + B2 * k2 * 4 + 2 * B2 * H * D * 2 + B2 * H * 4,
+               "hca_dense_mqa_attn": B2 * (n_h2 + W_) * row2 + 2 * B2 * H * D * 2 + B2 * H * 4}
+        st2 = sum(by2.values())
+        comp["decode_bf16_128k"] = {
+            "workload": f"decode, bf16 stores: batch {B2}, context {L2}, 64 heads MQA dim 512, CSA m=4 top-k={k2} "
+                        f"with bf16 indexer keys (4 heads x 64), HCA m'=128, window 128; caches generated "
+                        f"already compressed, {R2} rotating input copies",
+            "ms_per_step": round(t2, 5), "query_tokens_per_s": round(B2 / (t2 * 1e-3)),
+            "step_bytes": st2, "gb_per_s": round(st2 / (t2 * 1e-3) / 1e9, 1),
+            "frac_hbm_step": round(st2 / (t2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "breakdown_ms": {k_: round(v, 5) for k_, v in zip(by2, tb2)},
+            "rooflines": {k_: {"bound": "hbm", "achieved": round(by2[k_] / (v * 1e-3) / 1e9, 1),
+                               "frac": round(by2[k_] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                          for k_, v in zip(by2, tb2)}}
+        del g2, parts2, runs2, cases2, base2, ws2
 
         log("indexer-key compression and decode_append")
         # indexer keys: the CSA compressor on 2^20 raw 64-dim bf16 keys into MXFP4 rows
@@ -587,10 +669,10 @@ def main():
             if el >= args.cpu_seconds or n_done >= 1024:  # the time bound decides; the count only caps it
                 break
         cpu = {"value": round(n_done / el, 4), "unit": "query-tokens/s", "cores": int(blas_threads),
-               "kind": "oracle",
+               "host_cpus": os.cpu_count(), "kind": "oracle",
                "sample": f"{n_done} decode query-tokens of the same 1M-context batch (index + CSA + HCA per "
-                         f"query, float64 numpy) in {el:.1f} s; elementwise numpy single-threaded, BLAS "
-                         f"on {blas_threads} threads"}
+                         f"query, float64 numpy) in {el:.1f} s; the matrix products run on {blas_threads} BLAS "
+                         f"threads, the elementwise numpy on one; the host has {os.cpu_count()} CPUs"}
 
     out = {
         "metric": "CSA+HCA decode query-tokens/s at 1M ctx; achieved HBM GB/s vs peak",
@@ -599,13 +681,18 @@ def main():
         "n_gpus": 1, "steps": K, "warmup": Wm,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "mxfp4+bf16 (fp32 accumulate)", "data": "synthetic",
+        "dtype": "fp8+bf16 MFMA, mxfp4 indexer",
+        "dtype_detail": "KV stored FP8 E4M3 (448 dims, power-of-two row scale) + bf16 (64 RoPE dims); "
+                        "QK^T on FP8 MFMA with each bf16 query split into two FP8 parts (exact for elements "
+                        "at least 2^-14 of their 32-dim block's maximum), RoPE dims and PV on bf16 MFMA, "
+                        "indexer MXFP4 scaled MFMA; fp32 accumulation and softmax",
+        "data": "synthetic",
         "config": {"workload": "decode at 1M context: batch 4, 64 heads MQA, KV 448 FP8 E4M3 + 64 bf16, "
                                "CSA m=4 top-k=1024 with MXFP4 indexer (4 heads x 64), HCA m'=128, window 128",
                    "batch": B, "context": L, "heads": H, "head_dim": D, "topk": k, "window": W_,
                    "graph": f"{R} rotating input copies per replay"},
         "gb_per_s": round(gbs, 1), "frac_hbm_step": round(gbs / HBM_PEAK_GBS, 4),
-        "tflops": round(tfs, 2),
+        "tflops": round(tfs, 2), "frac_bf16_mfma_step": round(tfs / BF16_PEAK_TFLOPS, 4),
         "step_bytes": step_bytes, "step_flops": step_flops,
         "breakdown_ms": {"lightning_index_topk": round(t_idx, 5), "csa_sparse_mqa_attn": round(t_csa, 5),
                          "hca_dense_mqa_attn": round(t_hca, 5)},

@@ -41,7 +41,7 @@ def split_store(t, prefix):
 
 
 class Workspace:
-    """Grow-only byte buffers reused across calls."""
+    """Grow-only byte buffers reused across calls (zero-filled when allocated)."""
 
     def __init__(self, dev):
         self.dev = dev
@@ -50,7 +50,7 @@ class Workspace:
     def get(self, name, nbytes):
         b = self.bufs.get(name)
         if b is None or b.numel() < nbytes:
-            b = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.dev)
+            b = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.dev)
             self.bufs[name] = b
         return b
 
@@ -262,6 +262,61 @@ class Decode1M:
         self.index(phase="select")
         self.csa_attention()
         main.wait_stream(self.side)
+
+
+class DecodeBf16:
+    """Decode step over precompressed bf16 stores (dense [n, D] rows) with bf16 indexer keys: index
+    (top-k), CSA attention over the selected entries and the window, HCA attention over all
+    visible entries and the window; outputs and workspaces preallocated, so that `step()` only
+    enqueues kernels."""
+
+    def __init__(self, case, ws=None):
+        p, t = case.params, case.t
+        self.case = case
+        dev = t["q"].device
+        self.ws = ws or Workspace(dev)
+        B, L, m, mp, W, k = p["B"], p["L"], p["m"], p["m_prime"], p["W"], p["topk"]
+        dn, dr = p["d_nope"], p["d_rope"]
+        self.B, self.m, self.mp, self.W, self.k = B, m, mp, W, k
+        self.n_c, self.n_h = L // m, L // mp
+        self.csa = Store.dense(t["csa_data"], dn, dr)
+        self.hca = Store.dense(t["hca_data"], dn, dr)
+        self.win = Store.dense(t["win_data"], dn, dr)
+        self.crb = _i64([b * self.n_c for b in range(B)], dev)
+        self.hrb = _i64([b * self.n_h for b in range(B)], dev)
+        self.wrb = _i64([b * W for b in range(B)], dev)
+        self.wp0 = _i64([L - W] * B, dev)
+        self.q = t["q"].view(torch.bfloat16)
+        self.scale = 1.0 / math.sqrt(dn + dr)
+        H, D = p["heads"], dn + dr
+        self.idx = torch.empty(B, k, dtype=torch.int32, device=dev)
+        self.o_csa = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
+        self.o_hca = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
+        self.lse_csa = torch.empty(B, H, dtype=torch.float32, device=dev)
+        self.lse_hca = torch.empty(B, H, dtype=torch.float32, device=dev)
+        self.ws.get("index", lightning_index_topk_workspace(B, self.n_c, k))
+        self.ws.get("csa", mqa_attn_workspace(BF16, B, H, D, k + W))
+        self.ws.get("hca", mqa_attn_workspace(BF16, B, H, D, self.n_h + W))
+
+    def index(self):
+        t = self.case.t
+        return index_topk(t["q_idx"], t["w_idx"], t["k_idx"], self.crb, t["q_seq"], t["q_pos"], self.n_c, self.m,
+                          self.k, self.ws, out=self.idx)
+
+    def csa_attention(self):
+        t = self.case.t
+        return csa_attn(self.q, self.csa, self.crb, self.idx, self.win, self.wrb, self.wp0, self.W, t["q_seq"],
+                        t["q_pos"], self.scale, self.ws, o=self.o_csa, lse=self.lse_csa)
+
+    def hca_attention(self):
+        t = self.case.t
+        return hca_attn(self.q, self.hca, self.hrb, self.mp, self.n_h, self.win, self.wrb, self.wp0, self.W,
+                        t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_hca, lse=self.lse_hca)
+
+    def step(self):
+        self.index()
+        self.csa_attention()
+        self.hca_attention()
 
 
 def compress_1m(case, out_csa=None, out_hca=None, stream=None):

@@ -121,12 +121,14 @@ def decode_1m_query(p, a, b):
     return dict(idx=idx, scores=s, o_csa=o_c, lse_csa=l_c, o_hca=o_h, lse_hca=l_h)
 
 
-def prefill_query(p, a, qi, chunk_csa, chunk_hca, split_window=False):
+def prefill_query(p, a, qi, chunk_csa, chunk_hca, split_window=False, memo=None):
     """One chunked-prefill query. chunk_csa/chunk_hca: callables (b) -> the oracle's own decoded
     entries of sequence b's chunk (compressed from the raw chunk rows). split_window: the window
     rows are held in the cache layout (DeepSeek-V4 page, efficiency section: FP8 for the
     non-RoPE dims, BF16 for the RoPE dims), so attention sees each raw row after the oracle's
-    own split encoding and decoding; otherwise it sees the raw bf16 rows."""
+    own split encoding and decoding; otherwise it sees the raw bf16 rows. memo: an optional dict
+    that keeps each sequence's decoded keys, entries and window rows between calls (the same
+    arrays, decoded once)."""
     m, mp, W, k, chunk = p["m"], p["m_prime"], p["W"], p["topk"], p["chunk"]
     dn, dr = p["d_nope"], p["d_rope"]
     b = int(a["q_seq"][qi])
@@ -134,15 +136,20 @@ def prefill_query(p, a, qi, chunk_csa, chunk_hca, split_window=False):
     P = p["prefixes"][b]
     crb, hrb = p["csa_row_begin"][b], p["hca_row_begin"][b]
     n_c, n_h = (P + chunk) // m, (P + chunk) // mp
-    qd = codecs.decode_mxfp4(a["q_idx"][qi], a["q_idx_scale"][qi])
-    keys = codecs.decode_mxfp4(a["k_idx"][crb:crb + n_c], a["k_idx_scale"][crb:crb + n_c])
-    idx, s = _index_one(qd, a["w_idx"][qi], keys, t, m, k, True)
-    csa_ent = np.concatenate([split_rows(a, "csa", np.arange(crb, crb + P // m)), chunk_csa(b)])
-    hca_ent = np.concatenate([split_rows(a, "hca", np.arange(hrb, hrb + P // mp)), chunk_hca(b)])
     rows = W + chunk
-    raw = _f64(a["raw"][b * rows:(b + 1) * rows], "bf16")
-    if split_window:
-        raw = compress.decode(compress.encode(raw, "split", dn, dr), "split")
+    memo = {} if memo is None else memo
+    key = (b, bool(split_window))
+    if key not in memo:
+        keys = codecs.decode_mxfp4(a["k_idx"][crb:crb + n_c], a["k_idx_scale"][crb:crb + n_c])
+        csa_ent = np.concatenate([split_rows(a, "csa", np.arange(crb, crb + P // m)), chunk_csa(b)])
+        hca_ent = np.concatenate([split_rows(a, "hca", np.arange(hrb, hrb + P // mp)), chunk_hca(b)])
+        raw = _f64(a["raw"][b * rows:(b + 1) * rows], "bf16")
+        if split_window:
+            raw = compress.decode(compress.encode(raw, "split", dn, dr), "split")
+        memo[key] = (keys, csa_ent, hca_ent, raw)
+    keys, csa_ent, hca_ent, raw = memo[key]
+    qd = codecs.decode_mxfp4(a["q_idx"][qi], a["q_idx_scale"][qi])
+    idx, s = _index_one(qd, a["w_idx"][qi], keys, t, m, k, True)
     win = lambda pos: raw[np.asarray(pos) - (P - W)]
     scale = 1.0 / np.sqrt(dn + dr)
     q = _f64(a["q"][qi], "bf16")

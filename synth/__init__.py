@@ -162,6 +162,29 @@ def decode_1m(seed=1003, device="cpu", B=4, L=1 << 20, heads=64, d_nope=448, d_r
     return c
 
 
+def decode_bf16_caches(seed=1012, device="cpu", B=8, L=131072, heads=64, d_nope=448, d_rope=64, m=4, topk=512,
+                       n_idx_heads=4, d_idx=64, m_prime=128, W=128, csa_store=None):
+    """Decode over bf16 stores with the caches generated already compressed (for timing the
+    decode step at the bf16 configuration without compressing B * L raw tokens first): bf16
+    CSA and HCA entries [n, D] and window rows [B * W, D] N(0, 1), bf16 indexer keys and
+    queries N(0, 1), head weights N(0, 1)/8. `csa_store` lets draws share one CSA store."""
+    g = generator(seed, device)
+    D = d_nope + d_rope
+    n_c, n_h = L // m, L // m_prime
+    c = Case(dict(B=B, L=L, nq=B, heads=heads, d_nope=d_nope, d_rope=d_rope, D=D, m=m,
+                  topk=topk, n_idx_heads=n_idx_heads, d_idx=d_idx, m_prime=m_prime, W=W))
+    c.t["q"] = bf16_bits(normal(g, (B, heads, D)))
+    c.t["q_idx"] = bf16_bits(normal(g, (B, n_idx_heads, d_idx)))
+    c.t["w_idx"] = normal(g, (B, n_idx_heads), 0.125)
+    c.t["k_idx"] = bf16_bits(normal(g, (B * n_c, d_idx)))
+    c.t["hca_data"] = bf16_bits(normal(g, (B * n_h, D)))
+    c.t["win_data"] = bf16_bits(normal(g, (B * W, D)))
+    c.t["csa_data"] = csa_store if csa_store is not None else bf16_bits(normal(g, (B * n_c, D)))
+    c.t["q_pos"] = torch.full((B,), L - 1, dtype=torch.int64, device=device)
+    c.t["q_seq"] = torch.arange(B, dtype=torch.int32, device=device)
+    return c
+
+
 def compression(seed=1004, device="cpu", L=1 << 20, d_nope=448, d_rope=64, m=4, w=8, m_prime=128):
     """Compression throughput: one sequence of L raw bf16 tokens."""
     g = generator(seed, device)

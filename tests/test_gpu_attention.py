@@ -277,3 +277,54 @@ def test_fp32_sixteen_heads_of_512(hca):
         check_attention(o[i], lse[i], ro, rl, "fp32", f"hca q{i}")
         ro, rl = OA.csa(qd, t, dec, idx[i], dec, W, scale)
         check_attention(o2[i], lse2[i], ro, rl, "fp32", f"csa q{i}")
+
+
+@pytest.mark.parametrize("nq", [3, 300])
+def test_query_blocks_with_one_large_element(hca, nq):
+    """Adversarial queries for the FP8 score path, which splits each bf16 query into two FP8 parts
+    with one power-of-two scale per 32 dims: every 32-dim block holds one element of magnitude
+    ~30-60, the others N(0, 1), and a quarter of them near 1e-3 (below E4M3's normal range under
+    the block's scale). bf16 elements at least 2^-14 of their block's maximum are carried exactly
+    by the two parts and smaller ones to within 2^-21 of that maximum, so attention must match
+    the oracle at the usual tolerance. nq = 3 runs the per-head-group kernel, 300 the row-owning
+    one."""
+    m, W_ = hca
+    dev = "cuda"
+    n_cache, W, k, mp = 1200, 64, 256, 8
+    cache_st, cache_dec = make_store("split", n_cache, 61)
+    cache = to_store(m, cache_st, 448, 64)
+    g = synth.generator(63)
+    H, D = 64, 512
+    q = synth.normal(g, (nq, H, D))
+    tiny = torch.rand((nq, H, D), generator=g) < 0.25
+    q = torch.where(tiny, q * 1e-3, q)
+    big_at = torch.randint(0, 32, (nq, H, D // 32), generator=g) + 32 * torch.arange(D // 32)
+    big = (30.0 + 30.0 * torch.rand((nq, H, D // 32), generator=g)) * torch.sign(synth.normal(g, (nq, H, D // 32)))
+    q.scatter_(2, big_at, big)
+    q = q.bfloat16()
+    qdec = q.double().numpy()
+    rng = np.random.default_rng(64)
+    q_pos = rng.integers(W + 200, n_cache, nq).astype(np.int64)
+    idx = np.full((nq, k), -1, np.int32)
+    for i, t in enumerate(q_pos):
+        n = min(k, int(t + 1) // 4)
+        idx[i, :n] = np.sort(rng.choice(int(t + 1) // 4, size=n, replace=False))
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=dev)
+    seq = torch.zeros(nq, dtype=torch.int32, device=dev)
+    pos = torch.tensor(q_pos, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    ws = W_.Workspace(dev)
+    # the cache rows double as the window store (row p holds raw position p)
+    o, lse = W_.csa_attn(q.to(dev), cache, i64([0]), torch.tensor(idx, device=dev), cache, i64([0]), i64([0]), W, seq,
+                         pos, scale, ws, o_dtype=torch.float32)
+    o2, lse2 = W_.hca_attn(q.to(dev), cache, i64([0]), mp, n_cache, cache, i64([0]), i64([0]), W, seq, pos, scale, ws,
+                           o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o, lse, o2, lse2 = np_(o), np_(lse), np_(o2), np_(lse2)
+    for i in range(min(nq, 24)):
+        t = int(q_pos[i])
+        ro, rl = OA.csa(qdec[i], t, cache_dec, idx[i], cache_dec, W, scale)
+        check_attention(o[i], lse[i], ro, rl, "low", f"csa q{i}")
+        nv = (t + 1) // mp
+        ro, rl = OA.attend(qdec[i], np.concatenate([cache_dec[:nv], cache_dec[OA.window_positions(t, W)]]), scale)
+        check_attention(o2[i], lse2[i], ro, rl, "low", f"hca q{i}")

@@ -72,7 +72,7 @@ def _decode_bf16_case(B, L, topk, dev="cpu"):
     raise AssertionError("no tie-free draw")
 
 
-@pytest.mark.parametrize("B,L,topk,seqs", [(3, 8192, 512, [0, 1, 2]), (8, 131072, 512, [0, 7])])
+@pytest.mark.parametrize("B,L,topk,seqs", [(3, 8192, 512, [0, 1, 2]), (8, 131072, 512, [0, 3, 5, 7])])
 def test_decode_bf16(W, B, L, topk, seqs):
     _say(f"decode_bf16 B={B} L={L}")
     c = _decode_bf16_case(B, L, topk, dev="cuda" if L > 8192 else "cpu")
@@ -146,7 +146,7 @@ def test_compression_split(W, L):
 
 @pytest.mark.parametrize("prefixes,chunk,nsample,window", [((4096, 8192, 16384), 512, 24, "bf16"),
                                                             ((4096, 8192, 16384), 512, 24, "split"),
-                                                            ((32768, 131072, 262144), 8192, 6, "split")])
+                                                            ((32768, 131072, 262144), 8192, 256, "split")])
 def test_chunked_prefill(W, prefixes, chunk, nsample, window):
     _say(f"prefill prefixes={prefixes} chunk={chunk} window={window}")
     c = synth.chunked_prefill(seed=1005, prefixes=prefixes, chunk=chunk, device="cuda")
@@ -171,8 +171,13 @@ def test_chunked_prefill(W, prefixes, chunk, nsample, window):
     picks = []
     for b in range(S):
         base = b * chunk
-        picks += [base, base + 1, base + chunk - 1] + list(base + rng.integers(0, chunk, nsample - 3))
-    picks = sorted(set(picks))
+        if nsample >= 256:
+            # the first 64 and last 64 queries of the chunk and 128 strided ones between them
+            picks += list(range(base, base + 64)) + list(range(base + chunk - 64, base + chunk))
+            picks += list(base + 64 + (np.arange(128) * (chunk - 128)) // 128)
+        else:
+            picks += [base, base + 1, base + chunk - 1] + list(base + rng.integers(0, chunk, nsample - 3))
+    picks = sorted(set(int(x) for x in picks))
     t = c.t
     a = dict(a_in)
     for k in ("q", "q_idx", "q_idx_scale", "w_idx"):
@@ -194,9 +199,12 @@ def test_chunked_prefill(W, prefixes, chunk, nsample, window):
         check_split_entries(np_(st.data)[rows], np_(st.scale)[rows], np_(st.rope)[rows], y_h, dn, f"hca chunk {b}", ya_h)
     o_c, l_c = np_(got["o_csa"][picks].float()), np_(got["lse_csa"][picks])
     o_h, l_h = np_(got["o_hca"][picks].float()), np_(got["lse_hca"][picks])
+    memo = {}
+    if len(picks) > 100:
+        _say(f"oracle over {len(picks)} sampled queries")
     for n, qi in enumerate(picks):
         r = OP.prefill_query(p, a, qi, lambda b: chunk_ent[b][1], lambda b: chunk_ent[b][3],
-                             split_window=window == "split")
+                             split_window=window == "split", memo=memo)
         check_idx(idx[qi], r["idx"], f"top-k query {qi}")
         check_attention(o_c[n], l_c[n], r["o_csa"], r["lse_csa"], "low", f"csa attention query {qi}")
         check_attention(o_h[n], l_h[n], r["o_hca"], r["lse_hca"], "low", f"hca attention query {qi}")
