@@ -218,10 +218,22 @@ size_t index_ws(int64_t nq, int64_t max_visible) { return hca::index_ws_layout(n
 
 uint8_t* align256(uint8_t* p) { return reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255)); }
 
-size_t attn_ws(int q_dtype, int64_t nq, int H, int D, int64_t max_entries, int* n_split, int* per) {
-  hca::attn_split_policy((int)nq, H, D, max_entries, q_dtype == HCA_BF16, n_split, per);
+// Split-K workspace of a launch: partial outputs [nq, n_split, H, D] and lse [nq, n_split, H]
+// (float32). `wide`: the 64-head kernel's policy, else the other kernels'.
+size_t attn_ws(int q_dtype, int64_t nq, int H, int D, int64_t max_entries, bool wide, int* n_split, int* per) {
+  if (wide) hca::attn_split_policy_wide((int)nq, H, max_entries, n_split, per);
+  else hca::attn_split_policy((int)nq, H, D, max_entries, q_dtype == HCA_BF16, n_split, per);
   if (*n_split <= 1) return 0;
   return 512 + (size_t)nq * (size_t)(*n_split) * (size_t)H * ((size_t)D + 1) * 4;
+}
+
+// Workspace for any store layout: the larger of the two policies where the 64-head kernel may run.
+size_t attn_ws_any(int q_dtype, int64_t nq, int H, int D, int64_t max_entries) {
+  int n_split, per;
+  size_t need = attn_ws(q_dtype, nq, H, D, max_entries, false, &n_split, &per);
+  if (q_dtype == HCA_BF16 && H % 64 == 0)
+    need = std::max(need, attn_ws(q_dtype, nq, H, D, max_entries, true, &n_split, &per));
+  return need;
 }
 
 int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
@@ -257,7 +269,8 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
   if (nq == 0) return HCA_OK;
   const int64_t max_entries = (csa ? (int64_t)k : max_visible) + W;
   int n_split = 1, per = 1;
-  const size_t need = attn_ws(q_dtype, nq, n_heads, D, max_entries, &n_split, &per);
+  const bool wide = hca::attn_wide_supported(q_dtype, cv, wv, n_heads);
+  const size_t need = attn_ws(q_dtype, nq, n_heads, D, max_entries, wide, &n_split, &per);
   if (static_scratch) {
     // the library's static device scratch stands in for the workspace (no allocation)
     if (need > hca::kNoallocScratchBytes)
@@ -469,8 +482,7 @@ HCA_EXPORT int lightning_index_select(HCA_INDEX_ARGS) {
 
 HCA_EXPORT size_t mqa_attn_workspace(int32_t q_dtype, int32_t nq, int32_t n_heads, int32_t d, int64_t max_entries) {
   if (nq <= 0 || n_heads < 1 || d < 1 || max_entries < 0) return 0;
-  int n_split, per;
-  return attn_ws(q_dtype, nq, n_heads, d, max_entries, &n_split, &per);
+  return attn_ws_any(q_dtype, nq, n_heads, d, max_entries);
 }
 
 HCA_EXPORT int csa_sparse_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads, const hca_store* cache,

@@ -1269,6 +1269,329 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs a, int total
 }
 
 // ---------------------------------------------------------------------------------------
+// Wide FP8 kernel: one block serves 64 heads (a group of 64 of the query's heads), so every
+// staged row is used by all 64 heads (attn_fp8_kernel stages each row once per group of 16
+// heads, in four blocks). block = (query, 64-head group, split), 8 waves: wave w computes for
+// heads 16 (w & 3) .. +15 of the group, and works on half h = w >> 2 of each chunk.
+//  * chunks of 64 entries, double buffered in LDS; wave w stages entries 8w .. 8w + 7 of the
+//    next chunk with 5 lane-linear 1 KiB global_load_lds DMAs (the scales and validity of
+//    every entry go through LDS once a chunk's rows have landed);
+//  * S^T = K Q^T for entries 32h .. 32h + 31 (two tiles of 16) and the wave's 16 heads, on the
+//    scaled FP8 MFMA with the query split into two FP8 parts, RoPE dims on bf16 MFMA, as in
+//    attn_fp8_kernel;
+//  * the two waves of a head group (halves 0 and 1) share one reference maximum per head (their
+//    chunk maxima meet in LDS, lazy rescale) and write P for their 32 entries to LDS, with and
+//    without the entry scales;
+//  * O^T += V^T P^T over all 64 entries of the chunk, split by output dims: half 0 owns FP8
+//    dims 0 .. 255, half 1 FP8 dims 256 .. 447 and the 64 RoPE dims (16 tiles of 16 dims each),
+//    V^T from ds_read_b64_tr_b8 / tr_b16 transpose reads.
+constexpr int kWCh = 64;                                  // entries per chunk
+constexpr int kWBuf = kWCh * kRowF8;                      // 37,888 bytes
+constexpr int kWPRow = kWCh + 8;                          // bf16 per P row (padded)
+constexpr int kWStage = kWCh / 8;                         // rows staged per wave and chunk
+constexpr int kWDmas = (kWStage * kRowF8 + 1023) / 1024;  // 5 DMAs of up to 1 KiB
+
+// The rows one wave stages for a chunk (list positions base .. base + 7).
+struct WideRows {
+  uint64_t src;    // lane e < 8: FP8-row address of entry e; lane 8 + e: its RoPE-row address - 448
+  float esc;       // lane e < 8: entry scale (its load left in flight)
+  uint32_t vmask;  // valid entries, bits 0 .. 7
+};
+
+template <bool kSparse>
+__device__ __forceinline__ int32_t wide_slot(const AttnArgs& a, int qi, int64_t base, int lane) {
+  if (!kSparse) return 0;
+  const int64_t r = min<int64_t>(base + (lane & 7), (int64_t)a.k - 1);
+  return a.idx[(int64_t)qi * a.k + r];
+}
+
+template <bool kSparse>
+__device__ __forceinline__ WideRows wide_rows(const AttnArgs& a, const QueryCtx& ctx, int64_t base, int64_t hi,
+                                              int32_t slot, int lane) {
+  WideRows w;
+  const int e = lane & 7;
+  const int64_t r = base + e;
+  const bool win = r >= ctx.n_c;
+  int64_t row = -1;
+  if (lane < 16 && r < hi) {
+    if (!win) {
+      const int64_t j = kSparse ? (int64_t)slot : r;
+      const int64_t cr = ctx.cache_rb + j;
+      row = (j >= 0 && cr >= 0 && cr < a.cache.n_rows) ? cr : -1;
+    } else if (r < ctx.n_c + ctx.n_w) {
+      const int64_t pos = ctx.t - ctx.n_w + 1 + (r - ctx.n_c);
+      const int64_t wr = ctx.win_rb + (pos - ctx.win_p0);
+      row = (wr >= 0 && wr < a.win.n_rows) ? wr : -1;
+    }
+  }
+  const uint64_t data = win ? reinterpret_cast<uint64_t>(a.win.data) : reinterpret_cast<uint64_t>(a.cache.data);
+  const uint64_t rope = win ? reinterpret_cast<uint64_t>(a.win.rope) : reinterpret_cast<uint64_t>(a.cache.rope);
+  const int64_t rs = win ? a.win.row_stride : a.cache.row_stride;
+  const int64_t ps = win ? a.win.rope_stride : a.cache.rope_stride;
+  const float* scale = win ? a.win.scale : a.cache.scale;
+  const int64_t rr = row >= 0 ? row : 0;  // invalid entries are never loaded
+  w.src = lane < 8 ? data + (uint64_t)(rr * rs) : rope + (uint64_t)(rr * ps * 2) - kNope;
+  w.esc = (lane < 8 && row >= 0) ? scale[row] : 0.f;
+  w.vmask = (uint32_t)__ballot(lane < 8 && row >= 0) & 0xFFu;
+  return w;
+}
+
+// Invalid rows of a wave's 8 are zeroed (their masked P = 0 must never meet a NaN); this precedes
+// the DMAs into the same buffer.
+__device__ __forceinline__ void wide_zero_invalid(const WideRows& w, uint8_t* dst, int lane) {
+  uint32_t inval = ~w.vmask & 0xFFu;
+  while (inval) {
+    const int e = __builtin_ctz(inval);
+    inval &= inval - 1;
+    if (lane < kRowF8 / 16) *reinterpret_cast<uint4*>(dst + e * kRowF8 + 16 * lane) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// The wave's 8 rows (8 x 592 = 4,736 LDS bytes): LDS byte b = 1024 i + 16 lane is entry b / 592,
+// byte b % 592 (FP8 bytes, RoPE bytes, 16 pad bytes); lanes on padding, past the rows or on an
+// invalid row stay idle.
+__device__ __forceinline__ void wide_stage(const WideRows& w, uint8_t* dst, int lane) {
+#pragma unroll
+  for (int i = 0; i < kWDmas; ++i) {
+    const int b = 1024 * i + 16 * lane;
+    const int e = b / kRowF8, o = b - e * kRowF8;
+    const int sl = (o < kNope ? e : 8 + e) & 63;
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)w.src, sl, 64);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(w.src >> 32), sl, 64);
+    const uint64_t src = (((uint64_t)hi << 32) | lo) + (uint64_t)o;
+    if (e < kWStage && o < kNope + 2 * kRope && ((w.vmask >> (e & 7)) & 1))
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+  }
+}
+
+struct WideLds {
+  float esc[kWCh];            // entry scales of the chunk being computed
+  uint32_t vm[8];             // validity, 8 entries per staging wave
+  float wmax[8][16], wsum[8][16];
+};
+
+struct WideState {
+  f32x4 O[16];
+  float m_run, l_part;
+  WideRows cur, nxt;  // rows of this chunk (staged) and of the next one (known)
+  int32_t slot2;      // slot values of the chunk after next
+};
+
+// One chunk in buf whose rows this wave requested a chunk earlier: publish the chunk's scales and
+// validity, wait for every wave's rows, request the next chunk's rows into nbuf, then scores,
+// softmax, P to LDS and PV. The chunk buffers are distinct LDS objects, so reads of buf need not
+// wait for the DMAs into nbuf.
+template <bool kSparse>
+__device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ctx, int qi, int64_t base, int64_t hi,
+                                           const uint8_t* buf, uint8_t* nbuf, const F8Query& q, WideState& st,
+                                           uint16_t* ps, uint16_t* pp, WideLds& wl, float sl2, int wave, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int hg = wave & 3, hf = wave >> 2;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows and entry scales of the chunk have landed
+  if (lane < 8) wl.esc[8 * wave + lane] = st.cur.esc;
+  if (lane == 0) wl.vm[wave] = st.cur.vmask;
+  __syncthreads();  // every wave's rows; the other buffer is free
+  const bool more = base + kWCh < hi;
+  if (more) {
+    uint8_t* ndst = nbuf + kWStage * wave * kRowF8;
+    wide_zero_invalid(st.nxt, ndst, lane);
+    wide_stage(st.nxt, ndst, lane);
+  }
+  const int64_t b2 = base + 2 * kWCh + kWStage * wave;
+  st.cur = st.nxt;
+  st.nxt = wide_rows<kSparse>(a, ctx, b2, hi, st.slot2, lane);
+  st.slot2 = wide_slot<kSparse>(a, qi, b2 + kWCh, lane);
+
+  // scores of entries 32 hf + 16 u + 4 g + i (i < 4), head c of the wave's group
+  float sv[2][4];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e0 = 32 * hf + 16 * u;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, sr = s0;
+    const uint8_t* rowp = buf + (e0 + c) * kRowF8 + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(rowp + 128 * ks);
+      uint4 x1 = make_uint4(0, 0, 0, 0);  // dims 448.. (K step 3, bytes 16-31) are RoPE bytes: zero
+      if (ks < 3) x1 = *reinterpret_cast<const uint4*>(rowp + 128 * ks + 64);
+      const i32x8 A = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.qh[ks], s0, 0, 0, 0, 127, 0,
+                                                             (int)((q.sh >> (8 * ks)) & 255u));
+      s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.ql[ks], s1, 0, 0, 0, 127, 0,
+                                                             (int)((q.sl >> (8 * ks)) & 255u));
+    }
+    const uint8_t* ropep = buf + (e0 + c) * kRowF8 + kNope + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ropep + 64 * ks));
+      sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q.qr[ks], sr, 0, 0, 0);
+    }
+    const float4 e4 = *reinterpret_cast<const float4*>(wl.esc + e0 + 4 * g);
+    const float esc[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + 4 * g + i;
+      const float v = fmaf(esc[i], s0[i] + s1[i], sr[i]);
+      sv[u][i] = ((wl.vm[e >> 3] >> (e & 7)) & 1) ? v * sl2 : -INFINITY;
+      cmax = fmaxf(cmax, sv[u][i]);
+    }
+  }
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  if (g == 0) wl.wmax[wave][c] = cmax;
+  lds_barrier();
+  cmax = fmaxf(wl.wmax[hg][c], wl.wmax[hg + 4][c]);
+  // lazy rescaling (both waves of the group see the same maxima, so they agree on the reference)
+  const bool grow = cmax > st.m_run + 8.f;
+  const float m_ref = grow ? cmax : st.m_run;
+  const bool none = m_ref == -INFINITY;
+  const float corr = grow ? exp2f(st.m_run - cmax) : 1.f;
+  float psum = 0.f;
+  {
+    const int prow = (16 * hg + c) * kWPRow;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e0 = 32 * hf + 16 * u + 4 * g;
+      const float4 e4 = *reinterpret_cast<const float4*>(wl.esc + e0);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = none ? 0.f : exp2f(sv[u][i] - m_ref);
+        psum += p[i];
+      }
+      *reinterpret_cast<uint2*>(ps + prow + e0) =
+          make_uint2(pack_bf16x2(p[0] * e4.x, p[1] * e4.y), pack_bf16x2(p[2] * e4.z, p[3] * e4.w));
+      *reinterpret_cast<uint2*>(pp + prow + e0) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    }
+  }
+  st.l_part = st.l_part * corr + psum;
+  st.m_run = m_ref;
+  if (__ballot(grow)) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st.O[j] *= corr;
+  }
+  lds_barrier();
+  // O^T (16 tiles of 16 dims x the wave's 16 heads) += V^T P^T over the chunk's 64 entries
+  const int prow = (16 * hg + c) * kWPRow;
+  const int r = c >> 1, hsel = c & 1;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const bf16x8 Bs = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ps + prow + 32 * kk + 8 * g));
+    const uint8_t* vp = buf + (32 * kk + 8 * g + r) * kRowF8 + 256 * hf + 8 * hsel;
+    const int nf = hf == 0 ? 16 : 12;  // FP8 dim tiles of this half
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < nf) {
+        const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * j));
+        st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]), Bs,
+                                                          st.O[j], 0, 0, 0);
+      }
+    }
+    if (hf == 1) {
+      const bf16x8 Br = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pp + prow + 32 * kk + 8 * g));
+      const int rs = c >> 2, qd = c & 3;
+      const uint8_t* v0 = buf + (32 * kk + 8 * g + rs) * kRowF8 + kNope + 8 * qd;
+      const uint8_t* v1 = v0 + 4 * kRowF8;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * dt));
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * dt));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.O[12 + dt] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), Br, st.O[12 + dt], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <bool kSparse>
+__global__ __launch_bounds__(512, 1) void attn_wide_kernel(AttnArgs a, int n_hg, int total) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[kWBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[kWBuf];
+  __shared__ __attribute__((aligned(16))) uint16_t ps[64 * kWPRow];  // [64 heads][entries] P x entry scale
+  __shared__ __attribute__((aligned(16))) uint16_t pp[64 * kWPRow];  // [64 heads][entries] P
+  __shared__ __attribute__((aligned(16))) WideLds wl;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= total) return;
+  const int s = id % a.n_split;
+  const int rest = id / a.n_split;
+  const int hg64 = rest % n_hg;
+  const int qi = rest / n_hg;
+  const int H = a.H;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int hg = wave & 3, hf = wave >> 2;
+  const int head = 64 * hg64 + 16 * hg + c;
+
+  const int64_t lo = (int64_t)s * a.per_split;
+  const int64_t b0 = lo + kWStage * wave;
+  const int32_t s0 = wide_slot<kSparse>(a, qi, b0, lane), s1 = wide_slot<kSparse>(a, qi, b0 + kWCh, lane);
+  WideState st;
+  st.slot2 = wide_slot<kSparse>(a, qi, b0 + 2 * kWCh, lane);
+  const QueryCtx ctx = query_ctx(a, qi);
+  const int64_t N = ctx.n_c + ctx.n_w;
+  const int64_t hi = min<int64_t>(N, lo + a.per_split);
+  st.cur = wide_rows<kSparse>(a, ctx, b0, hi, s0, lane);
+  st.nxt = wide_rows<kSparse>(a, ctx, b0 + kWCh, hi, s1, lane);
+  if (lo < hi) {
+    uint8_t* dst = buf0 + kWStage * wave * kRowF8;
+    wide_zero_invalid(st.cur, dst, lane);
+    wide_stage(st.cur, dst, lane);
+  }
+  // the first chunk's rows are in flight while the query is split into its FP8 parts
+  const F8Query q = rows_query(static_cast<const uint16_t*>(a.q) + ((int64_t)qi * H + head) * kD, lane);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) st.O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
+  const float sl2 = a.scale * kLog2e;
+  // unrolled by two so that each call names its chunk buffers statically
+  for (int64_t base = lo; base < hi; base += 2 * kWCh) {
+    wide_chunk<kSparse>(a, ctx, qi, base, hi, buf0, buf1, q, st, ps, pp, wl, sl2, wave, lane);
+    if (base + kWCh >= hi) break;
+    wide_chunk<kSparse>(a, ctx, qi, base + kWCh, hi, buf1, buf0, q, st, ps, pp, wl, sl2, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // the softmax denominator of head c: this lane's entries, the lane groups, then the two halves
+  float L = st.l_part;
+  L += __shfl_xor(L, 16, 64);
+  L += __shfl_xor(L, 32, 64);
+  if (g == 0) wl.wsum[wave][c] = L;
+  __syncthreads();
+  L = wl.wsum[hg][c] + wl.wsum[hg + 4][c];
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float lse = L > 0.f ? (st.m_run + log2f(L)) * kLn2 : -INFINITY;
+  int head_o = head;
+  asm volatile("" : "+v"(head_o));
+  const int64_t hrow = (int64_t)qi * H + head_o;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    // half 0: FP8 dims 16 j + 4 g; half 1: FP8 dims 256 + 16 j (j < 12), then RoPE dims 448 + 16 (j - 12)
+    const int d = 256 * hf + 16 * j + 4 * g;
+    const f32x4 acc = st.O[j] * inv;
+    if (a.n_split == 1) {
+      if (a.o_dtype == HCA_BF16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + hrow * kD + d) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + hrow * kD + d) = acc;
+      }
+    } else {
+      const int64_t pi = ((int64_t)qi * a.n_split + s) * H + head_o;
+      *reinterpret_cast<f32x4*>(a.part_o + pi * kD + d) = acc;
+    }
+  }
+  if (hf == 0 && g == 0) {
+    if (a.n_split == 1) a.lse[hrow] = lse;
+    else a.part_lse[((int64_t)qi * a.n_split + s) * H + head_o] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Log-sum-exp merge of the split partials of one (query, head) over the dims held by a lane
 // (V = f32x4 for 4 dims at po + d, float for one). The lse values and partial outputs of kG
 // splits are loaded at once (positions past S clamp to the last split and get weight 0), so a
@@ -1374,6 +1697,21 @@ void attn_split_policy(int nq, int H, int D, int64_t max_entries, bool mfma, int
   *per_split = (int)per;
 }
 
+// The wide kernel: blocks of 64 heads and chunks of 64 entries; about 256 blocks in all (one per
+// CU), each split a whole number of chunks.
+void attn_split_policy_wide(int nq, int H, int64_t max_entries, int* n_split, int* per_split) {
+  const int64_t blocks_per_split = (int64_t)nq * std::max(1, H / 64);
+  const int64_t want = std::max<int64_t>(1, (256 + blocks_per_split - 1) / blocks_per_split);
+  const int64_t chunks = std::max<int64_t>(1, (max_entries + kWCh - 1) / kWCh);
+  const int64_t per = ((chunks + want - 1) / want) * kWCh;
+  *per_split = (int)per;
+  *n_split = (int)std::max<int64_t>(1, (max_entries + per - 1) / per);
+}
+
+bool attn_wide_supported(int q_dtype, const StoreView& c, const StoreView& w, int H) {
+  return q_dtype == HCA_BF16 && H % 64 == 0 && attn_fp8_supported(c, w);
+}
+
 // The row-owning kernel serves all 64 heads of a query per block. It is chosen when there are
 // enough (query, split) blocks to fill the chip on their own (many queries, as in prefill);
 // with few queries the per-head-group kernel's four blocks per split range fill it better.
@@ -1384,7 +1722,13 @@ bool attn_rows_eligible(const AttnArgs& a) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const bool mfma = a.q_dtype == HCA_BF16;
   const bool fp8 = mfma && attn_fp8_supported(a.cache, a.win);
-  if (fp8 && attn_rows_eligible(a)) {
+  if (attn_wide_supported(a.q_dtype, a.cache, a.win, a.H)) {
+    const int n_hg = a.H / 64;
+    const int total = a.nq * a.n_split * n_hg;
+    const int grid = (total + 7) / 8 * 8;
+    if (a.idx) hipLaunchKernelGGL(attn_wide_kernel<true>, dim3(grid), dim3(512), 0, s, a, n_hg, total);
+    else hipLaunchKernelGGL(attn_wide_kernel<false>, dim3(grid), dim3(512), 0, s, a, n_hg, total);
+  } else if (fp8 && attn_rows_eligible(a)) {
     const int total = a.nq * a.n_split;
     const int grid = (total + 7) / 8 * 8;
     if (a.idx) hipLaunchKernelGGL(attn_rows_kernel<true>, dim3(grid), dim3(64 * kRowsWaves), 0, s, a, total);
