@@ -231,7 +231,7 @@ size_t attn_ws(int q_dtype, int64_t nq, int H, int D, int64_t max_entries, bool 
 size_t attn_ws_any(int q_dtype, int64_t nq, int H, int D, int64_t max_entries) {
   int n_split, per;
   size_t need = attn_ws(q_dtype, nq, H, D, max_entries, false, &n_split, &per);
-  if (q_dtype == HCA_BF16 && H % 64 == 0)
+  if (q_dtype == HCA_BF16 && H % 64 == 0 && nq >= 64)
     need = std::max(need, attn_ws(q_dtype, nq, H, D, max_entries, true, &n_split, &per));
   return need;
 }
@@ -269,7 +269,7 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
   if (nq == 0) return HCA_OK;
   const int64_t max_entries = (csa ? (int64_t)k : max_visible) + W;
   int n_split = 1, per = 1;
-  const bool wide = hca::attn_wide_supported(q_dtype, cv, wv, n_heads);
+  const bool wide = hca::attn_wide_supported(q_dtype, cv, wv, n_heads, nq);
   const size_t need = attn_ws(q_dtype, nq, n_heads, D, max_entries, wide, &n_split, &per);
   if (static_scratch) {
     // the library's static device scratch stands in for the workspace (no allocation)

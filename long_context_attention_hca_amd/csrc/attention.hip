@@ -1708,8 +1708,10 @@ void attn_split_policy_wide(int nq, int H, int64_t max_entries, int* n_split, in
   *n_split = (int)std::max<int64_t>(1, (max_entries + per - 1) / per);
 }
 
-bool attn_wide_supported(int q_dtype, const StoreView& c, const StoreView& w, int H) {
-  return q_dtype == HCA_BF16 && H % 64 == 0 && attn_fp8_supported(c, w);
+// Taken for calls with many queries (prefill); decode keeps attn_fp8_kernel, whose 16-head blocks
+// write a quarter of the split-K partials.
+bool attn_wide_supported(int q_dtype, const StoreView& c, const StoreView& w, int H, int nq) {
+  return q_dtype == HCA_BF16 && H % 64 == 0 && nq >= 64 && attn_fp8_supported(c, w);
 }
 
 // The row-owning kernel serves all 64 heads of a query per block. It is chosen when there are
@@ -1722,7 +1724,7 @@ bool attn_rows_eligible(const AttnArgs& a) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const bool mfma = a.q_dtype == HCA_BF16;
   const bool fp8 = mfma && attn_fp8_supported(a.cache, a.win);
-  if (attn_wide_supported(a.q_dtype, a.cache, a.win, a.H)) {
+  if (attn_wide_supported(a.q_dtype, a.cache, a.win, a.H, a.nq)) {
     const int n_hg = a.H / 64;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;

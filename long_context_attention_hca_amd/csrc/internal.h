@@ -133,7 +133,7 @@ bool attn_mfma_supported(int q_dtype, int o_dtype, const StoreView& c, const Sto
                          int D);
 // The 64-head FP8 kernel (bf16 queries, split stores of 448 + 64 dims, H a multiple of 64) and its
 // split policy.
-bool attn_wide_supported(int q_dtype, const StoreView& c, const StoreView& w, int H);
+bool attn_wide_supported(int q_dtype, const StoreView& c, const StoreView& w, int H, int nq);
 void attn_split_policy_wide(int nq, int H, int64_t max_entries, int* n_split, int* per_split);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 // The static scratch of hca_dense_mqa_attn_noalloc: its size, and its device address on the
