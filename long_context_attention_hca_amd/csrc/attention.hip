@@ -1272,136 +1272,71 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs a, int total
 // Wide FP8 kernel: one block serves 64 heads (a group of 64 of the query's heads), so every
 // staged row is used by all 64 heads (attn_fp8_kernel stages each row once per group of 16
 // heads, in four blocks). block = (query, 64-head group, split), 8 waves: wave w computes for
-// heads 16 (w & 3) .. +15 of the group, and works on half h = w >> 2 of each chunk.
-//  * chunks of 64 entries, double buffered in LDS; wave w stages entries 8w .. 8w + 7 of the
-//    next chunk with 5 lane-linear 1 KiB global_load_lds DMAs (the scales and validity of
-//    every entry go through LDS once a chunk's rows have landed);
+// heads 16 (w & 3) .. +15 of the group and works on half h = w >> 2 of each chunk; the two waves
+// of a head group share a SIMD.
+//  * chunks of 64 entries, double buffered in LDS. The half-1 waves stage them: wave 4 + v
+//    requests entries 16v .. 16v + 15 of the next chunk with 10 lane-linear 1 KiB global_load_lds
+//    DMAs, while the half-0 wave on its SIMD starts the scores; a stager's rows for the chunk after
+//    next (with their scale loads) are found after PV, where no DMAs are queued. The scales and
+//    validity of every entry go through LDS once a chunk's rows have landed;
 //  * S^T = K Q^T for entries 32h .. 32h + 31 (two tiles of 16) and the wave's 16 heads, on the
 //    scaled FP8 MFMA with the query split into two FP8 parts, RoPE dims on bf16 MFMA, as in
 //    attn_fp8_kernel;
-//  * the two waves of a head group (halves 0 and 1) share one reference maximum per head (their
-//    chunk maxima meet in LDS, lazy rescale) and write P for their 32 entries to LDS, with and
-//    without the entry scales;
-//  * O^T += V^T P^T over all 64 entries of the chunk, split by output dims: half 0 owns FP8
-//    dims 0 .. 255, half 1 FP8 dims 256 .. 447 and the 64 RoPE dims (16 tiles of 16 dims each),
-//    V^T from ds_read_b64_tr_b8 / tr_b16 transpose reads.
-constexpr int kWCh = 64;                                  // entries per chunk
-constexpr int kWBuf = kWCh * kRowF8;                      // 37,888 bytes
-constexpr int kWPRow = kWCh + 8;                          // bf16 per P row (padded)
-constexpr int kWStage = kWCh / 8;                         // rows staged per wave and chunk
-constexpr int kWDmas = (kWStage * kRowF8 + 1023) / 1024;  // 5 DMAs of up to 1 KiB
-
-// The rows one wave stages for a chunk (list positions base .. base + 7).
-struct WideRows {
-  uint64_t src;    // lane e < 8: FP8-row address of entry e; lane 8 + e: its RoPE-row address - 448
-  float esc;       // lane e < 8: entry scale (its load left in flight)
-  uint32_t vmask;  // valid entries, bits 0 .. 7
-};
-
-template <bool kSparse>
-__device__ __forceinline__ int32_t wide_slot(const AttnArgs& a, int qi, int64_t base, int lane) {
-  if (!kSparse) return 0;
-  const int64_t r = min<int64_t>(base + (lane & 7), (int64_t)a.k - 1);
-  return a.idx[(int64_t)qi * a.k + r];
-}
-
-template <bool kSparse>
-__device__ __forceinline__ WideRows wide_rows(const AttnArgs& a, const QueryCtx& ctx, int64_t base, int64_t hi,
-                                              int32_t slot, int lane) {
-  WideRows w;
-  const int e = lane & 7;
-  const int64_t r = base + e;
-  const bool win = r >= ctx.n_c;
-  int64_t row = -1;
-  if (lane < 16 && r < hi) {
-    if (!win) {
-      const int64_t j = kSparse ? (int64_t)slot : r;
-      const int64_t cr = ctx.cache_rb + j;
-      row = (j >= 0 && cr >= 0 && cr < a.cache.n_rows) ? cr : -1;
-    } else if (r < ctx.n_c + ctx.n_w) {
-      const int64_t pos = ctx.t - ctx.n_w + 1 + (r - ctx.n_c);
-      const int64_t wr = ctx.win_rb + (pos - ctx.win_p0);
-      row = (wr >= 0 && wr < a.win.n_rows) ? wr : -1;
-    }
-  }
-  const uint64_t data = win ? reinterpret_cast<uint64_t>(a.win.data) : reinterpret_cast<uint64_t>(a.cache.data);
-  const uint64_t rope = win ? reinterpret_cast<uint64_t>(a.win.rope) : reinterpret_cast<uint64_t>(a.cache.rope);
-  const int64_t rs = win ? a.win.row_stride : a.cache.row_stride;
-  const int64_t ps = win ? a.win.rope_stride : a.cache.rope_stride;
-  const float* scale = win ? a.win.scale : a.cache.scale;
-  const int64_t rr = row >= 0 ? row : 0;  // invalid entries are never loaded
-  w.src = lane < 8 ? data + (uint64_t)(rr * rs) : rope + (uint64_t)(rr * ps * 2) - kNope;
-  w.esc = (lane < 8 && row >= 0) ? scale[row] : 0.f;
-  w.vmask = (uint32_t)__ballot(lane < 8 && row >= 0) & 0xFFu;
-  return w;
-}
-
-// Invalid rows of a wave's 8 are zeroed (their masked P = 0 must never meet a NaN); this precedes
-// the DMAs into the same buffer.
-__device__ __forceinline__ void wide_zero_invalid(const WideRows& w, uint8_t* dst, int lane) {
-  uint32_t inval = ~w.vmask & 0xFFu;
-  while (inval) {
-    const int e = __builtin_ctz(inval);
-    inval &= inval - 1;
-    if (lane < kRowF8 / 16) *reinterpret_cast<uint4*>(dst + e * kRowF8 + 16 * lane) = make_uint4(0, 0, 0, 0);
-  }
-}
-
-// The wave's 8 rows (8 x 592 = 4,736 LDS bytes): LDS byte b = 1024 i + 16 lane is entry b / 592,
-// byte b % 592 (FP8 bytes, RoPE bytes, 16 pad bytes); lanes on padding, past the rows or on an
-// invalid row stay idle.
-__device__ __forceinline__ void wide_stage(const WideRows& w, uint8_t* dst, int lane) {
-#pragma unroll
-  for (int i = 0; i < kWDmas; ++i) {
-    const int b = 1024 * i + 16 * lane;
-    const int e = b / kRowF8, o = b - e * kRowF8;
-    const int sl = (o < kNope ? e : 8 + e) & 63;
-    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)w.src, sl, 64);
-    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(w.src >> 32), sl, 64);
-    const uint64_t src = (((uint64_t)hi << 32) | lo) + (uint64_t)o;
-    if (e < kWStage && o < kNope + 2 * kRope && ((w.vmask >> (e & 7)) & 1))
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
-  }
-}
+//  * the two waves of a head group share one reference maximum per head (their chunk maxima meet
+//    in LDS, lazy rescale) and write P for their 32 entries to LDS, with and without the entry
+//    scales;
+//  * O^T += V^T P^T over all 64 entries of the chunk, split by output dims: half 0 owns FP8 dims
+//    0 .. 255, half 1 FP8 dims 256 .. 447 and the 64 RoPE dims (16 tiles of 16 dims each), V^T
+//    from ds_read_b64_tr_b8 / tr_b16 transpose reads.
+constexpr int kWCh = 64;                  // entries per chunk
+constexpr int kWBuf = kWCh * kRowF8;      // 37,888 bytes
+constexpr int kWPRow = kWCh + 8;          // bf16 per P row (padded)
 
 struct WideLds {
-  float esc[kWCh];            // entry scales of the chunk being computed
-  uint32_t vm[8];             // validity, 8 entries per staging wave
+  float esc[kWCh];      // entry scales of the chunk being computed
+  uint8_t valid[kWCh];  // 1 for a valid entry
   float wmax[8][16], wsum[8][16];
 };
 
 struct WideState {
   f32x4 O[16];
   float m_run, l_part;
-  WideRows cur, nxt;  // rows of this chunk (staged) and of the next one (known)
-  int32_t slot2;      // slot values of the chunk after next
+  WaveRows cur, nxt;  // stagers: rows of this chunk (staged) and of the next one (known)
+  int32_t slot2;      // stagers: slot values of the chunk after next
 };
 
-// One chunk in buf whose rows this wave requested a chunk earlier: publish the chunk's scales and
-// validity, wait for every wave's rows, request the next chunk's rows into nbuf, then scores,
-// softmax, P to LDS and PV. The chunk buffers are distinct LDS objects, so reads of buf need not
-// wait for the DMAs into nbuf.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// One chunk in buf whose rows the stagers requested a chunk earlier: publish the chunk's scales
+// and validity, wait for every stager's rows, request the next chunk's rows into nbuf, then
+// scores, softmax, P to LDS and PV. The chunk buffers are distinct LDS objects, so reads of buf
+// need not wait for the DMAs into nbuf.
 template <bool kSparse>
 __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ctx, int qi, int64_t base, int64_t hi,
                                            const uint8_t* buf, uint8_t* nbuf, const F8Query& q, WideState& st,
                                            uint16_t* ps, uint16_t* pp, WideLds& wl, float sl2, int wave, int lane) {
   const int g = lane >> 4, c = lane & 15;
   const int hg = wave & 3, hf = wave >> 2;
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows and entry scales of the chunk have landed
-  if (lane < 8) wl.esc[8 * wave + lane] = st.cur.esc;
-  if (lane == 0) wl.vm[wave] = st.cur.vmask;
-  __syncthreads();  // every wave's rows; the other buffer is free
-  const bool more = base + kWCh < hi;
-  if (more) {
-    uint8_t* ndst = nbuf + kWStage * wave * kRowF8;
-    wide_zero_invalid(st.nxt, ndst, lane);
-    wide_stage(st.nxt, ndst, lane);
+  __builtin_amdgcn_s_waitcnt(0);  // this stager's rows and the scales of its entries have landed
+  if (hf == 1 && lane < 16) {
+    wl.esc[16 * hg + lane] = st.cur.esc;
+    wl.valid[16 * hg + lane] = (uint8_t)((st.cur.vmask >> lane) & 1u);
   }
-  const int64_t b2 = base + 2 * kWCh + kWStage * wave;
-  st.cur = st.nxt;
-  st.nxt = wide_rows<kSparse>(a, ctx, b2, hi, st.slot2, lane);
-  st.slot2 = wide_slot<kSparse>(a, qi, b2 + kWCh, lane);
+  __syncthreads();  // every stager's rows; the other buffer is free
+  const bool more = base + kWCh < hi;
+  if (hf == 1 && more) {
+    // lane-only DMA offsets are derived from an opaque copy of the lane index, so that they are
+    // recomputed here instead of being kept live (and spilled) across the chunk loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    uint8_t* ndst = nbuf + 16 * hg * kRowF8;
+    zero_invalid_rows(st.nxt, ndst, ln);
+    stage_rows<0, 10>(st.nxt, ndst, ln);
+  }
 
   // scores of entries 32 hf + 16 u + 4 g + i (i < 4), head c of the wave's group
   float sv[2][4];
@@ -1429,12 +1364,12 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
       sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q.qr[ks], sr, 0, 0, 0);
     }
     const float4 e4 = *reinterpret_cast<const float4*>(wl.esc + e0 + 4 * g);
+    const uint32_t v4 = *reinterpret_cast<const uint32_t*>(wl.valid + e0 + 4 * g);
     const float esc[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = e0 + 4 * g + i;
       const float v = fmaf(esc[i], s0[i] + s1[i], sr[i]);
-      sv[u][i] = ((wl.vm[e >> 3] >> (e & 7)) & 1) ? v * sl2 : -INFINITY;
+      sv[u][i] = ((v4 >> (8 * i)) & 1u) ? v * sl2 : -INFINITY;
       cmax = fmaxf(cmax, sv[u][i]);
     }
   }
@@ -1447,24 +1382,21 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
   const bool grow = cmax > st.m_run + 8.f;
   const float m_ref = grow ? cmax : st.m_run;
   const bool none = m_ref == -INFINITY;
-  const float corr = grow ? exp2f(st.m_run - cmax) : 1.f;
+  const float corr = grow ? __builtin_amdgcn_exp2f(st.m_run - cmax) : 1.f;
   float psum = 0.f;
-  {
-    const int prow = (16 * hg + c) * kWPRow;
+  const int prow = (16 * hg + c) * kWPRow;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e0 = 32 * hf + 16 * u + 4 * g;
-      const float4 e4 = *reinterpret_cast<const float4*>(wl.esc + e0);
-      float p[4];
+  for (int u = 0; u < 2; ++u) {
+    const int e0 = 32 * hf + 16 * u + 4 * g;
+    const float4 e4 = *reinterpret_cast<const float4*>(wl.esc + e0);
+    float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = none ? 0.f : exp2f(sv[u][i] - m_ref);
-        psum += p[i];
-      }
-      *reinterpret_cast<uint2*>(ps + prow + e0) =
-          make_uint2(pack_bf16x2(p[0] * e4.x, p[1] * e4.y), pack_bf16x2(p[2] * e4.z, p[3] * e4.w));
-      *reinterpret_cast<uint2*>(pp + prow + e0) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    for (int i = 0; i < 4; ++i) {
+      p[i] = none ? 0.f : __builtin_amdgcn_exp2f(sv[u][i] - m_ref);
+      psum += p[i];
     }
+    *reinterpret_cast<uint2*>(ps + prow + e0) = make_uint2(pk_bf16(p[0] * e4.x, p[1] * e4.y), pk_bf16(p[2] * e4.z, p[3] * e4.w));
+    *reinterpret_cast<uint2*>(pp + prow + e0) = make_uint2(pk_bf16(p[0], p[1]), pk_bf16(p[2], p[3]));
   }
   st.l_part = st.l_part * corr + psum;
   st.m_run = m_ref;
@@ -1474,7 +1406,6 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
   }
   lds_barrier();
   // O^T (16 tiles of 16 dims x the wave's 16 heads) += V^T P^T over the chunk's 64 entries
-  const int prow = (16 * hg + c) * kWPRow;
   const int r = c >> 1, hsel = c & 1;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
@@ -1505,6 +1436,13 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
       }
     }
   }
+  if (hf == 1) {
+    // rows of the chunk after next from their prefetched slots; slots one further ahead
+    const int64_t b2 = base + 2 * kWCh + 16 * hg;
+    st.cur = st.nxt;
+    st.nxt = wave_rows<kSparse>(a, ctx, b2, hi, st.slot2, lane);
+    st.slot2 = prefetch_slot<kSparse>(a, qi, b2 + kWCh, lane);
+  }
 }
 
 template <bool kSparse>
@@ -1527,19 +1465,21 @@ __global__ __launch_bounds__(512, 1) void attn_wide_kernel(AttnArgs a, int n_hg,
   const int head = 64 * hg64 + 16 * hg + c;
 
   const int64_t lo = (int64_t)s * a.per_split;
-  const int64_t b0 = lo + kWStage * wave;
-  const int32_t s0 = wide_slot<kSparse>(a, qi, b0, lane), s1 = wide_slot<kSparse>(a, qi, b0 + kWCh, lane);
-  WideState st;
-  st.slot2 = wide_slot<kSparse>(a, qi, b0 + 2 * kWCh, lane);
   const QueryCtx ctx = query_ctx(a, qi);
   const int64_t N = ctx.n_c + ctx.n_w;
   const int64_t hi = min<int64_t>(N, lo + a.per_split);
-  st.cur = wide_rows<kSparse>(a, ctx, b0, hi, s0, lane);
-  st.nxt = wide_rows<kSparse>(a, ctx, b0 + kWCh, hi, s1, lane);
-  if (lo < hi) {
-    uint8_t* dst = buf0 + kWStage * wave * kRowF8;
-    wide_zero_invalid(st.cur, dst, lane);
-    wide_stage(st.cur, dst, lane);
+  WideState st;
+  if (hf == 1) {
+    const int64_t b0 = lo + 16 * hg;
+    const int32_t s0 = prefetch_slot<kSparse>(a, qi, b0, lane), s1 = prefetch_slot<kSparse>(a, qi, b0 + kWCh, lane);
+    st.slot2 = prefetch_slot<kSparse>(a, qi, b0 + 2 * kWCh, lane);
+    st.cur = wave_rows<kSparse>(a, ctx, b0, hi, s0, lane);
+    st.nxt = wave_rows<kSparse>(a, ctx, b0 + kWCh, hi, s1, lane);
+    if (lo < hi) {
+      uint8_t* dst = buf0 + 16 * hg * kRowF8;
+      zero_invalid_rows(st.cur, dst, lane);
+      stage_rows<0, 10>(st.cur, dst, lane);
+    }
   }
   // the first chunk's rows are in flight while the query is split into its FP8 parts
   const F8Query q = rows_query(static_cast<const uint16_t*>(a.q) + ((int64_t)qi * H + head) * kD, lane);
