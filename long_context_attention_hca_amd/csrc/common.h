@@ -41,8 +41,8 @@ __device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(uint32_t w, float scale, bool 
 
 // Order-preserving map of a float32 to uint32 (larger float -> larger key); -0 maps as +0.
 __device__ __forceinline__ uint32_t float_key(float f) {
-  uint32_t u = __float_as_uint(f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // negative: ~u; otherwise u | sign bit
 }
 
 // Wave64 inclusive prefix sum in lane order: DPP row shifts by 1, 2, 4, 8 within each row of

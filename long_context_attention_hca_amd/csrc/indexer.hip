@@ -16,7 +16,8 @@
 //    unused query rows of the 32-row tile cost nothing that matters.
 //  * Each per-head dot product of MXFP4 values is exact in float32; the score is
 //    folded in head order with separately rounded multiplies and adds
-//    (__fmul_rn / __fadd_rn), which makes it bit-exact and the top-k unique.
+//    (score_term / score_add, no fused multiply-add), which makes it bit-exact and the
+//    top-k unique.
 //  * Selection is on the 64-bit key (order-preserving score bits << 32 | ~j), which
 //    is unique per entry. Every score block (1024 entries) keeps its keys in LDS and
 //    emits, into a region of the workspace that only it writes, the keys at or above
@@ -37,6 +38,21 @@
 
 namespace hca {
 namespace {
+
+// The score fold: each head's term w_h * relu(r_h) and each partial sum rounded to float32 on
+// its own, in head order. hipcc contracts a multiply and an add into one fused multiply-add
+// unless told not to, which would round once where the fold rounds twice; these two helpers
+// switch contraction off, so that every scorer produces the same bits.
+__device__ __forceinline__ float score_term(float w, float r) {
+#pragma clang fp contract(off)
+  // relu of a finite dot product as one integer max on its bits (every negative float and -0
+  // is a negative int32); fmaxf would first quiet a signalling NaN with a second instruction
+  return w * __int_as_float(max(__float_as_int(r), 0));
+}
+__device__ __forceinline__ float score_add(float s, float t) {
+#pragma clang fp contract(off)
+  return s + t;
+}
 
 constexpr int kBlockKeys = 1024;        // entries per score block
 constexpr int kFinThreads = 512;        // finalize block
@@ -320,10 +336,10 @@ __device__ __forceinline__ void score_mxfp4_one(const IndexArgs& a, int qi, Bloc
     }
     const int pos = (wave * U + u) * 32 + row;
     if (lane < 32 && jb + pos < nv) {
-      float s = __fmul_rn(w[0], fmaxf(r[0], 0.f));
+      float s = score_term(w[0], r[0]);
 #pragma unroll
       for (int h = 1; h < 8; ++h)
-        if (h < a.H) s = __fadd_rn(s, __fmul_rn(w[h], fmaxf(r[h], 0.f)));
+        if (h < a.H) s = score_add(s, score_term(w[h], r[h]));
       const uint32_t key = float_key(s);
       lds.key[pos] = key;
       atomicAdd(&lds.hist[key >> 21], 1u);
@@ -427,17 +443,17 @@ __global__ __launch_bounds__(256) void score_mxfp4_q4_kernel(IndexArgs a) {
     const f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B[u], zero, 4, 4, 0, sa, 0, sb[u]);
     const int pos = (wave * U + u) * 32 + row;
     if (act_a && jb + pos < nv_a) {
-      float s = __fmul_rn(wa[0], fmaxf(acc[0], 0.f));
+      float s = score_term(wa[0], acc[0]);
 #pragma unroll
-      for (int h = 1; h < 4; ++h) s = __fadd_rn(s, __fmul_rn(wa[h], fmaxf(acc[h], 0.f)));
+      for (int h = 1; h < 4; ++h) s = score_add(s, score_term(wa[h], acc[h]));
       const uint32_t key = float_key(s);
       la.key[pos] = key;
       atomicAdd(&la.hist[key >> 21], 1u);
     }
     if (act_c && jb + pos < nv_c) {
-      float s = __fmul_rn(wc[0], fmaxf(acc[4], 0.f));
+      float s = score_term(wc[0], acc[4]);
 #pragma unroll
-      for (int h = 1; h < 4; ++h) s = __fadd_rn(s, __fmul_rn(wc[h], fmaxf(acc[4 + h], 0.f)));
+      for (int h = 1; h < 4; ++h) s = score_add(s, score_term(wc[h], acc[4 + h]));
       const uint32_t key = float_key(s);
       lc.key[pos] = key;
       atomicAdd(&lc.hist[key >> 21], 1u);
@@ -447,6 +463,348 @@ __global__ __launch_bounds__(256) void score_mxfp4_q4_kernel(IndexArgs a) {
 #pragma unroll
   for (int i = 0; i < kScoreQ; ++i)
     if (act[i]) emit_candidates(a, q0 + i, jb, nv[i], lds[i]);
+}
+
+// ---------------------------------------------------------------------------------------
+// Streaming top-k for calls with many queries (prefill), MXFP4 keys, 4 indexer heads, k <= 1536.
+// Block = 8 consecutive queries (the 32 MFMA rows are their (query, head) pairs), 8 waves. The
+// block streams its queries' keys in tiles of 512 (wave w scores keys 64w .. 64w + 63 of a tile
+// with two v_mfma_scale_f32_32x32x64_f8f6f4, the next tile's keys loaded meanwhile) and keeps,
+// per query, the keys above a floor in an LDS buffer of 2048 64-bit keys (score key << 32 | ~j),
+// in ascending j: every tile's candidates are placed in key order by a scan of the waves' counts.
+// When a buffer could overflow on the next tile, wave q cuts query q's buffer to exactly its k
+// largest keys (radix select on 8-bit digits below the bits that all its keys share, stable
+// compaction) and raises the floor to the lower edge of the last digit range kept, which bounds
+// the final k-th largest key from below; keys at or under the floor are never appended. At the
+// end each buffer is cut to k and written out in order. Scores are the same float32 fold as
+// score_mxfp4_one (bit-exact), so the result equals the oracle's stable sort. Queries whose
+// visible keys start at different rows (other sequences or documents) are streamed in separate
+// passes over their own rows. The counts of a tile are double-buffered, so a tile needs one
+// barrier (two more when a buffer is cut).
+constexpr int kSQ = 8;           // queries per block (one wave each for cuts and output)
+constexpr int kSThreads = 512;   // 8 waves
+constexpr int kSWaves = kSThreads / 64;
+constexpr int kSTile = 512;      // keys per tile
+constexpr int kSCap = 2048;      // buffered keys per query
+constexpr int kStreamMaxK = kSCap - kSTile;
+
+struct StreamLds {
+  uint64_t buf[kSQ][kSCap];
+  uint32_t hist[kSQ][256];             // radix-select counters, one set per cutting wave
+  uint64_t floor_key[kSQ];
+  uint32_t wcnt[2][kSQ][kSWaves];      // candidates of a tile per query and wave (by tile parity)
+  int64_t nv[kSQ];                     // visible keys per query
+};
+
+// Wave-wide minimum and maximum of 64-bit keys.
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64), hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o < v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64), hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Orders this wave's LDS accesses before and after it (the LDS serves a wave's operations in
+// order; the wait and the memory clobber keep the compiler from moving accesses across).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// OR over the wave (DPP row shifts and broadcasts as in wave_incl_scan_add; lane 63 holds it).
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Sum over each aligned group of 8 lanes, returned to all 8 (DPP: swap neighbours, swap pairs,
+// then mirror the halves of the group).
+__device__ __forceinline__ uint32_t group8_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false);   // quad_perm 1,0,3,2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false);   // quad_perm 2,3,0,1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  return x;
+}
+
+// One wave: cuts query q's buffer of n > K >= 1 keys to its K largest keys, keeping their order,
+// and raises the query's floor. The keys are held in registers (lane l: slots 64 u + l); the
+// first digit starts at the highest bit in which they differ (the bits above it are the same in
+// every key and would put all of them into one counter).
+__device__ void stream_cut(StreamLds& s, int q, uint32_t n, uint32_t K) {
+  const int lane = threadIdx.x & 63;
+  uint64_t* buf = s.buf[q];
+  uint32_t* hist = s.hist[q];
+  constexpr int kPer = kSCap / 64;
+  uint64_t v[kPer];
+  uint64_t any1 = 0, all1 = ~0ull;  // OR and AND of the keys
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    v[u] = buf[64 * u + lane];
+    if (64u * u + lane >= n) v[u] = 0;  // no key is 0 (its low word ~j is never zero)
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    any1 |= v[u];
+    all1 &= v[u] != 0 ? v[u] : ~0ull;
+  }
+  any1 = ((uint64_t)wave_or_u32((uint32_t)(any1 >> 32)) << 32) | wave_or_u32((uint32_t)any1);
+  all1 = ((uint64_t)~wave_or_u32(~(uint32_t)(all1 >> 32)) << 32) | ~wave_or_u32(~(uint32_t)all1);
+  // the highest bit in which the keys differ (n >= 2 distinct keys)
+  const int top = 63 - __builtin_clzll(any1 ^ all1);
+  int shift = max(top - 7, 0);
+  uint64_t mask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
+  uint64_t prefix = all1 & mask;
+  uint32_t rem = K;
+  for (int pass = 0; pass < 9; ++pass) {
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (v[u] != 0 && (v[u] & mask) == prefix) atomicAdd(&hist[(uint32_t)(v[u] >> shift) & 255u], 1u);
+    wave_lds_sync();
+    // the digit d where the count from the top reaches rem (lane l holds bins 4l .. 4l + 3)
+    const uint4 h = reinterpret_cast<const uint4*>(hist)[lane];
+    const uint32_t own = h.x + h.y + h.z + h.w;
+    const uint32_t pre = wave_incl_scan_add(own);
+    const uint32_t above_lane = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre;  // lanes > lane
+    const bool mine = above_lane < rem && above_lane + own >= rem;
+    uint32_t acc = above_lane;
+    int d = 4 * lane;
+    if (mine) {
+      const uint32_t hv[4] = {h.x, h.y, h.z, h.w};
+      for (int b = 3; b >= 0; --b) {
+        if (acc + hv[b] >= rem) { d = 4 * lane + b; break; }
+        acc += hv[b];
+      }
+    }
+    const int src = __builtin_ctzll(__ballot(mine));
+    d = __builtin_amdgcn_readlane(d, src);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)acc, src);
+    const uint32_t in_bin = hist[d];
+    wave_lds_sync();  // the counters are cleared by the next pass
+    rem -= above;
+    prefix |= (uint64_t)d << shift;
+    mask |= (uint64_t)255 << shift;
+    // every key of this digit range is kept; with all 64 bits fixed the range holds one key
+    if (in_bin == rem || shift == 0) break;
+    shift = max(shift - 8, 0);
+  }
+  // keep the keys whose masked bits are at least the prefix (exactly K), in slot order
+  uint32_t base = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const bool keep = (v[u] != 0) & ((v[u] & mask) >= prefix);
+    const uint64_t bal = __ballot(keep);
+    if (keep) buf[base + (uint32_t)__popcll(bal & below)] = v[u];
+    base += (uint32_t)__popcll(bal);
+  }
+  if (lane == 0 && prefix > s.floor_key[q]) s.floor_key[q] = prefix;
+  wave_lds_sync();
+}
+
+__global__ __launch_bounds__(kSThreads) void index_stream_kernel(IndexArgs a) {
+  __shared__ StreamLds s;
+  // the last queries first: in causal prefill they see the most keys, so the longest blocks
+  // start early and the short ones fill the tail
+  const int q0 = (int)(gridDim.x - 1 - blockIdx.x) * kSQ;
+  const int nqb = min(kSQ, a.nq - q0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 31, blk = lane >> 5;
+  int64_t rb[kSQ], nv[kSQ], j0[kSQ];
+#pragma unroll
+  for (int i = 0; i < kSQ; ++i) {
+    rb[i] = -1;
+    nv[i] = 0;
+    j0[i] = 0;
+    if (i < nqb) nv[i] = visible_keys(a, q0 + i, &rb[i], &j0[i]);
+  }
+  const int K = a.k;
+  // queries with at most k visible entries return all of them in order, padded with -1
+  uint32_t todo = 0;
+#pragma unroll
+  for (int i = 0; i < kSQ; ++i) {
+    if (i >= nqb) continue;
+    if (nv[i] <= K) {
+      int32_t* out = a.out + (int64_t)(q0 + i) * K;
+      for (int j = tid; j < K; j += kSThreads) out[j] = j < nv[i] ? (int32_t)(j + j0[i]) : -1;
+    } else {
+      todo |= 1u << i;
+    }
+  }
+  if (!todo) return;
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < kSQ; ++i) s.nv[i] = nv[i];
+  }
+
+  // A operand: row 4 q + h is query q0 + q, indexer head h (zero for queries past the batch)
+  const uint8_t* qb = static_cast<const uint8_t*>(a.q);
+  const uint8_t* kb = static_cast<const uint8_t*>(a.keys);
+  i32x8 A = {0, 0, 0, 0, 0, 0, 0, 0};
+  int sa = 127;
+  if ((row >> 2) < nqb) {
+    const int64_t qr = (int64_t)(q0 + (row >> 2)) * 4 + (row & 3);
+    const uint4 v = *reinterpret_cast<const uint4*>(qb + qr * 32 + blk * 16);
+    A[0] = (int)v.x; A[1] = (int)v.y; A[2] = (int)v.z; A[3] = (int)v.w;
+    sa = a.q_scale[qr * 2 + blk];
+  }
+  // accumulators 4 i + h of this lane hold query 2 i + blk, head h, of its key column
+  float wq[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) wq[i][h] = (2 * i + blk) < nqb ? a.w[(int64_t)(q0 + 2 * i + blk) * 4 + h] : 0.f;
+
+  int32_t jo_wave = 0;  // entry index of visible key 0 of query q0 + wave
+#pragma unroll
+  for (int i = 0; i < kSQ; ++i)
+    if (i == wave) jo_wave = (int32_t)j0[i];
+  // lane l of the count scan: query l / 8, wave l % 8
+  const int cq = lane >> 3, cw = lane & 7;
+
+  while (todo) {
+    // this pass: the pending queries whose visible keys start at the lowest pending query's row
+    int64_t R = 0;
+#pragma unroll
+    for (int i = kSQ - 1; i >= 0; --i)
+      if ((todo >> i) & 1) R = rb[i];
+    uint32_t set = 0;
+    int64_t nvmax = 0, nvmin = INT64_MAX;
+#pragma unroll
+    for (int i = 0; i < kSQ; ++i)
+      if (((todo >> i) & 1) && rb[i] == R) {
+        set |= 1u << i;
+        nvmax = max(nvmax, nv[i]);
+        nvmin = min(nvmin, nv[i]);
+      }
+    todo &= ~set;
+    if (tid < kSQ) s.floor_key[tid] = 0;  // below every key (the low word ~j is never zero)
+    // buffered keys of query q, held by lanes 8 q .. 8 q + 7 of every wave
+    uint32_t cnt = 0;
+    __syncthreads();
+    // the lane's 4 queries: visible counts and floors; the lanes of each pair of queries that
+    // belong to the pass
+    int64_t nvl[4];
+    uint64_t fl[4], inmask[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nvl[i] = s.nv[2 * i + blk];
+      fl[i] = 0;
+      inmask[i] = (((set >> (2 * i)) & 1) ? 0xFFFFFFFFull : 0ull) | (((set >> (2 * i + 1)) & 1) ? ~0xFFFFFFFFull : 0ull);
+    }
+
+    const int n_tiles = (int)((nvmax + kSTile - 1) / kSTile);
+    i32x8 B[2], Bn[2];
+    int sb[2], sbn[2];
+    auto load_b = [&](int t, i32x8(&Bx)[2], int(&sx)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t j = (int64_t)t * kSTile + 64 * wave + 32 * u + row;
+        const int64_t jr = R + (j < nvmax ? j : nvmax - 1);
+        const uint4 v = *reinterpret_cast<const uint4*>(kb + jr * 32 + blk * 16);
+        Bx[u] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        sx[u] = a.key_scale[jr * 2 + blk];
+      }
+    };
+    load_b(0, B, sb);
+    // wait for the first tile here: the loop's own waits then cover only the prefetched tile
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) load_b(t + 1, Bn, sbn);
+      // keys j = 512 t + 64 wave + 32 u + row for the lane's 4 queries
+      const bool full = (int64_t)(t + 1) * kSTile <= nvmin;  // every key of the tile visible to all
+      uint64_t key[2][4];
+      uint64_t bal[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x16 zero = {};
+        const f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B[u], zero, 4, 4, 0, sa, 0, sb[u]);
+        const int64_t j = (int64_t)t * kSTile + 64 * wave + 32 * u + row;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sc = score_term(wq[i][0], acc[4 * i]);
+#pragma unroll
+          for (int h = 1; h < 4; ++h) sc = score_add(sc, score_term(wq[i][h], acc[4 * i + h]));
+          key[u][i] = ((uint64_t)float_key(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+          uint64_t m = __ballot(key[u][i] > fl[i]) & inmask[i];
+          if (!full) m &= __ballot(j < nvl[i]);
+          bal[u][i] = m;
+        }
+      }
+      // per wave and query: the tile's candidates counted (u, then lane, is ascending j)
+      uint32_t (*wc)[kSWaves] = s.wcnt[t & 1];
+      if (lane < kSQ) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint64_t m = bal[u][i];
+            const uint32_t c0 = (uint32_t)__popcll(m & 0xFFFFFFFFull), c1 = (uint32_t)__popcll(m >> 32);
+            c += lane == 2 * i ? c0 : (lane == 2 * i + 1 ? c1 : 0u);
+          }
+        wc[lane][wave] = c;
+      }
+      __syncthreads();
+      // lane 8 q + w holds wave w's count for query q: per query, the tile's total and the
+      // count of the waves before this one
+      const uint32_t cc = wc[cq][cw];
+      const uint32_t bef = cnt + group8_sum(cw < wave ? cc : 0u);  // slot of this wave's first
+      const uint32_t below = (1u << row) - 1u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if ((bal[0][i] | bal[1][i]) == 0) continue;  // no candidate of these two queries in this wave
+        const int qq = 2 * i + blk;
+        const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bef, 16 * i);
+        const uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane((int)bef, 16 * i + 8);
+        const uint32_t base = blk ? b1 : b0;
+        const uint32_t m0 = (uint32_t)(blk ? (bal[0][i] >> 32) : bal[0][i]);
+        const uint32_t m1 = (uint32_t)(blk ? (bal[1][i] >> 32) : bal[1][i]);
+        if ((m0 >> row) & 1u) s.buf[qq][base + (uint32_t)__popc(m0 & below)] = key[0][i];
+        if ((m1 >> row) & 1u) s.buf[qq][base + (uint32_t)__popc(m0) + (uint32_t)__popc(m1 & below)] = key[1][i];
+      }
+      cnt += group8_sum(cc);
+      if (__ballot(cw == 0 && cnt > (uint32_t)(kSCap - kSTile))) {
+        // a buffer could overflow on the next tile: every buffer holding more than k keys is cut
+        // now, so that the cuts of the block's queries fall on the same tiles
+        __syncthreads();  // every placement of the tile is in the buffers
+        const uint32_t nw = (uint32_t)__builtin_amdgcn_readlane((int)cnt, 8 * wave);
+        if (nw > (uint32_t)K) stream_cut(s, wave, nw, (uint32_t)K);
+        cnt = min(cnt, (uint32_t)K);
+        __syncthreads();  // the floors are raised and the buffers compacted
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fl[i] = s.floor_key[2 * i + blk];
+      }
+      B[0] = Bn[0];
+      B[1] = Bn[1];
+      sb[0] = sbn[0];
+      sb[1] = sbn[1];
+    }
+    __syncthreads();  // every placement of the last tile is in the buffers
+    // wave q: the k largest keys of query q, in ascending j
+    if ((set >> wave) & 1u) {
+      const uint32_t nw = (uint32_t)__builtin_amdgcn_readlane((int)cnt, 8 * wave);
+      if (nw > (uint32_t)K) stream_cut(s, wave, nw, (uint32_t)K);
+      int32_t* out = a.out + (int64_t)(q0 + wave) * K;
+      for (int i = lane; i < K; i += 64) out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)s.buf[wave][i]) + jo_wave;
+    }
+    __syncthreads();
+  }
 }
 
 // fp32 / bf16 scores on the vector ALUs (4 keys per thread). grid = (nblk, nq).
@@ -499,8 +857,8 @@ __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
       float r = 0.f;
 #pragma unroll
       for (int d = 0; d < 64; ++d) r = fmaf(qs[h * 64 + d], kv[d], r);
-      const float p = __fmul_rn(w[h], fmaxf(r, 0.f));
-      s = h == 0 ? p : __fadd_rn(s, p);
+      const float p = score_term(w[h], r);
+      s = h == 0 ? p : score_add(s, p);
     }
     const uint32_t key = float_key(s);
     lds.key[t] = key;
@@ -545,27 +903,6 @@ __device__ __forceinline__ int32_t key_entry(uint64_t key) { return (int32_t)(0x
 // The score whose float_key is k (the top half of a candidate key).
 __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-
-
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64), hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o < v ? o : v;
-  }
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64), hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
 }
 
 // f.kmin / f.kmax <- the smallest and largest of the per-thread extremes lo / hi.
@@ -1071,7 +1408,19 @@ hipError_t index_init() {
   return hipSuccess;
 }
 
+// The streaming kernel serves many-query MXFP4 calls with 4 indexer heads; it needs no
+// workspace and writes the output itself (the scores phase of the split calls runs it, the
+// select phase then has nothing left to do).
+bool index_streams(const IndexArgs& a) {
+  return a.dtype == HCA_MXFP4 && a.H == 4 && a.nq >= 256 && a.k >= 1 && a.k <= kStreamMaxK;
+}
+
 hipError_t launch_index_topk(const IndexArgs& a, bool scores, bool select, hipStream_t s) {
+  if (index_streams(a)) {
+    if (scores)
+      hipLaunchKernelGGL(index_stream_kernel, dim3((unsigned)((a.nq + kSQ - 1) / kSQ)), dim3(kSThreads), 0, s, a);
+    return hipGetLastError();
+  }
   if (scores && a.max_visible > a.k) {
     const dim3 g((unsigned)a.nblk, (unsigned)a.nq);
     if (a.dtype == HCA_MXFP4 && a.H == 4 && a.nq >= 256) {

@@ -94,6 +94,101 @@ def test_mxfp4_many_queries_grouped_and_mixed(hca, k):
     check_idx(got, ref, f"mxfp4 many queries k={k}")
 
 
+@pytest.mark.parametrize("k", [1, 1536, 1537])
+def test_mxfp4_many_queries_ties(hca, k):
+    """Many queries (the streaming selector keeps each query's best keys in a bounded buffer
+    that it cuts to k whenever it could overflow) on keys copied from 6 distinct rows, so that
+    every score is shared by thousands of entries and the cuts fall inside runs of ties; the
+    queries with odd index have negative head weights (their best score is 0, held by most
+    entries). k = 1537 is just past what the streaming selector takes and checks the other
+    path on the same case. The split calls give the same result."""
+    nq, n = 264, 20000
+    q, qs, w, kp, ks = mx_case(41, n, nq, 4)
+    rng = np.random.default_rng(9)
+    pick = torch.from_numpy(rng.integers(0, 6, n))
+    kp, ks = kp[pick].contiguous(), ks[pick].contiguous()
+    w[1::2] = -w[1::2].abs()
+    q_pos = [int(rng.integers(0, 4 * n)) for _ in range(nq)]
+    q_pos[5] = 4 * n - 1
+    q_pos[6] = 3                                 # no visible entry
+    got = run(hca, q, w, kp, [0], [0] * nq, q_pos, n, 4, k, qs, ks)
+    ref = oracle_mxfp4(q, qs, w, kp, ks, [0], [0] * nq, q_pos, 4, k)
+    check_idx(got, ref, f"many queries, ties, k={k}")
+    dev = "cuda"
+    a = (q.to(dev), w.to(dev), kp.to(dev), torch.zeros(1, dtype=torch.int64, device=dev),
+         torch.zeros(nq, dtype=torch.int32, device=dev), torch.tensor(q_pos, dtype=torch.int64, device=dev), n, 4, k)
+    ws = torch.empty(hca.lightning_index_topk_workspace(nq, n, k), dtype=torch.uint8, device=dev)
+    two = torch.full((nq, k), -7, dtype=torch.int32, device=dev)
+    kw = dict(q_idx_scale=qs.to(dev), k_idx_scale=ks.to(dev))
+    hca.lightning_index_topk(*a, two, ws, phase="scores", **kw)
+    hca.lightning_index_topk(*a, two, ws, phase="select", **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(two), got)
+
+
+def _fold_sensitive_pairs(n, positive):
+    """n cases (w0, w1, a, b): two entries a = (a0, a1) and b = (b0, b1) of E2M1 values whose
+    scores w0 relu(x0) + w1 relu(x1), each product and the sum rounded to float32, give
+    score(a) >= score(b) (so a, the lower index, wins), while both ways of fusing one product
+    into the add (one rounding instead of two) rank b above a. A scorer that contracts the fold
+    into a fused multiply-add selects b."""
+    f32, f64 = np.float32, np.float64
+    grid = [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    two = lambda w0, w1, x: f32(f32(w0 * f32(x[0])) + f32(w1 * f32(x[1])))
+    fa = lambda w0, w1, x: f32(f64(w0) * x[0] + f64(f32(w1 * f32(x[1]))))
+    fb = lambda w0, w1, x: f32(f64(w1) * x[1] + f64(f32(w0 * f32(x[0]))))
+    rng = np.random.default_rng(77)
+    out = []
+    while len(out) < n:
+        a, b = rng.choice(grid, 2), rng.choice(grid, 2)
+        if a[0] == b[0] or a[1] == b[1] or (positive and max(a.max(), b.max()) == 6.0):
+            continue
+        w0 = f32(abs(rng.standard_normal()) * 0.125 if positive else rng.standard_normal() * 0.125)
+        base = f32(w0 * (a[0] - b[0]) / (b[1] - a[1]))
+        if positive and base <= 0:
+            continue
+        for d in range(-6, 7):
+            w1 = (np.array([base], f32).view(np.int32) + d).view(f32)[0]
+            if (two(w0, w1, a) >= two(w0, w1, b) and fa(w0, w1, a) < fa(w0, w1, b)
+                    and fb(w0, w1, a) < fb(w0, w1, b)):
+                out.append((w0, w1, a, b))
+                break
+    return out
+
+
+@pytest.mark.parametrize("nq", [8, 264])
+@pytest.mark.parametrize("n_fill,k", [(0, 1), (1024, 1025), (1536, 1537)])
+def test_mxfp4_score_fold_rounds_each_step(hca, nq, n_fill, k):
+    """Every scorer (one query at a time, 4 queries per block, the streaming selector) rounds
+    each product and each partial sum of the score to float32, as the oracle's fold does. Query
+    i sees its own entries: a and b (entries 0 and 1) of a fold-sensitive case, then n_fill
+    entries (6, 6) that outscore both, and k = n_fill + 1 selects all but the loser of a and b.
+    Heads 0 and 1 read dims 0 and 1 of the keys; heads 2 and 3 have zero queries and weights."""
+    cases = _fold_sensitive_pairs(nq, positive=n_fill > 0)
+    code = {v: c for c, v in enumerate([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])}
+    nv = n_fill + 2
+    keys = np.zeros((nq * nv, 32), np.uint8)
+    keys[:, 0] = code[6.0] | (code[6.0] << 4)
+    q = np.zeros((nq, 4, 32), np.uint8)
+    q[:, 0, 0] = code[1.0]                       # head 0: dim 0
+    q[:, 1, 0] = code[1.0] << 4                  # head 1: dim 1
+    w = np.zeros((nq, 4), np.float32)
+    for i, (w0, w1, a, b) in enumerate(cases):
+        keys[i * nv, 0] = code[a[0]] | (code[a[1]] << 4)
+        keys[i * nv + 1, 0] = code[b[0]] | (code[b[1]] << 4)
+        w[i, :2] = (w0, w1)
+    ks = np.full((nq * nv, 2), 127, np.uint8)
+    qs = np.full((nq, 4, 2), 127, np.uint8)
+    rb = [i * nv for i in range(nq)]
+    q_pos = [4 * nv - 1] * nq
+    T = torch.from_numpy
+    got = run(hca, T(q), T(w), T(keys), rb, list(range(nq)), q_pos, nv, 4, k, T(qs), T(ks))
+    want = np.array([0] + list(range(2, nv)), np.int32)
+    ref = oracle_mxfp4(T(q), T(qs), T(w), T(keys), T(ks), rb, list(range(nq)), q_pos, 4, k)
+    assert (ref == want).all(), "the oracle's fold does not round each step"
+    check_idx(got, ref, f"fold nq={nq} k={k}")
+
+
 def test_mxfp4_all_equal_keys(hca):
     q, qs, w, kp, ks = mx_case(3, 9000, 2)
     kp[:] = kp[0]
