@@ -543,7 +543,8 @@ __device__ __forceinline__ uint32_t group8_sum(uint32_t x) {
 // One wave: cuts query q's buffer of n > K >= 1 keys to its K largest keys, keeping their order,
 // and raises the query's floor. The keys are held in registers (lane l: slots 64 u + l); the
 // first digit starts at the highest bit in which they differ (the bits above it are the same in
-// every key and would put all of them into one counter).
+// every key and would put all of them into one counter). Once the digit range holding the K-th
+// largest key has at most 64 keys, they are ranked directly and the floor becomes that key.
 __device__ void stream_cut(StreamLds& s, int q, uint32_t n, uint32_t K) {
   const int lane = threadIdx.x & 63;
   uint64_t* buf = s.buf[q];
@@ -601,6 +602,37 @@ __device__ void stream_cut(StreamLds& s, int q, uint32_t n, uint32_t K) {
     mask |= (uint64_t)255 << shift;
     // every key of this digit range is kept; with all 64 bits fixed the range holds one key
     if (in_bin == rem || shift == 0) break;
+    if (in_bin <= 64) {
+      // few keys in the range: gather them (into the counters' space) and take the rem-th
+      // largest directly, lane l ranking gathered key l against all of them
+      uint64_t* g = reinterpret_cast<uint64_t*>(hist);
+      uint32_t pos = 0;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const bool in = (v[u] != 0) & ((v[u] & mask) == prefix);
+        const uint64_t bal = __ballot(in);
+        if (in) g[pos + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull))] = v[u];
+        pos += (uint32_t)__popcll(bal);
+      }
+      wave_lds_sync();
+      const uint64_t c = lane < (int)in_bin ? g[lane] : 0ull;
+      const uint32_t c_hi = (uint32_t)(c >> 32), c_lo = (uint32_t)c;
+      uint32_t rank = 0;  // gathered keys above this lane's
+      for (uint32_t m2 = 0; m2 < in_bin; ++m2) {
+        const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)c_hi, (int)m2) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)c_lo, (int)m2);
+        rank += x > c ? 1u : 0u;
+      }
+      const uint64_t hit = __ballot(lane < (int)in_bin && rank == rem - 1);
+      const int src2 = __builtin_ctzll(hit);
+      const uint64_t T = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(c >> 32), src2) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c, src2);
+      wave_lds_sync();  // the gathered keys are read before the counters are used again
+      // the K kept keys are exactly those at or above T, the K-th largest
+      prefix = T;
+      mask = ~0ull;
+      break;
+    }
     shift = max(shift - 8, 0);
   }
   // keep the keys whose masked bits are at least the prefix (exactly K), in slot order
