@@ -451,36 +451,37 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Row sources of one wave's 16 entries of a chunk (list positions base + e, e < 16).
+// Row sources of one wave's R (16, or 8 in the wide kernel) entries of a chunk (list positions
+// base + e, e < R).
 struct WaveRows {
-  uint64_t src;    // lane e < 16: FP8-row address of entry e; lane 16 + e: its RoPE-row address
+  uint64_t src;    // lane e < R: FP8-row address of entry e; lane R + e: its RoPE-row address
                    // minus 448, so that LDS row byte o >= 448 comes from src + o
-  float esc;       // lane e < 16: entry scale (its load is left in flight)
+  float esc;       // lane e < R: entry scale (its load is left in flight)
   uint32_t vmask;  // valid entries
 };
 
 // The top-k slot value of list position base + (lane & 15) (CSA), loaded one chunk before its
 // rows are computed so that no wait on it sits behind row loads in flight. Positions past the
 // top-k list are clamped to a valid slot; their value is not used.
-template <bool kSparse>
+template <bool kSparse, int R = 16>
 __device__ __forceinline__ int32_t prefetch_slot(const AttnArgs& a, int qi, int64_t base, int lane) {
   if (!kSparse) return 0;
-  const int64_t r = min<int64_t>(base + (lane & 15), (int64_t)a.k - 1);
+  const int64_t r = min<int64_t>(base + (lane & (R - 1)), (int64_t)a.k - 1);
   return a.idx[(int64_t)qi * a.k + r];
 }
 
-// The rows of positions base .. base + 15 from their prefetched slot values (no dependent
+// The rows of positions base .. base + R - 1 from their prefetched slot values (no dependent
 // loads; the entry-scale load is issued and left in flight). Store fields are selected one by
 // one so that they stay in scalar registers.
-template <bool kSparse>
+template <bool kSparse, int R = 16>
 __device__ __forceinline__ WaveRows wave_rows(const AttnArgs& a, const QueryCtx& ctx, int64_t base, int64_t hi,
                                               int32_t slot, int lane) {
   WaveRows w;
-  const int e = lane & 15;
+  const int e = lane & (R - 1);
   const int64_t r = base + e;
   const bool win = r >= ctx.n_c;
   int64_t row = -1;
-  if (lane < 32 && r < hi) {
+  if (lane < 2 * R && r < hi) {
     if (!win) {
       const int64_t j = kSparse ? (int64_t)slot : r;
       const int64_t cr = ctx.cache_rb + j;
@@ -496,16 +497,17 @@ __device__ __forceinline__ WaveRows wave_rows(const AttnArgs& a, const QueryCtx&
   const int64_t rs = win ? a.win.row_stride : a.cache.row_stride;
   const int64_t ps = win ? a.win.rope_stride : a.cache.rope_stride;
   const float* scale = win ? a.win.scale : a.cache.scale;
-  w.src = lane < 16 ? data + (uint64_t)(row * rs) : rope + (uint64_t)(row * ps * 2) - kNope;
-  w.esc = (lane < 16 && row >= 0) ? scale[row] : 0.f;
-  w.vmask = (uint32_t)__ballot(lane < 16 && row >= 0);
+  w.src = lane < R ? data + (uint64_t)(row * rs) : rope + (uint64_t)(row * ps * 2) - kNope;
+  w.esc = (lane < R && row >= 0) ? scale[row] : 0.f;
+  w.vmask = (uint32_t)__ballot(lane < R && row >= 0);
   return w;
 }
 
 // Invalid rows of a wave's 16 are zeroed so that their (masked) P = 0 never meets a NaN; this
 // precedes the row loads into the same buffer.
+template <int R = 16>
 __device__ __forceinline__ void zero_invalid_rows(const WaveRows& w, uint8_t* dst, int lane) {
-  uint32_t inval = ~w.vmask & 0xFFFFu;
+  uint32_t inval = ~w.vmask & ((1u << R) - 1u);
   while (inval) {
     const int e = __builtin_ctz(inval);
     inval &= inval - 1;
@@ -514,20 +516,20 @@ __device__ __forceinline__ void zero_invalid_rows(const WaveRows& w, uint8_t* ds
 }
 
 // A wave's 16 rows fill 16 * 592 = 9,472 LDS bytes, loaded by 10 lane-linear DMAs of up to
-// 1 KiB (16 bytes a lane); DMAs I0 .. I0 + kN - 1 here. The cost of a DMA is per instruction,
-// not per byte, so full 64-lane DMAs beat one 36-lane DMA per row. Lanes that fall on a row's
-// 16 padding bytes, past the 16 rows, or on an invalid row stay idle.
-template <int I0, int kN>
+// 1 KiB (16 bytes a lane); DMAs I0 .. I0 + kN - 1 here (8 rows: 5 DMAs). The cost of a DMA is
+// per instruction, not per byte, so full 64-lane DMAs beat one 36-lane DMA per row. Lanes that
+// fall on a row's 16 padding bytes, past the R rows, or on an invalid row stay idle.
+template <int I0, int kN, int R = 16>
 __device__ __forceinline__ void stage_rows(const WaveRows& w, uint8_t* dst, int lane) {
 #pragma unroll
   for (int i = I0; i < I0 + kN; ++i) {
     const int b = 1024 * i + 16 * lane;  // LDS byte within the wave's rows
     const int e = b / kRowF8, o = b - e * kRowF8;
-    const int sl = o < kNope ? e : 16 + e;
+    const int sl = o < kNope ? e : R + e;
     const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)w.src, sl, 64);
     const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(w.src >> 32), sl, 64);
     const uint64_t src = (((uint64_t)hi << 32) | lo) + (uint64_t)o;
-    if (e < 16 && o < kNope + 2 * kRope && ((w.vmask >> (e & 15)) & 1))
+    if (e < R && o < kNope + 2 * kRope && ((w.vmask >> (e & (R - 1))) & 1))
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                        (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
   }
@@ -1274,20 +1276,22 @@ __global__ __launch_bounds__(256, 1) void attn_rows_kernel(AttnArgs a, int total
 // heads, in four blocks). block = (query, 64-head group, split), 8 waves: wave w computes for
 // heads 16 (w & 3) .. +15 of the group and works on half h = w >> 2 of each chunk; the two waves
 // of a head group share a SIMD.
-//  * chunks of 64 entries, double buffered in LDS. The half-1 waves stage them: wave 4 + v
-//    requests entries 16v .. 16v + 15 of the next chunk with 10 lane-linear 1 KiB global_load_lds
-//    DMAs, while the half-0 wave on its SIMD starts the scores; a stager's rows for the chunk after
-//    next (with their scale loads) are found after PV, where no DMAs are queued. The scales and
-//    validity of every entry go through LDS once a chunk's rows have landed;
+//  * chunks of 64 entries, double buffered in LDS. Every wave stages a share: wave w requests
+//    entries 8 w .. 8 w + 7 of the next chunk with 5 lane-linear 1 KiB global_load_lds DMAs
+//    before its scores; its rows for the chunk after next (with their scale loads) are found
+//    after PV, where no DMAs are queued. The scales and validity of every entry go through LDS
+//    once a chunk's rows have landed;
 //  * S^T = K Q^T for entries 32h .. 32h + 31 (two tiles of 16) and the wave's 16 heads, on the
 //    scaled FP8 MFMA with the query split into two FP8 parts, RoPE dims on bf16 MFMA, as in
 //    attn_fp8_kernel;
 //  * the two waves of a head group share one reference maximum per head (their chunk maxima meet
 //    in LDS, lazy rescale) and write P for their 32 entries to LDS, with and without the entry
 //    scales;
-//  * O^T += V^T P^T over all 64 entries of the chunk, split by output dims: half 0 owns FP8 dims
-//    0 .. 255, half 1 FP8 dims 256 .. 447 and the 64 RoPE dims (16 tiles of 16 dims each), V^T
-//    from ds_read_b64_tr_b8 / tr_b16 transpose reads.
+//  * O^T += V^T P^T over all 64 entries of the chunk, split by output dims and heads: wave w owns
+//    dims 128 (w & 3) .. + 127 (FP8 dims 0 .. 447, then the 64 RoPE dims) of heads 32 (w >> 2)
+//    .. + 31 (8 x 2 tiles of 16 dims x 16 heads), so each V^T tile is read (ds_read_b64_tr_b8 /
+//    tr_b16) and converted to bf16 by two waves of the block and feeds 2 MFMAs in each. The head
+//    groups' rescale factors reach the dim owners through LDS with P.
 constexpr int kWCh = 64;                  // entries per chunk
 constexpr int kWBuf = kWCh * kRowF8;      // 37,888 bytes
 constexpr int kWPRow = kWCh + 8;          // bf16 per P row (padded)
@@ -1296,13 +1300,14 @@ struct WideLds {
   float esc[kWCh];      // entry scales of the chunk being computed
   uint8_t valid[kWCh];  // 1 for a valid entry
   float wmax[8][16], wsum[8][16];
+  float corr[16][4];    // [c][hg]: the chunk's rescale factor of head 16 hg + c
 };
 
 struct WideState {
   f32x4 O[16];
   float m_run, l_part;
-  WaveRows cur, nxt;  // stagers: rows of this chunk (staged) and of the next one (known)
-  int32_t slot2;      // stagers: slot values of the chunk after next
+  WaveRows cur, nxt;  // this wave's 8 rows of this chunk (staged) and of the next one (known)
+  int32_t slot2;      // slot values of the chunk after next
 };
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
@@ -1311,8 +1316,8 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// One chunk in buf whose rows the stagers requested a chunk earlier: publish the chunk's scales
-// and validity, wait for every stager's rows, request the next chunk's rows into nbuf, then
+// One chunk in buf whose rows the waves requested a chunk earlier: publish the chunk's scales
+// and validity, wait for every wave's rows, request the next chunk's rows into nbuf, then
 // scores, softmax, P to LDS and PV. The chunk buffers are distinct LDS objects, so reads of buf
 // need not wait for the DMAs into nbuf.
 template <bool kSparse>
@@ -1321,21 +1326,21 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
                                            uint16_t* ps, uint16_t* pp, WideLds& wl, float sl2, int wave, int lane) {
   const int g = lane >> 4, c = lane & 15;
   const int hg = wave & 3, hf = wave >> 2;
-  __builtin_amdgcn_s_waitcnt(0);  // this stager's rows and the scales of its entries have landed
-  if (hf == 1 && lane < 16) {
-    wl.esc[16 * hg + lane] = st.cur.esc;
-    wl.valid[16 * hg + lane] = (uint8_t)((st.cur.vmask >> lane) & 1u);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows and the scales of its entries have landed
+  if (lane < 8) {
+    wl.esc[8 * wave + lane] = st.cur.esc;
+    wl.valid[8 * wave + lane] = (uint8_t)((st.cur.vmask >> lane) & 1u);
   }
-  __syncthreads();  // every stager's rows; the other buffer is free
+  __syncthreads();  // every wave's rows; the other buffer is free
   const bool more = base + kWCh < hi;
-  if (hf == 1 && more) {
+  if (more) {
     // lane-only DMA offsets are derived from an opaque copy of the lane index, so that they are
     // recomputed here instead of being kept live (and spilled) across the chunk loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    uint8_t* ndst = nbuf + 16 * hg * kRowF8;
-    zero_invalid_rows(st.nxt, ndst, ln);
-    stage_rows<0, 10>(st.nxt, ndst, ln);
+    uint8_t* ndst = nbuf + 8 * wave * kRowF8;
+    zero_invalid_rows<8>(st.nxt, ndst, ln);
+    stage_rows<0, 5, 8>(st.nxt, ndst, ln);
   }
 
   // scores of entries 32 hf + 16 u + 4 g + i (i < 4), head c of the wave's group
@@ -1400,28 +1405,45 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
   }
   st.l_part = st.l_part * corr + psum;
   st.m_run = m_ref;
-  if (__ballot(grow)) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) st.O[j] *= corr;
-  }
+  if (hf == 0 && g == 0) wl.corr[c][hg] = corr;
   lds_barrier();
-  // O^T (16 tiles of 16 dims x the wave's 16 heads) += V^T P^T over the chunk's 64 entries
+  // O^T (8 x 2 tiles of 16 dims x 16 heads: this wave's 128 dims of 32 heads) += V^T P^T over
+  // the chunk's 64 entries; first the rescale of the heads whose reference maximum grew
+  const int dq = wave & 3, hh = wave >> 2;
+  const float2 cr = *reinterpret_cast<const float2*>(&wl.corr[c][2 * hh]);
+  if (__ballot(cr.x != 1.f || cr.y != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      st.O[dt] *= cr.x;
+      st.O[8 + dt] *= cr.y;
+    }
+  }
   const int r = c >> 1, hsel = c & 1;
+  const int nf = dq < 3 ? 8 : 4;  // FP8 dim tiles of this wave; the last quarter ends with RoPE
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    const bf16x8 Bs = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ps + prow + 32 * kk + 8 * g));
-    const uint8_t* vp = buf + (32 * kk + 8 * g + r) * kRowF8 + 256 * hf + 8 * hsel;
-    const int nf = hf == 0 ? 16 : 12;  // FP8 dim tiles of this half
+    bf16x8 Bh[2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j < nf) {
-        const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * j));
-        st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]), Bs,
-                                                          st.O[j], 0, 0, 0);
+    for (int ht = 0; ht < 2; ++ht)
+      Bh[ht] = __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const uint4*>(ps + (32 * hh + 16 * ht + c) * kWPRow + 32 * kk + 8 * g));
+    const uint8_t* vp = buf + (32 * kk + 8 * g + r) * kRowF8 + 128 * dq + 8 * hsel;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      if (dt < nf) {
+        const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 16 * dt));
+        const bf16x8 av = fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]);
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+          st.O[8 * ht + dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bh[ht], st.O[8 * ht + dt], 0, 0, 0);
       }
     }
-    if (hf == 1) {
-      const bf16x8 Br = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pp + prow + 32 * kk + 8 * g));
+    if (dq == 3) {
+      // RoPE dims: bf16 rows, P without the entry scales
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+        Bh[ht] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(pp + (32 * hh + 16 * ht + c) * kWPRow + 32 * kk + 8 * g));
       const int rs = c >> 2, qd = c & 3;
       const uint8_t* v0 = buf + (32 * kk + 8 * g + rs) * kRowF8 + kNope + 8 * qd;
       const uint8_t* v1 = v0 + 4 * kRowF8;
@@ -1430,18 +1452,19 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
         const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * dt));
         const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * dt));
         typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const i16x8 av = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
-        st.O[12 + dt] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), Br, st.O[12 + dt], 0, 0, 0);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+          st.O[8 * ht + 4 + dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bh[ht], st.O[8 * ht + 4 + dt], 0, 0, 0);
       }
     }
   }
-  if (hf == 1) {
+  {
     // rows of the chunk after next from their prefetched slots; slots one further ahead
-    const int64_t b2 = base + 2 * kWCh + 16 * hg;
+    const int64_t b2 = base + 2 * kWCh + 8 * wave;
     st.cur = st.nxt;
-    st.nxt = wave_rows<kSparse>(a, ctx, b2, hi, st.slot2, lane);
-    st.slot2 = prefetch_slot<kSparse>(a, qi, b2 + kWCh, lane);
+    st.nxt = wave_rows<kSparse, 8>(a, ctx, b2, hi, st.slot2, lane);
+    st.slot2 = prefetch_slot<kSparse, 8>(a, qi, b2 + kWCh, lane);
   }
 }
 
@@ -1469,16 +1492,17 @@ __global__ __launch_bounds__(512, 1) void attn_wide_kernel(AttnArgs a, int n_hg,
   const int64_t N = ctx.n_c + ctx.n_w;
   const int64_t hi = min<int64_t>(N, lo + a.per_split);
   WideState st;
-  if (hf == 1) {
-    const int64_t b0 = lo + 16 * hg;
-    const int32_t s0 = prefetch_slot<kSparse>(a, qi, b0, lane), s1 = prefetch_slot<kSparse>(a, qi, b0 + kWCh, lane);
-    st.slot2 = prefetch_slot<kSparse>(a, qi, b0 + 2 * kWCh, lane);
-    st.cur = wave_rows<kSparse>(a, ctx, b0, hi, s0, lane);
-    st.nxt = wave_rows<kSparse>(a, ctx, b0 + kWCh, hi, s1, lane);
+  {
+    const int64_t b0 = lo + 8 * wave;
+    const int32_t s0 = prefetch_slot<kSparse, 8>(a, qi, b0, lane);
+    const int32_t s1 = prefetch_slot<kSparse, 8>(a, qi, b0 + kWCh, lane);
+    st.slot2 = prefetch_slot<kSparse, 8>(a, qi, b0 + 2 * kWCh, lane);
+    st.cur = wave_rows<kSparse, 8>(a, ctx, b0, hi, s0, lane);
+    st.nxt = wave_rows<kSparse, 8>(a, ctx, b0 + kWCh, hi, s1, lane);
     if (lo < hi) {
-      uint8_t* dst = buf0 + 16 * hg * kRowF8;
-      zero_invalid_rows(st.cur, dst, lane);
-      stage_rows<0, 10>(st.cur, dst, lane);
+      uint8_t* dst = buf0 + 8 * wave * kRowF8;
+      zero_invalid_rows<8>(st.cur, dst, lane);
+      stage_rows<0, 5, 8>(st.cur, dst, lane);
     }
   }
   // the first chunk's rows are in flight while the query is split into its FP8 parts
@@ -1503,31 +1527,38 @@ __global__ __launch_bounds__(512, 1) void attn_wide_kernel(AttnArgs a, int n_hg,
   if (g == 0) wl.wsum[wave][c] = L;
   __syncthreads();
   L = wl.wsum[hg][c] + wl.wsum[hg + 4][c];
-  const float inv = L > 0.f ? 1.f / L : 0.f;
   const float lse = L > 0.f ? (st.m_run + log2f(L)) * kLn2 : -INFINITY;
-  int head_o = head;
-  asm volatile("" : "+v"(head_o));
-  const int64_t hrow = (int64_t)qi * H + head_o;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    // half 0: FP8 dims 16 j + 4 g; half 1: FP8 dims 256 + 16 j (j < 12), then RoPE dims 448 + 16 (j - 12)
-    const int d = 256 * hf + 16 * j + 4 * g;
-    const f32x4 acc = st.O[j] * inv;
-    if (a.n_split == 1) {
-      if (a.o_dtype == HCA_BF16) {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + hrow * kD + d) =
-            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-      } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + hrow * kD + d) = acc;
-      }
-    } else {
-      const int64_t pi = ((int64_t)qi * a.n_split + s) * H + head_o;
-      *reinterpret_cast<f32x4*>(a.part_o + pi * kD + d) = acc;
-    }
-  }
   if (hf == 0 && g == 0) {
+    const int64_t hrow = (int64_t)qi * H + head;
     if (a.n_split == 1) a.lse[hrow] = lse;
-    else a.part_lse[((int64_t)qi * a.n_split + s) * H + head_o] = lse;
+    else a.part_lse[((int64_t)qi * a.n_split + s) * H + head] = lse;
+  }
+  // this wave's output: dims 128 (wave & 3) + 16 dt + 4 g of head 64 hg64 + 32 (wave >> 2) + 16 ht + c
+  // (the RoPE dims follow the FP8 dims 384 .. 447, so the dims stay contiguous)
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int hl = 32 * (wave >> 2) + 16 * ht;  // head tile within the 64
+    const float Lh = wl.wsum[hl >> 4][c] + wl.wsum[(hl >> 4) + 4][c];
+    const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
+    int head_o = 64 * hg64 + hl + c;
+    asm volatile("" : "+v"(head_o));
+    const int64_t hrow = (int64_t)qi * H + head_o;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 128 * (wave & 3) + 16 * dt + 4 * g;
+      const f32x4 acc = st.O[8 * ht + dt] * inv;
+      if (a.n_split == 1) {
+        if (a.o_dtype == HCA_BF16) {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + hrow * kD + d) =
+              make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + hrow * kD + d) = acc;
+        }
+      } else {
+        const int64_t pi = ((int64_t)qi * a.n_split + s) * H + head_o;
+        *reinterpret_cast<f32x4*>(a.part_o + pi * kD + d) = acc;
+      }
+    }
   }
 }
 
