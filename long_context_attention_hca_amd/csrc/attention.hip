@@ -521,24 +521,18 @@ __device__ __forceinline__ void zero_invalid_rows(const WaveRows& w, uint8_t* ds
 // fall on a row's 16 padding bytes, past the R rows, or on an invalid row stay idle.
 template <int I0, int kN, int R = 16>
 __device__ __forceinline__ void stage_rows(const WaveRows& w, uint8_t* dst, int lane) {
-  // every lane's source addresses first (lane shuffles), then the DMAs back to back
-  uint64_t src[kN];
-  bool on[kN];
 #pragma unroll
-  for (int k = 0; k < kN; ++k) {
-    const int b = 1024 * (I0 + k) + 16 * lane;  // LDS byte within the wave's rows
+  for (int i = I0; i < I0 + kN; ++i) {
+    const int b = 1024 * i + 16 * lane;  // LDS byte within the wave's rows
     const int e = b / kRowF8, o = b - e * kRowF8;
     const int sl = o < kNope ? e : R + e;
     const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)w.src, sl, 64);
     const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(w.src >> 32), sl, 64);
-    src[k] = (((uint64_t)hi << 32) | lo) + (uint64_t)o;
-    on[k] = e < R && o < kNope + 2 * kRope && ((w.vmask >> (e & (R - 1))) & 1);
+    const uint64_t src = (((uint64_t)hi << 32) | lo) + (uint64_t)o;
+    if (e < R && o < kNope + 2 * kRope && ((w.vmask >> (e & (R - 1))) & 1))
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
   }
-#pragma unroll
-  for (int k = 0; k < kN; ++k)
-    if (on[k])
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src[k]),
-                                       (__attribute__((address_space(3))) void*)(dst + 1024 * (I0 + k)), 16, 0, 0);
 }
 
 // Workgroup barrier that waits for this wave's LDS accesses only: row loads into the other
