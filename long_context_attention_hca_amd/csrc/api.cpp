@@ -419,7 +419,8 @@ int index_impl(const char* fn, int phase, const void* q_idx, const uint8_t* q_id
   if (phase != kIndexBoth && ws_bytes < index_ws(nq, max_visible))
     return fail(HCA_ERR_WORKSPACE, fn, "the split calls need the workspace of all nq queries");
   int64_t batch = nq;
-  while (batch > 1 && index_ws(batch, max_visible) > ws_bytes) batch = std::max<int64_t>(1, batch / 2);
+  if (!hca::index_stream_path(idx_dtype, n_idx_heads, nq, k))
+    while (batch > 1 && index_ws(batch, max_visible) > ws_bytes) batch = std::max<int64_t>(1, batch / 2);
   const int64_t q_row = idx_dtype == HCA_MXFP4 ? (int64_t)n_idx_heads * d_idx / 2
                                                : (int64_t)n_idx_heads * d_idx * (idx_dtype == HCA_F32 ? 4 : 2);
   int st = ensure_init(fn);

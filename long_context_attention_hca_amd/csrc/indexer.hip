@@ -1443,9 +1443,8 @@ hipError_t index_init() {
 // The streaming kernel serves many-query MXFP4 calls with 4 indexer heads; it needs no
 // workspace and writes the output itself (the scores phase of the split calls runs it, the
 // select phase then has nothing left to do).
-bool index_streams(const IndexArgs& a) {
-  return a.dtype == HCA_MXFP4 && a.H == 4 && a.nq >= 256 && a.k >= 1 && a.k <= kStreamMaxK;
-}
+static_assert(kStreamMaxK == kStreamMaxTopK, "the streaming indexer's k bound");
+bool index_streams(const IndexArgs& a) { return index_stream_path(a.dtype, a.H, a.nq, a.k); }
 
 hipError_t launch_index_topk(const IndexArgs& a, bool scores, bool select, hipStream_t s) {
   if (index_streams(a)) {

@@ -59,6 +59,12 @@ size_t index_ws_layout(int64_t nq, int64_t max_visible, void* ws, IndexArgs* a);
 // scores: the score kernel (the candidates and block thresholds it leaves in the workspace);
 // select: the selection kernel that reads them
 hipError_t launch_index_topk(const IndexArgs& a, bool scores, bool select, hipStream_t stream);
+// Calls taken by the streaming indexer (many queries, MXFP4 keys, 4 indexer heads, k <= 1536):
+// one kernel with no workspace, so such a call is never cut into workspace-sized batches.
+constexpr int kStreamMaxTopK = 1536;
+inline bool index_stream_path(int dtype, int H, int64_t nq, int k) {
+  return dtype == HCA_MXFP4 && H == 4 && nq >= 256 && k >= 1 && k <= kStreamMaxTopK;
+}
 hipError_t index_init();
 
 struct StoreView {
