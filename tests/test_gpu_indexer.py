@@ -114,6 +114,10 @@ def test_mxfp4_many_queries_ties(hca, k):
     got = run(hca, q, w, kp, [0], [0] * nq, q_pos, n, 4, k, qs, ks)
     ref = oracle_mxfp4(q, qs, w, kp, ks, [0], [0] * nq, q_pos, 4, k)
     check_idx(got, ref, f"many queries, ties, k={k}")
+    # with the smallest workspace the call accepts (other paths then batch the queries)
+    small = run(hca, q, w, kp, [0], [0] * nq, q_pos, n, 4, k, qs, ks,
+                ws_bytes=hca.lightning_index_topk_workspace(1, n, k))
+    assert np.array_equal(small, got)
     dev = "cuda"
     a = (q.to(dev), w.to(dev), kp.to(dev), torch.zeros(1, dtype=torch.int64, device=dev),
          torch.zeros(nq, dtype=torch.int32, device=dev), torch.tensor(q_pos, dtype=torch.int64, device=dev), n, 4, k)
