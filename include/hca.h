@@ -357,6 +357,47 @@ int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_hea
                        int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Deferred merge of the split-K partials (both mechanisms end in one joint
+ * softmax per query and head; CSA and HCA paragraphs: the compressed part and
+ * the sliding-window branch). A call may split each query's entry list into
+ * ranges whose normalised partial outputs and log-sum-exps are merged by
+ * log-sum-exp. csa_sparse_mqa_attn_partials / hca_dense_mqa_attn_partials
+ * take the same arguments as csa_sparse_mqa_attn / hca_dense_mqa_attn plus
+ * `out`, run the attention and stop before that merge: when the call splits
+ * (out->n_split > 1) its partials stay in ws and o/lse are not written until
+ * mqa_attn_merge runs; otherwise o/lse are final and the merge skips the call.
+ * mqa_attn_merge(a, b, stream) merges one call (b NULL) or two calls in one
+ * launch, giving the same o/lse bits as the undeferred calls. It must run
+ * after the partial calls (same stream, or ordered by events) and before
+ * their workspaces are reused. hca_attn_partials holds device pointers and
+ * sizes filled by the partial calls; the caller keeps it in host memory.
+ * Errors as the undeferred calls; bad sizes or NULL pointers in a or b:
+ * HCA_ERR_INVALID_ARG.
+ */
+typedef struct hca_attn_partials {
+  float* part_o;    /* [nq][n_split][n_heads][d] float32, inside the call's ws */
+  float* part_lse;  /* [nq][n_split][n_heads] float32 */
+  void* o;          /* the call's o and lse */
+  float* lse;
+  int32_t nq, n_heads, d, n_split, o_dtype;
+} hca_attn_partials;
+int csa_sparse_mqa_attn_partials(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                                 const hca_store* cache, const int64_t* cache_row_begin,
+                                 const int32_t* idx, int32_t k, const hca_store* window,
+                                 const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W,
+                                 const int32_t* q_seq, const int64_t* q_pos, const int64_t* q_lo,
+                                 float scale, void* o, int32_t o_dtype, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream, hca_attn_partials* out);
+int hca_dense_mqa_attn_partials(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                                const hca_store* cache, const int64_t* cache_row_begin,
+                                int32_t m_prime, int64_t max_visible, const hca_store* window,
+                                const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W,
+                                const int32_t* q_seq, const int64_t* q_pos, const int64_t* q_lo,
+                                float scale, void* o, int32_t o_dtype, float* lse, void* ws,
+                                size_t ws_bytes, void* stream, hca_attn_partials* out);
+int mqa_attn_merge(const hca_attn_partials* a, const hca_attn_partials* b, void* stream);
+
+/*
  * hca_dense_mqa_attn_noalloc — hca_dense_mqa_attn for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Same arguments and results as

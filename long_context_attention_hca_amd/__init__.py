@@ -18,7 +18,8 @@ __all__ = [
     "F32", "BF16", "FP8_E4M3", "MXFP4", "LAYOUT_F32", "LAYOUT_BF16", "LAYOUT_SPLIT", "LAYOUT_MXFP4",
     "HcaError", "Store", "DecodeLayer", "abi_version", "csa_compress", "hca_compress", "decode_append",
     "lightning_index_topk_workspace", "lightning_index_topk", "mqa_attn_workspace",
-    "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "hca_dense_mqa_attn_noalloc", "grouped_out_proj",
+    "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "hca_dense_mqa_attn_noalloc", "AttnPartials",
+    "csa_sparse_mqa_attn_partials", "hca_dense_mqa_attn_partials", "mqa_attn_merge", "grouped_out_proj",
     "library_path",
 ]
 
@@ -85,6 +86,21 @@ _csa_attn = _sig("csa_sparse_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP
 _hca_attn = _sig("hca_dense_mqa_attn", ctypes.c_int, [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail)
 _hca_attn_noalloc = _sig("hca_dense_mqa_attn_noalloc", ctypes.c_int,
                          [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail[:-3] + [_P])
+
+
+class AttnPartials(ctypes.Structure):
+    """hca_attn_partials: where a deferred attention call left its split-K partials."""
+    _fields_ = [("part_o", ctypes.c_void_p), ("part_lse", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("nq", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("n_split", ctypes.c_int32), ("o_dtype", ctypes.c_int32)]
+
+
+_AP = ctypes.POINTER(AttnPartials)
+_csa_attn_partials = _sig("csa_sparse_mqa_attn_partials", ctypes.c_int,
+                          [_P, _I32, _I32, _I32, _SP, _P, _P, _I32] + _attn_tail + [_AP])
+_hca_attn_partials = _sig("hca_dense_mqa_attn_partials", ctypes.c_int,
+                          [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail + [_AP])
+_attn_merge = _sig("mqa_attn_merge", ctypes.c_int, [_AP, _AP, _P])
 
 
 class HcaError(RuntimeError):
@@ -262,6 +278,37 @@ def hca_dense_mqa_attn(q, cache, cache_row_begin, m_prime, max_visible, window, 
     _check(_hca_attn(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin), m_prime,
                      max_visible, window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq), _ptr(q_pos),
                      _ptr(q_lo), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb, _stream(stream)))
+
+
+def csa_sparse_mqa_attn_partials(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos,
+                                 scale, o, lse, ws=None, q_lo=None, stream=None):
+    """csa_sparse_mqa_attn without its split-K merge: returns the AttnPartials that mqa_attn_merge takes."""
+    if not idx.is_contiguous():
+        raise ValueError("idx must be contiguous [nq, k] (rows of k slots)")
+    wp, wb = _ws_args(ws)
+    out = AttnPartials()
+    _check(_csa_attn_partials(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin),
+                              _ptr(idx), idx.shape[1], window.c(), _ptr(win_row_begin), _ptr(win_pos0), W,
+                              _ptr(q_seq), _ptr(q_pos), _ptr(q_lo), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb,
+                              _stream(stream), ctypes.byref(out)))
+    return out
+
+
+def hca_dense_mqa_attn_partials(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W,
+                                q_seq, q_pos, scale, o, lse, ws=None, q_lo=None, stream=None):
+    """hca_dense_mqa_attn without its split-K merge: returns the AttnPartials that mqa_attn_merge takes."""
+    wp, wb = _ws_args(ws)
+    out = AttnPartials()
+    _check(_hca_attn_partials(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(), _ptr(cache_row_begin),
+                              m_prime, max_visible, window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq),
+                              _ptr(q_pos), _ptr(q_lo), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb,
+                              _stream(stream), ctypes.byref(out)))
+    return out
+
+
+def mqa_attn_merge(a, b=None, stream=None):
+    """Merges the partials of one deferred attention call, or of two in one launch."""
+    _check(_attn_merge(ctypes.byref(a), None if b is None else ctypes.byref(b), _stream(stream)))
 
 
 def hca_dense_mqa_attn_noalloc(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W,

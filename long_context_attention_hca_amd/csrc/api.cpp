@@ -242,7 +242,7 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
               const int64_t* win_pos0, int32_t W, const int32_t* q_seq, const int64_t* q_pos,
               const int64_t* q_lo, float scale,
               void* o, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream,
-              bool static_scratch = false) {
+              bool static_scratch = false, hca_attn_partials* defer = nullptr) {
   if (!q || !cache_row_begin || !win_row_begin || !win_pos0 || !q_seq || !q_pos || !o || !lse)
     return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
   if (csa && k > 0 && !idx) return fail(HCA_ERR_INVALID_ARG, fn, "NULL idx");
@@ -266,6 +266,7 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
                       hca::attn_valu_lds_bytes(n_heads, D) <= hca::kAttnValuMaxLds;
     if (!valu) return fail(HCA_ERR_UNSUPPORTED, fn, "unsupported dtype/layout/shape combination");
   }
+  if (defer) *defer = hca_attn_partials{nullptr, nullptr, o, lse, 0, n_heads, D, 1, o_dtype};
   if (nq == 0) return HCA_OK;
   const int64_t max_entries = (csa ? (int64_t)k : max_visible) + W;
   int n_split = 1, per = 1;
@@ -309,7 +310,32 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
     a.part_o = reinterpret_cast<float*>(p);
     a.part_lse = a.part_o + (size_t)nq * n_split * n_heads * D;
   }
-  return launched(fn, hca::launch_attention(a, static_cast<hipStream_t>(stream)));
+  if (defer) *defer = hca_attn_partials{a.part_o, a.part_lse, o, lse, nq, n_heads, D, n_split, o_dtype};
+  return launched(fn, hca::launch_attention(a, static_cast<hipStream_t>(stream), /*combine=*/defer == nullptr));
+}
+
+int check_partials(const char* fn, const hca_attn_partials* p, const char* which) {
+  std::string m = std::string(which) + ": ";
+  if (p->nq < 0 || p->n_heads < 1 || p->d < 1 || p->n_split < 1) return fail(HCA_ERR_INVALID_ARG, fn, (m + "bad sizes").c_str());
+  if (p->o_dtype != HCA_BF16 && p->o_dtype != HCA_F32) return fail(HCA_ERR_INVALID_ARG, fn, (m + "bad o_dtype").c_str());
+  if (p->nq > 0 && (!p->o || !p->lse)) return fail(HCA_ERR_INVALID_ARG, fn, (m + "NULL output").c_str());
+  if (p->nq > 0 && p->n_split > 1 && (!p->part_o || !p->part_lse))
+    return fail(HCA_ERR_INVALID_ARG, fn, (m + "NULL partials").c_str());
+  return HCA_OK;
+}
+
+hca::MergeArgs merge_of(const hca_attn_partials* p) {
+  hca::MergeArgs m;
+  m.part_o = p->part_o;
+  m.part_lse = p->part_lse;
+  m.o = p->o;
+  m.lse = p->lse;
+  m.nq = p->nq;
+  m.H = p->n_heads;
+  m.D = p->d;
+  m.n_split = p->n_split;
+  m.o_dtype = p->o_dtype;
+  return m;
 }
 
 }  // namespace
@@ -505,6 +531,48 @@ HCA_EXPORT int hca_dense_mqa_attn_noalloc(const void* q, int32_t q_dtype, int32_
   return attn_impl("hca_dense_mqa_attn_noalloc", false, q, q_dtype, nq, n_heads, cache, cache_row_begin, nullptr, 0,
                    m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype,
                    lse, nullptr, 0, stream, /*static_scratch=*/true);
+}
+
+HCA_EXPORT int csa_sparse_mqa_attn_partials(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                                            const hca_store* cache, const int64_t* cache_row_begin, const int32_t* idx,
+                                            int32_t k, const hca_store* window, const int64_t* win_row_begin,
+                                            const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
+                                            const int64_t* q_pos, const int64_t* q_lo, float scale, void* o,
+                                            int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream,
+                                            hca_attn_partials* out) {
+  const char* fn = "csa_sparse_mqa_attn_partials";
+  if (!out) return fail(HCA_ERR_INVALID_ARG, fn, "NULL out");
+  return attn_impl(fn, true, q, q_dtype, nq, n_heads, cache, cache_row_begin, idx, k, 1, 0, window, win_row_begin,
+                   win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype, lse, ws, ws_bytes, stream, false, out);
+}
+
+HCA_EXPORT int hca_dense_mqa_attn_partials(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                                           const hca_store* cache, const int64_t* cache_row_begin, int32_t m_prime,
+                                           int64_t max_visible, const hca_store* window, const int64_t* win_row_begin,
+                                           const int64_t* win_pos0, int32_t W, const int32_t* q_seq,
+                                           const int64_t* q_pos, const int64_t* q_lo, float scale, void* o,
+                                           int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream,
+                                           hca_attn_partials* out) {
+  const char* fn = "hca_dense_mqa_attn_partials";
+  if (!out) return fail(HCA_ERR_INVALID_ARG, fn, "NULL out");
+  return attn_impl(fn, false, q, q_dtype, nq, n_heads, cache, cache_row_begin, nullptr, 0, m_prime, max_visible,
+                   window, win_row_begin, win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype, lse, ws, ws_bytes,
+                   stream, false, out);
+}
+
+HCA_EXPORT int mqa_attn_merge(const hca_attn_partials* a, const hca_attn_partials* b, void* stream) {
+  const char* fn = "mqa_attn_merge";
+  if (!a) return fail(HCA_ERR_INVALID_ARG, fn, "NULL a");
+  int st = check_partials(fn, a, "a");
+  if (st != HCA_OK) return st;
+  if (b && (st = check_partials(fn, b, "b")) != HCA_OK) return st;
+  if ((a->n_split > 1 ? a->nq : 0) + (b && b->n_split > 1 ? b->nq : 0) == 0) return HCA_OK;
+  st = ensure_init(fn);
+  if (st != HCA_OK) return st;
+  const hca::MergeArgs ma = merge_of(a);
+  hca::MergeArgs mb;
+  if (b) mb = merge_of(b);
+  return launched(fn, hca::launch_merge(ma, b ? &mb : nullptr, static_cast<hipStream_t>(stream)));
 }
 
 HCA_EXPORT int hca_dense_mqa_attn(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads, const hca_store* cache,

@@ -1606,8 +1606,8 @@ __device__ __forceinline__ V merge_splits(const float* pl, const float* po, int 
 
 // Merge of the split partials. grid = (H, nq), 128 threads; a thread takes 4 dims (a vector
 // pass over D & ~3 dims, then single dims).
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
-  const int h = blockIdx.x, qi = blockIdx.y, tid = threadIdx.x;
+__device__ __forceinline__ void combine_one(const MergeArgs& a, int h, int qi) {
+  const int tid = threadIdx.x;
   const int S = a.n_split, H = a.H, D = a.D;
   const float* pl = a.part_lse + (int64_t)qi * S * H + h;
   const float* po = a.part_o + ((int64_t)qi * S * H + h) * D;
@@ -1632,6 +1632,34 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
   }
   // thread 0 merged dim 0 (vector or single pass), so it holds the (dim-independent) M and L
   if (tid == 0) a.lse[(int64_t)qi * H + h] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+__device__ __forceinline__ MergeArgs merge_args(const AttnArgs& a) {
+  MergeArgs m;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.o = a.o;
+  m.lse = a.lse;
+  m.nq = a.nq;
+  m.H = a.H;
+  m.D = a.D;
+  m.n_split = a.n_split;
+  m.o_dtype = a.o_dtype;
+  return m;
+}
+
+__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
+  combine_one(merge_args(a), blockIdx.x, blockIdx.y);
+}
+
+// Deferred merge of up to two calls: grid = (max heads, nq_a + nq_b); rows y < nq_a are call a's.
+__global__ __launch_bounds__(128) void merge2_kernel(MergeArgs a, MergeArgs b) {
+  const int y = blockIdx.y;
+  const bool first = y < a.nq;
+  const MergeArgs& m = first ? a : b;
+  const int qi = first ? y : y - a.nq;
+  if ((int)blockIdx.x >= m.H) return;
+  combine_one(m, blockIdx.x, qi);
 }
 
 }  // namespace
@@ -1692,7 +1720,7 @@ bool attn_rows_eligible(const AttnArgs& a) {
   return a.H == 16 * kRowsWaves && (int64_t)a.nq * a.n_split >= 256;
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s, bool combine) {
   const bool mfma = a.q_dtype == HCA_BF16;
   const bool fp8 = mfma && attn_fp8_supported(a.cache, a.win);
   if (attn_wide_supported(a.q_dtype, a.cache, a.win, a.H, a.nq)) {
@@ -1723,11 +1751,26 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.n_split > 1) {
+  if (a.n_split > 1 && combine) {
     hipLaunchKernelGGL(combine_kernel, dim3(a.H, a.nq), dim3(128), 0, s, a);
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_merge(const MergeArgs& a, const MergeArgs* b, hipStream_t s) {
+  // a call that was not split wrote its output itself: it takes no rows of the merge grid
+  MergeArgs ma = a, mb{};
+  if (ma.n_split <= 1) ma.nq = 0;
+  if (b) {
+    mb = *b;
+    if (mb.n_split <= 1) mb.nq = 0;
+  }
+  const int rows = ma.nq + mb.nq;
+  if (rows == 0) return hipSuccess;
+  const int heads = std::max(ma.nq > 0 ? ma.H : 0, mb.nq > 0 ? mb.H : 0);
+  hipLaunchKernelGGL(merge2_kernel, dim3(heads, rows), dim3(128), 0, s, ma, mb);
+  return hipGetLastError();
 }
 
 // Scratch of hca_dense_mqa_attn_noalloc (its split-K partials): a file-scope device array, one

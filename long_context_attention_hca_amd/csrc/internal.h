@@ -141,7 +141,17 @@ bool attn_mfma_supported(int q_dtype, int o_dtype, const StoreView& c, const Sto
 // split policy.
 bool attn_wide_supported(int q_dtype, const StoreView& c, const StoreView& w, int H, int nq);
 void attn_split_policy_wide(int nq, int H, int64_t max_entries, int* n_split, int* per_split);
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+// combine = false leaves a split call's partials for a later launch_merge (deferred merge).
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, bool combine = true);
+// The LSE merge of one call's split-K partials, or of two calls' in one launch (b may be null).
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;
+  int nq, H, D, n_split, o_dtype;
+};
+hipError_t launch_merge(const MergeArgs& a, const MergeArgs* b, hipStream_t stream);
 // The static scratch of hca_dense_mqa_attn_noalloc: its size, and its device address on the
 // current device (looked up once per device).
 constexpr size_t kNoallocScratchBytes = 16u << 20;

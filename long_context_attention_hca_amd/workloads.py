@@ -12,9 +12,10 @@ import math
 
 import torch
 
-from . import (BF16, F32, LAYOUT_BF16, LAYOUT_F32, LAYOUT_MXFP4, LAYOUT_SPLIT, DecodeLayer, Store, csa_compress,
-               csa_sparse_mqa_attn, decode_append, hca_compress, hca_dense_mqa_attn, lightning_index_topk,
-               lightning_index_topk_workspace, mqa_attn_workspace)
+from . import (BF16, DecodeLayer, F32, LAYOUT_BF16, LAYOUT_F32, LAYOUT_MXFP4, LAYOUT_SPLIT, Store, csa_compress,
+               csa_sparse_mqa_attn, csa_sparse_mqa_attn_partials, decode_append, hca_compress, hca_dense_mqa_attn,
+               hca_dense_mqa_attn_partials, lightning_index_topk, lightning_index_topk_workspace, mqa_attn_merge,
+               mqa_attn_workspace)
 
 
 def _i64(vals, dev):
@@ -72,7 +73,9 @@ def index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k
 
 
 def csa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale, ws,
-             o_dtype=None, o=None, lse=None, q_lo=None, stream=None):
+             o_dtype=None, o=None, lse=None, q_lo=None, stream=None, defer=False):
+    """CSA attention; with defer=True the split-K merge is left for mqa_attn_merge and the
+    call's AttnPartials is returned as a third value."""
     nq, H, D = q.shape
     if o is None:
         o = torch.empty(nq, H, D, dtype=o_dtype or q.dtype, device=q.device)
@@ -80,13 +83,18 @@ def csa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W,
         lse = torch.empty(nq, H, dtype=torch.float32, device=q.device)
     qd = F32 if q.dtype == torch.float32 else BF16
     buf = ws.get("csa", mqa_attn_workspace(qd, nq, H, D, idx.shape[1] + W))
+    if defer:
+        part = csa_sparse_mqa_attn_partials(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq,
+                                            q_pos, scale, o, lse, buf, q_lo=q_lo, stream=stream)
+        return o, lse, part
     csa_sparse_mqa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W, q_seq, q_pos, scale,
                         o, lse, buf, q_lo=q_lo, stream=stream)
     return o, lse
 
 
 def hca_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos,
-             scale, ws, o_dtype=None, o=None, lse=None, q_lo=None, stream=None):
+             scale, ws, o_dtype=None, o=None, lse=None, q_lo=None, stream=None, defer=False):
+    """HCA attention; defer as in csa_attn."""
     nq, H, D = q.shape
     if o is None:
         o = torch.empty(nq, H, D, dtype=o_dtype or q.dtype, device=q.device)
@@ -94,6 +102,10 @@ def hca_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_be
         lse = torch.empty(nq, H, dtype=torch.float32, device=q.device)
     qd = F32 if q.dtype == torch.float32 else BF16
     buf = ws.get("hca", mqa_attn_workspace(qd, nq, H, D, max_visible + W))
+    if defer:
+        part = hca_dense_mqa_attn_partials(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin,
+                                           win_pos0, W, q_seq, q_pos, scale, o, lse, buf, q_lo=q_lo, stream=stream)
+        return o, lse, part
     hca_dense_mqa_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq,
                        q_pos, scale, o, lse, buf, q_lo=q_lo, stream=stream)
     return o, lse
@@ -198,7 +210,8 @@ class Decode1M:
     HCA attention does not depend on the indexer. `step()` runs the indexer's scores,
     then forks HCA attention onto a side stream (default priority), where it runs beside
     the top-k selection (one block per query) and CSA attention, and joins it back; on
-    the GPU and inside a captured graph alike. Beside the scores instead, HCA attention
+    the GPU and inside a captured graph alike. Both attention calls defer their split-K
+    merge, and one mqa_attn_merge launch after the join merges the two. Beside the scores instead, HCA attention
     and the bandwidth-bound scoring slow each other down about as much as they overlap."""
 
     def __init__(self, case, ws=None, overlap=True):
@@ -238,15 +251,17 @@ class Decode1M:
                           self.k, self.ws, q_idx_scale=t["q_idx_scale"], k_idx_scale=t["k_idx_scale"], out=self.idx,
                           phase=phase, stream=stream)
 
-    def csa_attention(self, stream=None):
+    def csa_attention(self, stream=None, defer=False):
         t = self.case.t
         return csa_attn(self.q_csa, self.csa, self.crb, self.idx, self.win_csa, self.wrb, self.wp0, self.W,
-                        t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_csa, lse=self.lse_csa, stream=stream)
+                        t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_csa, lse=self.lse_csa, stream=stream,
+                        defer=defer)
 
-    def hca_attention(self, stream=None):
+    def hca_attention(self, stream=None, defer=False):
         t = self.case.t
         return hca_attn(self.q_hca, self.hca, self.hrb, self.mp, self.n_h, self.win_hca, self.wrb, self.wp0, self.W,
-                        t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_hca, lse=self.lse_hca, stream=stream)
+                        t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_hca, lse=self.lse_hca, stream=stream,
+                        defer=defer)
 
     def step(self):
         if self.side is None:
@@ -258,10 +273,12 @@ class Decode1M:
         self.index(phase="scores")
         self.side.wait_stream(main)
         with torch.cuda.stream(self.side):
-            self.hca_attention()
+            hp = self.hca_attention(defer=True)[2]
         self.index(phase="select")
-        self.csa_attention()
+        cp = self.csa_attention(defer=True)[2]
         main.wait_stream(self.side)
+        # one launch merges both calls' split-K partials after the join
+        mqa_attn_merge(cp, hp)
 
 
 class DecodeBf16:
@@ -315,8 +332,13 @@ class DecodeBf16:
 
     def step(self):
         self.index()
-        self.csa_attention()
-        self.hca_attention()
+        _, _, cp = csa_attn(self.q, self.csa, self.crb, self.idx, self.win, self.wrb, self.wp0, self.W,
+                            self.case.t["q_seq"], self.case.t["q_pos"], self.scale, self.ws, o=self.o_csa,
+                            lse=self.lse_csa, defer=True)
+        _, _, hp = hca_attn(self.q, self.hca, self.hrb, self.mp, self.n_h, self.win, self.wrb, self.wp0, self.W,
+                            self.case.t["q_seq"], self.case.t["q_pos"], self.scale, self.ws, o=self.o_hca,
+                            lse=self.lse_hca, defer=True)
+        mqa_attn_merge(cp, hp)  # both calls' split-K partials in one launch
 
 
 def compress_1m(case, out_csa=None, out_hca=None, stream=None):

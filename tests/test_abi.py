@@ -282,3 +282,31 @@ def test_noalloc_attention_rejects_calls_beyond_its_scratch():
     bad = hca._StoreC(7, 448, 64, 0, 100, 0x9000000, 512, 0, 0, 0)
     assert hca._hca_attn_noalloc(P[0], 0, 1, 16, ctypes.byref(bad), P[1], 1, 100, ctypes.byref(f32), P[3], P[4], 0,
                                  P[5], P[6], None, 0.04, P[7], 0, P[8], None) == -1
+
+
+def test_deferred_merge_validation():
+    """mqa_attn_merge rejects NULL or malformed partial records on the host; records of calls that
+    were not split (or had no queries) need no launch, so they succeed without a GPU; the partial
+    calls validate their arguments as the undeferred calls do and need an output record."""
+    AP = hca.AttnPartials
+    assert hca._attn_merge(None, None, None) == -1
+    assert hca._attn_merge(ctypes.byref(AP(None, None, P[7], P[8], 4, 0, 512, 2, 1)), None, None) == -1
+    assert hca._attn_merge(ctypes.byref(AP(None, None, P[7], P[8], 4, 64, 512, 2, 1)), None, None) == -1  # no partials
+    assert hca._attn_merge(ctypes.byref(AP(P[9], P[9], P[7], P[8], 4, 64, 512, 2, 9)), None, None) == -1  # o dtype
+    assert hca._attn_merge(ctypes.byref(AP(P[9], P[9], None, P[8], 4, 64, 512, 2, 1)), None, None) == -1  # no output
+    done = AP(None, None, P[7], P[8], 4, 64, 512, 1, 1)  # one split: the call wrote its output itself
+    empty = AP(None, None, None, None, 0, 64, 512, 1, 1)
+    assert hca._attn_merge(ctypes.byref(done), ctypes.byref(empty), None) == 0
+    bad = AP(P[9], P[9], P[7], P[8], -1, 64, 512, 2, 1)
+    assert hca._attn_merge(ctypes.byref(done), ctypes.byref(bad), None) == -1
+    a = dict(q=P[0], qdt=1, nq=4, H=64, crb=P[1], idx=P[2], k=64, wrb=P[3], wp0=P[4], W=128, qseq=P[5],
+             qpos=P[6], o=P[7], lse=P[8], ws=P[9])
+    out = AP()
+    c, w = store(), store()
+    args = (a["q"], a["qdt"], a["nq"], 40, ctypes.byref(c), a["crb"], a["idx"], a["k"], ctypes.byref(w), a["wrb"],
+            a["wp0"], a["W"], a["qseq"], a["qpos"], None, 0.04, a["o"], 1, a["lse"], a["ws"], 1 << 30, None)
+    assert hca._csa_attn_partials(*args, ctypes.byref(out)) == -2          # 40 heads: unsupported, as undeferred
+    assert hca._csa_attn_partials(*args, None) == -1                       # no record
+    hargs = (a["q"], a["qdt"], a["nq"], 64, ctypes.byref(c), a["crb"], 128, 100, ctypes.byref(w), a["wrb"],
+             a["wp0"], a["W"], a["qseq"], a["qpos"], None, 0.04, a["o"], 1, a["lse"], a["ws"], 16, None)
+    assert hca._hca_attn_partials(*hargs, ctypes.byref(out)) == -3         # workspace too small
