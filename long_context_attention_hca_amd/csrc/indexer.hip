@@ -349,6 +349,78 @@ __device__ __forceinline__ void score_mxfp4_one(const IndexArgs& a, int qi, Bloc
   emit_candidates(a, qi, jb, nv, lds);
 }
 
+// bf16 keys on v_mfma_f32_32x32x16_bf16, laid out as the MXFP4 scorer: the A rows are the
+// query's heads (rows H..31 zero), the 32 columns 32 keys, K 16 dims per step (lane l: dims
+// 8 (l / 32) .. + 7 of the step), 4 steps for 64 dims, so a lane loads 16 bytes of one key row
+// per step and the accumulators hold the same heads as the MXFP4 scorer's. The dot products
+// are float32 sums of exact bf16 products in the MFMA's order (not the oracle's); bf16 scores
+// are compared with the oracle within its error bound, so only the fold is shared.
+// grid = (nblk, nq), 256 threads, 1024 keys per block.
+__global__ __launch_bounds__(256) void score_bf16_kernel(IndexArgs a) {
+  __shared__ BlockLds lds;
+  const int qi = blockIdx.y;
+  int64_t rb;
+  const int64_t nv = visible_keys(a, qi, &rb);
+  if (nv <= a.k) return;  // every visible entry is selected; no scores needed
+  const int64_t jb = (int64_t)blockIdx.x * kBlockKeys;
+  if (jb >= nv) return;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) lds.hist[i] = 0;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 31, blk = lane >> 5;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kp = static_cast<const uint16_t*>(a.keys);
+  bf16x8 A[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < a.H) v = *reinterpret_cast<const uint4*>(qp + ((int64_t)qi * a.H + row) * 64 + 16 * st + 8 * blk);
+    A[st] = __builtin_bit_cast(bf16x8, v);
+  }
+  float w[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) w[h] = h < a.H ? a.w[(int64_t)qi * a.H + h] : 0.f;
+  __syncthreads();
+  // 8 groups of 32 keys per wave, loaded 4 groups at a time (16 registers a group)
+  constexpr int U = 8, UH = 4;
+#pragma unroll
+  for (int u0 = 0; u0 < U; u0 += UH) {
+    bf16x8 Bk[UH][4];
+#pragma unroll
+    for (int u = 0; u < UH; ++u) {
+      const int64_t j = jb + (int64_t)(wave * U + u0 + u) * 32 + row;
+      const int64_t jc = rb + (j < nv ? j : nv - 1);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        Bk[u][st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kp + jc * 64 + 16 * st + 8 * blk));
+    }
+#pragma unroll
+    for (int u = 0; u < UH; ++u) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st], Bk[u][st], acc, 0, 0, 0);
+      // heads 0..3 in acc[0..3] of lanes 0..31, heads 4..7 in acc[0..3] of lanes 32..63
+      float r[8];
+      r[0] = acc[0]; r[1] = acc[1]; r[2] = acc[2]; r[3] = acc[3];
+      if (a.H > 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[4 + i] = __shfl(acc[i], (lane & 31) + 32, 64);
+      }
+      const int pos = (wave * U + u0 + u) * 32 + row;
+      if (lane < 32 && jb + pos < nv) {
+        float sc = score_term(w[0], r[0]);
+#pragma unroll
+        for (int h = 1; h < 8; ++h)
+          if (h < a.H) sc = score_add(sc, score_term(w[h], r[h]));
+        const uint32_t key = float_key(sc);
+        lds.key[pos] = key;
+        atomicAdd(&lds.hist[key >> 21], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  emit_candidates(a, qi, jb, nv, lds);
+}
+
 // MXFP4 scores via the scaled MFMA. grid = (nblk, nq), 256 threads, 1024 keys per block.
 __global__ __launch_bounds__(256) void score_mxfp4_kernel(IndexArgs a) {
   __shared__ BlockLds lds;
@@ -839,7 +911,8 @@ __global__ __launch_bounds__(kSThreads) void index_stream_kernel(IndexArgs a) {
   }
 }
 
-// fp32 / bf16 scores on the vector ALUs (4 keys per thread). grid = (nblk, nq).
+// fp32 scores on the vector ALUs (4 keys per thread; the bf16 instantiation is kept for
+// reference, bf16 keys take score_bf16_kernel). grid = (nblk, nq).
 template <typename T>
 __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
   __shared__ BlockLds lds;
@@ -1459,7 +1532,7 @@ hipError_t launch_index_topk(const IndexArgs& a, bool scores, bool select, hipSt
       hipLaunchKernelGGL(score_mxfp4_q4_kernel, g4, dim3(256), 0, s, a);
     } else if (a.dtype == HCA_MXFP4) hipLaunchKernelGGL(score_mxfp4_kernel, g, dim3(256), 0, s, a);
     else if (a.dtype == HCA_F32) hipLaunchKernelGGL(score_valu_kernel<float>, g, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(score_valu_kernel<uint16_t>, g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(score_bf16_kernel, g, dim3(256), 0, s, a);
   }
   if (select) hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.nq), dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
