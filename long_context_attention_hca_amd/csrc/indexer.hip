@@ -911,8 +911,8 @@ __global__ __launch_bounds__(kSThreads) void index_stream_kernel(IndexArgs a) {
   }
 }
 
-// fp32 scores on the vector ALUs (4 keys per thread; the bf16 instantiation is kept for
-// reference, bf16 keys take score_bf16_kernel). grid = (nblk, nq).
+// Scores on the vector ALUs (4 keys per thread), launched for fp32 keys (bf16 keys take
+// score_bf16_kernel). grid = (nblk, nq).
 template <typename T>
 __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
   __shared__ BlockLds lds;
