@@ -130,6 +130,21 @@ def test_mxfp4_many_queries_ties(hca, k):
     assert np.array_equal(np_(two), got)
 
 
+def test_mxfp4_many_queries_long_range(hca):
+    """The streaming selector over 2^20 visible entries (2048 tiles of 512 keys, dozens of
+    buffer cuts per query): 256 queries made of two distinct queries alternating, so the oracle
+    scores two; every row is checked."""
+    n, nq, k = 1 << 20, 256, 1024
+    q2, qs2, w2, kp, ks = mx_case(51, n, 2, 4)
+    q = q2.repeat(nq // 2, 1, 1)
+    qs = qs2.repeat(nq // 2, 1, 1)
+    w = w2.repeat(nq // 2, 1)
+    q_pos = [4 * n - 1, 4 * n - 3001] * (nq // 2)
+    got = run(hca, q, w, kp, [0], [0] * nq, q_pos, n, 4, k, qs, ks)
+    ref = oracle_mxfp4(q2, qs2, w2, kp, ks, [0], [0, 0], q_pos[:2], 4, k)
+    check_idx(got, np.tile(ref, (nq // 2, 1)), "2^20 visible, streaming")
+
+
 def _fold_sensitive_pairs(n, positive):
     """n cases (w0, w1, a, b): two entries a = (a0, a1) and b = (b0, b1) of E2M1 values whose
     scores w0 relu(x0) + w1 relu(x1), each product and the sum rounded to float32, give
