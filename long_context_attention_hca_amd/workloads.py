@@ -382,10 +382,13 @@ def chunked_prefill(case, ws=None, window="split"):
                      out_row0=p["csa_row_begin"][b] + P // m)
         hca_compress(raw[b], first_pos, lh[b], t["bias_hca"], mp, P // mp, chunk // mp, hca,
                      out_row0=p["hca_row_begin"][b] + P // mp)
-    crb = _i64(p["csa_row_begin"], dev)
-    hrb = _i64(p["hca_row_begin"], dev)
-    wrb = _i64(p["win_row_begin"], dev)
-    wp0 = _i64(p["win_pos0"], dev)
+    # the per-sequence offsets go to the device once per case (a copy from host lists waits for
+    # the stream, which would serialise the calls around it)
+    offs = getattr(case, "_device_offsets", None)
+    if offs is None:
+        offs = tuple(_i64(p[name], dev) for name in ("csa_row_begin", "hca_row_begin", "win_row_begin", "win_pos0"))
+        case._device_offsets = offs
+    crb, hrb, wrb, wp0 = offs
     max_c = max((P + chunk) // m for P in p["prefixes"])
     max_h = max((P + chunk) // mp for P in p["prefixes"])
     idx = index_topk(t["q_idx"], t["w_idx"], t["k_idx"], crb, t["q_seq"], t["q_pos"], max_c, m, k, ws,
