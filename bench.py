@@ -143,7 +143,7 @@ def main():
     ap.add_argument("--no-compress", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(a decode batch shards by sequence with no communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
