@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define HCA_ABI_VERSION 2
+#define HCA_ABI_VERSION 3
 
 /* Status codes. */
 #define HCA_OK 0
@@ -304,6 +304,30 @@ int lightning_index_select(const void* q_idx, const uint8_t* q_idx_scale, const 
                            int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * lightning_index_select_pending — lightning_index_select recorded instead of
+ * enqueued (CSA paragraph: the indexer's top-k selection), for a call that
+ * runs it inside its own launch: hca_dense_mqa_attn_partials_select. It takes
+ * lightning_index_select's arguments (stream unused) plus `out`, a host
+ * struct it fills (opaque contents: the validated arguments). Nothing is
+ * enqueued. The recorded selection reads the workspace that
+ * lightning_index_scores left and writes out_idx when it runs; the workspace,
+ * out_idx and the query arrays must stay valid and unchanged until then.
+ * Errors as lightning_index_select (out untouched on error; NULL out:
+ * HCA_ERR_INVALID_ARG).
+ */
+typedef struct hca_pending_select {
+  uint64_t opaque[48];
+} hca_pending_select;
+int lightning_index_select_pending(const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx,
+                                   int32_t n_idx_heads, int32_t d_idx, int32_t idx_dtype,
+                                   const void* k_idx, const uint8_t* k_idx_scale, int64_t k_rows,
+                                   const int64_t* k_row_begin, const int32_t* q_seq,
+                                   const int64_t* q_pos, const int64_t* q_lo, int32_t nq,
+                                   int64_t max_visible, int32_t m, int32_t w, int32_t k,
+                                   int32_t* out_idx, void* ws, size_t ws_bytes, void* stream,
+                                   hca_pending_select* out);
+
+/*
  * csa_sparse_mqa_attn — CSA core attention (CSA paragraph: MQA with shared
  * keys and values over the selected entries; HCA paragraph: plus a
  * sliding-window branch).
@@ -396,6 +420,32 @@ int hca_dense_mqa_attn_partials(const void* q, int32_t q_dtype, int32_t nq, int3
                                 float scale, void* o, int32_t o_dtype, float* lse, void* ws,
                                 size_t ws_bytes, void* stream, hca_attn_partials* out);
 int mqa_attn_merge(const hca_attn_partials* a, const hca_attn_partials* b, void* stream);
+
+/*
+ * hca_dense_mqa_attn_partials_select — hca_dense_mqa_attn_partials and a
+ * recorded top-k selection (lightning_index_select_pending) enqueued as one
+ * unit on `stream` (HCA paragraph: dense attention over the heavily
+ * compressed entries; CSA paragraph: the indexer's top-k, which only the
+ * later CSA call reads). For a decode step whose HCA call does not depend on
+ * the selection: when the HCA call takes the FP8 split-store kernel, the
+ * selection's blocks run in the same grid as the attention's (one launch
+ * instead of two streams joined by events); otherwise the selection is
+ * launched first on the stream. Results are bit-identical to the two calls
+ * made separately: out_idx as lightning_index_select writes it, o/lse and the
+ * partials as hca_dense_mqa_attn_partials. The selection must not read what
+ * the attention writes (its workspace and out_idx are disjoint from the HCA
+ * call's ws, o and lse). Errors as hca_dense_mqa_attn_partials; sel NULL or
+ * not filled by lightning_index_select_pending: HCA_ERR_INVALID_ARG. An
+ * inactive selection (no query, or the streaming indexer path) adds nothing.
+ */
+int hca_dense_mqa_attn_partials_select(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                                       const hca_store* cache, const int64_t* cache_row_begin,
+                                       int32_t m_prime, int64_t max_visible, const hca_store* window,
+                                       const int64_t* win_row_begin, const int64_t* win_pos0,
+                                       int32_t W, const int32_t* q_seq, const int64_t* q_pos,
+                                       const int64_t* q_lo, float scale, void* o, int32_t o_dtype,
+                                       float* lse, void* ws, size_t ws_bytes, void* stream,
+                                       const hca_pending_select* sel, hca_attn_partials* out);
 
 /*
  * hca_dense_mqa_attn_noalloc — hca_dense_mqa_attn for callers that cannot

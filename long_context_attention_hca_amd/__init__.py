@@ -19,7 +19,8 @@ __all__ = [
     "HcaError", "Store", "DecodeLayer", "abi_version", "csa_compress", "hca_compress", "decode_append",
     "lightning_index_topk_workspace", "lightning_index_topk", "mqa_attn_workspace",
     "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "hca_dense_mqa_attn_noalloc", "AttnPartials",
-    "csa_sparse_mqa_attn_partials", "hca_dense_mqa_attn_partials", "mqa_attn_merge", "grouped_out_proj",
+    "csa_sparse_mqa_attn_partials", "hca_dense_mqa_attn_partials", "mqa_attn_merge", "PendingSelect",
+    "lightning_index_select_pending", "hca_dense_mqa_attn_partials_select", "grouped_out_proj",
     "library_path",
 ]
 
@@ -101,6 +102,17 @@ _csa_attn_partials = _sig("csa_sparse_mqa_attn_partials", ctypes.c_int,
 _hca_attn_partials = _sig("hca_dense_mqa_attn_partials", ctypes.c_int,
                           [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail + [_AP])
 _attn_merge = _sig("mqa_attn_merge", ctypes.c_int, [_AP, _AP, _P])
+
+
+class PendingSelect(ctypes.Structure):
+    """hca_pending_select: a top-k selection recorded by lightning_index_select_pending."""
+    _fields_ = [("opaque", ctypes.c_uint64 * 48)]
+
+
+_PS = ctypes.POINTER(PendingSelect)
+_index_pending = _sig("lightning_index_select_pending", ctypes.c_int, _index_argtypes + [_PS])
+_hca_attn_partials_select = _sig("hca_dense_mqa_attn_partials_select", ctypes.c_int,
+                                 [_P, _I32, _I32, _I32, _SP, _P, _I32, _I64] + _attn_tail + [_PS, _AP])
 
 
 class HcaError(RuntimeError):
@@ -243,13 +255,29 @@ def lightning_index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_vis
     """q_idx [nq, H, d] (f32/bf16) or [nq, H, d/2] uint8 (MXFP4, with scales). q_lo: int64 [nq]
     document starts (None: no document mask); w: the CSA window (default 2m). phase "scores" /
     "select" calls lightning_index_scores / lightning_index_select (the two halves)."""
+    _check(_index_phase[phase](*_index_call_args(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k,
+                                                 out_idx, ws, q_idx_scale, k_idx_scale, idx_dtype, q_lo, w, stream)))
+
+
+def _index_call_args(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out_idx, ws, q_idx_scale,
+                     k_idx_scale, idx_dtype, q_lo, w, stream):
     dt = _dtype_code(q_idx) if idx_dtype is None else idx_dtype
     nq, H = q_idx.shape[0], q_idx.shape[1]
     d = q_idx.shape[2] * (2 if dt == MXFP4 else 1)
-    _check(_index_phase[phase](_ptr(q_idx), _ptr(q_idx_scale), _ptr(w_idx), H, d, dt, _ptr(k_idx), _ptr(k_idx_scale),
-                  k_idx.shape[0], _ptr(k_row_begin), _ptr(q_seq), _ptr(q_pos), _ptr(q_lo), nq, max_visible, m,
-                  2 * m if w is None else w, k, _ptr(out_idx), _ptr(ws), ws.numel() * ws.element_size(),
-                  _stream(stream)))
+    return (_ptr(q_idx), _ptr(q_idx_scale), _ptr(w_idx), H, d, dt, _ptr(k_idx), _ptr(k_idx_scale), k_idx.shape[0],
+            _ptr(k_row_begin), _ptr(q_seq), _ptr(q_pos), _ptr(q_lo), nq, max_visible, m, 2 * m if w is None else w, k,
+            _ptr(out_idx), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
+def lightning_index_select_pending(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out_idx, ws,
+                                   q_idx_scale=None, k_idx_scale=None, idx_dtype=None, q_lo=None, w=None):
+    """lightning_index_topk's selection phase recorded, not enqueued: returns the PendingSelect that
+    hca_dense_mqa_attn_partials_select runs. The tensors must stay alive until then."""
+    out = PendingSelect()
+    _check(_index_pending(*_index_call_args(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k,
+                                            out_idx, ws, q_idx_scale, k_idx_scale, idx_dtype, q_lo, w, None),
+                          ctypes.byref(out)))
+    return out
 
 
 def mqa_attn_workspace(q_dtype, nq, n_heads, d, max_entries):
@@ -303,6 +331,21 @@ def hca_dense_mqa_attn_partials(q, cache, cache_row_begin, m_prime, max_visible,
                               m_prime, max_visible, window.c(), _ptr(win_row_begin), _ptr(win_pos0), W, _ptr(q_seq),
                               _ptr(q_pos), _ptr(q_lo), scale, _ptr(o), _dtype_code(o), _ptr(lse), wp, wb,
                               _stream(stream), ctypes.byref(out)))
+    return out
+
+
+def hca_dense_mqa_attn_partials_select(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin,
+                                       win_pos0, W, q_seq, q_pos, scale, o, lse, sel, ws=None, q_lo=None,
+                                       stream=None):
+    """hca_dense_mqa_attn_partials with the recorded selection `sel` (a PendingSelect) enqueued as one
+    unit: returns the AttnPartials that mqa_attn_merge takes."""
+    wp, wb = _ws_args(ws)
+    out = AttnPartials()
+    _check(_hca_attn_partials_select(_ptr(q), _dtype_code(q), q.shape[0], q.shape[1], cache.c(),
+                                     _ptr(cache_row_begin), m_prime, max_visible, window.c(), _ptr(win_row_begin),
+                                     _ptr(win_pos0), W, _ptr(q_seq), _ptr(q_pos), _ptr(q_lo), scale, _ptr(o),
+                                     _dtype_code(o), _ptr(lse), wp, wb, _stream(stream), ctypes.byref(sel),
+                                     ctypes.byref(out)))
     return out
 
 

@@ -242,7 +242,8 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
               const int64_t* win_pos0, int32_t W, const int32_t* q_seq, const int64_t* q_pos,
               const int64_t* q_lo, float scale,
               void* o, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream,
-              bool static_scratch = false, hca_attn_partials* defer = nullptr) {
+              bool static_scratch = false, hca_attn_partials* defer = nullptr,
+              const hca::IndexArgs* sel = nullptr) {
   if (!q || !cache_row_begin || !win_row_begin || !win_pos0 || !q_seq || !q_pos || !o || !lse)
     return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
   if (csa && k > 0 && !idx) return fail(HCA_ERR_INVALID_ARG, fn, "NULL idx");
@@ -267,7 +268,12 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
     if (!valu) return fail(HCA_ERR_UNSUPPORTED, fn, "unsupported dtype/layout/shape combination");
   }
   if (defer) *defer = hca_attn_partials{nullptr, nullptr, o, lse, 0, n_heads, D, 1, o_dtype};
-  if (nq == 0) return HCA_OK;
+  if (nq == 0) {
+    if (!sel) return HCA_OK;
+    const int st = ensure_init(fn);
+    if (st != HCA_OK) return st;
+    return launched(fn, hca::launch_index_topk(*sel, false, true, static_cast<hipStream_t>(stream)));
+  }
   const int64_t max_entries = (csa ? (int64_t)k : max_visible) + W;
   int n_split = 1, per = 1;
   const bool wide = hca::attn_wide_supported(q_dtype, cv, wv, n_heads, nq);
@@ -311,7 +317,7 @@ int attn_impl(const char* fn, bool csa, const void* q, int32_t q_dtype, int32_t 
     a.part_lse = a.part_o + (size_t)nq * n_split * n_heads * D;
   }
   if (defer) *defer = hca_attn_partials{a.part_o, a.part_lse, o, lse, nq, n_heads, D, n_split, o_dtype};
-  return launched(fn, hca::launch_attention(a, static_cast<hipStream_t>(stream), /*combine=*/defer == nullptr));
+  return launched(fn, hca::launch_attention(a, static_cast<hipStream_t>(stream), /*combine=*/defer == nullptr, sel));
 }
 
 int check_partials(const char* fn, const hca_attn_partials* p, const char* which) {
@@ -421,13 +427,24 @@ namespace {
 // The indexer's two phases: kIndexBoth (lightning_index_topk), kIndexScores or kIndexSelect
 // (the split calls, which keep every query's intermediate state in the workspace in between
 // and so need the workspace of all nq queries at once).
-enum IndexPhase { kIndexBoth = 0, kIndexScores = 1, kIndexSelect = 2 };
+enum IndexPhase { kIndexBoth = 0, kIndexScores = 1, kIndexSelect = 2, kIndexPending = 3 };
+
+// What lightning_index_select_pending records in a hca_pending_select.
+struct PendingSelect {
+  uint64_t magic;  // kPendingMagic once recorded
+  int32_t active;  // 0: the selection has nothing to launch (no query, or the streaming path)
+  int32_t pad;
+  hca::IndexArgs a;
+};
+constexpr uint64_t kPendingMagic = 0x5345'4c45'4354'3031ull;
+static_assert(sizeof(PendingSelect) <= sizeof(hca_pending_select), "hca_pending_select too small");
 
 int index_impl(const char* fn, int phase, const void* q_idx, const uint8_t* q_idx_scale, const float* w_idx,
                int32_t n_idx_heads, int32_t d_idx, int32_t idx_dtype, const void* k_idx,
                const uint8_t* k_idx_scale, int64_t k_rows, const int64_t* k_row_begin, const int32_t* q_seq,
                const int64_t* q_pos, const int64_t* q_lo, int32_t nq, int64_t max_visible, int32_t m, int32_t w,
-               int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
+               int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream,
+               PendingSelect* pending = nullptr) {
   if (!q_idx || !w_idx || !k_idx || !k_row_begin || !q_seq || !q_pos || !out_idx)
     return fail(HCA_ERR_INVALID_ARG, fn, "NULL argument");
   if (idx_dtype != HCA_F32 && idx_dtype != HCA_BF16 && idx_dtype != HCA_MXFP4)
@@ -449,8 +466,10 @@ int index_impl(const char* fn, int phase, const void* q_idx, const uint8_t* q_id
     while (batch > 1 && index_ws(batch, max_visible) > ws_bytes) batch = std::max<int64_t>(1, batch / 2);
   const int64_t q_row = idx_dtype == HCA_MXFP4 ? (int64_t)n_idx_heads * d_idx / 2
                                                : (int64_t)n_idx_heads * d_idx * (idx_dtype == HCA_F32 ? 4 : 2);
-  int st = ensure_init(fn);
-  if (st != HCA_OK) return st;
+  if (phase != kIndexPending) {  // recording a selection touches no device
+    const int st = ensure_init(fn);
+    if (st != HCA_OK) return st;
+  }
   for (int64_t q0 = 0; q0 < nq; q0 += batch) {
     const int64_t nb = std::min<int64_t>(batch, nq - q0);
     hca::IndexArgs a;
@@ -474,6 +493,13 @@ int index_impl(const char* fn, int phase, const void* q_idx, const uint8_t* q_id
     a.m = m;
     a.k = k;
     a.out = out_idx + q0 * k;
+    if (phase == kIndexPending) {
+      // the split calls take every query in one batch; the streaming path's selection phase has
+      // nothing to launch
+      pending->a = a;
+      pending->active = hca::index_stream_path(idx_dtype, n_idx_heads, nq, k) ? 0 : 1;
+      return HCA_OK;
+    }
     hipError_t e = hca::launch_index_topk(a, phase != kIndexSelect, phase != kIndexScores,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return launched(fn, e);
@@ -505,6 +531,18 @@ HCA_EXPORT int lightning_index_scores(HCA_INDEX_ARGS) {
 
 HCA_EXPORT int lightning_index_select(HCA_INDEX_ARGS) {
   return index_impl("lightning_index_select", kIndexSelect, HCA_INDEX_PASS);
+}
+
+HCA_EXPORT int lightning_index_select_pending(HCA_INDEX_ARGS, hca_pending_select* out) {
+  const char* fn = "lightning_index_select_pending";
+  if (!out) return fail(HCA_ERR_INVALID_ARG, fn, "NULL out");
+  PendingSelect ps{};
+  const int st = index_impl(fn, kIndexPending, HCA_INDEX_PASS, &ps);
+  if (st != HCA_OK) return st;
+  ps.magic = kPendingMagic;
+  std::memset(out, 0, sizeof(*out));
+  std::memcpy(out, &ps, sizeof(ps));
+  return HCA_OK;
 }
 
 HCA_EXPORT size_t mqa_attn_workspace(int32_t q_dtype, int32_t nq, int32_t n_heads, int32_t d, int64_t max_entries) {
@@ -558,6 +596,24 @@ HCA_EXPORT int hca_dense_mqa_attn_partials(const void* q, int32_t q_dtype, int32
   return attn_impl(fn, false, q, q_dtype, nq, n_heads, cache, cache_row_begin, nullptr, 0, m_prime, max_visible,
                    window, win_row_begin, win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype, lse, ws, ws_bytes,
                    stream, false, out);
+}
+
+HCA_EXPORT int hca_dense_mqa_attn_partials_select(const void* q, int32_t q_dtype, int32_t nq, int32_t n_heads,
+                                                  const hca_store* cache, const int64_t* cache_row_begin,
+                                                  int32_t m_prime, int64_t max_visible, const hca_store* window,
+                                                  const int64_t* win_row_begin, const int64_t* win_pos0, int32_t W,
+                                                  const int32_t* q_seq, const int64_t* q_pos, const int64_t* q_lo,
+                                                  float scale, void* o, int32_t o_dtype, float* lse, void* ws,
+                                                  size_t ws_bytes, void* stream, const hca_pending_select* sel,
+                                                  hca_attn_partials* out) {
+  const char* fn = "hca_dense_mqa_attn_partials_select";
+  if (!out || !sel) return fail(HCA_ERR_INVALID_ARG, fn, "NULL out or sel");
+  PendingSelect ps;
+  std::memcpy(&ps, sel, sizeof(ps));
+  if (ps.magic != kPendingMagic) return fail(HCA_ERR_INVALID_ARG, fn, "sel was not filled by lightning_index_select_pending");
+  return attn_impl(fn, false, q, q_dtype, nq, n_heads, cache, cache_row_begin, nullptr, 0, m_prime, max_visible,
+                   window, win_row_begin, win_pos0, W, q_seq, q_pos, q_lo, scale, o, o_dtype, lse, ws, ws_bytes,
+                   stream, false, out, ps.active ? &ps.a : nullptr);
 }
 
 HCA_EXPORT int mqa_attn_merge(const hca_attn_partials* a, const hca_attn_partials* b, void* stream) {

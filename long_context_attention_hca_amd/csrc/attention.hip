@@ -33,6 +33,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "topk_select.h"
 
 namespace hca {
 namespace {
@@ -681,17 +682,22 @@ __device__ __forceinline__ void f8_chunk(const AttnArgs& a, const QueryCtx& ctx,
   if (more) stage_rows<8, 2>(nxt, ndst, lane);
 }
 
+// The LDS of one attn_fp8 block: two chunk buffers as separate LDS objects (see f8_chunk), then
+// the P tiles and maxima. A kernel declares them and hands them to attn_fp8_block.
+#define ATTN_FP8_LDS                                                                             \
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBufF8];                                  \
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[kBufF8];                                  \
+  __shared__ __attribute__((aligned(16))) uint16_t pbs[16 * kPRow]; /* [16][kPRow] P x scale */  \
+  __shared__ __attribute__((aligned(16))) uint16_t pb[16 * kPRow];  /* [16][kPRow] P */          \
+  __shared__ float wmax[8 * 16], wsum[8 * 16];
+
+// Work item id < total of an attn_fp8 grid: (query, split, 16-head group).
 // kSparse: CSA (entries listed by idx, a.idx set) or HCA (dense, a.idx null).
 template <bool kSparse>
-__global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, int total) {
-  // two chunk buffers as separate LDS objects (see f8_chunk), then the P tiles and maxima
-  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBufF8];
-  __shared__ __attribute__((aligned(16))) uint8_t buf1[kBufF8];
-  __shared__ __attribute__((aligned(16))) uint16_t pbs[16 * kPRow];  // [16][kPRow] P x entry scale
-  __shared__ __attribute__((aligned(16))) uint16_t pb[16 * kPRow];   // [16][kPRow] P
-  __shared__ float wmax[8 * 16], wsum[8 * 16];
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  if (id >= total) return;
+__device__ __forceinline__ void attn_fp8_block(const AttnArgs& a, int n_hg, int id, uint8_t (&buf0)[kBufF8],
+                                               uint8_t (&buf1)[kBufF8], uint16_t (&pbs)[16 * kPRow],
+                                               uint16_t (&pb)[16 * kPRow], float (&wmax)[8 * 16],
+                                               float (&wsum)[8 * 16]) {
   const int hg = id % n_hg;
   const int rest = id / n_hg;
   const int s = rest % a.n_split;
@@ -860,6 +866,35 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, 
     if (a.n_split == 1) a.lse[hrow] = lse;
     else a.part_lse[((int64_t)qi * a.n_split + s) * H + head_o] = lse;
   }
+}
+
+template <bool kSparse>
+__global__ __launch_bounds__(512, 1) void attn_fp8_kernel(AttnArgs a, int n_hg, int total) {
+  ATTN_FP8_LDS
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= total) return;
+  attn_fp8_block<kSparse>(a, n_hg, id, buf0, buf1, pbs, pb, wmax, wsum);
+}
+
+// The indexer's top-k selection and an HCA attention call in one grid, for callers whose
+// selection and attention are independent (the selection feeds a later CSA call): blocks
+// b < n_sel (a multiple of 8) select query b of `sel` (b < sel.nq), the others are the
+// attention call's blocks b - n_sel, so their XCD placement is the attention kernel's own.
+// The selection takes one block of the 8 that share an XCD slot and its LDS aliases the chunk
+// buffers. One launch instead of two on separate streams, whose cross-stream waits cost more
+// than the selection itself.
+static_assert(kFinThreads == 512, "the selection runs in 512-thread attention blocks");
+static_assert(sizeof(FinLds) <= kBufF8 && sizeof(OutLds) <= kBufF8, "selection LDS inside the chunk buffers");
+__global__ __launch_bounds__(512, 1) void select_attn_fp8_kernel(IndexArgs sel, int n_sel, AttnArgs a, int n_hg,
+                                                                 int total) {
+  ATTN_FP8_LDS
+  const int b = blockIdx.x;
+  if (b >= n_sel) {
+    const int id = xcd_remap(b - n_sel, (int)gridDim.x - n_sel);
+    if (id < total) attn_fp8_block<false>(a, n_hg, id, buf0, buf1, pbs, pb, wmax, wsum);
+    return;
+  }
+  if (b < sel.nq) finalize_block(sel, b, *reinterpret_cast<FinLds*>(buf0), *reinterpret_cast<OutLds*>(buf1));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1720,10 +1755,18 @@ bool attn_rows_eligible(const AttnArgs& a) {
   return a.H == 16 * kRowsWaves && (int64_t)a.nq * a.n_split >= 256;
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s, bool combine) {
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s, bool combine, const IndexArgs* sel) {
   const bool mfma = a.q_dtype == HCA_BF16;
   const bool fp8 = mfma && attn_fp8_supported(a.cache, a.win);
-  if (attn_wide_supported(a.q_dtype, a.cache, a.win, a.H, a.nq)) {
+  const bool wide = attn_wide_supported(a.q_dtype, a.cache, a.win, a.H, a.nq);
+  // a selection to run with this call shares the grid of the dense attn_fp8 kernel; beside any
+  // other kernel it is launched first on the same stream
+  const bool fused = sel && sel->nq > 0 && !wide && fp8 && !attn_rows_eligible(a) && !a.idx;
+  if (sel && !fused) {
+    const hipError_t e = launch_index_topk(*sel, false, true, s);
+    if (e != hipSuccess) return e;
+  }
+  if (wide) {
     const int n_hg = a.H / 64;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;
@@ -1738,8 +1781,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s, bool combine) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;
-    if (a.idx) hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(grid), dim3(512), 0, s, a, n_hg, total);
-    else hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(grid), dim3(512), 0, s, a, n_hg, total);
+    if (fused) {
+      const int n_sel = (sel->nq + 7) / 8 * 8;
+      hipLaunchKernelGGL(select_attn_fp8_kernel, dim3(n_sel + grid), dim3(512), 0, s, *sel, n_sel, a, n_hg, total);
+    } else if (a.idx) {
+      hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(grid), dim3(512), 0, s, a, n_hg, total);
+    } else {
+      hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(grid), dim3(512), 0, s, a, n_hg, total);
+    }
   } else if (mfma) {
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;

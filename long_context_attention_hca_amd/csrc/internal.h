@@ -142,7 +142,10 @@ bool attn_mfma_supported(int q_dtype, int o_dtype, const StoreView& c, const Sto
 bool attn_wide_supported(int q_dtype, const StoreView& c, const StoreView& w, int H, int nq);
 void attn_split_policy_wide(int nq, int H, int64_t max_entries, int* n_split, int* per_split);
 // combine = false leaves a split call's partials for a later launch_merge (deferred merge).
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, bool combine = true);
+// sel: an index selection (launch_index_topk's select phase) to run with this call: in the same
+// grid when the call takes the dense attn_fp8 kernel, else launched just before it
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, bool combine = true,
+                            const IndexArgs* sel = nullptr);
 // The LSE merge of one call's split-K partials, or of two calls' in one launch (b may be null).
 struct MergeArgs {
   const float* part_o;

@@ -14,8 +14,8 @@ import torch
 
 from . import (BF16, DecodeLayer, F32, LAYOUT_BF16, LAYOUT_F32, LAYOUT_MXFP4, LAYOUT_SPLIT, Store, csa_compress,
                csa_sparse_mqa_attn, csa_sparse_mqa_attn_partials, decode_append, hca_compress, hca_dense_mqa_attn,
-               hca_dense_mqa_attn_partials, lightning_index_topk, lightning_index_topk_workspace, mqa_attn_merge,
-               mqa_attn_workspace)
+               hca_dense_mqa_attn_partials, hca_dense_mqa_attn_partials_select, lightning_index_select_pending,
+               lightning_index_topk, lightning_index_topk_workspace, mqa_attn_merge, mqa_attn_workspace)
 
 
 def _i64(vals, dev):
@@ -66,6 +66,10 @@ def index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k
     need = lightning_index_topk_workspace(nq, max_visible, k)
     one = lightning_index_topk_workspace(1, max_visible, k)
     buf = ws.get("index", need if phase != "both" else min(need, max(one, 4 << 30)))
+    if phase == "pending":
+        # the selection recorded for hca_attn(..., sel=...), which runs it in its own launch
+        return lightning_index_select_pending(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out,
+                                              buf, q_idx_scale=q_idx_scale, k_idx_scale=k_idx_scale, q_lo=q_lo, w=w)
     lightning_index_topk(q_idx, w_idx, k_idx, k_row_begin, q_seq, q_pos, max_visible, m, k, out, buf,
                          q_idx_scale=q_idx_scale, k_idx_scale=k_idx_scale, q_lo=q_lo, w=w, phase=phase,
                          stream=stream)
@@ -93,8 +97,9 @@ def csa_attn(q, cache, cache_row_begin, idx, window, win_row_begin, win_pos0, W,
 
 
 def hca_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin, win_pos0, W, q_seq, q_pos,
-             scale, ws, o_dtype=None, o=None, lse=None, q_lo=None, stream=None, defer=False):
-    """HCA attention; defer as in csa_attn."""
+             scale, ws, o_dtype=None, o=None, lse=None, q_lo=None, stream=None, defer=False, sel=None):
+    """HCA attention; defer as in csa_attn. sel: a PendingSelect (index_topk(..., phase="pending"))
+    enqueued with the call (deferred calls only)."""
     nq, H, D = q.shape
     if o is None:
         o = torch.empty(nq, H, D, dtype=o_dtype or q.dtype, device=q.device)
@@ -102,6 +107,13 @@ def hca_attn(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_be
         lse = torch.empty(nq, H, dtype=torch.float32, device=q.device)
     qd = F32 if q.dtype == torch.float32 else BF16
     buf = ws.get("hca", mqa_attn_workspace(qd, nq, H, D, max_visible + W))
+    if sel is not None and not defer:
+        raise ValueError("sel needs defer=True")
+    if sel is not None:
+        part = hca_dense_mqa_attn_partials_select(q, cache, cache_row_begin, m_prime, max_visible, window,
+                                                  win_row_begin, win_pos0, W, q_seq, q_pos, scale, o, lse, sel, buf,
+                                                  q_lo=q_lo, stream=stream)
+        return o, lse, part
     if defer:
         part = hca_dense_mqa_attn_partials(q, cache, cache_row_begin, m_prime, max_visible, window, win_row_begin,
                                            win_pos0, W, q_seq, q_pos, scale, o, lse, buf, q_lo=q_lo, stream=stream)
@@ -207,12 +219,15 @@ class Decode1M:
     (index + CSA attention for one layer, HCA attention for another), with all
     outputs and workspaces preallocated so that `step()` only enqueues kernels.
 
-    HCA attention does not depend on the indexer. `step()` runs the indexer's scores,
-    then forks HCA attention onto a side stream (default priority), where it runs beside
-    the top-k selection (one block per query) and CSA attention, and joins it back; on
-    the GPU and inside a captured graph alike. Both attention calls defer their split-K
-    merge, and one mqa_attn_merge launch after the join merges the two. Beside the scores instead, HCA attention
-    and the bandwidth-bound scoring slow each other down about as much as they overlap."""
+    HCA attention does not depend on the indexer. `step()` runs on one stream: the indexer's
+    scores, then one launch holding the top-k selection (one block per query) beside HCA
+    attention (hca_dense_mqa_attn_partials_select with the selection recorded by
+    lightning_index_select_pending), then CSA attention over the selected entries, and one
+    mqa_attn_merge launch for both calls' split-K partials. Running HCA attention on a second
+    stream instead, forked after the scores and joined before the merge, costs the step the
+    latency of two cross-stream waits. Beside the scores, HCA attention and the
+    bandwidth-bound scoring slow each other down about as much as they overlap.
+    overlap=False runs the index, CSA and HCA calls one after another, undeferred."""
 
     def __init__(self, case, ws=None, overlap=True):
         p, t = case.params, case.t
@@ -243,7 +258,7 @@ class Decode1M:
         self.ws.get("index", lightning_index_topk_workspace(B, self.n_c, k))
         self.ws.get("csa", mqa_attn_workspace(BF16, B, H, D, k + W))
         self.ws.get("hca", mqa_attn_workspace(BF16, B, H, D, self.n_h + W))
-        self.side = torch.cuda.Stream(device=dev) if overlap else None
+        self.overlap = overlap
 
     def index(self, stream=None, phase="both"):
         t = self.case.t
@@ -257,27 +272,23 @@ class Decode1M:
                         t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_csa, lse=self.lse_csa, stream=stream,
                         defer=defer)
 
-    def hca_attention(self, stream=None, defer=False):
+    def hca_attention(self, stream=None, defer=False, sel=None):
         t = self.case.t
         return hca_attn(self.q_hca, self.hca, self.hrb, self.mp, self.n_h, self.win_hca, self.wrb, self.wp0, self.W,
                         t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_hca, lse=self.lse_hca, stream=stream,
-                        defer=defer)
+                        defer=defer, sel=sel)
 
     def step(self):
-        if self.side is None:
+        if not self.overlap:
             self.index()
             self.csa_attention()
             self.hca_attention()
             return
-        main = torch.cuda.current_stream()
         self.index(phase="scores")
-        self.side.wait_stream(main)
-        with torch.cuda.stream(self.side):
-            hp = self.hca_attention(defer=True)[2]
-        self.index(phase="select")
+        sel = self.index(phase="pending")
+        hp = self.hca_attention(defer=True, sel=sel)[2]
         cp = self.csa_attention(defer=True)[2]
-        main.wait_stream(self.side)
-        # one launch merges both calls' split-K partials after the join
+        # one launch merges both calls' split-K partials
         mqa_attn_merge(cp, hp)
 
 

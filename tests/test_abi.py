@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert hca.abi_version() == 2
+    assert hca.abi_version() == 3
     for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small")]:
         assert hca._status_string(code) == text
 
@@ -310,3 +310,39 @@ def test_deferred_merge_validation():
     hargs = (a["q"], a["qdt"], a["nq"], 64, ctypes.byref(c), a["crb"], 128, 100, ctypes.byref(w), a["wrb"],
              a["wp0"], a["W"], a["qseq"], a["qpos"], None, 0.04, a["o"], 1, a["lse"], a["ws"], 16, None)
     assert hca._hca_attn_partials(*hargs, ctypes.byref(out)) == -3         # workspace too small
+
+
+def pending_call(out, **kw):
+    a = dict(q=P[0], qs=P[1], w=P[2], H=4, d=64, dt=3, k_idx=P[3], ks=P[4], k_rows=1000, krb=P[5], qseq=P[6],
+             qpos=P[7], qlo=None, nq=4, mv=1000, m=4, cw=8, k=64, out=P[8], ws=P[9], wsb=1 << 30)
+    a.update(kw)
+    return hca._index_pending(a["q"], a["qs"], a["w"], a["H"], a["d"], a["dt"], a["k_idx"], a["ks"], a["k_rows"],
+                              a["krb"], a["qseq"], a["qpos"], a["qlo"], a["nq"], a["mv"], a["m"], a["cw"], a["k"],
+                              a["out"], a["ws"], a["wsb"], None, out)
+
+
+def test_pending_select_records_and_validates():
+    """lightning_index_select_pending validates as lightning_index_select (the split calls' whole-
+    workspace rule included) and records without touching a device; the combined HCA call rejects
+    a missing record or one the library did not fill before anything is enqueued."""
+    sel = hca.PendingSelect()
+    assert pending_call(None) == -1                                  # no record
+    assert pending_call(ctypes.byref(sel), k=0) == -1
+    assert pending_call(ctypes.byref(sel), dt=2) == -2
+    one = hca._index_ws(1, 1000, 64)
+    assert pending_call(ctypes.byref(sel), wsb=one) == -3            # not the workspace of all 4 queries
+    assert not any(sel.opaque)                                        # untouched on error
+    assert pending_call(ctypes.byref(sel)) == 0                       # recorded on the host
+    assert any(sel.opaque)
+    empty = hca.PendingSelect()
+    assert pending_call(ctypes.byref(empty), nq=0) == 0               # nothing to select: an inactive record
+    c, w = store(), store()
+    out = hca.AttnPartials()
+    hargs = (P[0], 1, 4, 64, ctypes.byref(c), P[1], 128, 100, ctypes.byref(w), P[3], P[4], 128, P[5], P[6], None,
+             0.04, P[7], 1, P[8], P[9], 1 << 30, None)
+    assert hca._hca_attn_partials_select(*hargs, None, ctypes.byref(out)) == -1
+    assert hca._hca_attn_partials_select(*hargs, ctypes.byref(sel), None) == -1
+    assert hca._hca_attn_partials_select(*hargs, ctypes.byref(hca.PendingSelect()), ctypes.byref(out)) == -1
+    assert "lightning_index_select_pending" in hca._last_error().decode()
+    bad_heads = (P[0], 1, 4, 40) + hargs[4:]
+    assert hca._hca_attn_partials_select(*bad_heads, ctypes.byref(sel), ctypes.byref(out)) == -2
