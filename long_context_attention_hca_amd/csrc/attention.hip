@@ -536,6 +536,53 @@ __device__ __forceinline__ void stage_rows(const WaveRows& w, uint8_t* dst, int 
   }
 }
 
+// Dense calls (HCA): a wave's R rows from list position p0 are consecutive cache rows, all
+// valid, when they end before the split and the cache part of the list and lie inside the
+// store (a uniform test; away from the window and the store's end this holds for every chunk).
+// Their DMA sources then follow from the store's bases, the row and the lane's byte offset,
+// with no shuffle of per-row addresses, and their row sources are just the entry scales.
+template <int R>
+__device__ __forceinline__ bool dense_run(const AttnArgs& a, const QueryCtx& ctx, int64_t p0, int64_t hi,
+                                          int64_t* row0) {
+  const int64_t r0 = ctx.cache_rb + p0;
+  *row0 = r0;
+  return p0 + R <= min(hi, ctx.n_c) && r0 >= 0 && r0 + R <= a.cache.n_rows;
+}
+
+// stage_rows<I0, kN, R> for a dense run starting at cache row row0 (all R rows valid).
+template <int I0, int kN, int R>
+__device__ __forceinline__ void stage_dense(const AttnArgs& a, int64_t row0, uint8_t* dst, int lane_in) {
+  // the lane-only offsets come from an opaque copy of the lane index, so that they are
+  // recomputed at each call instead of being kept live (and spilled) across the chunk loop
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  const int64_t rs = a.cache.row_stride, rps = 2 * a.cache.rope_stride;
+  const uint64_t fp8 = reinterpret_cast<uint64_t>(a.cache.data) + (uint64_t)(row0 * rs);
+  const uint64_t rope = reinterpret_cast<uint64_t>(a.cache.rope) + (uint64_t)(row0 * rps) - kNope;
+#pragma unroll
+  for (int i = I0; i < I0 + kN; ++i) {
+    const int b = 1024 * i + 16 * lane;  // LDS byte within the wave's rows
+    const int e = b / kRowF8, o = b - e * kRowF8;
+    const uint64_t src = o < kNope ? fp8 + (uint64_t)(e * rs) + (uint64_t)o : rope + (uint64_t)(e * rps) + (uint64_t)o;
+    if (e < R && o < kNope + 2 * kRope)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+  }
+}
+
+// wave_rows<false, R> for a dense run starting at cache row row0: src is unused (stage_dense
+// computes the sources), the scales of the R entries are requested and left in flight. Every
+// lane loads (lane e + R i holds entry e's scale; only lanes below R are read), so the load is
+// one unconditional instruction.
+template <int R>
+__device__ __forceinline__ WaveRows dense_rows(const AttnArgs& a, int64_t row0, int lane) {
+  WaveRows w;
+  w.src = 0;
+  w.esc = a.cache.scale[row0 + (lane & (R - 1))];
+  w.vmask = (1u << R) - 1u;
+  return w;
+}
+
 // Workgroup barrier that waits for this wave's LDS accesses only: row loads into the other
 // chunk buffer stay in flight across it. The signal fences stop the compiler from moving LDS
 // accesses over the barrier.
@@ -1374,8 +1421,13 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
     int ln = lane;
     asm volatile("" : "+v"(ln));
     uint8_t* ndst = nbuf + 8 * wave * kRowF8;
-    zero_invalid_rows<8>(st.nxt, ndst, ln);
-    stage_rows<0, 5, 8>(st.nxt, ndst, ln);
+    int64_t row0;
+    if (!kSparse && dense_run<8>(a, ctx, base + kWCh + 8 * wave, hi, &row0)) {
+      stage_dense<0, 5, 8>(a, row0, ndst, ln);
+    } else {
+      zero_invalid_rows<8>(st.nxt, ndst, ln);
+      stage_rows<0, 5, 8>(st.nxt, ndst, ln);
+    }
   }
 
   // scores of entries 32 hf + 16 u + 4 g + i (i < 4), head c of the wave's group
@@ -1498,7 +1550,9 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
     // rows of the chunk after next from their prefetched slots; slots one further ahead
     const int64_t b2 = base + 2 * kWCh + 8 * wave;
     st.cur = st.nxt;
-    st.nxt = wave_rows<kSparse, 8>(a, ctx, b2, hi, st.slot2, lane);
+    int64_t row0;
+    if (!kSparse && dense_run<8>(a, ctx, b2, hi, &row0)) st.nxt = dense_rows<8>(a, row0, lane);
+    else st.nxt = wave_rows<kSparse, 8>(a, ctx, b2, hi, st.slot2, lane);
     st.slot2 = prefetch_slot<kSparse, 8>(a, qi, b2 + kWCh, lane);
   }
 }
