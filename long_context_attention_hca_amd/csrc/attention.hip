@@ -461,6 +461,9 @@ struct WaveRows {
   uint32_t vmask;  // valid entries
 };
 
+// Zero: the entry scale that lanes without a row read in the wide kernel's wave_rows.
+__device__ float g_zero_scale;
+
 // The top-k slot value of list position base + (lane & 15) (CSA), loaded one chunk before its
 // rows are computed so that no wait on it sits behind row loads in flight. Positions past the
 // top-k list are clamped to a valid slot; their value is not used.
@@ -499,7 +502,13 @@ __device__ __forceinline__ WaveRows wave_rows(const AttnArgs& a, const QueryCtx&
   const int64_t ps = win ? a.win.rope_stride : a.cache.rope_stride;
   const float* scale = win ? a.win.scale : a.cache.scale;
   w.src = lane < R ? data + (uint64_t)(row * rs) : rope + (uint64_t)(row * ps * 2) - kNope;
-  w.esc = (lane < R && row >= 0) ? scale[row] : 0.f;
+  if constexpr (R == 8) {
+    // one unconditional load (lanes without a row read g_zero_scale): the wide kernel counts
+    // the loads it issues after its DMAs
+    w.esc = *((lane < R && row >= 0) ? scale + row : &g_zero_scale);
+  } else {
+    w.esc = (lane < R && row >= 0) ? scale[row] : 0.f;
+  }
   w.vmask = (uint32_t)__ballot(lane < R && row >= 0);
   return w;
 }
@@ -1408,12 +1417,16 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
                                            uint16_t* ps, uint16_t* pp, WideLds& wl, float sl2, int wave, int lane) {
   const int g = lane >> 4, c = lane & 15;
   const int hg = wave & 3, hf = wave >> 2;
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows and the scales of its entries have landed
+  // this wave's rows of the chunk and the scales of its entries have landed: the memory
+  // instructions issued after its DMAs are the previous chunk's last ones, one scale load and,
+  // for listed rows, one slot load (each a single unconditional instruction), which may stay
+  // in flight
+  __builtin_amdgcn_s_waitcnt(kSparse ? 0x0F72 : 0x0F71);  // vmcnt(2) / vmcnt(1)
   if (lane < 8) {
     wl.esc[8 * wave + lane] = st.cur.esc;
     wl.valid[8 * wave + lane] = (uint8_t)((st.cur.vmask >> lane) & 1u);
   }
-  __syncthreads();  // every wave's rows; the other buffer is free
+  lds_barrier();  // every wave's rows; the other buffer is free
   const bool more = base + kWCh < hi;
   if (more) {
     // lane-only DMA offsets are derived from an opaque copy of the lane index, so that they are
