@@ -286,8 +286,8 @@ def test_query_blocks_with_one_large_element(hca, nq):
     ~30-60, the others N(0, 1), and a quarter of them near 1e-3 (below E4M3's normal range under
     the block's scale). bf16 elements at least 2^-14 of their block's maximum are carried exactly
     by the two parts and smaller ones to within 2^-21 of that maximum, so attention must match
-    the oracle at the usual tolerance. nq = 3 runs the per-head-group kernel, 300 the row-owning
-    one."""
+    the oracle at the usual tolerance. nq = 3 runs the per-head-group kernel, 300 the 64-head
+    prefill kernel."""
     m, W_ = hca
     dev = "cuda"
     n_cache, W, k, mp = 1200, 64, 256, 8
@@ -328,3 +328,46 @@ def test_query_blocks_with_one_large_element(hca, nq):
         nv = (t + 1) // mp
         ro, rl = OA.attend(qdec[i], np.concatenate([cache_dec[:nv], cache_dec[OA.window_positions(t, W)]]), scale)
         check_attention(o2[i], lse2[i], ro, rl, "low", f"hca q{i}")
+
+
+def test_wide_dense_runs_at_store_end_and_documents(hca):
+    """HCA on the 64-head prefill kernel, whose waves take 8 consecutive cache rows as one dense
+    run when they are all valid and stage them row by row otherwise: two sequences share one
+    split store (rows 0..699 and 700..1356, so the second ends at the store's last row), visible
+    counts that end inside a wave's 8 rows, queries that see every row up to the store's end, and
+    document starts that shift the first cache row by amounts that are no multiple of 8."""
+    m, W_ = hca
+    dev = "cuda"
+    n0, n1 = 700, 657
+    mp, W, H, D = 4, 64, 64, 512
+    cache_st, cache_dec = make_store("split", n0 + n1, 71)
+    cache = to_store(m, cache_st, 448, 64)
+    L = 2816  # window rows of raw positions 0 .. L - 1 for each sequence
+    win_st, win_dec = make_store("split", 2 * L, 72)
+    win = to_store(m, win_st, 448, 64)
+    rng = np.random.default_rng(73)
+    nq = 96
+    q_seq = np.repeat([0, 1], nq // 2).astype(np.int32)
+    t0 = rng.integers(4 * 600, 4 * n0, nq // 2)
+    t1 = rng.integers(4 * 500, 4 * n1, nq // 2)
+    t1[:4] = [4 * n1 - 1, 4 * n1 - 2, 4 * n1 - 3, 4 * n1 - 4]  # all 657 rows of the last sequence
+    q_pos = np.concatenate([t0, t1]).astype(np.int64)
+    q_lo = np.zeros(nq, np.int64)
+    q_lo[1::2] = rng.integers(1, 1500, nq // 2)
+    g = synth.generator(74)
+    q = synth.normal(g, (nq, H, D)).bfloat16()
+    qdec = q.double().numpy()
+    i64 = lambda v: torch.tensor(v, dtype=torch.int64, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    ws = W_.Workspace(dev)
+    o, lse = W_.hca_attn(q.to(dev), cache, i64([0, n0]), mp, n0, win, i64([0, L]), i64([0, 0]), W,
+                         torch.tensor(q_seq, device=dev), torch.tensor(q_pos, device=dev), scale, ws,
+                         o_dtype=torch.float32, q_lo=torch.tensor(q_lo, device=dev))
+    torch.cuda.synchronize()
+    o, lse = np_(o), np_(lse)
+    for i in range(nq):
+        b, t, lo = int(q_seq[i]), int(q_pos[i]), int(q_lo[i])
+        entries = cache_dec[:n0] if b == 0 else cache_dec[n0:]
+        raw = win_dec[b * L:(b + 1) * L]
+        ro, rl = OA.hca(qdec[i], t, entries, mp, raw, W, scale, lo)
+        check_attention(o[i], lse[i], ro, rl, "low", f"hca q{i} seq {b} t={t} lo={lo}")
