@@ -251,6 +251,8 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg,
   for (int i = 0; i < kD / 16; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
+  // both stores bf16 rows of 512 dims: rows go to LDS unconverted, by DMA
+  const bool dense_bf16 = a.cache.layout == HCA_LAYOUT_BF16 && a.win.layout == HCA_LAYOUT_BF16;
 
   for (int64_t base = lo + (int64_t)wave * kChunk; base < hi; base += 4 * kChunk) {
     // rows of the chunk: lane e < 32 resolves list position base + e once; the wave then
@@ -264,19 +266,40 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg,
     const uint64_t vmask = __ballot(lane < kChunk && myrow >= 0);
     const uint64_t wmask = __ballot(lane < kChunk && mywin);
     const int row_lo = (int)(uint32_t)myrow, row_hi = (int)((uint64_t)myrow >> 32);
+    if (dense_bf16) {
+      // bf16 rows are 64 lanes x 16 bytes: one LDS DMA per valid row, all 32 requested before
+      // one wait. The waits are explicit: hipcc does not order reads of this dynamically sized
+      // LDS after the DMAs into it. The previous chunk's reads of these rows are done first.
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 #pragma unroll
-    for (int e0 = 0; e0 < kChunk; e0 += 8) {
-      uint4 val[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u;
-        const int64_t row = (int64_t)(((uint64_t)(uint32_t)__shfl(row_hi, e, 64) << 32) |
-                                      (uint64_t)(uint32_t)__shfl(row_lo, e, 64));
-        val[u] = make_uint4(0, 0, 0, 0);
-        if ((vmask >> e) & 1) val[u] = load_seg8(((wmask >> e) & 1) ? a.win : a.cache, row, lane);
+      for (int e = 0; e < kChunk; ++e) {
+        uint8_t* dst = lds + e * kRowB;
+        if ((vmask >> e) & 1) {
+          const int64_t row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_hi, e) << 32) |
+                                        (uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_lo, e));
+          const StoreView& v = ((wmask >> e) & 1) ? a.win : a.cache;
+          const uint16_t* src = static_cast<const uint16_t*>(v.data) + row * v.row_stride + 8 * lane;
+          __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        } else {
+          *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+        }
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows have landed
+    } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(lds + (e0 + u) * kRowB + lane * 16) = val[u];
+      for (int e0 = 0; e0 < kChunk; e0 += 8) {
+        uint4 val[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u;
+          const int64_t row = (int64_t)(((uint64_t)(uint32_t)__shfl(row_hi, e, 64) << 32) |
+                                        (uint64_t)(uint32_t)__shfl(row_lo, e, 64));
+          val[u] = make_uint4(0, 0, 0, 0);
+          if ((vmask >> e) & 1) val[u] = load_seg8(((wmask >> e) & 1) ? a.win : a.cache, row, lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(lds + (e0 + u) * kRowB + lane * 16) = val[u];
+      }
     }
     // validity of the 8 entries this lane scores: 16mt + 4g + i
     bool vld[2][4];
