@@ -220,10 +220,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-__global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg, int total) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  if (id >= total) return;
+// Work item id < total of an attn_mfma grid: (query, split, 16-head group); smem is the
+// block's kMfmaLds bytes of dynamic LDS.
+__device__ __forceinline__ void attn_mfma_block(const AttnArgs& a, int n_hg, int id, uint8_t* smem) {
   const int hg = id % n_hg;
   const int rest = id / n_hg;
   const int s = rest % a.n_split;
@@ -427,6 +426,33 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg,
     if (a.n_split == 1) a.lse[(int64_t)qi * H + hd] = lse;
     else a.part_lse[((int64_t)qi * a.n_split + s) * H + hd] = lse;
   }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int n_hg, int total) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= total) return;
+  attn_mfma_block(a, n_hg, id, smem);
+}
+
+// The indexer's top-k selection and an HCA attention call on bf16 stores in one grid, as
+// select_attn_fp8_kernel for the FP8 stores: blocks b < n_sel (a multiple of 8) select query b
+// of `sel` (b < sel.nq) with the selection's 256-thread variant, the others are the attention
+// call's blocks b - n_sel; the selection's LDS lies in the attention's dynamic LDS.
+constexpr int kSelOutOff = 32768;  // OutLds of the selection after its FinLdsT<256>
+static_assert(sizeof(FinLdsT<256>) <= kSelOutOff && kSelOutOff + sizeof(OutLds) <= kMfmaLds,
+              "selection LDS inside the bf16 attention's LDS");
+__global__ __launch_bounds__(256, 1) void select_attn_mfma_kernel(IndexArgs sel, int n_sel, AttnArgs a, int n_hg,
+                                                                  int total) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int b = blockIdx.x;
+  if (b >= n_sel) {
+    const int id = xcd_remap(b - n_sel, (int)gridDim.x - n_sel);
+    if (id < total) attn_mfma_block(a, n_hg, id, smem);
+    return;
+  }
+  if (b < sel.nq)
+    finalize_block(sel, b, *reinterpret_cast<FinLdsT<256>*>(smem), *reinterpret_cast<OutLds*>(smem + kSelOutOff));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1849,10 +1875,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s, bool combine, cons
   const bool mfma = a.q_dtype == HCA_BF16;
   const bool fp8 = mfma && attn_fp8_supported(a.cache, a.win);
   const bool wide = attn_wide_supported(a.q_dtype, a.cache, a.win, a.H, a.nq);
-  // a selection to run with this call shares the grid of the dense attn_fp8 kernel; beside any
-  // other kernel it is launched first on the same stream
-  const bool fused = sel && sel->nq > 0 && !wide && fp8 && !attn_rows_eligible(a) && !a.idx;
-  if (sel && !fused) {
+  // a selection to run with this call shares the grid of the dense attn_fp8 or attn_mfma kernel;
+  // beside any other kernel it is launched first on the same stream
+  const bool dense_sel = sel && sel->nq > 0 && !wide && !a.idx;
+  const bool fused = dense_sel && fp8 && !attn_rows_eligible(a);
+  const bool fused_bf16 = dense_sel && !fp8 && mfma;
+  if (sel && !fused && !fused_bf16) {
     const hipError_t e = launch_index_topk(*sel, false, true, s);
     if (e != hipSuccess) return e;
   }
@@ -1883,7 +1911,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s, bool combine, cons
     const int n_hg = a.H / 16;
     const int total = a.nq * a.n_split * n_hg;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL(attn_mfma_kernel, dim3(grid), dim3(256), kMfmaLds, s, a, n_hg, total);
+    if (fused_bf16) {
+      const int n_sel = (sel->nq + 7) / 8 * 8;
+      hipLaunchKernelGGL(select_attn_mfma_kernel, dim3(n_sel + grid), dim3(256), kMfmaLds, s, *sel, n_sel, a, n_hg,
+                         total);
+    } else {
+      hipLaunchKernelGGL(attn_mfma_kernel, dim3(grid), dim3(256), kMfmaLds, s, a, n_hg, total);
+    }
   } else {
     static_assert(kValuChunk == 16, "attn_valu_lds_bytes assumes 16-entry chunks");
     hipLaunchKernelGGL(attn_valu_kernel, dim3(a.n_split, a.nq), dim3(256), attn_valu_lds_bytes(a.H, a.D), s, a);
@@ -1943,6 +1977,8 @@ hipError_t noalloc_scratch(void** ptr) {
 
 hipError_t attention_init() {
   hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)select_attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
   if (e != hipSuccess) return e;
   // the float32 kernel's LDS grows with H * D (66,752 bytes at 16 heads of 512)
   return hipFuncSetAttribute((const void*)attn_valu_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,

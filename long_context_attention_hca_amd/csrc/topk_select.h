@@ -166,22 +166,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Finalisation: one block of kFinThreads threads per query.
+// Finalisation: one block of NT threads per query (NT = kFinThreads = 512 for finalize_kernel
+// and HCA attention's FP8 grid, 256 for the bf16-store attention grid).
 
 constexpr int kListCap = kHistBins / 2;         // keys of one bin ranked exactly (the histogram's LDS)
-constexpr int kPer = kCandCap / kFinThreads;    // candidates per thread, held in registers
 
-struct FinLds {
+template <int NT>
+struct FinLdsT {
   uint32_t h[kHistBins];  // histogram; keys of the crossing bin (as u64); flagged blocks; output
   uint64_t sel[kMaxTopK];  // keys of the selected entries
   uint64_t sel_sink[64];   // per-lane targets of writes that select nothing (branch-free code)
   uint64_t list_sink[64];
-  uint32_t part[kFinThreads];
+  uint32_t part[NT];
   uint32_t tmp[32];
   CrossLds cx;
   uint64_t kmin, kmax, T;
   uint32_t smin, smax, nsel, nflag, novf;
 };
+using FinLds = FinLdsT<kFinThreads>;
 
 // The candidates of one query: ns slots of the score blocks (0 = empty) and novf rescanned keys.
 struct CandSet {
@@ -203,7 +205,8 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 }
 
 // f.kmin / f.kmax <- the smallest and largest of the per-thread extremes lo / hi.
-__device__ __forceinline__ void block_min_max(uint64_t lo, uint64_t hi, FinLds& f) {
+template <int NT>
+__device__ __forceinline__ void block_min_max(uint64_t lo, uint64_t hi, FinLdsT<NT>& f) {
   lo = wave_min_u64(lo);
   hi = wave_max_u64(hi);
   if (threadIdx.x == 0) {
@@ -252,8 +255,9 @@ __device__ __forceinline__ void wave_append(bool p, Tv x, Tv* list, uint32_t* n,
 // selected key is placed by a block scan or by its rank). Equal scores throughout, or a
 // crossing bin with more than kListCap keys (heavy ties), are resolved by 11-bit radix passes
 // below the bits all candidates share.
-template <bool kSel>
-__device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint32_t K, FinLds& f) {
+template <bool kSel, int NT>
+__device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kCandCap / NT], uint32_t K, FinLdsT<NT>& f) {
+  constexpr int kPer = kCandCap / NT;
   const int tid = threadIdx.x;
   // Elementwise steps below are written without branches (selects, sink addresses): in this
   // one-pass kernel every taken branch is a likely instruction-cache miss.
@@ -271,7 +275,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
     f.smin = 0xFFFFFFFFu;
     f.smax = 0;
   }
-  for (int i = tid; i < kHistBins; i += kFinThreads) f.h[i] = 0;
+  for (int i = tid; i < kHistBins; i += NT) f.h[i] = 0;
   __syncthreads();
   if ((tid & 63) == 0) {
     atomicMin(&f.smin, lo);
@@ -290,7 +294,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
     __syncthreads();
     int d;
     uint32_t above;
-    crossing2048<kFinThreads>(f.h, f.part, K, f.cx, &d, &above);
+    crossing2048<NT>(f.h, f.part, K, f.cx, &d, &above);
     const uint32_t rem = K - above, cd = f.h[d];
     if (tid == 0) f.nsel = 0;
     __syncthreads();
@@ -300,7 +304,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
 #pragma unroll
       for (int i = 0; i < kPer; ++i) wave_append<uint64_t>(bn[i] == d, v[i], list, &f.nsel, (uint32_t)kListCap);
       __syncthreads();
-      for (uint32_t i = tid; i < cd; i += kFinThreads) {
+      for (uint32_t i = tid; i < cd; i += NT) {
         const uint64_t x = list[i];
         uint32_t g = 0;
         for (uint32_t j = 0; j < cd; ++j) g += list[j] > x;
@@ -318,7 +322,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
         nl += bn[i] == d;
       }
       uint32_t tot;
-      const uint32_t off = block_exclusive_scan<kFinThreads>(na | (nl << 16), f.tmp, &tot);
+      const uint32_t off = block_exclusive_scan<NT>(na | (nl << 16), f.tmp, &tot);
       uint32_t oa = off & 0xFFFFu, ol = off >> 16;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
@@ -330,7 +334,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
       }
       __syncthreads();
       // rank within the bin: a key with g larger keys is selected iff g < rem
-      for (uint32_t i = tid; i < cd; i += kFinThreads) {
+      for (uint32_t i = tid; i < cd; i += NT) {
         const uint64_t x = list[i];
         uint32_t g = 0;
         for (uint32_t j = 0; j < cd; ++j) g += list[j] > x;
@@ -358,7 +362,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
     while (true) {
       const int hb = lb, width = min(11, lb);
       lb -= width;
-      for (int i = tid; i < kHistBins; i += kFinThreads) f.h[i] = 0;
+      for (int i = tid; i < kHistBins; i += NT) f.h[i] = 0;
       __syncthreads();
       const uint64_t want = hb >= 64 ? 0ull : prefix >> hb;
       const uint32_t dmask = (1u << width) - 1u;
@@ -370,7 +374,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
       __syncthreads();
       int d;
       uint32_t above;
-      crossing2048<kFinThreads>(f.h, f.part, rem, f.cx, &d, &above);
+      crossing2048<NT>(f.h, f.part, rem, f.cx, &d, &above);
       rem -= above;
       prefix |= (uint64_t)d << lb;
       const bool done = f.h[d] == rem || lb == 0;
@@ -384,7 +388,7 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
 #pragma unroll
   for (int i = 0; i < kPer; ++i) n += v[i] >= T;  // T > 0, so empty slots never count
   uint32_t tot;
-  uint32_t o = block_exclusive_scan<kFinThreads>(n, f.tmp, &tot);
+  uint32_t o = block_exclusive_scan<NT>(n, f.tmp, &tot);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const bool s = v[i] >= T;
@@ -396,21 +400,22 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[kPer], uint3
 }
 
 // Calls fn(key) for every candidate held in global memory (empty slots skipped).
-template <class F>
+template <int NT, class F>
 __device__ __forceinline__ void for_each_global(const CandSet& cs, F fn) {
-  for (uint32_t i = threadIdx.x; i < cs.ns; i += kFinThreads) {
+  for (uint32_t i = threadIdx.x; i < cs.ns; i += NT) {
     const uint64_t key = cs.slots[i];
     if (key) fn(key);
   }
-  for (uint32_t i = threadIdx.x; i < cs.novf; i += kFinThreads) fn(cs.ovf[i]);
+  for (uint32_t i = threadIdx.x; i < cs.novf; i += NT) fn(cs.ovf[i]);
 }
 
 // Selection over more candidates than the registers hold: the same steps as select_regs, with
 // every pass reading the candidates from global memory and LDS atomics for the appends.
-__device__ uint64_t select_global(const CandSet& cs, uint32_t K, FinLds& f) {
+template <int NT>
+__device__ uint64_t select_global(const CandSet& cs, uint32_t K, FinLdsT<NT>& f) {
   const int tid = threadIdx.x;
   uint64_t lo = ~0ull, hi = 0;
-  for_each_global(cs, [&](uint64_t x) {
+  for_each_global<NT>(cs, [&](uint64_t x) {
     lo = x < lo ? x : lo;
     hi = x > hi ? x : hi;
   });
@@ -425,17 +430,17 @@ __device__ uint64_t select_global(const CandSet& cs, uint32_t K, FinLds& f) {
     while (true) {
       const int hb = lb, width = min(11, lb);
       lb -= width;
-      for (int i = tid; i < kHistBins; i += kFinThreads) f.h[i] = 0;
+      for (int i = tid; i < kHistBins; i += NT) f.h[i] = 0;
       __syncthreads();
       const uint64_t want = hb >= 64 ? 0ull : prefix >> hb;
       const uint32_t dmask = (1u << width) - 1u;
-      for_each_global(cs, [&](uint64_t key) {
+      for_each_global<NT>(cs, [&](uint64_t key) {
         if (hb >= 64 || (key >> hb) == want) atomicAdd(&f.h[(uint32_t)(key >> lb) & dmask], 1u);
       });
       __syncthreads();
       int d;
       uint32_t above;
-      crossing2048<kFinThreads>(f.h, f.part, rem, f.cx, &d, &above);
+      crossing2048<NT>(f.h, f.part, rem, f.cx, &d, &above);
       rem -= above;
       prefix |= (uint64_t)d << lb;
       const bool done = f.h[d] == rem || lb == 0;
@@ -445,29 +450,33 @@ __device__ uint64_t select_global(const CandSet& cs, uint32_t K, FinLds& f) {
     T = prefix;
   }
   __syncthreads();
-  for_each_global(cs, [&](uint64_t key) { wave_append<uint64_t>(key >= T, key, f.sel, &f.nsel, K); });
+  for_each_global<NT>(cs, [&](uint64_t key) { wave_append<uint64_t>(key >= T, key, f.sel, &f.nsel, K); });
   __syncthreads();
   return T;
 }
 
-// Candidates tid + kFinThreads * i of cs into registers (0 past the end). Unconditional loads
+// Candidates tid + NT * i of cs into registers (0 past the end). Unconditional loads
 // from clamped slots stay in flight together.
-__device__ __forceinline__ void load_candidates(const CandSet& cs, uint64_t (&v)[kPer]) {
+template <int NT>
+__device__ __forceinline__ void load_candidates(const CandSet& cs, uint64_t (&v)[kCandCap / NT]) {
+  constexpr int kPer = kCandCap / NT;
   const int tid = threadIdx.x;
   const uint32_t n = cs.ns + cs.novf;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const uint32_t s = min((uint32_t)(tid + kFinThreads * i), n - 1);
+    const uint32_t s = min((uint32_t)(tid + NT * i), n - 1);
     v[i] = *(s < cs.ns ? cs.slots + s : cs.ovf + (s - cs.ns));
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (tid + kFinThreads * i >= (int)n) v[i] = 0;
+    if (tid + NT * i >= (int)n) v[i] = 0;
 }
 
 // Score blocks whose unemitted keys (all below the block's threshold) may reach T; their
 // numbers go to f.h. Returns how many.
-__device__ __forceinline__ uint32_t flag_blocks(const uint64_t (&tq)[kBpt], uint64_t T, FinLds& f) {
+template <int NT>
+__device__ __forceinline__ uint32_t flag_blocks(const uint64_t (&tq)[kMaxBlk / NT], uint64_t T, FinLdsT<NT>& f) {
+  constexpr int kBpt = kMaxBlk / NT;
   const int tid = threadIdx.x;
   if (tid == 0) f.nflag = 0;
   __syncthreads();
@@ -481,19 +490,21 @@ __device__ __forceinline__ uint32_t flag_blocks(const uint64_t (&tq)[kBpt], uint
 // Output of the K keys >= T when they are all among the emitted candidates. The candidate slots
 // are in ascending entry order (score blocks in order, each block's keys ascending, empty slots
 // 0 < T), so compacting the selected slots in slot order gives the ascending answer. Slot
-// tid + kFinThreads * i is position (i, wave, lane) in row-major order: per-wave ballots give
-// the lane offsets, a scan of the kPer x 8 wave counts the rest.
-__device__ __forceinline__ void ordered_output(const uint64_t (&v)[kPer], uint64_t T, int K, int32_t* out, int32_t j0,
-                                               FinLds& f) {
-  static_assert(kPer * (kFinThreads / 64) == 128, "two counts per lane of one wave");
+// tid + NT * i is position (i, wave, lane) in row-major order: per-wave ballots give
+// the lane offsets, a scan of the kPer x (NT / 64) wave counts the rest.
+template <int NT>
+__device__ __forceinline__ void ordered_output(const uint64_t (&v)[kCandCap / NT], uint64_t T, int K, int32_t* out,
+                                               int32_t j0, FinLdsT<NT>& f) {
+  constexpr int kPer = kCandCap / NT, kW = NT / 64;
+  static_assert(kPer * kW == 128, "two counts per lane of one wave");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t* cnt = f.h;  // [kPer][8] wave counts, then their exclusive prefix
+  uint32_t* cnt = f.h;  // [kPer][kW] wave counts, then their exclusive prefix
   uint32_t mb[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const uint64_t bal = __ballot(v[i] >= T);
     mb[i] = lanes_below(bal);
-    if (lane == 0) cnt[i * 8 + wave] = (uint32_t)__popcll(bal);
+    if (lane == 0) cnt[i * kW + wave] = (uint32_t)__popcll(bal);
   }
   __syncthreads();
   if (wave == 0) {
@@ -505,7 +516,7 @@ __device__ __forceinline__ void ordered_output(const uint64_t (&v)[kPer], uint64
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (v[i] >= T) out[min(cnt[i * 8 + wave] + mb[i], (uint32_t)K - 1)] = key_entry(v[i]) + j0;
+    if (v[i] >= T) out[min(cnt[i * kW + wave] + mb[i], (uint32_t)K - 1)] = key_entry(v[i]) + j0;
 }
 
 // Output LDS: per-block counts (then their prefix), per-block cursors, entries bucketed by block.
@@ -515,8 +526,10 @@ struct OutLds {
   int32_t bucket[kMaxTopK];
 };
 
-// The selection of query qi by one block of kFinThreads threads; f and ol are its LDS.
-__device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLds& f, OutLds& ol) {
+// The selection of query qi by one block of NT threads; f and ol are its LDS.
+template <int NT>
+__device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLdsT<NT>& f, OutLds& ol) {
+  constexpr int kPer = kCandCap / NT, kBpt = kMaxBlk / NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.k;
   const int64_t q_blk = (int64_t)qi * a.nblk;
@@ -528,7 +541,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
   {
     const uint32_t region = (uint32_t)a.nblk * kBlockKeys;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) v[i] = slots[min((uint32_t)(tid + kFinThreads * i), region - 1)];
+    for (int i = 0; i < kPer; ++i) v[i] = slots[min((uint32_t)(tid + NT * i), region - 1)];
 #pragma unroll
     for (int i = 0; i < kBpt; ++i) tq[i] = thr[min(kBpt * tid + i, a.nblk - 1)];
   }
@@ -537,7 +550,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
   const int32_t jo = (int32_t)j0;  // entry index of visible key 0
   int32_t* out = a.out + (int64_t)qi * K;
   if (nv <= K) {  // every visible entry is selected, ascending; pad with -1
-    for (int j = tid; j < K; j += kFinThreads) out[j] = j < nv ? j + jo : -1;
+    for (int j = tid; j < K; j += NT) out[j] = j < nv ? j + jo : -1;
     return;
   }
   const int nb = (int)((nv + kBlockKeys - 1) / kBlockKeys);
@@ -560,7 +573,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
   if (cs.ns <= (uint32_t)kCandCap) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      if ((uint32_t)(tid + kFinThreads * i) >= cs.ns) v[i] = 0;
+      if ((uint32_t)(tid + NT * i) >= cs.ns) v[i] = 0;
     T = select_regs<false>(v, (uint32_t)K, f);
     nflag = flag_blocks(tq, T, f);
     if (nflag == 0) {
@@ -572,7 +585,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
 #pragma unroll
     for (int i = 0; i < kPer; ++i) c += v[i] >= T;
     uint32_t tot;
-    uint32_t o = block_exclusive_scan<kFinThreads>(c, f.tmp, &tot);
+    uint32_t o = block_exclusive_scan<NT>(c, f.tmp, &tot);
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (v[i] >= T) ovf[min(o++, (uint32_t)K - 1)] = v[i];
@@ -580,7 +593,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
     T = select_global(cs, (uint32_t)K, f);
     nflag = flag_blocks(tq, T, f);
     if (nflag > 0)
-      for (int i = tid; i < K; i += kFinThreads) ovf[i] = f.sel[i];
+      for (int i = tid; i < K; i += NT) ovf[i] = f.sel[i];
   }
   if (nflag > 0) {
     // round 2 selects among the round-1 winners (every candidate >= T) and the unemitted keys
@@ -598,7 +611,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
 #pragma unroll
     for (int r = 0; r < kR; ++r) kv[r] = sk[min<int64_t>((int64_t)b * kBlockKeys + lane + 64 * r, nv - 1)];
     while (fi < nflag) {
-      const uint32_t fn = fi + kFinThreads / 64;
+      const uint32_t fn = fi + NT / 64;
       const int bn = fn < nflag ? (int)f.h[fn] : b;
       uint32_t kn[kR];
       const uint64_t tbn = thr[bn];
@@ -624,7 +637,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
     __syncthreads();
     if (cs.novf <= (uint32_t)kCandCap) {
       uint64_t v[kPer];
-      load_candidates(cs, v);
+      load_candidates<NT>(cs, v);
       T = select_regs<true>(v, (uint32_t)K, f);
     } else {
       T = select_global(cs, (uint32_t)K, f);
@@ -632,10 +645,10 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
   }
   // ascending order: bucket the K entries by score block, then rank each within its bucket
   const uint64_t* sel = f.sel;
-  for (int b = tid; b < nb; b += kFinThreads) ol.pre[b] = 0;
+  for (int b = tid; b < nb; b += NT) ol.pre[b] = 0;
   __syncthreads();
   const uint32_t last = (uint32_t)nb - 1;
-  for (int i = tid; i < K; i += kFinThreads) atomicAdd(&ol.pre[min((uint32_t)key_entry(sel[i]) >> 10, last)], 1u);
+  for (int i = tid; i < K; i += NT) atomicAdd(&ol.pre[min((uint32_t)key_entry(sel[i]) >> 10, last)], 1u);
   __syncthreads();
   {
     uint32_t c[kBpt], sum = 0;
@@ -646,7 +659,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
       sum += c[i];
     }
     uint32_t tot;
-    uint32_t off = block_exclusive_scan<kFinThreads>(sum, f.tmp, &tot);
+    uint32_t off = block_exclusive_scan<NT>(sum, f.tmp, &tot);
 #pragma unroll
     for (int i = 0; i < kBpt; ++i) {
       const int b = kBpt * tid + i;
@@ -657,13 +670,13 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
     if (tid == 0) ol.pre[nb] = tot;
   }
   __syncthreads();
-  for (int i = tid; i < K; i += kFinThreads) {
+  for (int i = tid; i < K; i += NT) {
     const int32_t j = key_entry(sel[i]);
     ol.bucket[min(atomicAdd(&ol.cur[min((uint32_t)j >> 10, last)], 1u), (uint32_t)K - 1)] = j;
   }
   __syncthreads();
   int32_t* sorted = reinterpret_cast<int32_t*>(f.h);
-  for (int i = tid; i < K; i += kFinThreads) {
+  for (int i = tid; i < K; i += NT) {
     const int32_t j = ol.bucket[i];
     const uint32_t b = min((uint32_t)j >> 10, last);
     const uint32_t s0 = ol.pre[b], s1 = ol.pre[b + 1];
@@ -672,7 +685,7 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
     sorted[min(s0 + r, (uint32_t)K - 1)] = j;
   }
   __syncthreads();
-  for (int i = tid; i < K; i += kFinThreads) out[i] = sorted[i] + jo;
+  for (int i = tid; i < K; i += NT) out[i] = sorted[i] + jo;
 }
 
 }  // namespace

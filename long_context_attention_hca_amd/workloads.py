@@ -296,9 +296,10 @@ class DecodeBf16:
     """Decode step over precompressed bf16 stores (dense [n, D] rows) with bf16 indexer keys: index
     (top-k), CSA attention over the selected entries and the window, HCA attention over all
     visible entries and the window; outputs and workspaces preallocated, so that `step()` only
-    enqueues kernels."""
+    enqueues kernels. As in Decode1M, `step()` runs on one stream with the top-k selection inside
+    HCA attention's launch; fused=False runs the calls one after another."""
 
-    def __init__(self, case, ws=None):
+    def __init__(self, case, ws=None, fused=True):
         p, t = case.params, case.t
         self.case = case
         dev = t["q"].device
@@ -325,11 +326,12 @@ class DecodeBf16:
         self.ws.get("index", lightning_index_topk_workspace(B, self.n_c, k))
         self.ws.get("csa", mqa_attn_workspace(BF16, B, H, D, k + W))
         self.ws.get("hca", mqa_attn_workspace(BF16, B, H, D, self.n_h + W))
+        self.fused = fused
 
-    def index(self):
+    def index(self, phase="both"):
         t = self.case.t
         return index_topk(t["q_idx"], t["w_idx"], t["k_idx"], self.crb, t["q_seq"], t["q_pos"], self.n_c, self.m,
-                          self.k, self.ws, out=self.idx)
+                          self.k, self.ws, out=self.idx, phase=phase)
 
     def csa_attention(self):
         t = self.case.t
@@ -342,13 +344,18 @@ class DecodeBf16:
                         t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_hca, lse=self.lse_hca)
 
     def step(self):
-        self.index()
-        _, _, cp = csa_attn(self.q, self.csa, self.crb, self.idx, self.win, self.wrb, self.wp0, self.W,
-                            self.case.t["q_seq"], self.case.t["q_pos"], self.scale, self.ws, o=self.o_csa,
-                            lse=self.lse_csa, defer=True)
+        t = self.case.t
+        sel = None
+        if self.fused:
+            self.index(phase="scores")
+            sel = self.index(phase="pending")
+        else:
+            self.index()
         _, _, hp = hca_attn(self.q, self.hca, self.hrb, self.mp, self.n_h, self.win, self.wrb, self.wp0, self.W,
-                            self.case.t["q_seq"], self.case.t["q_pos"], self.scale, self.ws, o=self.o_hca,
-                            lse=self.lse_hca, defer=True)
+                            t["q_seq"], t["q_pos"], self.scale, self.ws, o=self.o_hca, lse=self.lse_hca, defer=True,
+                            sel=sel)
+        _, _, cp = csa_attn(self.q, self.csa, self.crb, self.idx, self.win, self.wrb, self.wp0, self.W, t["q_seq"],
+                            t["q_pos"], self.scale, self.ws, o=self.o_csa, lse=self.lse_csa, defer=True)
         mqa_attn_merge(cp, hp)  # both calls' split-K partials in one launch
 
 
