@@ -427,10 +427,10 @@ int mqa_attn_merge(const hca_attn_partials* a, const hca_attn_partials* b, void*
  * unit on `stream` (HCA paragraph: dense attention over the heavily
  * compressed entries; CSA paragraph: the indexer's top-k, which only the
  * later CSA call reads). For a decode step whose HCA call does not depend on
- * the selection: when the HCA call takes the FP8 split-store kernel, the
- * selection's blocks run in the same grid as the attention's (one launch
- * instead of two streams joined by events); otherwise the selection is
- * launched first on the stream. Results are bit-identical to the two calls
+ * the selection: when the HCA call takes the FP8 split-store kernel or the
+ * bf16-store MFMA kernel (bf16 queries), the selection's blocks run in the
+ * same grid as the attention's (one launch instead of two streams joined by
+ * events); otherwise the selection is launched first on the stream. Results are bit-identical to the two calls
  * made separately: out_idx as lightning_index_select writes it, o/lse and the
  * partials as hca_dense_mqa_attn_partials. The selection must not read what
  * the attention writes (its workspace and out_idx are disjoint from the HCA

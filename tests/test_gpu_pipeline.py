@@ -99,6 +99,63 @@ def test_decode_bf16(W, B, L, topk, seqs):
         check_attention(o_h[b], l_h[b], r["o_hca"], r["lse_hca"], "low", f"hca attention seq {b}")
 
 
+def test_decode_bf16_step(W):
+    """The timed bf16 decode step (8 sequences at 128K over bf16 stores generated already
+    compressed, k = 512): the step with the top-k selection in HCA attention's launch equals,
+    bit for bit, the calls one after another, and sampled sequences match the oracle's index,
+    CSA and HCA attention computed from the stored rows."""
+    from oracle import attention as OA
+    from oracle import indexer as OI
+    from oracle.codecs import decode_bf16
+    B, L, k, seqs = 8, 131072, 512, [0, 3, 5, 7]
+    _say(f"decode_bf16 step B={B} L={L}")
+    for s in range(1021, 1031):
+        c = synth.decode_bf16_caches(seed=s, B=B, L=L, topk=k, device="cuda")
+        p = c.params
+        n_c = L // p["m"]
+        qi = np_(c.t["q_idx"].cpu())
+        wi = np_(c.t["w_idx"].cpu()).astype(np.float64)
+        ki = np_(c.t["k_idx"].cpu())
+        if all(tie_margin_ok(decode_bf16(qi[b].view(np.uint16)), wi[b],
+                             decode_bf16(ki[b * n_c:(b + 1) * n_c].view(np.uint16)), n_c, k) for b in seqs):
+            break
+    else:
+        raise AssertionError("no tie-free draw")
+    fused = W.DecodeBf16(c, ws=W.Workspace("cuda"))
+    serial = W.DecodeBf16(c, ws=W.Workspace("cuda"), fused=False)
+    fused.step()
+    serial.step()
+    torch.cuda.synchronize()
+    for name in ("idx", "o_csa", "lse_csa", "o_hca", "lse_hca"):
+        x, y = getattr(fused, name), getattr(serial, name)
+        if x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), f"fused step differs from the serial calls: {name}"
+    mp, Wn = p["m_prime"], p["W"]
+    n_h, t = L // mp, L - 1
+    scale = 1.0 / np.sqrt(p["D"])
+    idx = np_(fused.idx)
+    o_c, o_h = np_(fused.o_csa.float()), np_(fused.o_hca.float())
+    l_c, l_h = np_(fused.lse_csa), np_(fused.lse_hca)
+    csa, hca, win = (np_(c.t[n].cpu()) for n in ("csa_data", "hca_data", "win_data"))
+    q = np_(c.t["q"].cpu())
+    for b in seqs:
+        keys = decode_bf16(ki[b * n_c:(b + 1) * n_c].view(np.uint16))
+        n_vis = OI.n_visible(t, p["m"])
+        ref_idx = OI.topk(OI.scores(decode_bf16(qi[b].view(np.uint16)), wi[b], keys[:n_vis]), n_vis, k)
+        check_idx(idx[b], ref_idx, f"top-k seq {b}")
+        rows = decode_bf16(win[b * Wn:(b + 1) * Wn].view(np.uint16))
+        window = lambda pos, rows=rows: rows[np.asarray(pos) - (L - Wn)]
+        ent = np.zeros((n_c, p["D"]))
+        sel = ref_idx[ref_idx >= 0]
+        ent[sel] = decode_bf16(csa[b * n_c + sel].view(np.uint16))
+        qb = decode_bf16(q[b].view(np.uint16))
+        ro, rl = OA.csa(qb, t, ent, ref_idx, window, Wn, scale)
+        check_attention(o_c[b], l_c[b], ro, rl, "low", f"csa attention seq {b}")
+        ro, rl = OA.hca(qb, t, decode_bf16(hca[b * n_h:(b + 1) * n_h].view(np.uint16)), mp, window, Wn, scale)
+        check_attention(o_h[b], l_h[b], ro, rl, "low", f"hca attention seq {b}")
+
+
 @pytest.mark.parametrize("B,L,seqs", [(3, 1 << 16, [0, 1, 2]), (4, 1 << 20, [0, 1, 2, 3])])
 def test_decode_1m(W, B, L, seqs):
     _say(f"decode_1m B={B} L={L}")

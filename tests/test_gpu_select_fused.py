@@ -4,8 +4,8 @@ hca_dense_mqa_attn_partials_select): at the decode configuration (4 sequences at
 HCA kernel, and the step's top-k, CSA and HCA outputs equal, bit for bit, the calls made one
 after another. Also: a query whose indexer weights are all negative (its top-k is a run of
 exact-zero ties: the selection's second round), an HCA call with no query (the selection runs alone), an HCA
-call on the bf16 store path (the selection is launched before it), and an inactive record (an
-index call with no query)."""
+call on the bf16 store path (the selection's 256-thread variant in the grid of the bf16 MFMA
+kernel), and an inactive record (an index call with no query)."""
 import ctypes
 import sys
 
@@ -97,7 +97,8 @@ def test_selection_beside_no_hca_query_and_inactive_record(mods):
 
 
 def test_selection_beside_bf16_hca_store(mods):
-    """The HCA call takes the bf16-store kernel, so the selection is launched before it."""
+    """The HCA call takes the bf16-store kernel, whose 256-thread blocks run the selection's
+    256-thread variant in the same grid."""
     m, W_ = mods
     _say("selection beside a bf16-store HCA call")
     c = synth.decode_1m(seed=1013, B=4, L=1 << 18, device="cuda")
