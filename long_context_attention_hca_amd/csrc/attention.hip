@@ -614,14 +614,22 @@ __device__ __forceinline__ void stage_dense(const AttnArgs& a, int64_t row0, uin
   // recomputed at each call instead of being kept live (and spilled) across the chunk loop
   int lane = lane_in;
   asm volatile("" : "+v"(lane));
+  // the run's first row is the same in every lane: its part bases are scalar
+  const int64_t r0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(row0 >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)row0));
   const int64_t rs = a.cache.row_stride, rps = 2 * a.cache.rope_stride;
-  const uint64_t fp8 = reinterpret_cast<uint64_t>(a.cache.data) + (uint64_t)(row0 * rs);
-  const uint64_t rope = reinterpret_cast<uint64_t>(a.cache.rope) + (uint64_t)(row0 * rps) - kNope;
+  const uint64_t fp8 = reinterpret_cast<uint64_t>(a.cache.data) + (uint64_t)(r0 * rs);
+  const uint64_t rope = reinterpret_cast<uint64_t>(a.cache.rope) + (uint64_t)(r0 * rps) - kNope;
+  // a lane's byte offset from its part's base (rows e < R of the run) fits in 32 bits: the
+  // strides are bounded on the host, so only the base is 64-bit
+  const uint32_t rs32 = (uint32_t)rs, rps32 = (uint32_t)rps;
 #pragma unroll
   for (int i = I0; i < I0 + kN; ++i) {
     const int b = 1024 * i + 16 * lane;  // LDS byte within the wave's rows
     const int e = b / kRowF8, o = b - e * kRowF8;
-    const uint64_t src = o < kNope ? fp8 + (uint64_t)(e * rs) + (uint64_t)o : rope + (uint64_t)(e * rps) + (uint64_t)o;
+    const bool nope = o < kNope;
+    const uint32_t off = (uint32_t)e * (nope ? rs32 : rps32) + (uint32_t)o;
+    const uint64_t src = (nope ? fp8 : rope) + (uint64_t)off;
     if (e < R && o < kNope + 2 * kRope)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                        (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
@@ -1817,8 +1825,10 @@ __global__ __launch_bounds__(128) void merge2_kernel(MergeArgs a, MergeArgs b) {
 
 // Both stores split with 448 FP8 + 64 bf16 dims, rows addressable with 32-bit indices.
 bool attn_fp8_supported(const StoreView& c, const StoreView& w) {
+  // row strides below 2^26 bytes keep the byte offsets within a wave's rows in 32 bits
   auto ok = [](const StoreView& v) {
-    return v.layout == HCA_LAYOUT_SPLIT && v.d_nope == kNope && v.d_rope == kRope && v.n_rows < (1ll << 31);
+    return v.layout == HCA_LAYOUT_SPLIT && v.d_nope == kNope && v.d_rope == kRope && v.n_rows < (1ll << 31) &&
+           v.row_stride < (1ll << 26) && v.rope_stride < (1ll << 25);
   };
   return ok(c) && ok(w);
 }
