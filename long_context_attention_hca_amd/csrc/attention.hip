@@ -1458,6 +1458,68 @@ struct WideState {
   int32_t slot2;      // slot values of the chunk after next
 };
 
+// Per-lane constants of a wave's 5 row DMAs (8 rows of 592 LDS bytes from LDS byte 1024 i +
+// 16 lane), the same for every wave and chunk, so they are computed once per block:
+//  * dense[i][lane]: bit 31 set for a byte of the FP8 part, bit 30 for a lane inside the 8 rows;
+//    low bits the byte offset from the part's base at the run's first row (e * stride + o);
+//  * listed[i][lane]: bits 16.. the lane holding the row's source address (e, or 8 + e for the
+//    RoPE part), bit 15 for a lane inside the 8 rows, bits 0..9 the row byte o.
+// A lane on a row's 16 padding bytes reads the row's last 16 RoPE bytes again (they land in the
+// padding, which nothing reads), so only the lanes past the 8 rows stay idle.
+struct WideDmaTab {
+  uint32_t dense[5][64];
+  uint32_t listed[5][64];
+};
+
+__device__ __forceinline__ void wide_dma_table(const AttnArgs& a, WideDmaTab& t, int tid) {
+  if (tid < 5 * 64) {
+    const int i = tid >> 6, ln = tid & 63;
+    const int b = 1024 * i + 16 * ln;
+    const int e = b / kRowF8, o = min(b - e * kRowF8, kNope + 2 * kRope - 16);
+    const bool nope = o < kNope, in = e < 8;
+    const uint32_t stride = nope ? (uint32_t)a.cache.row_stride : (uint32_t)(2 * a.cache.rope_stride);
+    const uint32_t off = in ? (uint32_t)e * stride + (uint32_t)o : 0u;
+    t.dense[i][ln] = off | (nope ? 0x80000000u : 0u) | (in ? 0x40000000u : 0u);
+    t.listed[i][ln] = ((uint32_t)(nope ? e : 8 + e) << 16) | (in ? 0x8000u : 0u) | (uint32_t)o;
+  }
+}
+
+// stage_dense<0, 5, 8> from the table: the part bases are scalar, each lane adds its offset.
+__device__ __forceinline__ void wide_stage_dense(const AttnArgs& a, int64_t row0, const WideDmaTab& t, uint8_t* dst,
+                                                 int lane) {
+  const int64_t r0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(row0 >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)row0));
+  const uint64_t fp8 = reinterpret_cast<uint64_t>(a.cache.data) + (uint64_t)(r0 * a.cache.row_stride);
+  const uint64_t rope = reinterpret_cast<uint64_t>(a.cache.rope) + (uint64_t)(r0 * 2 * a.cache.rope_stride) - kNope;
+  uint32_t v[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) v[i] = t.dense[i][lane];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t src = ((int32_t)v[i] < 0 ? fp8 : rope) + (uint64_t)(v[i] & 0x3FFFFFFFu);
+    if (i < 4 || (v[i] & 0x40000000u))
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+  }
+}
+
+// stage_rows<0, 5, 8> from the table (rows listed by address in w.src; invalid rows skipped).
+__device__ __forceinline__ void wide_stage_rows(const WaveRows& w, const WideDmaTab& t, uint8_t* dst, int lane) {
+  uint32_t v[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) v[i] = t.listed[i][lane];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int sl = (int)(v[i] >> 16);
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)w.src, sl, 64);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(w.src >> 32), sl, 64);
+    const uint64_t src = (((uint64_t)hi << 32) | lo) + (uint64_t)(v[i] & 0x3FFu);
+    if ((v[i] & 0x8000u) && ((w.vmask >> (sl & 7)) & 1))
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+  }
+}
+
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32, round to nearest even
@@ -1471,7 +1533,8 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 template <bool kSparse>
 __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ctx, int qi, int64_t base, int64_t hi,
                                            const uint8_t* buf, uint8_t* nbuf, const F8Query& q, WideState& st,
-                                           uint16_t* ps, uint16_t* pp, WideLds& wl, float sl2, int wave, int lane) {
+                                           uint16_t* ps, uint16_t* pp, WideLds& wl, const WideDmaTab& dt, float sl2,
+                                           int wave, int lane) {
   const int g = lane >> 4, c = lane & 15;
   const int hg = wave & 3, hf = wave >> 2;
   // this wave's rows of the chunk and the scales of its entries have landed: the memory
@@ -1493,10 +1556,10 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
     uint8_t* ndst = nbuf + 8 * wave * kRowF8;
     int64_t row0;
     if (!kSparse && dense_run<8>(a, ctx, base + kWCh + 8 * wave, hi, &row0)) {
-      stage_dense<0, 5, 8>(a, row0, ndst, ln);
+      wide_stage_dense(a, row0, dt, ndst, ln);
     } else {
       zero_invalid_rows<8>(st.nxt, ndst, ln);
-      stage_rows<0, 5, 8>(st.nxt, ndst, ln);
+      wide_stage_rows(st.nxt, dt, ndst, ln);
     }
   }
 
@@ -1634,8 +1697,10 @@ __global__ __launch_bounds__(512, 1) void attn_wide_kernel(AttnArgs a, int n_hg,
   __shared__ __attribute__((aligned(16))) uint16_t ps[64 * kWPRow];  // [64 heads][entries] P x entry scale
   __shared__ __attribute__((aligned(16))) uint16_t pp[64 * kWPRow];  // [64 heads][entries] P
   __shared__ __attribute__((aligned(16))) WideLds wl;
+  __shared__ WideDmaTab dt;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= total) return;
+  wide_dma_table(a, dt, threadIdx.x);
   const int s = id % a.n_split;
   const int rest = id / a.n_split;
   const int hg64 = rest % n_hg;
@@ -1658,10 +1723,11 @@ __global__ __launch_bounds__(512, 1) void attn_wide_kernel(AttnArgs a, int n_hg,
     st.slot2 = prefetch_slot<kSparse, 8>(a, qi, b0 + 2 * kWCh, lane);
     st.cur = wave_rows<kSparse, 8>(a, ctx, b0, hi, s0, lane);
     st.nxt = wave_rows<kSparse, 8>(a, ctx, b0 + kWCh, hi, s1, lane);
+    lds_barrier();  // the DMA table
     if (lo < hi) {
       uint8_t* dst = buf0 + 8 * wave * kRowF8;
       zero_invalid_rows<8>(st.cur, dst, lane);
-      stage_rows<0, 5, 8>(st.cur, dst, lane);
+      wide_stage_rows(st.cur, dt, dst, lane);
     }
   }
   // the first chunk's rows are in flight while the query is split into its FP8 parts
@@ -1671,11 +1737,14 @@ __global__ __launch_bounds__(512, 1) void attn_wide_kernel(AttnArgs a, int n_hg,
   st.m_run = -INFINITY;
   st.l_part = 0.f;
   const float sl2 = a.scale * kLog2e;
+  // the query's loads and the first chunk's rows have landed (the first chunk waits for its rows
+  // anyway); without this wait hipcc may wait for every load before the chunks' RoPE scores
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // unrolled by two so that each call names its chunk buffers statically
   for (int64_t base = lo; base < hi; base += 2 * kWCh) {
-    wide_chunk<kSparse>(a, ctx, qi, base, hi, buf0, buf1, q, st, ps, pp, wl, sl2, wave, lane);
+    wide_chunk<kSparse>(a, ctx, qi, base, hi, buf0, buf1, q, st, ps, pp, wl, dt, sl2, wave, lane);
     if (base + kWCh >= hi) break;
-    wide_chunk<kSparse>(a, ctx, qi, base + kWCh, hi, buf1, buf0, q, st, ps, pp, wl, sl2, wave, lane);
+    wide_chunk<kSparse>(a, ctx, qi, base + kWCh, hi, buf1, buf0, q, st, ps, pp, wl, dt, sl2, wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
