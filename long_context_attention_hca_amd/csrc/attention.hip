@@ -1446,7 +1446,8 @@ constexpr int kWPRow = kWCh + 8;          // bf16 per P row (padded)
 
 struct WideLds {
   float esc[kWCh];      // entry scales of the chunk being computed
-  uint8_t valid[kWCh];  // 1 for a valid entry
+  float esc2[kWCh];     // the scale times scale * log2(e) for a valid entry, 0 otherwise
+  float bias[kWCh];     // 0 for a valid entry, -inf otherwise
   float wmax[8][16], wsum[8][16];
   float corr[16][4];    // [c][hg]: the chunk's rescale factor of head 16 hg + c
 };
@@ -1543,8 +1544,10 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
   // in flight
   __builtin_amdgcn_s_waitcnt(kSparse ? 0x0F72 : 0x0F71);  // vmcnt(2) / vmcnt(1)
   if (lane < 8) {
+    const bool ok = (st.cur.vmask >> lane) & 1u;
     wl.esc[8 * wave + lane] = st.cur.esc;
-    wl.valid[8 * wave + lane] = (uint8_t)((st.cur.vmask >> lane) & 1u);
+    wl.esc2[8 * wave + lane] = ok ? st.cur.esc * sl2 : 0.f;
+    wl.bias[8 * wave + lane] = ok ? 0.f : -INFINITY;
   }
   lds_barrier();  // every wave's rows; the other buffer is free
   const bool more = base + kWCh < hi;
@@ -1588,13 +1591,14 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
       const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ropep + 64 * ks));
       sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q.qr[ks], sr, 0, 0, 0);
     }
-    const float4 e4 = *reinterpret_cast<const float4*>(wl.esc + e0 + 4 * g);
-    const uint32_t v4 = *reinterpret_cast<const uint32_t*>(wl.valid + e0 + 4 * g);
-    const float esc[4] = {e4.x, e4.y, e4.z, e4.w};
+    // scale * log2(e) * (entry scale * FP8 part + RoPE part); an invalid entry (zero row, zero
+    // scale) scores -inf through its bias
+    const float4 e4 = *reinterpret_cast<const float4*>(wl.esc2 + e0 + 4 * g);
+    const float4 b4 = *reinterpret_cast<const float4*>(wl.bias + e0 + 4 * g);
+    const float esc[4] = {e4.x, e4.y, e4.z, e4.w}, bias[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float v = fmaf(esc[i], s0[i] + s1[i], sr[i]);
-      sv[u][i] = ((v4 >> (8 * i)) & 1u) ? v * sl2 : -INFINITY;
+      sv[u][i] = fmaf(esc[i], s0[i] + s1[i], fmaf(sr[i], sl2, bias[i]));
       cmax = fmaxf(cmax, sv[u][i]);
     }
   }
