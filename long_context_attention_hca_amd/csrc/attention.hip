@@ -732,35 +732,44 @@ __device__ __forceinline__ void f8_chunk(const AttnArgs& a, const QueryCtx& ctx,
   cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
   cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
   if (g == 0) wmax[16 * wave + c] = cmax;
-  lds_barrier();
-#pragma unroll
-  for (int w = 0; w < 8; ++w) cmax = fmaxf(cmax, wmax[16 * w + c]);
   // lazy rescaling: the reference max moves only when a score exceeds it by more than 2^8
-  // (log2 units), so p <= 256 and O is rescaled rarely instead of every chunk
-  const bool grow = cmax > st.m_run + 8.f;
-  const float m_ref = grow ? cmax : st.m_run;
-  const bool none = m_ref == -INFINITY;
-  const float corr = grow ? exp2f(st.m_run - cmax) : 1.f;
-  float p[4], psum = 0.f;
+  // (log2 units), so p <= 256 and O is rescaled rarely instead of every chunk. P is written
+  // against the current reference before the block's maxima are known (one barrier publishes
+  // both); when some head's block maximum does move the reference, every wave sees it in the
+  // same maxima, rewrites its P with the new reference and waits once more.
+  const int pe = c * kPRow + 16 * wave + 4 * g;
+  auto put_p = [&](float m_ref, float* p) {
+    const bool none = m_ref == -INFINITY;
+    float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = none ? 0.f : exp2f(sv[i] - m_ref);
-    psum += p[i];
-  }
-  st.l_part = st.l_part * corr + psum;
-  st.m_run = m_ref;
-  if (__ballot(grow)) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.O[dt] *= corr;
-  }
-  {
-    const int pe = c * kPRow + 16 * wave + 4 * g;
+    for (int i = 0; i < 4; ++i) {
+      p[i] = none ? 0.f : exp2f(sv[i] - m_ref);
+      psum += p[i];
+    }
     *reinterpret_cast<uint2*>(pbs + pe) =
         make_uint2(pack_bf16x2(p[0] * escl[0], p[1] * escl[1]), pack_bf16x2(p[2] * escl[2], p[3] * escl[3]));
     *reinterpret_cast<uint2*>(pb + pe) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-  }
+    return psum;
+  };
+  float p[4];
+  float psum = put_p(st.m_run, p);
   if (more) stage_rows<6, 2>(nxt, ndst, lane);
   lds_barrier();
+#pragma unroll
+  for (int w = 0; w < 8; ++w) cmax = fmaxf(cmax, wmax[16 * w + c]);
+  const bool grow = cmax > st.m_run + 8.f;
+  if (__ballot(grow)) {  // the same in every wave of the block
+    const float m_ref = grow ? cmax : st.m_run;
+    const float corr = grow ? exp2f(st.m_run - cmax) : 1.f;
+    psum = put_p(m_ref, p);
+    st.l_part = st.l_part * corr + psum;
+    st.m_run = m_ref;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.O[dt] *= corr;
+    lds_barrier();
+  } else {
+    st.l_part = st.l_part * 1.f + psum;
+  }
   // O^T (this wave's 64 dims x 16 heads) += V^T P^T over the chunk's 128 entries
   if (wave < 7) {
     const int r = c >> 1, hsel = c & 1;
@@ -1450,6 +1459,7 @@ struct WideLds {
   float bias[kWCh];     // 0 for a valid entry, -inf otherwise
   float wmax[8][16], wsum[8][16];
   float corr[16][4];    // [c][hg]: the chunk's rescale factor of head 16 hg + c
+  uint64_t grow[8];     // [wave]: lanes (heads) whose chunk maximum moves the reference
 };
 
 struct WideState {
@@ -1605,37 +1615,57 @@ __device__ __forceinline__ void wide_chunk(const AttnArgs& a, const QueryCtx& ct
   cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
   cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
   if (g == 0) wl.wmax[wave][c] = cmax;
-  lds_barrier();
-  cmax = fmaxf(wl.wmax[hg][c], wl.wmax[hg + 4][c]);
-  // lazy rescaling (both waves of the group see the same maxima, so they agree on the reference)
-  const bool grow = cmax > st.m_run + 8.f;
-  const float m_ref = grow ? cmax : st.m_run;
-  const bool none = m_ref == -INFINITY;
-  const float corr = grow ? __builtin_amdgcn_exp2f(st.m_run - cmax) : 1.f;
-  float psum = 0.f;
+  // lazy rescaling (both waves of the group see the same maxima, so they agree on the reference).
+  // P is written against the current reference before the group's maxima are known, and each
+  // wave publishes which of its heads would move the reference (a group's maximum exceeds it
+  // by more than 2^8 exactly when one of its two halves does); one barrier publishes both. If
+  // any head of the block moves its reference, every wave sees it in the same flags and the
+  // block rewrites P, publishes the rescale factors and waits once more.
   const int prow = (16 * hg + c) * kWPRow;
+  auto put_p = [&](float m_ref) {
+    const bool none = m_ref == -INFINITY;
+    float psum = 0.f;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e0 = 32 * hf + 16 * u + 4 * g;
-    const float4 e4 = *reinterpret_cast<const float4*>(wl.esc + e0);
-    float p[4];
+    for (int u = 0; u < 2; ++u) {
+      const int e0 = 32 * hf + 16 * u + 4 * g;
+      const float4 e4 = *reinterpret_cast<const float4*>(wl.esc + e0);
+      float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = none ? 0.f : __builtin_amdgcn_exp2f(sv[u][i] - m_ref);
-      psum += p[i];
+      for (int i = 0; i < 4; ++i) {
+        p[i] = none ? 0.f : __builtin_amdgcn_exp2f(sv[u][i] - m_ref);
+        psum += p[i];
+      }
+      *reinterpret_cast<uint2*>(ps + prow + e0) = make_uint2(pk_bf16(p[0] * e4.x, p[1] * e4.y), pk_bf16(p[2] * e4.z, p[3] * e4.w));
+      *reinterpret_cast<uint2*>(pp + prow + e0) = make_uint2(pk_bf16(p[0], p[1]), pk_bf16(p[2], p[3]));
     }
-    *reinterpret_cast<uint2*>(ps + prow + e0) = make_uint2(pk_bf16(p[0] * e4.x, p[1] * e4.y), pk_bf16(p[2] * e4.z, p[3] * e4.w));
-    *reinterpret_cast<uint2*>(pp + prow + e0) = make_uint2(pk_bf16(p[0], p[1]), pk_bf16(p[2], p[3]));
-  }
-  st.l_part = st.l_part * corr + psum;
-  st.m_run = m_ref;
-  if (hf == 0 && g == 0) wl.corr[c][hg] = corr;
+    return psum;
+  };
+  float psum = put_p(st.m_run);
+  const uint64_t mine = __ballot(cmax > st.m_run + 8.f);
+  if (lane == 0) wl.grow[wave] = mine;
   lds_barrier();
+  uint64_t any = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) any |= wl.grow[w];
+  const bool rescale = any != 0;  // the same in every wave of the block
+  if (rescale) {
+    cmax = fmaxf(wl.wmax[hg][c], wl.wmax[hg + 4][c]);
+    const bool grow = cmax > st.m_run + 8.f;
+    const float m_ref = grow ? cmax : st.m_run;
+    const float corr = grow ? __builtin_amdgcn_exp2f(st.m_run - cmax) : 1.f;
+    psum = put_p(m_ref);
+    st.l_part = st.l_part * corr + psum;
+    st.m_run = m_ref;
+    if (hf == 0 && g == 0) wl.corr[c][hg] = corr;
+    lds_barrier();
+  } else {
+    st.l_part = st.l_part * 1.f + psum;
+  }
   // O^T (8 x 2 tiles of 16 dims x 16 heads: this wave's 128 dims of 32 heads) += V^T P^T over
   // the chunk's 64 entries; first the rescale of the heads whose reference maximum grew
   const int dq = wave & 3, hh = wave >> 2;
-  const float2 cr = *reinterpret_cast<const float2*>(&wl.corr[c][2 * hh]);
-  if (__ballot(cr.x != 1.f || cr.y != 1.f)) {
+  if (rescale) {
+    const float2 cr = *reinterpret_cast<const float2*>(&wl.corr[c][2 * hh]);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       st.O[dt] *= cr.x;
