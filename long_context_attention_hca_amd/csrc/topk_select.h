@@ -523,7 +523,7 @@ __device__ __forceinline__ void ordered_output(const uint64_t (&v)[kCandCap / NT
 struct OutLds {
   uint32_t pre[kMaxBlk + 1];
   uint32_t cur[kMaxBlk];
-  int32_t bucket[kMaxTopK];
+  alignas(16) int32_t bucket[kMaxTopK];
 };
 
 // The selection of query qi by one block of NT threads; f and ol are its LDS.
@@ -601,34 +601,60 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
     // together they hold every key >= T, hence the whole top-k
     if (tid == 0) f.novf = (uint32_t)K;
     __syncthreads();
-    // one wave per flagged block; the next block's keys are loaded before this block's are
-    // appended, so each block's load time overlaps the previous block's appends
-    constexpr int kR = kBlockKeys / 64;
-    uint32_t fi = wave;
-    int b = fi < nflag ? (int)f.h[fi] : 0;
-    uint32_t kv[kR];
-    uint64_t tb = thr[b];
+    // Each wave takes flagged blocks wave, wave + W, ... (W waves), two per step, with the next
+    // two blocks' keys already in flight; a block's keys >= T that it did not emit (those below
+    // its threshold) are appended with one LDS atomic per wave and block.
+    constexpr int kR = kBlockKeys / 64, kW = NT / 64;
+    struct Blk {
+      uint32_t kv[kR];
+      uint64_t tb;
+      int b;
+    };
+    auto load_blk = [&](uint32_t fi, Blk& x) {
+      x.b = (int)f.h[min(fi, nflag - 1)];
+      x.tb = thr[x.b];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) kv[r] = sk[min<int64_t>((int64_t)b * kBlockKeys + lane + 64 * r, nv - 1)];
-    while (fi < nflag) {
-      const uint32_t fn = fi + NT / 64;
-      const int bn = fn < nflag ? (int)f.h[fn] : b;
-      uint32_t kn[kR];
-      const uint64_t tbn = thr[bn];
-#pragma unroll
-      for (int r = 0; r < kR; ++r) kn[r] = sk[min<int64_t>((int64_t)bn * kBlockKeys + lane + 64 * r, nv - 1)];
-      const int64_t jb = (int64_t)b * kBlockKeys;
+      for (int r = 0; r < kR; ++r) x.kv[r] = sk[min<int64_t>((int64_t)x.b * kBlockKeys + lane + 64 * r, nv - 1)];
+    };
+    auto append_blk = [&](const Blk& x) {
+      const int64_t jb = (int64_t)x.b * kBlockKeys;
+      uint64_t k64[kR];
+      uint32_t pm = 0, c = 0;
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         const int64_t j = jb + lane + 64 * r;
-        const uint64_t k64 = ((uint64_t)kv[r] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-        wave_append<uint64_t>(j < nv && k64 < tb && k64 >= T, k64, ovf, &f.novf, (uint32_t)ovf_cap);
+        k64[r] = ((uint64_t)x.kv[r] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+        const bool p = j < nv && k64[r] < x.tb && k64[r] >= T;
+        pm |= (uint32_t)p << r;
+        c += p;
       }
-      fi = fn;
-      b = bn;
-      tb = tbn;
+      const uint32_t incl = wave_incl_scan_add(c);
+      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      if (total == 0) return;
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&f.novf, total);
+      uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + incl - c;
 #pragma unroll
-      for (int r = 0; r < kR; ++r) kv[r] = kn[r];
+      for (int r = 0; r < kR; ++r) {
+        if ((pm >> r) & 1u) {
+          if (o < (uint32_t)ovf_cap) ovf[o] = k64[r];
+          ++o;
+        }
+      }
+    };
+    uint32_t fi = wave;
+    Blk c0, c1;
+    load_blk(fi, c0);
+    load_blk(fi + kW, c1);
+    while (fi < nflag) {
+      Blk n0, n1;
+      load_blk(fi + 2 * kW, n0);
+      load_blk(fi + 3 * kW, n1);
+      append_blk(c0);
+      if (fi + kW < nflag) append_blk(c1);
+      fi += 2 * kW;
+      c0 = n0;
+      c1 = n1;
     }
     __threadfence_block();
     __syncthreads();
@@ -680,8 +706,13 @@ __device__ __forceinline__ void finalize_block(const IndexArgs& a, int qi, FinLd
     const int32_t j = ol.bucket[i];
     const uint32_t b = min((uint32_t)j >> 10, last);
     const uint32_t s0 = ol.pre[b], s1 = ol.pre[b + 1];
+    // rank among the bucket's entries, read four at a time from the aligned words covering it
     uint32_t r = 0;
-    for (uint32_t s = s0; s < s1; ++s) r += ol.bucket[s] < j;
+    for (uint32_t s = s0 & ~3u; s < s1; s += 4) {
+      const int4 w = *reinterpret_cast<const int4*>(ol.bucket + s);
+      r += (s >= s0 && w.x < j) + (s + 1 >= s0 && s + 1 < s1 && w.y < j) + (s + 2 >= s0 && s + 2 < s1 && w.z < j) +
+           (s + 3 >= s0 && s + 3 < s1 && w.w < j);
+    }
     sorted[min(s0 + r, (uint32_t)K - 1)] = j;
   }
   __syncthreads();
